@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A4 ConvRot linear on one MI355X.
+
+One step = one pass of the layer over a resident batch: the fused activation
+rotate + int4 quantise kernel, then the s4 x s4 int8-MFMA GEMM with its bf16
+rank-one epilogue, back to back on one stream. The weight is prepared once,
+before timing (offline weight prep). Workload: 4608 tokens through a 3072 x
+3072 projection (M=4608, K=N=3072, Hadamard block 128), bf16 activations drawn
+N(0,1) with 1 % outlier channels x20, weights N(0, 0.02).
+
+Prints one JSON line. ``value`` is the layer's int8-op throughput in TOP/s
+(2 M N K per step / step time), ``roofline`` reports the GEMM kernel against
+the int8 dense MFMA peak using HIP-event kernel times taken inside the timed
+region, and ``cpu_baseline`` times the CPU oracle on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "W4A4 linear TOPS & ms/layer (quantize+GEMM), M=4608 K=N=3072; % int8 MFMA peak"
+INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_square_3072_traffic.json")
+
+
+def _kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "int4_w4a4_quantized_amd", "csrc", "gemm.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_for_current_kernel():
+    """Measured HBM bytes per GEMM launch, if taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != _kernel_source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(m: int, k: int, n: int, rows: int, reps: int = 3) -> dict:
+    """The CPU oracle, as it stands, on the first `rows` rows of the workload
+    (median of `reps` runs)."""
+    import oracle
+
+    rows = min(rows, m)
+    lay = workloads.make_layer(m, k, n, seed=0)
+    wp, ws = oracle.quantize_weight_convrot(lay.weights[0])  # offline, untimed
+    x = np.ascontiguousarray(lay.x_bf16[:rows])
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        xq, sx = oracle.rotate_quantize_act(x)
+        acc = oracle.gemm_acc(xq, wp, k)
+        oracle.epilogue_bf16(acc, sx, ws)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {
+        "value": round(2.0 * rows * n * k / dt / 1e12, 6),
+        "unit": "TOPS",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} of {m} rows, whole layer (rotate+quantise, int32 GEMM, epilogue), "
+                  f"median of {reps} runs: {dt:.3f} s per run",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's CPU sample (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import int4_w4a4_quantized_amd as ck
+
+    cfg = workloads.WORKLOADS["square_3072"]
+    m, k, n = cfg["m"], cfg["k"], cfg["n"]
+    lay = workloads.make_layer(m, k, n, seed=0)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = torch.from_numpy(lay.x_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(lay.weights[0]).to(dev)
+    wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+    xq = torch.empty((m, k // 2), dtype=torch.int8, device=dev)
+    sx = torch.empty((m,), dtype=torch.float32, device=dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+        ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+        e1.record(stream)
+        ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    gemm_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    ms_per_step = wall * 1e3 / args.steps
+    ops = 2.0 * m * n * k
+    tops = ops / (ms_per_step * 1e-3) / 1e12
+    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
+    quant_bytes = m * k * 2 + m * k // 2 + m * 4
+    gemm_bytes = m * k // 2 + n * k // 2 + m * 4 + n * 4 + m * n * 2
+    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": "square_3072 (W4A4 ConvRot linear M=4608 K=3072 N=3072, Hadamard block 128)",
+                   "m": m, "k": k, "n": n, "rot_block": 128, "parallelism": "single GPU"},
+        "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_kernel<s4, 128x128> (W4A4 GEMM + epilogue)",
+            "achieved": round(gemm_tops, 2),
+            "peak": INT8_PEAK_TOPS,
+            "unit": "TOP/s",
+            "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
+            "traffic": _traffic_for_current_kernel(),
+            "algorithmic_bytes": gemm_bytes,
+            "avg_kernel_ms": round(gemm_ms, 5),
+        },
+        "kernels": {
+            "rotate_quant_ms": round(quant_ms, 5),
+            "rotate_quant_GBps": round(quant_gbs, 1),
+            "rotate_quant_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+            "gemm_ms": round(gemm_ms, 5),
+            "gemm_TOPS": round(gemm_tops, 2),
+        },
+        "context": {"L4_ms_per_layer_same_shape": 0.54, "note": "another machine's number; context only"},
+    }
+    if args.cpu_rows > 0:
+        out["cpu_baseline"] = cpu_baseline(m, k, n, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

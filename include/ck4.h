@@ -1,0 +1,192 @@
+/*
+ * ck4 -- W4A4 ConvRot linear layer for AMD MI355X (gfx950), C ABI.
+ *
+ * The layer (comfy-kitchen "[PR #63] int4_tensorwise: W4A4 layout (+ConvRot)
+ * with fused CUDA kernels", Description):
+ *   1. rotate activations along K with a block Hadamard transform (ConvRot),
+ *   2. quantise each activation row to symmetric int4 (scale = absmax / 7,
+ *      codes in [-7, 7]) and pack two codes per byte, low nibble first,
+ *   3. multiply against int4 weights rotated and quantised the same way with
+ *      an s4 x s4 GEMM accumulating in int32 (|acc| <= 49 K),
+ *   4. apply the per-row activation scale and per-row weight scale once, in a
+ *      rank-one epilogue, and write bf16.
+ * The grouped W4A8 variant ("[PR #97] HIP port of #90: grouped W4A8 over the
+ * INT8 GEMM", What this adds / Chunk sizing) decodes int4 weights with
+ * per-group scales into int8 codes with one scale per row, and runs the
+ * rowwise int8 GEMM against int8 activations.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    never allocates, frees or retains them.
+ *  - Matrices are row-major; ld* arguments are row strides in ELEMENTS of the
+ *    pointed-to type (bytes for int8 containers).
+ *  - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it; none synchronises the host. Device faults surface
+ *    at the caller's next synchronisation.
+ *  - Errors are returned, never thrown: CK4_ERR_INVALID for a null pointer,
+ *    a non-positive size, a row stride smaller than the row, or a pointer or
+ *    stride that breaks the stated alignment; CK4_ERR_UNSUPPORTED for a shape
+ *    or option outside what the kernels implement (listed per call);
+ *    CK4_ERR_DEVICE when no gfx950 device is current or a launch fails.
+ *    Nothing is launched when validation fails. ck4_last_error() returns a
+ *    thread-local description of the last failure.
+ *  - There is no fallback path: an unsupported call fails.
+ */
+#ifndef CK4_H
+#define CK4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CK4_OK = 0,
+    CK4_ERR_INVALID = 1,
+    CK4_ERR_UNSUPPORTED = 2,
+    CK4_ERR_DEVICE = 3
+} ck4_status;
+
+/* Library version string, e.g. "ck4 0.1.0 gfx950". */
+const char *ck4_version(void);
+/* Static description of a status code. */
+const char *ck4_status_string(ck4_status s);
+/* Thread-local description of the most recent failure on this thread ("" if
+ * none). The pointer stays valid until the next ck4 call on this thread. */
+const char *ck4_last_error(void);
+
+/*
+ * Offline weight preparation ([PR #63] Description: quantize_int4_convrot_weight;
+ * [PR #97] What this adds: int4 codes with per-group scales).
+ *
+ *   w        fp32 [n, ldw], the unrotated weight (out_features x in_features).
+ *   rot_block  Hadamard block along K: a power of two in [16, 1024], k % rot_block == 0.
+ *   group    0: one scale per output row (W4A4 layout), w_scales is fp32 [n].
+ *            g > 0: one scale per contiguous group of g elements along K
+ *            (grouped W4A8 layout), w_scales is fp32 [n, k/g]; g must be a
+ *            power of two in [16, 1024] dividing k.
+ *   w_packed int8 [n, k/2] (row stride k/2): codes in [-7, 7], element 2j of a
+ *            row in the low nibble of byte j, element 2j+1 in the high nibble.
+ * Each row is rotated in fp32 (butterfly strides ascending, then one multiply
+ * by fp32(1/sqrt(rot_block))), scaled by absmax/7 (fp32 divide) and rounded
+ * half to even after an fp32 divide; an all-zero row or group has scale 0
+ * and codes 0.
+ * Alignment: w and ldw*4 bytes 16-byte aligned; w_packed 8-byte aligned.
+ * Unsupported: k > 16384.
+ */
+ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                       int group, int8_t *w_packed, float *w_scales, void *stream);
+
+/*
+ * Dynamic activation rotation + quantisation, one fused pass per row
+ * ([PR #63] Description: fused activation kernel, FHT rotation + rowwise int4
+ * quantize + pack; [PR #97] What this adds: the int8 quantiser with
+ * convrot=True for the W4A8 path).
+ *
+ *   x        bf16 [m, ldx].
+ *   bits     4: x_q is packed int8 [m, k/2] (row stride k/2), codes in [-7, 7],
+ *               low nibble first, scale = absmax / 7;
+ *            8: x_q is int8 [m, k] (row stride k), codes in [-127, 127],
+ *               scale = absmax / 127.
+ *   x_scales fp32 [m], one per row over the whole K.
+ * Same rotation and rounding as ck4_quantize_weight_convrot.
+ * Alignment: x and ldx*2 bytes 16-byte aligned; x_q 8-byte (bits 4) or
+ * 16-byte (bits 8) aligned. Unsupported: k > 16384.
+ */
+ck4_status ck4_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                   int bits, int8_t *x_q, float *x_scales, void *stream);
+
+/*
+ * The fp32 rotation alone: r[m, k] = x * blockdiag(H, ..., H) * fp32(1/sqrt(rot_block)),
+ * the first stage of ck4_rotate_quantize_act (same kernel, fp32 store).
+ * Also the input basis of a rotated low-rank side path ([FAST] Features:
+ * dynamic LoRA patching with a Hadamard-rotated down projection).
+ * r is fp32 [m, k], row stride k, 16-byte aligned.
+ */
+ck4_status ck4_rotate_act_f32(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, float *r,
+                              void *stream);
+
+/*
+ * W4A4 linear: y = bf16((sum_k qx[m,k] qw[n,k]) * x_scales[m] * w_scales[n] + bias[n])
+ * ([PR #63] Description: s4.s4 GEMM with int32 accumulators, rank-one
+ * epilogue; scales factor out of the K loop).
+ *
+ *   x_q, x_scales  from ck4_rotate_quantize_act(bits = 4); reusing them for
+ *                  several weights is the caller's choice ([PR #63]: q/k/v
+ *                  projections share one quantised activation).
+ *   w_packed, w_scales  from ck4_quantize_weight_convrot(group = 0).
+ *   bias     fp32 [n] or NULL.
+ *   y        bf16 [m, ldy]; only columns [0, n) of each row are written.
+ * The epilogue is fp32 ((acc * x_scale) * w_scale + bias) rounded once to
+ * bf16, nearest even.
+ * Alignment: x_q and w_packed 16-byte aligned; y 8-byte aligned and ldy a
+ * multiple of 4. Unsupported: k % 256 != 0, k > 131072.
+ */
+ck4_status ck4_linear_w4a4(const int8_t *x_q, const float *x_scales, const int8_t *w_packed,
+                           const float *w_scales, const float *bias, int64_t m, int64_t n, int64_t k,
+                           uint16_t *y, int64_t ldy, void *stream);
+
+/*
+ * The integer part of ck4_linear_w4a4 alone: acc[m, n] (int32, row stride
+ * ldacc) = sum_k qx[m,k] qw[n,k], exact. Same kernel as ck4_linear_w4a4 with
+ * an int32 store in place of the epilogue. Same alignment and shape rules;
+ * acc 16-byte aligned and ldacc a multiple of 4.
+ */
+ck4_status ck4_gemm_w4a4_acc_i32(const int8_t *x_q, const int8_t *w_packed, int64_t m, int64_t n, int64_t k,
+                                 int32_t *acc, int64_t ldacc, void *stream);
+
+/*
+ * Grouped int4 -> int8 weight decode of rows [n0, n0 + nc) ([PR #97] What
+ * this adds: grouped int4 -> int8 weight decode; Chunk sizing: one chunk of
+ * output columns at a time).
+ *
+ *   w_packed      int8 [n, k/2] codes from ck4_quantize_weight_convrot(group = g).
+ *   group_scales  fp32 [n, k/g].
+ *   w8            int8 [nc, k] (row stride k), codes in [-127, 127].
+ *   row_scales    fp32 [nc].
+ * s_row = (max_j s[row, j] * 7) / 127, w8 = clamp(rint(q * (s[row, j] / s_row)), -127, 127),
+ * all fp32; an all-zero row gives s_row = 0 and w8 = 0.
+ * Alignment: w_packed and w8 16-byte aligned. Unsupported: g not a power of two in
+ * [16, 1024].
+ */
+ck4_status ck4_dequant_w4a8_grouped(const int8_t *w_packed, const float *group_scales, int64_t n, int64_t k,
+                                    int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales,
+                                    void *stream);
+
+/*
+ * Rowwise int8 linear: y = bf16(sum_k qx[m,k] qw[n,k] * x_scales[m] * w_scales[n] + bias[n])
+ * with int8 codes on both sides (the int8 GEMM that the grouped W4A8 path
+ * feeds, [PR #97] What this adds). Same epilogue as ck4_linear_w4a4.
+ * x_q8 int8 [m, k] from ck4_rotate_quantize_act(bits = 8); w8 int8 [n, k].
+ * Alignment as ck4_linear_w4a4. Unsupported: k % 128 != 0, k > 131072.
+ */
+ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8_t *w8, const float *w_scales,
+                           const float *bias, int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy,
+                           void *stream);
+
+/*
+ * Grouped W4A8 linear ([PR #97] What this adds, Chunk sizing): for each chunk
+ * of `chunk_cols` output columns, decode that slice of the weight into the
+ * workspace and run the int8 GEMM writing the chunk's column slice of y
+ * through ldy. The result is bit-identical for every chunk width.
+ *
+ *   chunk_cols  0: the default policy (chunking only when m <= 64; width =
+ *               the device L2 size / k rounded down to 128, clamped to
+ *               [1024, 4096]); > 0: that width (a multiple of 16);
+ *               < 0: one pass over all n.
+ *   workspace   device memory of at least ck4_w4a8_workspace_bytes(...) bytes,
+ *               16-byte aligned; its contents are scratch.
+ */
+size_t ck4_w4a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t chunk_cols);
+ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                   const float *group_scales, int64_t m, int64_t n, int64_t k, int group,
+                                   uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace,
+                                   size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CK4_H */

@@ -1,0 +1,217 @@
+"""W4A4 ConvRot linear for AMD MI355X (gfx950): Python binding of libck4.so.
+
+Argument marshalling only. Every step of the layer runs in the HIP kernels
+behind the C ABI declared in ``include/ck4.h``; PyTorch provides device
+memory and the current stream. If ``libck4.so`` has not been built, every call
+raises: there is no CPU fallback.
+
+The layer ("[PR #63] int4_tensorwise: W4A4 layout (+ConvRot) with fused CUDA
+kernels", Description): rotate the activation rows with a block Hadamard
+transform, quantise each row to int4 (absmax / 7) and pack it low nibble
+first, multiply against int4 weights prepared the same way with an int32
+GEMM, apply the row and column scales once in the epilogue, write bf16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libck4.so")
+
+CK4_OK, CK4_ERR_INVALID, CK4_ERR_UNSUPPORTED, CK4_ERR_DEVICE = 0, 1, 2, 3
+
+
+class Ck4Error(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+
+SIGNATURES = {
+    "ck4_version": ([], ctypes.c_char_p),
+    "ck4_status_string": ([_I], ctypes.c_char_p),
+    "ck4_last_error": ([], ctypes.c_char_p),
+    "ck4_quantize_weight_convrot": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
+    "ck4_rotate_quantize_act": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
+    "ck4_rotate_act_f32": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
+    "ck4_linear_w4a4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_gemm_w4a4_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_dequant_w4a8_grouped": ([_P, _P, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
+    "ck4_linear_w8a8": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_w4a8_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
+    "ck4_linear_w4a8_grouped": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t, _P], _I),
+}
+
+
+def lib():
+    """The loaded libck4.so (ctypes). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libck4.so not found at {LIB_PATH}: build it with "
+                "`python -m int4_w4a4_quantized_amd._build` (there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().ck4_version().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != CK4_OK:
+        raise Ck4Error(fn, status, lib().ck4_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str, dims: int | None = None) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride in its last dim")
+
+
+def _out_bf16(m: int, n: int, device) -> torch.Tensor:
+    # the kernels store 4 columns per lane: keep the row stride a multiple of 4
+    ld = (n + 3) // 4 * 4
+    return torch.empty((m, ld), dtype=torch.bfloat16, device=device)[:, :n]
+
+
+def quantize_weight_convrot(w: torch.Tensor, rot_block: int = 128, group: int = 0):
+    """Offline ConvRot weight prep: fp32 [n, k] -> (int8 [n, k/2], fp32 [n] or [n, k/group])."""
+    _need(w, torch.float32, "w", 2)
+    n, k = w.shape
+    wp = torch.empty((n, k // 2), dtype=torch.int8, device=w.device)
+    ws = torch.empty((n,) if group == 0 else (n, k // group), dtype=torch.float32, device=w.device)
+    _check("ck4_quantize_weight_convrot",
+           lib().ck4_quantize_weight_convrot(_ptr(w), n, k, w.stride(0), rot_block, group, _ptr(wp), _ptr(ws),
+                                             _stream(w.device)))
+    return wp, ws
+
+
+def rotate_quantize_act(x: torch.Tensor, rot_block: int = 128, bits: int = 4, out=None, scales=None):
+    """Dynamic rotate + quantise: bf16 [m, k] -> (int8 [m, k/2] (bits 4) or [m, k] (bits 8), fp32 [m])."""
+    _need(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    if out is None:
+        out = torch.empty((m, k // 2 if bits == 4 else k), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check("ck4_rotate_quantize_act",
+           lib().ck4_rotate_quantize_act(_ptr(x), m, k, x.stride(0), rot_block, bits, _ptr(out), _ptr(scales),
+                                         _stream(x.device)))
+    return out, scales
+
+
+def rotate_act_f32(x: torch.Tensor, rot_block: int = 128):
+    """fp32 block-Hadamard rotation of bf16 rows: [m, k] -> fp32 [m, k]."""
+    _need(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    r = torch.empty((m, k), dtype=torch.float32, device=x.device)
+    _check("ck4_rotate_act_f32",
+           lib().ck4_rotate_act_f32(_ptr(x), m, k, x.stride(0), rot_block, _ptr(r), _stream(x.device)))
+    return r
+
+
+def linear_w4a4(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
+                bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """y bf16 [m, n] from a quantised activation and a prepared weight."""
+    m, k = x_q.shape[0], x_q.shape[1] * 2
+    n = w_packed.shape[0]
+    if out is None:
+        out = _out_bf16(m, n, x_q.device)
+    _need(out, torch.bfloat16, "out", 2)
+    _check("ck4_linear_w4a4",
+           lib().ck4_linear_w4a4(_ptr(x_q), _ptr(x_scales), _ptr(w_packed), _ptr(w_scales), _ptr(bias), m, n, k,
+                                 _ptr(out), out.stride(0), _stream(x_q.device)))
+    return out
+
+
+def gemm_w4a4_acc_i32(x_q: torch.Tensor, w_packed: torch.Tensor):
+    """Exact int32 accumulators [m, n] of the W4A4 GEMM (same kernel, int32 store)."""
+    m, k = x_q.shape[0], x_q.shape[1] * 2
+    n = w_packed.shape[0]
+    ldacc = (n + 3) // 4 * 4
+    acc = torch.empty((m, ldacc), dtype=torch.int32, device=x_q.device)
+    _check("ck4_gemm_w4a4_acc_i32",
+           lib().ck4_gemm_w4a4_acc_i32(_ptr(x_q), _ptr(w_packed), m, n, k, _ptr(acc), ldacc, _stream(x_q.device)))
+    return acc[:, :n]
+
+
+def w4a4_linear(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, bias=None, rot_block: int = 128):
+    """The whole layer: rotate + quantise x, then the W4A4 GEMM + epilogue."""
+    x_q, sx = rotate_quantize_act(x, rot_block, 4)
+    return linear_w4a4(x_q, sx, w_packed, w_scales, bias)
+
+
+def dequant_w4a8_grouped(w_packed: torch.Tensor, group_scales: torch.Tensor, group: int = 128, n0: int = 0,
+                         nc: int | None = None):
+    """Grouped int4 -> int8 decode of weight rows [n0, n0+nc) -> (int8 [nc, k], fp32 [nc])."""
+    n, k = w_packed.shape[0], w_packed.shape[1] * 2
+    if nc is None:
+        nc = n - n0
+    w8 = torch.empty((nc, k), dtype=torch.int8, device=w_packed.device)
+    sr = torch.empty((nc,), dtype=torch.float32, device=w_packed.device)
+    _check("ck4_dequant_w4a8_grouped",
+           lib().ck4_dequant_w4a8_grouped(_ptr(w_packed), _ptr(group_scales), n, k, group, n0, nc, _ptr(w8),
+                                          _ptr(sr), _stream(w_packed.device)))
+    return w8, sr
+
+
+def linear_w8a8(x_q8, x_scales, w8, w_scales, bias=None, out=None):
+    m, k = x_q8.shape
+    n = w8.shape[0]
+    if out is None:
+        out = _out_bf16(m, n, x_q8.device)
+    _check("ck4_linear_w8a8",
+           lib().ck4_linear_w8a8(_ptr(x_q8), _ptr(x_scales), _ptr(w8), _ptr(w_scales), _ptr(bias), m, n, k,
+                                 _ptr(out), out.stride(0), _stream(x_q8.device)))
+    return out
+
+
+def w4a8_workspace_bytes(m: int, n: int, k: int, chunk_cols: int = 0) -> int:
+    return int(lib().ck4_w4a8_workspace_bytes(m, n, k, chunk_cols))
+
+
+def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128, chunk_cols: int = 0,
+                        out=None, workspace=None):
+    """Grouped W4A8 linear (decode per column chunk + int8 GEMM) -> bf16 [m, n]."""
+    m, k = x_q8.shape
+    n = w_packed.shape[0]
+    if out is None:
+        out = _out_bf16(m, n, x_q8.device)
+    need = w4a8_workspace_bytes(m, n, k, chunk_cols)
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x_q8.device)
+    _check("ck4_linear_w4a8_grouped",
+           lib().ck4_linear_w4a8_grouped(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales), m, n, k,
+                                         group, _ptr(out), out.stride(0), chunk_cols, _ptr(workspace),
+                                         workspace.numel(), _stream(x_q8.device)))
+    return out

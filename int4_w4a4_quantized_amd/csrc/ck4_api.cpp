@@ -1,0 +1,277 @@
+// C ABI of the ck4 library: argument validation, launch selection, errors.
+// Every entry point validates everything before it touches the device, so a
+// rejected call launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/ck4.h"
+#include "ck4_kernels.h"
+
+#define CK4_VERSION_STRING "ck4 0.1.0 gfx950"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ck4_status fail(ck4_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+ck4_status ok() {
+    g_last_error.clear();
+    return CK4_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once[kMaxDevices];
+int g_dev_ok[kMaxDevices];
+int64_t g_l2_bytes[kMaxDevices];
+
+// The kernels are built for gfx950 only; refuse any other device.
+ck4_status check_device(const char *fn, int *dev_out = nullptr) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(CK4_ERR_DEVICE, "%s: no current HIP device", fn);
+    std::call_once(g_dev_once[dev], [dev]() {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            g_dev_ok[dev] = 0;
+            return;
+        }
+        g_dev_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+        g_l2_bytes[dev] = prop.l2CacheSize;
+    });
+    if (!g_dev_ok[dev]) return fail(CK4_ERR_DEVICE, "%s: current device is not gfx950", fn);
+    if (dev_out) *dev_out = dev;
+    return CK4_OK;
+}
+
+ck4_status launched(const char *fn, hipError_t e) {
+    if (e != hipSuccess) return fail(CK4_ERR_DEVICE, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr int64_t kMaxActK = 16384;     // rotate/quantise kernels hold a row in VGPRs
+constexpr int64_t kMaxGemmK = 131072;   // 256 * 49 * K < 2^31 for the widened int4 products
+constexpr int64_t kMaxRows = 0x7FFFFFFF;
+
+ck4_status check_rot(const char *fn, int64_t k, int rot_block) {
+    if (!pow2(rot_block) || rot_block < 16 || rot_block > 1024)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d (need a power of two in [16, 1024])", fn, rot_block);
+    if (k % rot_block != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of rot_block=%d", fn, (long long)k,
+                    rot_block);
+    if (k > kMaxActK) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld > %lld", fn, (long long)k, (long long)kMaxActK);
+    return CK4_OK;
+}
+
+ck4_status check_gemm_common(const char *fn, int64_t m, int64_t n, int64_t k, int64_t ldy, const void *y,
+                             size_t y_align) {
+    if (m <= 0 || n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m, n, k must be positive", fn);
+    if (m > kMaxRows || n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m or n too large", fn);
+    if (ldy < n) return fail(CK4_ERR_INVALID, "%s: ldy=%lld < n=%lld", fn, (long long)ldy, (long long)n);
+    if (ldy % 4 != 0) return fail(CK4_ERR_INVALID, "%s: ldy=%lld is not a multiple of 4", fn, (long long)ldy);
+    if (!aligned(y, y_align)) return fail(CK4_ERR_INVALID, "%s: output pointer not %zu-byte aligned", fn, y_align);
+    if (k > kMaxGemmK) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld > %lld", fn, (long long)k, (long long)kMaxGemmK);
+    return CK4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *ck4_version(void) { return CK4_VERSION_STRING; }
+
+const char *ck4_status_string(ck4_status s) {
+    switch (s) {
+    case CK4_OK: return "ok";
+    case CK4_ERR_INVALID: return "invalid argument";
+    case CK4_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case CK4_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char *ck4_last_error(void) { return g_last_error.c_str(); }
+
+ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block, int group,
+                                       int8_t *w_packed, float *w_scales, void *stream) {
+    const char *fn = "ck4_quantize_weight_convrot";
+    if (!w || !w_packed || !w_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
+    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
+    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (!aligned(w_packed, 8) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
+    if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (group != 0 && (!pow2(group) || group < 16 || group > 1024 || k % group != 0))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need 0 or a power of two in [16, 1024] dividing k)", fn,
+                    group);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2, w_scales,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, int bits,
+                                   int8_t *x_q, float *x_scales, void *stream) {
+    const char *fn = "ck4_rotate_quantize_act";
+    if (!x || !x_q || !x_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (m <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m and k must be positive", fn);
+    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
+    if (bits != 4 && bits != 8) return fail(CK4_ERR_UNSUPPORTED, "%s: bits=%d (need 4 or 8)", fn, bits);
+    if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: x/ldx not 16-byte aligned", fn);
+    if (!aligned(x_q, bits == 4 ? 8 : 16) || !aligned(x_scales, 4))
+        return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
+    if (m > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m too large", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(x, 0, m, k, ldx, rot_block, bits == 4 ? 0 : 1, 0, x_q,
+                                                  bits == 4 ? k / 2 : k, x_scales, static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_rotate_act_f32(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, float *r,
+                              void *stream) {
+    const char *fn = "ck4_rotate_act_f32";
+    if (!x || !r) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (m <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m and k must be positive", fn);
+    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
+    if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: x/ldx not 16-byte aligned", fn);
+    if (!aligned(r, 16)) return fail(CK4_ERR_INVALID, "%s: r not 16-byte aligned", fn);
+    if (m > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m too large", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(x, 0, m, k, ldx, rot_block, 2, 0, r, k, nullptr,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+static ck4_status gemm_entry(const char *fn, bool s4, const int8_t *a, const float *sa, const int8_t *b,
+                             const float *sb, const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32,
+                             void *y, int64_t ldy, void *stream) {
+    if (!a || !b || !y || (!out_i32 && (!sa || !sb))) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, out_i32 ? 16 : 8)) return s;
+    if (!aligned(a, 16) || !aligned(b, 16)) return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
+    const int64_t step_k = s4 ? 256 : 128;
+    if (k % step_k != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of %lld", fn, (long long)k,
+                    (long long)step_k);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_gemm(s4, a, b, sa, sb, bias, m, n, k, out_i32, y, ldy,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_linear_w4a4(const int8_t *x_q, const float *x_scales, const int8_t *w_packed, const float *w_scales,
+                           const float *bias, int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy,
+                           void *stream) {
+    return gemm_entry("ck4_linear_w4a4", true, x_q, x_scales, w_packed, w_scales, bias, m, n, k, false, y, ldy,
+                      stream);
+}
+
+ck4_status ck4_gemm_w4a4_acc_i32(const int8_t *x_q, const int8_t *w_packed, int64_t m, int64_t n, int64_t k,
+                                 int32_t *acc, int64_t ldacc, void *stream) {
+    return gemm_entry("ck4_gemm_w4a4_acc_i32", true, x_q, nullptr, w_packed, nullptr, nullptr, m, n, k, true, acc,
+                      ldacc, stream);
+}
+
+ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8_t *w8, const float *w_scales,
+                           const float *bias, int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy,
+                           void *stream) {
+    return gemm_entry("ck4_linear_w8a8", false, x_q8, x_scales, w8, w_scales, bias, m, n, k, false, y, ldy,
+                      stream);
+}
+
+ck4_status ck4_dequant_w4a8_grouped(const int8_t *w_packed, const float *group_scales, int64_t n, int64_t k,
+                                    int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales,
+                                    void *stream) {
+    const char *fn = "ck4_dequant_w4a8_grouped";
+    if (!w_packed || !group_scales || !w8 || !row_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (n <= 0 || k <= 0 || nc <= 0) return fail(CK4_ERR_INVALID, "%s: n, k, nc must be positive", fn);
+    if (n0 < 0 || n0 + nc > n) return fail(CK4_ERR_INVALID, "%s: rows [n0, n0+nc) outside [0, n)", fn);
+    if (!pow2(group) || group < 16 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [16, 1024] dividing k)", fn, group);
+    if (!aligned(w_packed, 16) || !aligned(w8, 16) || (k / 2) % 8 != 0)
+        return fail(CK4_ERR_INVALID, "%s: w_packed / w8 not 16-byte aligned", fn);
+    if (nc > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: nc too large", fn);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_w4a8_decode(w_packed, group_scales, k, group, n0, nc, w8, row_scales,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+static int64_t w4a8_chunk(int64_t m, int64_t n, int64_t k, int64_t chunk_cols, int64_t l2_bytes) {
+    if (chunk_cols < 0) return n;
+    if (chunk_cols > 0) return chunk_cols < n ? chunk_cols : n;
+    const char *e_rows = std::getenv("CK4_W4A8_CHUNK_MAX_ROWS");
+    const int64_t max_rows = e_rows ? std::atoll(e_rows) : 64;
+    if (m > max_rows) return n;
+    const char *e_cols = std::getenv("CK4_W4A8_CHUNK_COLS");
+    int64_t c = e_cols ? std::atoll(e_cols) : 0;
+    if (c <= 0) {
+        c = (l2_bytes / k) / 128 * 128;
+        if (c < 1024) c = 1024;
+        if (c > 4096) c = 4096;
+    }
+    c = (c + 15) / 16 * 16;
+    return c < n ? c : n;
+}
+
+static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+size_t ck4_w4a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t chunk_cols) {
+    if (m <= 0 || n <= 0 || k <= 0) return 0;
+    int dev = 0;
+    int64_t l2 = 4 << 20;
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices && check_device("ws", &dev) == CK4_OK)
+        l2 = g_l2_bytes[dev];
+    const int64_t c = w4a8_chunk(m, n, k, chunk_cols, l2);
+    return (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));
+}
+
+ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                   const float *group_scales, int64_t m, int64_t n, int64_t k, int group,
+                                   uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace, size_t ws_bytes,
+                                   void *stream) {
+    const char *fn = "ck4_linear_w4a8_grouped";
+    if (!x_q8 || !x_scales || !w_packed || !group_scales || !y || !workspace)
+        return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, 8)) return s;
+    if (!aligned(x_q8, 16) || !aligned(w_packed, 16) || !aligned(workspace, 16))
+        return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
+    if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
+    if (!pow2(group) || group < 16 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [16, 1024] dividing k)", fn, group);
+    if (chunk_cols > 0 && chunk_cols % 16 != 0)
+        return fail(CK4_ERR_INVALID, "%s: chunk_cols=%lld is not a multiple of 16", fn, (long long)chunk_cols);
+    int dev = 0;
+    if (ck4_status s = check_device(fn, &dev)) return s;
+    const int64_t c = w4a8_chunk(m, n, k, chunk_cols, g_l2_bytes[dev]);
+    const size_t need = (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));
+    if (ws_bytes < need)
+        return fail(CK4_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    int8_t *w8 = static_cast<int8_t *>(workspace);
+    float *srow = reinterpret_cast<float *>(static_cast<char *>(workspace) + align_up(c * k, 256));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int64_t n0 = 0; n0 < n; n0 += c) {
+        const int64_t nc = (n - n0) < c ? (n - n0) : c;
+        hipError_t e = ck4::launch_w4a8_decode(w_packed, group_scales, k, group, n0, nc, w8, srow, st);
+        if (e != hipSuccess) return launched(fn, e);
+        e = ck4::launch_gemm(false, x_q8, w8, x_scales, srow, nullptr, m, nc, k, false, y + n0, ldy, st);
+        if (e != hipSuccess) return launched(fn, e);
+    }
+    return ok();
+}
+
+}  // extern "C"

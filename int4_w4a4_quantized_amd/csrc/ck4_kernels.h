@@ -1,0 +1,29 @@
+// Internal launchers of the ck4 HIP kernels (gfx950). Not part of the C ABI:
+// ck4_api.cpp validates arguments and then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ck4 {
+
+// Rotation + quantisation of rows (one workgroup per row).
+//   in_kind   0: bf16 input, 1: fp32 input
+//   out_kind  0: packed int4 (+ scales), 1: int8 codes (+ scales), 2: fp32 rotation
+//   group     0: one scale per row; > 0: one scale per `group` elements (int4 only)
+hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
+                               int out_kind, int group, void *out, int64_t ldo, float *scales,
+                               hipStream_t stream);
+
+// Integer GEMM acc[m, n] = sum_k a[m, k] b[n, k] on int8 MFMA, with a rank-one
+// bf16 epilogue (out_i32 == false) or an int32 store (out_i32 == true).
+//   s4 true:  a, b packed int4 [rows, k/2]; false: int8 codes [rows, k].
+hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *sa, const float *sb,
+                       const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
+                       hipStream_t stream);
+
+// Grouped int4 -> int8 decode of weight rows [n0, n0 + nc).
+hipError_t launch_w4a8_decode(const int8_t *w_packed, const float *group_scales, int64_t k, int group,
+                              int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream);
+
+}  // namespace ck4

@@ -1,0 +1,283 @@
+// Integer GEMM on the gfx950 int8 matrix cores, with the rank-one epilogue.
+//
+// What it computes ("[PR #63] int4_tensorwise: W4A4 layout (+ConvRot) with
+// fused CUDA kernels", Description: s4.s4 GEMM with carried int32
+// accumulators, |acc| <= 49 K, and the per-row / per-column scales applied
+// once after the K loop):
+//   acc[m, n] = sum_k a[m, k] * b[n, k]                    (exact, int32)
+//   y[m, n]   = bf16(((float)acc * sa[m]) * sb[n] (+ bias[n]))
+// a = quantised activations, b = quantised weights, both K-major.
+//
+// gfx950 has no int4 matrix instruction (the assembler rejects every i4 MFMA
+// mnemonic), so int4 operands are widened in registers and fed to
+// v_mfma_i32_16x16x64_i8. The widening uses two facts:
+//  * for a packed byte B (low nibble = code of element 2j, high = 2j+1),
+//    B & 0xF0 read as int8 is exactly 16 * hi, and (B << 4) & 0xF0 is exactly
+//    16 * lo, so a 32-bit word of 8 codes widens to two words of 4 int8 each
+//    with one AND (high) and one shift + AND (low): the products carry a factor
+//    256, removed by an exact arithmetic shift after the K loop
+//    (|256 acc| <= 12544 K < 2^31 for K <= 131072);
+//  * the low-nibble words hold the even k and the high-nibble words the odd
+//    k; both operands are split the same way, and a permutation of k shared
+//    by both operands leaves every dot product unchanged ([PR #63]: both
+//    operands share the fragment k-permutation).
+//
+// Tiling: a workgroup of 256 threads (4 wavefronts) computes a BM x BN tile
+// of y. Each K step stages 128 bytes of every row of both operands in LDS
+// (256 int4 or 128 int8 values), double buffered with one barrier per step.
+// Rows are stored as 8 chunks of 16 bytes with the chunk index XORed with
+// (row & 7), so the 16 rows read by one fragment load land on distinct banks.
+// The MFMA's first operand is the weight fragment and its second the
+// activation fragment, so each lane's 4 accumulators are 4 consecutive
+// output columns of one row: the epilogue stores 8 contiguous bytes per lane.
+// Workgroup ids are remapped so that each XCD (ids are dealt round-robin to
+// the 8 XCDs) walks a contiguous run of tiles and reuses its L2.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ck4_kernels.h"
+
+namespace ck4 {
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kRowBytes = 128;          // bytes of each row per K step
+constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row per step
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ v4i as_v4i(uint4 u) {
+    v4i r;
+    r.x = (int)u.x;
+    r.y = (int)u.y;
+    r.z = (int)u.z;
+    r.w = (int)u.w;
+    return r;
+}
+
+__device__ __forceinline__ v4i widen_hi(uint4 p) {
+    return as_v4i(make_uint4(p.x & 0xF0F0F0F0u, p.y & 0xF0F0F0F0u, p.z & 0xF0F0F0F0u, p.w & 0xF0F0F0F0u));
+}
+
+__device__ __forceinline__ v4i widen_lo(uint4 p) {
+    return as_v4i(make_uint4((p.x << 4) & 0xF0F0F0F0u, (p.y << 4) & 0xF0F0F0F0u, (p.z << 4) & 0xF0F0F0F0u,
+                             (p.w << 4) & 0xF0F0F0F0u));
+}
+
+__device__ __forceinline__ int lds_index(int row, int chunk) { return row * kChunks + (chunk ^ (row & 7)); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+template <bool S4, int BM, int BN, int WAVES_M, bool OUT_I32>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B,
+                                                        const float *__restrict__ sa, const float *__restrict__ sb,
+                                                        const float *__restrict__ bias, int M, int N,
+                                                        int64_t row_bytes, int ksteps, void *__restrict__ Y,
+                                                        int64_t ldy, int tiles_n, int tiles_total) {
+    constexpr int WAVES_N = 4 / WAVES_M;
+    constexpr int WTM = BM / WAVES_M;
+    constexpr int WTN = BN / WAVES_N;
+    constexpr int FM = WTM / 16;
+    constexpr int FN = WTN / 16;
+    constexpr int ROWS = BM + BN;
+    constexpr int TOTAL_CHUNKS = ROWS * kChunks;
+    constexpr int LOADS = (TOTAL_CHUNKS + kThreads - 1) / kThreads;
+    static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "bad tile");
+
+    __shared__ uint4 lds[2][TOTAL_CHUNKS];
+
+    int tile = blockIdx.x;
+    if ((tiles_total & 7) == 0) tile = (tile & 7) * (tiles_total >> 3) + (tile >> 3);
+    const int tm = tile / tiles_n;
+    const int tn = tile - tm * tiles_n;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WAVES_N;
+    const int wn = wave - wm * WAVES_N;
+
+    // Global -> LDS staging: chunk q = tid + i * 256 is row q / 8, chunk q % 8.
+    const int8_t *gp[LOADS];
+    bool gv[LOADS];
+    int lo[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int q = tid + i * kThreads;
+        const int r = q / kChunks;
+        const int c = q % kChunks;
+        bool valid = q < TOTAL_CHUNKS;
+        const int8_t *base = A;
+        if (r < BM) {
+            const int gr = m0 + r;
+            valid = valid && gr < M;
+            base = A + (int64_t)(valid ? gr : 0) * row_bytes;
+        } else {
+            const int gr = n0 + (r - BM);
+            valid = valid && gr < N;
+            base = B + (int64_t)(valid ? gr : 0) * row_bytes;
+        }
+        gp[i] = base + c * 16;
+        gv[i] = valid;
+        lo[i] = q < TOTAL_CHUNKS ? lds_index(r, c) : 0;
+    }
+
+    uint4 pre[LOADS];
+    auto gload = [&](int step) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            pre[i] = gv[i] ? *reinterpret_cast<const uint4 *>(gp[i] + (int64_t)step * kRowBytes)
+                           : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            if (tid + i * kThreads < TOTAL_CHUNKS) lds[buf][lo[i]] = pre[i];
+        }
+    };
+
+    v4i acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+
+    const int frow = lane & 15;
+    const int fgrp = lane >> 4;
+    for (int s = 0; s < ksteps; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < ksteps) gload(s + 1);
+        const uint4 *As = lds[buf];
+        const uint4 *Bs = lds[buf] + BM * kChunks;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int c = half * 4 + fgrp;
+            uint4 xa[FM], wb[FN];
+#pragma unroll
+            for (int j = 0; j < FM; ++j) {
+                const int r = wm * WTM + j * 16 + frow;
+                xa[j] = As[lds_index(r, c)];
+            }
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int r = wn * WTN + i * 16 + frow;
+                wb[i] = Bs[lds_index(r, c)];
+            }
+            if constexpr (S4) {
+                v4i xl[FM], xh[FM];
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    xl[j] = widen_lo(xa[j]);
+                    xh[j] = widen_hi(xa[j]);
+                }
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    const v4i wl = widen_lo(wb[i]);
+                    const v4i wh = widen_hi(wb[i]);
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) {
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, xl[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, xh[j], acc[i][j], 0, 0, 0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(wb[i]), as_v4i(xa[j]),
+                                                                          acc[i][j], 0, 0, 0);
+            }
+        }
+        if (s + 1 < ksteps) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Epilogue. Lane holds acc[i][j][r] = y[m][n] with
+    //   m = m0 + wm*WTM + j*16 + (lane & 15), n = n0 + wn*WTN + i*16 + 4*(lane >> 4) + r.
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * WTM + j * 16 + frow;
+        if (m >= M) continue;
+        const float sam = OUT_I32 ? 0.0f : sa[m];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int nb = n0 + wn * WTN + i * 16 + 4 * fgrp;
+            if (nb >= N) continue;
+            int a4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a4[r] = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+            if constexpr (OUT_I32) {
+                int32_t *yr = reinterpret_cast<int32_t *>(Y) + (int64_t)m * ldy + nb;
+                if (nb + 3 < N) {
+                    *reinterpret_cast<int4 *>(yr) = make_int4(a4[0], a4[1], a4[2], a4[3]);
+                } else {
+                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = a4[r];
+                }
+            } else {
+                uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + nb;
+                uint16_t o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = nb + r < N ? nb + r : N - 1;
+                    float v = ((float)a4[r] * sam) * sb[n];
+                    if (bias) v = v + bias[n];
+                    o[r] = f32_to_bf16(v);
+                }
+                if (nb + 3 < N) {
+                    *reinterpret_cast<uint2 *>(yr) =
+                        make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+                } else {
+                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = o[r];
+                }
+            }
+        }
+    }
+}
+
+template <bool S4, int BM, int BN, int WAVES_M>
+hipError_t launch_cfg(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
+                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+    const int64_t row_bytes = S4 ? k / 2 : k;
+    const int ksteps = (int)(row_bytes / kRowBytes);
+    const int tiles_m = (int)((m + BM - 1) / BM);
+    const int tiles_n = (int)((n + BN - 1) / BN);
+    const int total = tiles_m * tiles_n;
+    dim3 grid((unsigned)total), block(kThreads);
+    if (out_i32)
+        gemm_kernel<S4, BM, BN, WAVES_M, true><<<grid, block, 0, stream>>>(a, b, sa, sb, bias, (int)m, (int)n,
+                                                                          row_bytes, ksteps, y, ldy, tiles_n, total);
+    else
+        gemm_kernel<S4, BM, BN, WAVES_M, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, row_bytes, ksteps, y, ldy, tiles_n, total);
+    return hipGetLastError();
+}
+
+template <bool S4>
+hipError_t launch_s(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias, int64_t m,
+                    int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+    if (m <= 16) return launch_cfg<S4, 16, 64, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    if (m <= 64) return launch_cfg<S4, 64, 64, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    return launch_cfg<S4, 128, 128, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *sa, const float *sb,
+                       const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
+                       hipStream_t stream) {
+    if (s4) return launch_s<true>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    return launch_s<false>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+}
+
+}  // namespace ck4

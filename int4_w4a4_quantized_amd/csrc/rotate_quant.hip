@@ -1,0 +1,232 @@
+// Fused ConvRot rotation + symmetric quantisation + packing, one row per
+// workgroup, for gfx950.
+//
+// What it computes ("[PR #63] int4_tensorwise: W4A4 layout (+ConvRot) with
+// fused CUDA kernels", Description: fused activation kernel = FHT rotation +
+// rowwise int4 quantize + pack in one pass; weights are packed signed int4
+// pairs, low nibble first, with one fp32 scale per row):
+//   r = x * blockdiag(H_b, ..., H_b) * fp32(1/sqrt(b))     (fp32, b = rot_block)
+//   s = absmax(r) / qmax                                  (fp32 divide)
+//   q = clamp(rint(r / s), -qmax, qmax)                    (fp32 divide, ties to even)
+// with H_b the Sylvester Hadamard matrix and the butterflies taken with
+// ascending stride, so the fp32 rotation is one fixed sequence of roundings.
+//
+// Data layout in registers: each lane owns "chunks" of 16 contiguous elements
+// of the row. Chunk c of a row covers elements [16c, 16c + 16); chunk c is
+// owned by thread c mod blockDim. A Hadamard block of b elements is b/16
+// consecutive chunks, which sit in b/16 consecutive lanes of one wavefront
+// (blockDim is a multiple of 64 and b <= 1024). Butterfly strides 1..8 are
+// inside a lane; strides 16..b/2 pair lane L with lane L ^ (stride/16).
+// The whole row stays in VGPRs between the rotation and the quantisation, so
+// HBM is read once and written once.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ck4_kernels.h"
+
+namespace ck4 {
+namespace {
+
+constexpr int kElems = 16;   // contiguous elements per chunk
+constexpr int kMaxChunks = 4;  // chunks per thread: k <= 16 * 256 * 4 = 16384
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void load_chunk(const uint16_t *p, float v[kElems]) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    uint4 a = q[0], b = q[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+__device__ __forceinline__ void load_chunk(const float *p, float v[kElems]) {
+    const float4 *q = reinterpret_cast<const float4 *>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float4 t = q[i];
+        v[4 * i] = t.x;
+        v[4 * i + 1] = t.y;
+        v[4 * i + 2] = t.z;
+        v[4 * i + 3] = t.w;
+    }
+}
+
+// Butterflies with stride 1, 2, 4, 8 inside the chunk (ascending).
+__device__ __forceinline__ void fwht_in_lane(float v[kElems]) {
+#pragma unroll
+    for (int h = 1; h < kElems; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < kElems; ++i) {
+            if (i & h) continue;
+            float a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = a - b;
+        }
+    }
+}
+
+// Butterflies with stride 16 * mask, for mask = 1, 2, ..., b/32 (ascending):
+// the lower lane of a pair keeps a + b, the upper keeps a - b.
+__device__ __forceinline__ void fwht_cross_lane(float v[kElems], int lane, int lanes_per_block) {
+    for (int mask = 1; mask < lanes_per_block; mask <<= 1) {
+        const bool upper = (lane & mask) != 0;
+#pragma unroll
+        for (int i = 0; i < kElems; ++i) {
+            float p = __shfl_xor(v[i], mask, 64);
+            v[i] = upper ? (p - v[i]) : (v[i] + p);
+        }
+    }
+}
+
+__device__ __forceinline__ float wave_max(float a) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
+    return a;
+}
+
+__device__ __forceinline__ int quant_code(float r, float s, float qmax) {
+    if (s == 0.0f) return 0;
+    float t = rintf(r / s);
+    t = fminf(fmaxf(t, -qmax), qmax);
+    return (int)t;
+}
+
+// out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation.
+template <typename TIn, int OUT>
+__global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__restrict__ x, int64_t ldx, int k,
+                                                                  int lanes_per_block, float c, int group,
+                                                                  void *__restrict__ out, int64_t ldo,
+                                                                  float *__restrict__ scales) {
+    __shared__ float red[kThreads / 64];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int nthreads = blockDim.x;
+    const int nchunks = k / kElems;
+    const TIn *xr = x + (int64_t)row * ldx;
+
+    float v[kMaxChunks][kElems];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxChunks; ++j) {
+        const int ch = tid + j * nthreads;
+        if (ch < nchunks) {
+            load_chunk(xr + (int64_t)ch * kElems, v[j]);
+            fwht_in_lane(v[j]);
+            fwht_cross_lane(v[j], lane, lanes_per_block);
+#pragma unroll
+            for (int i = 0; i < kElems; ++i) {
+                v[j][i] = v[j][i] * c;
+                amax = fmaxf(amax, fabsf(v[j][i]));
+            }
+        }
+    }
+
+    if constexpr (OUT == 2) {
+        float *o = reinterpret_cast<float *>(out) + (int64_t)row * ldo;
+#pragma unroll
+        for (int j = 0; j < kMaxChunks; ++j) {
+            const int ch = tid + j * nthreads;
+            if (ch < nchunks) {
+                float4 *d = reinterpret_cast<float4 *>(o + (int64_t)ch * kElems);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    d[i] = make_float4(v[j][4 * i], v[j][4 * i + 1], v[j][4 * i + 2], v[j][4 * i + 3]);
+            }
+        }
+        return;
+    } else {
+        const float qmax = OUT == 0 ? 7.0f : 127.0f;
+        if (group == 0) {
+            // absmax over the whole row: wavefront reduction, then across waves.
+            amax = wave_max(amax);
+            if (lane == 0) red[tid >> 6] = amax;
+            __syncthreads();
+            amax = red[0];
+            for (int w = 1; w < nthreads / 64; ++w) amax = fmaxf(amax, red[w]);
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxChunks; ++j) {
+            const int ch = tid + j * nthreads;
+            if (ch >= nchunks) continue;
+            float s;
+            if (group == 0) {
+                s = amax / qmax;
+                if (tid == 0 && j == 0) scales[row] = s;
+            } else {
+                // one scale per `group` elements = group/16 consecutive lanes
+                float gmax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < kElems; ++i) gmax = fmaxf(gmax, fabsf(v[j][i]));
+                for (int off = 1; off < group / kElems; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
+                s = gmax / qmax;
+                const int lanes_per_group = group / kElems;
+                if ((ch % lanes_per_group) == 0) scales[(int64_t)row * (k / group) + ch / lanes_per_group] = s;
+            }
+            if constexpr (OUT == 0) {
+                uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w0 |= (uint32_t)(quant_code(v[j][i], s, qmax) & 0xF) << (4 * i);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) w1 |= (uint32_t)(quant_code(v[j][8 + i], s, qmax) & 0xF) << (4 * i);
+                int8_t *o = reinterpret_cast<int8_t *>(out) + (int64_t)row * ldo + (int64_t)ch * (kElems / 2);
+                *reinterpret_cast<uint2 *>(o) = make_uint2(w0, w1);
+            } else {
+                uint32_t w[4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    w[d] = 0;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        w[d] |= (uint32_t)(quant_code(v[j][4 * d + i], s, qmax) & 0xFF) << (8 * i);
+                }
+                int8_t *o = reinterpret_cast<int8_t *>(out) + (int64_t)row * ldo + (int64_t)ch * kElems;
+                *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+    }
+}
+
+template <typename TIn>
+hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int rot_block, int out_kind, int group,
+                        void *out, int64_t ldo, float *scales, hipStream_t stream) {
+    const int nchunks = (int)(k / kElems);
+    const int per_thread = (nchunks + kThreads - 1) / kThreads;
+    int threads = (nchunks + per_thread - 1) / per_thread;
+    threads = (threads + 63) / 64 * 64;
+    const float c = (float)(1.0 / __builtin_sqrt((double)rot_block));
+    const int lanes_per_block = rot_block / kElems;
+    dim3 grid((unsigned)rows), block((unsigned)threads);
+    switch (out_kind) {
+    case 0:
+        rotate_quant_kernel<TIn, 0><<<grid, block, 0, stream>>>(x, ldx, (int)k, lanes_per_block, c, group, out,
+                                                                 ldo, scales);
+        break;
+    case 1:
+        rotate_quant_kernel<TIn, 1><<<grid, block, 0, stream>>>(x, ldx, (int)k, lanes_per_block, c, group, out,
+                                                                 ldo, scales);
+        break;
+    default:
+        rotate_quant_kernel<TIn, 2><<<grid, block, 0, stream>>>(x, ldx, (int)k, lanes_per_block, c, group, out,
+                                                                 ldo, scales);
+        break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
+                               int out_kind, int group, void *out, int64_t ldo, float *scales,
+                               hipStream_t stream) {
+    if (in_kind == 0)
+        return launch_typed(static_cast<const uint16_t *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo,
+                            scales, stream);
+    return launch_typed(static_cast<const float *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo, scales,
+                        stream);
+}
+
+}  // namespace ck4

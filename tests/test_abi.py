@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+The library must load, export every function that include/ck4.h declares, and
+reject invalid or unsupported arguments with the documented status before it
+touches a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import int4_w4a4_quantized_amd as ck
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ck4.h")
+
+FAKE = ctypes.c_void_p(1 << 20)      # 16-byte aligned, never dereferenced
+ODD = ctypes.c_void_p((1 << 20) + 4)  # misaligned
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ck4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ck.LIB_PATH):
+        pytest.fail("libck4.so is not built: run __graft_entry__.build()")
+    return ck.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(ck.SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_status_strings(L):
+    assert L.ck4_version().decode().startswith("ck4 ")
+    assert L.ck4_status_string(0) == b"ok"
+    assert L.ck4_status_string(1) == b"invalid argument"
+    assert L.ck4_status_string(2) == b"unsupported shape or option"
+    assert L.ck4_status_string(3) == b"device error"
+
+
+def last(L):
+    return L.ck4_last_error().decode()
+
+
+def test_linear_validation(L):
+    f = L.ck4_linear_w4a4
+    assert f(NULL, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
+    assert "null" in last(L)
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 0, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 4, NULL) == ck.CK4_ERR_INVALID  # ldy < n
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 10, NULL) == ck.CK4_ERR_INVALID  # ldy % 4
+    assert f(ODD, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID  # alignment
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 384, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 256
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 262144, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k too big
+    g = L.ck4_gemm_w4a4_acc_i32
+    assert g(FAKE, FAKE, 8, 8, 256, ODD, 8, NULL) == ck.CK4_ERR_INVALID
+
+
+def test_rotate_validation(L):
+    f = L.ck4_rotate_quantize_act
+    assert f(FAKE, 4, 256, 256, 128, 5, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # bits
+    assert f(FAKE, 4, 256, 256, 96, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rot_block
+    assert f(FAKE, 4, 256, 256, 8, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 384, 384, 256, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % rot_block
+    assert f(FAKE, 4, 32768, 32768, 128, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k > 16384
+    assert f(FAKE, 4, 256, 200, 128, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID  # ldx < k
+    assert f(ODD, 4, 256, 256, 128, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, -1, 256, 256, 128, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    r = L.ck4_rotate_act_f32
+    assert r(FAKE, 4, 256, 256, 128, NULL, NULL) == ck.CK4_ERR_INVALID
+    w = L.ck4_quantize_weight_convrot
+    assert w(FAKE, 4, 256, 256, 128, 48, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group
+    assert w(FAKE, 4, 256, 256, 128, 512, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group > k
+    assert w(FAKE, 4, 256, 250, 128, 0, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+
+
+def test_w4a8_validation(L):
+    d = L.ck4_dequant_w4a8_grouped
+    assert d(FAKE, FAKE, 64, 256, 128, 32, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID  # n0 + nc > n
+    assert d(FAKE, FAKE, 64, 256, 100, 0, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED
+    f = L.ck4_linear_w4a8_grouped
+    assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, 0, NULL, 0, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 200, 128, FAKE, 64, 0, FAKE, 1 << 20, NULL) == ck.CK4_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, 24, FAKE, 1 << 20, NULL) == ck.CK4_ERR_INVALID
+    l8 = L.ck4_linear_w8a8
+    assert l8(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 192, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
+
+
+def test_no_cpu_fallback_without_library(tmp_path, monkeypatch):
+    # The binding must fail loudly, not compute elsewhere, when the library is absent.
+    monkeypatch.setattr(ck, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ck, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        ck.lib()

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: packed int4 bytes, int8 codes, fp32 scales and int32 accumulators are
+bit-exact; the fp32 rotation is within 1e-6 relative (bitwise equal in
+practice: both sides take the same fp32 butterflies in the same order); bf16
+outputs are within 1e-2 relative of the oracle's single-rounded fp64 value and
+exactly 0 where the oracle's is 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+ROT_CASES = [
+    (64, 256, 128), (17, 384, 128), (5, 3072, 128), (3, 12288, 128), (7, 5120, 128),
+    (9, 1024, 16), (9, 1024, 32), (9, 1024, 64), (9, 2048, 256), (4, 4096, 1024), (2, 16384, 128),
+]
+GEMM_CASES = [
+    (64, 256, 256), (1, 1, 256), (3, 17, 256), (17, 3, 512), (130, 200, 768), (16, 64, 3072),
+    (64, 130, 1024), (257, 129, 512), (33, 77, 256), (8, 1000, 512), (200, 8, 1280),
+]
+
+
+@pytest.fixture(scope="module")
+def ck():
+    import int4_w4a4_quantized_amd as ck
+    name = torch.cuda.get_device_properties(0).gcnArchName
+    assert name.startswith("gfx950"), name
+    return ck
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bf16_host_bits(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_bf16_close(got_bits: np.ndarray, ref_bits: np.ndarray, rtol: float = 1e-2, atol=None) -> None:
+    """|gpu - oracle| <= rtol |oracle| (+ atol where a bias add can cancel), exact zeros."""
+    g = workloads.bf16_bits_to_f32(got_bits).astype(np.float64)
+    r = workloads.bf16_bits_to_f32(ref_bits).astype(np.float64)
+    assert np.all(np.isfinite(g))
+    if atol is None:
+        assert np.all(g[r == 0] == 0)
+        atol = 0.0
+    bad = np.abs(g - r) > rtol * np.abs(r) + atol
+    assert not bad.any(), f"{bad.sum()} of {bad.size} outside {rtol} rel; first at {np.argwhere(bad)[0]}"
+
+
+def act(m, k, seed):
+    rng = np.random.default_rng(seed)
+    return workloads.make_activations(rng, m, k)
+
+
+# --------------------------------------------------------------------------
+
+
+def test_library_identity(ck):
+    assert ck.version().startswith("ck4")
+
+
+@pytest.mark.parametrize("m,k,rb", ROT_CASES)
+def test_rotation_f32(ck, m, k, rb):
+    xb = act(m, k, 100 + m)
+    r = host(ck.rotate_act_f32(dev_bf16(xb), rb))
+    ref = oracle.rotate_bf16(xb, rb)
+    rel = np.abs(r.astype(np.float64) - ref) / np.maximum(np.abs(ref).max(axis=1, keepdims=True), 1e-30)
+    assert rel.max() <= 1e-6
+    assert np.array_equal(r, ref)  # numerically equal element by element (+0 == -0)
+
+
+@pytest.mark.parametrize("m,k,rb", ROT_CASES)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_activation_quant_bitexact(ck, m, k, rb, bits):
+    xb = act(m, k, 200 + m)
+    xb[0, :] = 0  # all-zero row: scale 0, codes 0
+    q, s = ck.rotate_quantize_act(dev_bf16(xb), rb, bits)
+    q_ref, s_ref = oracle.rotate_quantize_act(xb, rb, bits)
+    assert np.array_equal(host(s).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(host(q), q_ref)
+    assert host(s)[0] == 0 and not host(q)[0].any()
+
+
+@pytest.mark.parametrize("n,k,rb,group", [
+    (64, 256, 128, 0), (17, 384, 128, 0), (300, 3072, 128, 0), (5, 12288, 128, 0),
+    (33, 1024, 64, 0), (40, 2048, 256, 0), (64, 512, 128, 128), (37, 3072, 128, 128),
+    (16, 1024, 128, 16), (16, 1024, 128, 32), (16, 1024, 128, 64), (16, 1024, 128, 256), (8, 5120, 128, 128),
+])
+def test_weight_quant_bitexact(ck, n, k, rb, group):
+    rng = np.random.default_rng(300 + n)
+    w = workloads.make_weight(rng, n, k)
+    w[1, :] = 0.0
+    w[2, 5] = 3.0  # an outlier
+    wp, ws = ck.quantize_weight_convrot(torch.from_numpy(w).cuda(), rb, group)
+    wp_ref, ws_ref = oracle.quantize_weight_convrot(w, rb, group)
+    assert np.array_equal(host(ws).view(np.uint32), ws_ref.view(np.uint32))
+    assert np.array_equal(host(wp), wp_ref)
+
+
+def _quantised_pair(m, n, k, seed):
+    rng = np.random.default_rng(seed)
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    xq, sx = oracle.rotate_quantize_act(xb)
+    wp, ws = oracle.quantize_weight_convrot(w)
+    return xb, xq, sx, wp, ws
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_CASES)
+def test_gemm_acc_i32_bitexact(ck, m, n, k):
+    _, xq, _, wp, _ = _quantised_pair(m, n, k, 400 + m + n)
+    acc = host(ck.gemm_w4a4_acc_i32(torch.from_numpy(xq).cuda(), torch.from_numpy(wp).cuda()))
+    assert np.array_equal(acc, oracle.gemm_acc(xq, wp, k, bits=4))
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_CASES)
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear_w4a4(ck, m, n, k, with_bias):
+    _, xq, sx, wp, ws = _quantised_pair(m, n, k, 500 + m + n)
+    bias = np.random.default_rng(1).standard_normal(n).astype(np.float32) if with_bias else None
+    y = ck.linear_w4a4(torch.from_numpy(xq).cuda(), torch.from_numpy(sx).cuda(), torch.from_numpy(wp).cuda(),
+                       torch.from_numpy(ws).cuda(), None if bias is None else torch.from_numpy(bias).cuda())
+    acc = oracle.gemm_acc(xq, wp, k)
+    y_ref = oracle.epilogue_bf16(acc, sx, ws, bias)
+    atol = None
+    if bias is not None:
+        # fp32 epilogue: a few fp32 roundings of the two summands, then bf16
+        terms = np.abs(acc * sx.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]) + np.abs(bias)
+        atol = 2.0 ** -21 * terms
+    assert_bf16_close(bf16_host_bits(y), y_ref, atol=atol)
+
+
+def test_linear_zero_rows_and_columns(ck):
+    m, n, k = 40, 72, 512
+    xb = act(m, k, 7)
+    xb[3] = 0
+    rng = np.random.default_rng(8)
+    w = workloads.make_weight(rng, n, k)
+    w[5] = 0
+    wp, ws = oracle.quantize_weight_convrot(w)
+    y = ck.w4a4_linear(dev_bf16(xb), torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda())
+    yb = bf16_host_bits(y)
+    assert not yb[3].any() and not yb[:, 5].any()
+    assert_bf16_close(yb, oracle.linear_w4a4(xb, wp, ws))
+
+
+@pytest.mark.parametrize("k", [256, 3072, 12288, 131072])
+def test_accumulator_bound_is_reached_exactly(ck, k):
+    # codes +7 everywhere (byte 0x77) against +7 / -7 (0x99) rows: acc = +-49 K
+    m, n = 16, 8
+    a = torch.full((m, k // 2), 0x77, dtype=torch.int8, device="cuda")
+    b = torch.full((n, k // 2), 0x77, dtype=torch.int8, device="cuda")
+    b[1::2] = torch.tensor(0x99 - 256, dtype=torch.int8)
+    acc = host(ck.gemm_w4a4_acc_i32(a, b))
+    expect = np.where(np.arange(n) % 2 == 0, 49 * k, -49 * k)
+    assert np.array_equal(acc, np.broadcast_to(expect, (m, n)))
+
+
+def test_repeatable_bitwise(ck):
+    xb, xq, sx, wp, ws = _quantised_pair(512, 384, 1024, 9)
+    args = [torch.from_numpy(a).cuda() for a in (xq, sx, wp, ws)]
+    outs = [bf16_host_bits(ck.linear_w4a4(*args)) for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+# --------------------------------------------------------------------------
+# Grouped W4A8
+
+
+@pytest.mark.parametrize("n,k,group", [(64, 256, 128), (1152, 512, 128), (100, 3072, 128), (48, 1024, 16),
+                                       (48, 1024, 32), (48, 1024, 64), (48, 2048, 256)])
+def test_w4a8_decode_bitexact(ck, n, k, group):
+    rng = np.random.default_rng(600 + n)
+    w = workloads.make_weight(rng, n, k)
+    w[0] = 0
+    wp, gs = oracle.quantize_weight_convrot(w, group=group)
+    w8, sr = ck.dequant_w4a8_grouped(torch.from_numpy(wp).cuda(), torch.from_numpy(gs).cuda(), group)
+    w8_ref, sr_ref = oracle.decode_w4a8(wp, gs, group)
+    assert np.array_equal(host(sr).view(np.uint32), sr_ref.view(np.uint32))
+    assert np.array_equal(host(w8), w8_ref)
+
+
+def test_w4a8_decode_chunks_bitexact(ck):
+    rng = np.random.default_rng(601)
+    n, k = 1152, 512
+    wp, gs = oracle.quantize_weight_convrot(workloads.make_weight(rng, n, k), group=128)
+    wpd, gsd = torch.from_numpy(wp).cuda(), torch.from_numpy(gs).cuda()
+    full8, fulls = oracle.decode_w4a8(wp, gs, 128)
+    for n0 in range(0, n, 384):
+        w8, sr = ck.dequant_w4a8_grouped(wpd, gsd, 128, n0, min(384, n - n0))
+        assert np.array_equal(host(w8), full8[n0:n0 + 384])
+        assert np.array_equal(host(sr), fulls[n0:n0 + 384])
+
+
+@pytest.mark.parametrize("m,n,k,chunk", [(8, 1152, 512, 384), (8, 1152, 512, 400), (1, 1152, 512, -1),
+                                         (64, 1500, 1024, 0), (100, 300, 512, 0), (16, 5120, 5120, 0)])
+def test_w4a8_linear_chunked_equals_single_pass_and_oracle(ck, m, n, k, chunk):
+    rng = np.random.default_rng(700 + m + n)
+    xb = workloads.make_activations(rng, m, k)
+    wp, gs = oracle.quantize_weight_convrot(workloads.make_weight(rng, n, k), group=128)
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    wpd, gsd = torch.from_numpy(wp).cuda(), torch.from_numpy(gs).cuda()
+    y = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, 128, chunk))
+    y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, 128, -1))
+    assert np.array_equal(y, y1)
+    assert_bf16_close(y, oracle.linear_w4a8_grouped(xb, wp, gs))
+
+
+# --------------------------------------------------------------------------
+# Full-size layers, in the launch configuration the benchmark times
+
+
+def _sample_rows(m, count, seed):
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, count, replace=False)]))
+    return rows
+
+
+@pytest.mark.parametrize("name", ["square_3072", "up_3072_12288", "down_12288_3072", "qkv_3x3072"])
+def test_full_size_layer(ck, name):
+    cfg = workloads.WORKLOADS[name]
+    lay = workloads.make_layer(seed=0, **cfg)
+    m, k, n = lay.m, lay.k, lay.n
+    xd = dev_bf16(lay.x_bf16)
+    xq, sx = ck.rotate_quantize_act(xd, 128, 4)
+    xq_ref, sx_ref = oracle.rotate_quantize_act(lay.x_bf16)
+    assert np.array_equal(host(sx).view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(host(xq), xq_ref)
+    rows = _sample_rows(m, 30, 1)
+    for w in lay.weights:
+        wp, ws = ck.quantize_weight_convrot(torch.from_numpy(w).cuda(), 128, 0)
+        wp_ref, ws_ref = oracle.quantize_weight_convrot(w)
+        assert np.array_equal(host(ws).view(np.uint32), ws_ref.view(np.uint32))
+        assert np.array_equal(host(wp), wp_ref)
+        y = bf16_host_bits(ck.linear_w4a4(xq, sx, wp, ws))
+        acc = host(ck.gemm_w4a4_acc_i32(xq, wp))
+        acc_ref = oracle.gemm_acc(np.ascontiguousarray(xq_ref[rows]), wp_ref, k)
+        assert np.array_equal(acc[rows], acc_ref)
+        assert np.abs(acc).max() <= 49 * k
+        assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], ws_ref))
+
+
+@pytest.mark.parametrize("m", [1, 8, 16, 64])
+@pytest.mark.parametrize("n,k", [(12288, 3072), (5120, 5120)])
+def test_skinny_layers(ck, m, n, k):
+    rng = np.random.default_rng(800 + m)
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    wp, ws = oracle.quantize_weight_convrot(w)
+    y = bf16_host_bits(ck.w4a4_linear(dev_bf16(xb), torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda()))
+    assert_bf16_close(y, oracle.linear_w4a4(xb, wp, ws))
+    wpg, gs = oracle.quantize_weight_convrot(w, group=128)
+    xq8, sx8 = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    y8 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx8, torch.from_numpy(wpg).cuda(), torch.from_numpy(gs).cuda()))
+    assert_bf16_close(y8, oracle.linear_w4a8_grouped(xb, wpg, gs))
