@@ -245,6 +245,205 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
     }
 }
 
+// Large-tile kernel: BM x BN tile, WGM x WGN wavefronts, one workgroup per CU.
+// Operands are staged global -> LDS with buffer_load ... lds (no VGPR round
+// trip); the buffer range of each operand ends at the last valid row of the
+// tile, so rows past M or N read as zeros. Two LDS stages of 128 bytes per
+// row; the loads for stage s+1 are issued right after the barrier that opens
+// stage s and land while stage s is multiplied. Within a stage, the fragments
+// are read from LDS per 64-byte half; two wavefronts per SIMD hide the LDS
+// latency of one behind the MFMAs of the other.
+template <bool S4, int BM, int BN, int WGM, int WGN, int WPE, bool OUT_I32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
+                          amdgpu_waves_per_eu(WPE, WPE))) void
+gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
+                const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes,
+                int ksteps, void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WTM = BM / WGM;
+    constexpr int WTN = BN / WGN;
+    constexpr int FM = WTM / 16;
+    constexpr int FN = WTN / 16;
+    constexpr int STAGE = (BM + BN) * kRowBytes;
+    constexpr int NINSTR = (BM + BN) / 8;  // one wave instruction fills 8 rows x 128 bytes
+    constexpr int PER_WAVE = (NINSTR + NW - 1) / NW;
+    static_assert(BM % 8 == 0 && BN % 8 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "bad tile");
+    __shared__ __attribute__((aligned(1024))) uint4 smem[2 * STAGE / 16];
+
+    int tile = blockIdx.x;
+    if ((tiles_total & 7) == 0) tile = (tile & 7) * (tiles_total >> 3) + (tile >> 3);
+    const int tm = tile / tiles_n;
+    const int tn = tile - tm * tiles_n;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN;
+    const int wn = wave - wm * WGN;
+
+    const int rows_a = min(BM, M - m0);
+    const int rows_b = min(BN, N - n0);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(A) + (int64_t)m0 * row_bytes, (short)0, rows_a * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(B) + (int64_t)n0 * row_bytes, (short)0, rows_b * row_bytes, 0x00020000);
+
+    // Lane l of a staging instruction fills LDS slot l of an 8-row group:
+    // row 8q + (l >> 3), physical chunk l & 7, holding logical chunk
+    // (l & 7) ^ (row & 7) of that row.
+    const uint32_t lane_off =
+        (uint32_t)(lane >> 3) * (uint32_t)row_bytes + (uint32_t)(((lane & 7) ^ (lane >> 3)) * 16);
+    auto issue_stage = [&](uint4 *dst, int s) {
+        char *base = reinterpret_cast<char *>(dst);
+#pragma unroll
+        for (int t = 0; t < PER_WAVE; ++t) {
+            const int q = t * NW + wave;
+            if (q < NINSTR) {
+                const bool is_a = q < BM / 8;
+                const int qr = is_a ? q : q - BM / 8;
+                // per-lane part in the VGPR offset, per-instruction part in soffset
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    is_a ? ra : rb, (__attribute__((address_space(3))) void *)(base + q * 1024), 16, lane_off,
+                    (uint32_t)(qr * 8) * (uint32_t)row_bytes + (uint32_t)(s * kRowBytes), 0, 0);
+            }
+        }
+    };
+
+    v4i acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    // LDS byte offsets of this lane's fragment rows (row & 7 == lane & 7).
+    const int frow = lane & 15;
+    const int fgrp = lane >> 4;
+    const int a_row0 = (wm * WTM + frow) * kRowBytes;
+    const int b_row0 = (BM + wn * WTN + frow) * kRowBytes;
+    const int chunk_off0 = ((0 * 4 + fgrp) ^ (lane & 7)) * 16;
+    const int chunk_off1 = ((1 * 4 + fgrp) ^ (lane & 7)) * 16;
+
+    auto compute_stage = [&](const uint4 *src) {
+        const char *base = reinterpret_cast<const char *>(src);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // keep each half's fragments live only within the half
+            __builtin_amdgcn_sched_barrier(0);
+            const int coff = h ? chunk_off1 : chunk_off0;
+            uint4 xa[FM], wb[FN];
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                wb[i] = *reinterpret_cast<const uint4 *>(base + b_row0 + i * 16 * kRowBytes + coff);
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                xa[j] = *reinterpret_cast<const uint4 *>(base + a_row0 + j * 16 * kRowBytes + coff);
+            if constexpr (S4) {
+                v4i wl[FN], wh[FN];
+#pragma unroll
+                for (int i = 0; i < FN; ++i) {
+                    wl[i] = widen_lo(wb[i]);
+                    wh[i] = widen_hi(wb[i]);
+                }
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const v4i xl = widen_lo(xa[j]);
+                    const v4i xh = widen_hi(xa[j]);
+#pragma unroll
+                    for (int i = 0; i < FN; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl[i], xl, acc[i][j], 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < FN; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh[i], xh, acc[i][j], 0, 0, 0);
+                    // one widened activation fragment live at a time
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int i = 0; i < FN; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(wb[i]), as_v4i(xa[j]), acc[i][j],
+                                                                          0, 0, 0);
+            }
+        }
+    };
+
+    // The stage body issues the DMA for stage s+1 into one LDS half and reads
+    // stage s from the other. Passing the two halves as __restrict__ pointers
+    // of an inlined function tells the compiler they never alias, so it does
+    // not make the fragment reads wait for the DMA.
+    auto body = [&](uint4 *__restrict__ dst, const uint4 *__restrict__ src, int s) {
+        if (s + 1 < ksteps) issue_stage(dst, s + 1);
+        compute_stage(src);
+    };
+    issue_stage(smem, 0);
+    for (int s = 0; s < ksteps; ++s) {
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's stage-s loads have landed
+        __syncthreads();                // ... and every thread's; stage s-1 is no longer read
+        uint4 *cur = smem + (s & 1) * (STAGE / 16);
+        uint4 *nxt = smem + ((s + 1) & 1) * (STAGE / 16);
+        body(nxt, cur, s);
+    }
+
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * WTM + j * 16 + frow;
+        if (m >= M) continue;
+        const float sam = OUT_I32 ? 0.0f : sa[m];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const int nb = n0 + wn * WTN + i * 16 + 4 * fgrp;
+            if (nb >= N) continue;
+            int a4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a4[r] = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+            if constexpr (OUT_I32) {
+                int32_t *yr = reinterpret_cast<int32_t *>(Y) + (int64_t)m * ldy + nb;
+                if (nb + 3 < N) {
+                    *reinterpret_cast<int4 *>(yr) = make_int4(a4[0], a4[1], a4[2], a4[3]);
+                } else {
+                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = a4[r];
+                }
+            } else {
+                uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + nb;
+                uint16_t o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = nb + r < N ? nb + r : N - 1;
+                    float v = ((float)a4[r] * sam) * sb[n];
+                    if (bias) v = v + bias[n];
+                    o[r] = f32_to_bf16(v);
+                }
+                if (nb + 3 < N) {
+                    *reinterpret_cast<uint2 *>(yr) =
+                        make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+                } else {
+                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = o[r];
+                }
+            }
+        }
+    }
+}
+
+template <bool S4, int BM, int BN, int WGM, int WGN, int WPE>
+hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
+                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+    const int64_t row_bytes = S4 ? k / 2 : k;
+    const int ksteps = (int)(row_bytes / kRowBytes);
+    const int tiles_m = (int)((m + BM - 1) / BM);
+    const int tiles_n = (int)((n + BN - 1) / BN);
+    const int total = tiles_m * tiles_n;
+    dim3 grid((unsigned)total), block(64 * WGM * WGN);
+    if (out_i32)
+        gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, true><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total);
+    else
+        gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total);
+    return hipGetLastError();
+}
+
 template <bool S4, int BM, int BN, int WAVES_M>
 hipError_t launch_cfg(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                       int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
@@ -268,7 +467,11 @@ hipError_t launch_s(const int8_t *a, const int8_t *b, const float *sa, const flo
                     int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
     if (m <= 16) return launch_cfg<S4, 16, 64, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
     if (m <= 64) return launch_cfg<S4, 64, 64, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    return launch_cfg<S4, 128, 128, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    // large shapes: one 288 x 192 tile per CU when that fills the chip
+    const int64_t big_tiles = ((m + 287) / 288) * ((n + 191) / 192);
+    if (big_tiles >= 192)
+        return launch_big<S4, 288, 192, 2, 4, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    return launch_big<S4, 128, 128, 2, 2, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
 }
 
 }  // namespace
