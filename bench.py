@@ -87,6 +87,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's CPU sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device-to-device copy (scales the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -96,6 +98,15 @@ def main() -> int:
 
     import torch
     import int4_w4a4_quantized_amd as ck
+
+    if args.copy_calibration:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": src.numel(), "launches": max(args.steps, 1)}))
+        return 0
 
     cfg = workloads.WORKLOADS["square_3072"]
     m, k, n = cfg["m"], cfg["k"], cfg["n"]
@@ -159,7 +170,7 @@ def main() -> int:
         "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_kernel<s4, 128x128> (W4A4 GEMM + epilogue)",
+            "kernel": "gemm_big_kernel<s4, 288x192 tile, 8 waves> (W4A4 GEMM + rank-one epilogue)",
             "achieved": round(gemm_tops, 2),
             "peak": INT8_PEAK_TOPS,
             "unit": "TOP/s",

@@ -324,47 +324,88 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
     const int chunk_off0 = ((0 * 4 + fgrp) ^ (lane & 7)) * 16;
     const int chunk_off1 = ((1 * 4 + fgrp) ^ (lane & 7)) * 16;
 
+    // The epilogue's scales, fetched before the K loop so their latency hides.
+    float sa_r[FM], sb_r[FN][4];
+    if constexpr (!OUT_I32) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) sa_r[j] = sa[min(m0 + wm * WTM + j * 16 + frow, M - 1)];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sb_r[i][r] = sb[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
+    }
+
+    // One stage = two 64-byte halves. Per half: the FN weight fragments are
+    // read and widened once. The activation fragments flow through a
+    // three-deep pipeline: while the MFMAs of fragment j run, fragment j+1 is
+    // widened and fragment j+2 is read from LDS. The scheduling groups put two
+    // VALU instructions between consecutive MFMAs, so the widening of the next
+    // fragment hides under the matrix-core time of the current one.
     auto compute_stage = [&](const uint4 *src) {
         const char *base = reinterpret_cast<const char *>(src);
+        auto xptr = [&](int j, int coff) {
+            return reinterpret_cast<const uint4 *>(base + a_row0 + j * 16 * kRowBytes + coff);
+        };
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            // keep each half's fragments live only within the half
             __builtin_amdgcn_sched_barrier(0);
             const int coff = h ? chunk_off1 : chunk_off0;
-            uint4 xa[FM], wb[FN];
+            uint4 wb[FN];
 #pragma unroll
             for (int i = 0; i < FN; ++i)
                 wb[i] = *reinterpret_cast<const uint4 *>(base + b_row0 + i * 16 * kRowBytes + coff);
-#pragma unroll
-            for (int j = 0; j < FM; ++j)
-                xa[j] = *reinterpret_cast<const uint4 *>(base + a_row0 + j * 16 * kRowBytes + coff);
             if constexpr (S4) {
+                uint4 xraw = *xptr(0, coff);
+                uint4 xnext = FM > 1 ? *xptr(1, coff) : xraw;
                 v4i wl[FN], wh[FN];
 #pragma unroll
                 for (int i = 0; i < FN; ++i) {
                     wl[i] = widen_lo(wb[i]);
                     wh[i] = widen_hi(wb[i]);
                 }
+                v4i xl = widen_lo(xraw);
+                v4i xh = widen_hi(xraw);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < FM; ++j) {
-                    const v4i xl = widen_lo(xa[j]);
-                    const v4i xh = widen_hi(xa[j]);
+                    v4i nl = xl, nh = xh;
+                    if (j + 1 < FM) {
+                        const uint4 cur = xnext;
+                        if (j + 2 < FM) xnext = *xptr(j + 2, coff);
+                        nl = widen_lo(cur);
+                        nh = widen_hi(cur);
+                    }
 #pragma unroll
                     for (int i = 0; i < FN; ++i)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl[i], xl, acc[i][j], 0, 0, 0);
 #pragma unroll
                     for (int i = 0; i < FN; ++i)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh[i], xh, acc[i][j], 0, 0, 0);
-                    // one widened activation fragment live at a time
+                    if (j + 1 < FM) {
+                        // the LDS read first: it has the whole iteration to land
+                        if (j + 2 < FM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                        for (int t = 0; t < 2 * FN; ++t) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU
+                        }
+                    }
                     __builtin_amdgcn_sched_barrier(0);
+                    xl = nl;
+                    xh = nh;
                 }
             } else {
+                uint4 xnext = *xptr(0, coff);
 #pragma unroll
-                for (int j = 0; j < FM; ++j)
+                for (int j = 0; j < FM; ++j) {
+                    const uint4 xcur = xnext;
+                    if (j + 1 < FM) xnext = *xptr(j + 1, coff);
 #pragma unroll
                     for (int i = 0; i < FN; ++i)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(wb[i]), as_v4i(xa[j]), acc[i][j],
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(wb[i]), as_v4i(xcur), acc[i][j],
                                                                           0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     };
@@ -386,41 +427,69 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
         body(nxt, cur, s);
     }
 
+    if constexpr (OUT_I32) {
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * WTM + j * 16 + frow;
-        if (m >= M) continue;
-        const float sam = OUT_I32 ? 0.0f : sa[m];
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + wm * WTM + j * 16 + frow;
+            if (m >= M) continue;
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int nb = n0 + wn * WTN + i * 16 + 4 * fgrp;
-            if (nb >= N) continue;
-            int a4[4];
+            for (int i = 0; i < FN; ++i) {
+                const int nb = n0 + wn * WTN + i * 16 + 4 * fgrp;
+                if (nb >= N) continue;
+                int a4[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) a4[r] = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-            if constexpr (OUT_I32) {
+                for (int r = 0; r < 4; ++r) a4[r] = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
                 int32_t *yr = reinterpret_cast<int32_t *>(Y) + (int64_t)m * ldy + nb;
                 if (nb + 3 < N) {
                     *reinterpret_cast<int4 *>(yr) = make_int4(a4[0], a4[1], a4[2], a4[3]);
                 } else {
                     for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = a4[r];
                 }
-            } else {
-                uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + nb;
+            }
+        }
+    } else {
+        // Rank-one epilogue, staged through LDS so that the tile leaves as
+        // whole rows: y = bf16((acc * sa[m]) * sb[n] (+ bias[n])) into a
+        // [BM][BN + 8] bf16 tile, then 16-byte row-contiguous stores.
+        constexpr int LD = BN + 8;
+        static_assert(BM * LD * 2 <= 2 * STAGE, "output tile does not fit in LDS");
+        uint16_t *tile_lds = reinterpret_cast<uint16_t *>(smem);
+        __syncthreads();  // every wave has finished reading the last stage
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int ml = wm * WTM + j * 16 + frow;
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int nl = wn * WTN + i * 16 + 4 * fgrp;
                 uint16_t o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = nb + r < N ? nb + r : N - 1;
-                    float v = ((float)a4[r] * sam) * sb[n];
-                    if (bias) v = v + bias[n];
+                    const int a = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+                    float v = ((float)a * sa_r[j]) * sb_r[i][r];
+                    if (bias) v = v + bias[min(n0 + nl + r, N - 1)];
                     o[r] = f32_to_bf16(v);
                 }
-                if (nb + 3 < N) {
-                    *reinterpret_cast<uint2 *>(yr) =
-                        make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-                } else {
-                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = o[r];
-                }
+                *reinterpret_cast<uint2 *>(tile_lds + ml * LD + nl) =
+                    make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+        for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+            const int r = c / CPR;
+            const int cn = (c - r * CPR) * 8;
+            const int m = m0 + r;
+            const int n = n0 + cn;
+            if (m >= M || n >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile_lds + r * LD + cn);
+            uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + n;
+            if (n + 7 < N && ((reinterpret_cast<uintptr_t>(yr) & 15) == 0)) {
+                *reinterpret_cast<uint4 *>(yr) = v;
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (n + t < N) yr[t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
             }
         }
     }
