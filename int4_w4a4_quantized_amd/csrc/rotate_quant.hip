@@ -7,7 +7,7 @@
 // pairs, low nibble first, with one fp32 scale per row):
 //   r = x * blockdiag(H_b, ..., H_b) * fp32(1/sqrt(b))     (fp32, b = rot_block)
 //   s = absmax(r) / qmax                                  (fp32 divide)
-//   q = clamp(rint(r / s), -qmax, qmax)                    (fp32 divide, ties to even)
+//   q = clamp(rint(r / s), -qmax, qmax)                    (fp32 quotient, ties to even)
 // with H_b the Sylvester Hadamard matrix and the butterflies taken with
 // ascending stride, so the fp32 rotation is one fixed sequence of roundings.
 //
@@ -16,9 +16,33 @@
 // owned by thread c mod blockDim. A Hadamard block of b elements is b/16
 // consecutive chunks, which sit in b/16 consecutive lanes of one wavefront
 // (blockDim is a multiple of 64 and b <= 1024). Butterfly strides 1..8 are
-// inside a lane; strides 16..b/2 pair lane L with lane L ^ (stride/16).
-// The whole row stays in VGPRs between the rotation and the quantisation, so
-// HBM is read once and written once.
+// inside a lane; stride 16*m pairs lane L with lane L ^ m. The whole row stays
+// in VGPRs between the rotation and the quantisation, so HBM is read once and
+// written once.
+//
+// Cross-lane butterflies with one instruction per element. A butterfly keeps
+// a + b in the lower lane and a - b in the upper one. Each lane instead keeps
+// u = sigma * v for a known sign sigma and computes u' = u + k * u_partner
+// with k = -1 in the upper lane and +1 in the lower one: one fused
+// multiply-add whose product is exact (k = +-1), so u' is the correctly
+// rounded sum, equal to sigma' times the butterfly output because IEEE
+// round-to-nearest commutes with negation. After all cross-lane stages,
+// sigma = (-1)^popcount(lane & (b/16 - 1)); it is folded into the final
+// multiply by the normalisation constant, so the rotated values are bitwise
+// those of the plain butterflies (up to the sign of an exact zero). The
+// partner value comes through DPP (strides 16 and 32) or ds_swizzle (64, 128,
+// 256) or ds_bpermute (512).
+//
+// The quotient r / s without a divide per element. With y = RN(1/s) computed
+// once per row by the IEEE divide, q0 = RN(r y), e = fma(-q0, s, r) (exact),
+// q1 = fma(e, y, q0) is the correctly rounded r / s (Markstein's division
+// theorem); it is used when s is a normal number in [2^-120, 2^120], where no
+// step overflows or underflows, and the IEEE divide is used otherwise.
+// Rounding to the nearest integer (ties to even) is one fp32 addition of
+// 1.5 * 2^23: for |q1| < 2^22 the sum's bit pattern is 0x4B400000 + rint(q1),
+// whose low byte is the two's-complement int8 code and whose low nibble is
+// the int4 code. |q1| <= qmax (1 + 2^-23) when s is normal, so no clamp is
+// needed on that path.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,7 +51,7 @@
 namespace ck4 {
 namespace {
 
-constexpr int kElems = 16;   // contiguous elements per chunk
+constexpr int kElems = 16;     // contiguous elements per chunk
 constexpr int kMaxChunks = 4;  // chunks per thread: k <= 16 * 256 * 4 = 16384
 constexpr int kThreads = 256;
 
@@ -68,17 +92,38 @@ __device__ __forceinline__ void fwht_in_lane(float v[kElems]) {
     }
 }
 
-// Butterflies with stride 16 * mask, for mask = 1, 2, ..., b/32 (ascending):
-// the lower lane of a pair keeps a + b, the upper keeps a - b.
-__device__ __forceinline__ void fwht_cross_lane(float v[kElems], int lane, int lanes_per_block) {
-    for (int mask = 1; mask < lanes_per_block; mask <<= 1) {
-        const bool upper = (lane & mask) != 0;
-#pragma unroll
-        for (int i = 0; i < kElems; ++i) {
-            float p = __shfl_xor(v[i], mask, 64);
-            v[i] = upper ? (p - v[i]) : (v[i] + p);
-        }
+// The value held by lane L ^ mask.
+template <int MASK>
+__device__ __forceinline__ float partner(float x) {
+    const int xi = __float_as_int(x);
+    int r;
+    if constexpr (MASK == 1) {
+        r = __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    } else if constexpr (MASK == 2) {
+        r = __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+    } else if constexpr (MASK <= 16) {
+        r = __builtin_amdgcn_ds_swizzle(xi, 0x1F | (MASK << 10));  // bitmask mode, xor MASK
+    } else {
+        r = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ MASK) << 2), xi);
     }
+    return __int_as_float(r);
+}
+
+template <int MASK>
+__device__ __forceinline__ void cross_stage(float v[kElems], int lane) {
+    const float k = (lane & MASK) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < kElems; ++i) v[i] = __builtin_fmaf(partner<MASK>(v[i]), k, v[i]);
+}
+
+// All cross-lane stages for a block of lanes_per_block lanes (ascending mask).
+__device__ __forceinline__ void fwht_cross_lane(float v[kElems], int lane, int lanes_per_block) {
+    if (lanes_per_block > 1) cross_stage<1>(v, lane);
+    if (lanes_per_block > 2) cross_stage<2>(v, lane);
+    if (lanes_per_block > 4) cross_stage<4>(v, lane);
+    if (lanes_per_block > 8) cross_stage<8>(v, lane);
+    if (lanes_per_block > 16) cross_stage<16>(v, lane);
+    if (lanes_per_block > 32) cross_stage<32>(v, lane);
 }
 
 __device__ __forceinline__ float wave_max(float a) {
@@ -87,11 +132,19 @@ __device__ __forceinline__ float wave_max(float a) {
     return a;
 }
 
-__device__ __forceinline__ int quant_code(float r, float s, float qmax) {
-    if (s == 0.0f) return 0;
+// Integer code of r / s: the bit pattern whose low byte is the int8 code.
+__device__ __forceinline__ uint32_t code_fast(float r, float s, float y) {
+    const float q0 = r * y;
+    const float e = __builtin_fmaf(-q0, s, r);
+    const float q1 = __builtin_fmaf(e, y, q0);
+    return __float_as_uint(q1 + 12582912.0f);  // 1.5 * 2^23
+}
+
+__device__ __forceinline__ uint32_t code_exact(float r, float s, float qmax) {
+    if (s == 0.0f) return 0u;
     float t = rintf(r / s);
     t = fminf(fmaxf(t, -qmax), qmax);
-    return (int)t;
+    return (uint32_t)(int)t;
 }
 
 // out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation.
@@ -107,6 +160,8 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
     const int nthreads = blockDim.x;
     const int nchunks = k / kElems;
     const TIn *xr = x + (int64_t)row * ldx;
+    // the sign carried by the cross-lane stages, folded into the scale
+    const float c_lane = (__popc(lane & (lanes_per_block - 1)) & 1) ? -c : c;
 
     float v[kMaxChunks][kElems];
     float amax = 0.0f;
@@ -119,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             fwht_cross_lane(v[j], lane, lanes_per_block);
 #pragma unroll
             for (int i = 0; i < kElems; ++i) {
-                v[j][i] = v[j][i] * c;
+                v[j][i] = v[j][i] * c_lane;
                 amax = fmaxf(amax, fabsf(v[j][i]));
             }
         }
@@ -140,6 +195,8 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
         return;
     } else {
         const float qmax = OUT == 0 ? 7.0f : 127.0f;
+        float s_row = 0.0f, y_row = 0.0f;
+        bool fast_row = false;
         if (group == 0) {
             // absmax over the whole row: wavefront reduction, then across waves.
             amax = wave_max(amax);
@@ -147,31 +204,43 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             __syncthreads();
             amax = red[0];
             for (int w = 1; w < nthreads / 64; ++w) amax = fmaxf(amax, red[w]);
+            s_row = amax / qmax;
+            fast_row = s_row >= 0x1p-120f && s_row <= 0x1p120f;
+            y_row = fast_row ? 1.0f / s_row : 0.0f;
+            if (tid == 0) scales[row] = s_row;
         }
 #pragma unroll
         for (int j = 0; j < kMaxChunks; ++j) {
             const int ch = tid + j * nthreads;
             if (ch >= nchunks) continue;
-            float s;
+            uint32_t code[kElems];
             if (group == 0) {
-                s = amax / qmax;
-                if (tid == 0 && j == 0) scales[row] = s;
+                if (fast_row) {
+#pragma unroll
+                    for (int i = 0; i < kElems; ++i) code[i] = code_fast(v[j][i], s_row, y_row);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kElems; ++i) code[i] = code_exact(v[j][i], s_row, qmax);
+                }
             } else {
                 // one scale per `group` elements = group/16 consecutive lanes
+                // (offline weight preparation: the IEEE divide throughout)
                 float gmax = 0.0f;
 #pragma unroll
                 for (int i = 0; i < kElems; ++i) gmax = fmaxf(gmax, fabsf(v[j][i]));
                 for (int off = 1; off < group / kElems; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
-                s = gmax / qmax;
+                const float s = gmax / qmax;
                 const int lanes_per_group = group / kElems;
                 if ((ch % lanes_per_group) == 0) scales[(int64_t)row * (k / group) + ch / lanes_per_group] = s;
+#pragma unroll
+                for (int i = 0; i < kElems; ++i) code[i] = code_exact(v[j][i], s, qmax);
             }
             if constexpr (OUT == 0) {
                 uint32_t w0 = 0, w1 = 0;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) w0 |= (uint32_t)(quant_code(v[j][i], s, qmax) & 0xF) << (4 * i);
+                for (int i = 0; i < 8; ++i) w0 |= (code[i] & 0xFu) << (4 * i);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) w1 |= (uint32_t)(quant_code(v[j][8 + i], s, qmax) & 0xF) << (4 * i);
+                for (int i = 0; i < 8; ++i) w1 |= (code[8 + i] & 0xFu) << (4 * i);
                 int8_t *o = reinterpret_cast<int8_t *>(out) + (int64_t)row * ldo + (int64_t)ch * (kElems / 2);
                 *reinterpret_cast<uint2 *>(o) = make_uint2(w0, w1);
             } else {
@@ -180,8 +249,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
                 for (int d = 0; d < 4; ++d) {
                     w[d] = 0;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        w[d] |= (uint32_t)(quant_code(v[j][4 * d + i], s, qmax) & 0xFF) << (8 * i);
+                    for (int i = 0; i < 4; ++i) w[d] |= (code[4 * d + i] & 0xFFu) << (8 * i);
                 }
                 int8_t *o = reinterpret_cast<int8_t *>(out) + (int64_t)row * ldo + (int64_t)ch * kElems;
                 *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
