@@ -54,6 +54,8 @@ namespace {
 constexpr int kElems = 16;     // contiguous elements per chunk
 constexpr int kMaxChunks = 4;  // chunks per thread: k <= 16 * 256 * 4 = 16384
 constexpr int kThreads = 256;
+// The kernel is instantiated per chunks-per-thread count NCH (1..4), so a row
+// of K <= 4096 keeps 16 values per lane in VGPRs and the occupancy stays high.
 
 __device__ __forceinline__ void load_chunk(const uint16_t *p, float v[kElems]) {
     const uint4 *q = reinterpret_cast<const uint4 *>(p);
@@ -148,7 +150,7 @@ __device__ __forceinline__ uint32_t code_exact(float r, float s, float qmax) {
 }
 
 // out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation.
-template <typename TIn, int OUT>
+template <typename TIn, int OUT, int NCH>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__restrict__ x, int64_t ldx, int k,
                                                                   int lanes_per_block, float c, int group,
                                                                   void *__restrict__ out, int64_t ldo,
@@ -163,10 +165,10 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
     // the sign carried by the cross-lane stages, folded into the scale
     const float c_lane = (__popc(lane & (lanes_per_block - 1)) & 1) ? -c : c;
 
-    float v[kMaxChunks][kElems];
+    float v[NCH][kElems];
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kMaxChunks; ++j) {
+    for (int j = 0; j < NCH; ++j) {
         const int ch = tid + j * nthreads;
         if (ch < nchunks) {
             load_chunk(xr + (int64_t)ch * kElems, v[j]);
@@ -183,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
     if constexpr (OUT == 2) {
         float *o = reinterpret_cast<float *>(out) + (int64_t)row * ldo;
 #pragma unroll
-        for (int j = 0; j < kMaxChunks; ++j) {
+        for (int j = 0; j < NCH; ++j) {
             const int ch = tid + j * nthreads;
             if (ch < nchunks) {
                 float4 *d = reinterpret_cast<float4 *>(o + (int64_t)ch * kElems);
@@ -210,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             if (tid == 0) scales[row] = s_row;
         }
 #pragma unroll
-        for (int j = 0; j < kMaxChunks; ++j) {
+        for (int j = 0; j < NCH; ++j) {
             const int ch = tid + j * nthreads;
             if (ch >= nchunks) continue;
             uint32_t code[kElems];
@@ -258,30 +260,45 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
     }
 }
 
+template <typename TIn, int OUT>
+void launch_out(const TIn *x, int nch, dim3 grid, dim3 block, int64_t ldx, int k, int lanes_per_block, float c,
+                int group, void *out, int64_t ldo, float *scales, hipStream_t stream) {
+    switch (nch) {
+    case 1:
+        rotate_quant_kernel<TIn, OUT, 1><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
+                                                                      scales);
+        break;
+    case 2:
+        rotate_quant_kernel<TIn, OUT, 2><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
+                                                                      scales);
+        break;
+    case 3:
+        rotate_quant_kernel<TIn, OUT, 3><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
+                                                                      scales);
+        break;
+    default:
+        rotate_quant_kernel<TIn, OUT, 4><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
+                                                                      scales);
+        break;
+    }
+}
+
 template <typename TIn>
 hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int rot_block, int out_kind, int group,
                         void *out, int64_t ldo, float *scales, hipStream_t stream) {
     const int nchunks = (int)(k / kElems);
-    const int per_thread = (nchunks + kThreads - 1) / kThreads;
+    const int per_thread = (nchunks + kThreads - 1) / kThreads;  // 1..kMaxChunks
     int threads = (nchunks + per_thread - 1) / per_thread;
     threads = (threads + 63) / 64 * 64;
     const float c = (float)(1.0 / __builtin_sqrt((double)rot_block));
     const int lanes_per_block = rot_block / kElems;
     dim3 grid((unsigned)rows), block((unsigned)threads);
-    switch (out_kind) {
-    case 0:
-        rotate_quant_kernel<TIn, 0><<<grid, block, 0, stream>>>(x, ldx, (int)k, lanes_per_block, c, group, out,
-                                                                 ldo, scales);
-        break;
-    case 1:
-        rotate_quant_kernel<TIn, 1><<<grid, block, 0, stream>>>(x, ldx, (int)k, lanes_per_block, c, group, out,
-                                                                 ldo, scales);
-        break;
-    default:
-        rotate_quant_kernel<TIn, 2><<<grid, block, 0, stream>>>(x, ldx, (int)k, lanes_per_block, c, group, out,
-                                                                 ldo, scales);
-        break;
-    }
+    if (out_kind == 0)
+        launch_out<TIn, 0>(x, per_thread, grid, block, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales, stream);
+    else if (out_kind == 1)
+        launch_out<TIn, 1>(x, per_thread, grid, block, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales, stream);
+    else
+        launch_out<TIn, 2>(x, per_thread, grid, block, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales, stream);
     return hipGetLastError();
 }
 
