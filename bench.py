@@ -81,6 +81,46 @@ def cpu_baseline(m: int, k: int, n: int, rows: int, reps: int = 3) -> dict:
     }
 
 
+def skinny_sweep(ck, torch, args) -> int:
+    """Memory-bound decode shapes. Each case replays a graph of 32 launches,
+    each on a different weight copy (32 copies exceed the 256 MB Infinity
+    Cache), and reports GB/s on the algorithmic bytes of one launch."""
+    dev = torch.device("cuda:0")
+    copies = 32
+    for n, k in workloads.SKINNY_NK:
+        rng = np.random.default_rng(1)
+        wts = []
+        for _ in range(copies):
+            w = torch.from_numpy(workloads.make_weight(rng, n, k)).to(dev)
+            wts.append(ck.quantize_weight_convrot(w, 128, 0))
+            del w
+        for m in workloads.SKINNY_M:
+            x = torch.from_numpy(workloads.make_activations(rng, m, k).view(np.int16)).view(torch.bfloat16).to(dev)
+            xq, sx = ck.rotate_quantize_act(x, 128, 4)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(copies):
+                    ck.linear_w4a4(xq, sx, wts[c][0], wts[c][1], None, out=y)
+            for _ in range(max(args.warmup // 10, 1)):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = max(args.steps // 20, 2)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            byts = n * k // 2 + 4 * n + m * k // 2 + 4 * m + 2 * m * n
+            print(json.dumps({"case": f"w4a4 skinny m={m} n={n} k={k}", "us_per_launch_graph": round(us, 3),
+                              "algorithmic_bytes": byts, "GBps": round(byts / us / 1e3, 1),
+                              "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +129,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=4608, help="rows of the oracle's CPU sample (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device-to-device copy (scales the HBM byte counters)")
+    ap.add_argument("--skinny", action="store_true",
+                    help="run the skinny-M sweep (M in 1, 8, 16, 64; N,K = 12288,3072 and 5120,5120) instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -107,6 +149,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_per_launch": src.numel(), "launches": max(args.steps, 1)}))
         return 0
+
+    if args.skinny:
+        return skinny_sweep(ck, torch, args)
 
     cfg = workloads.WORKLOADS["square_3072"]
     m, k, n = cfg["m"], cfg["k"], cfg["n"]

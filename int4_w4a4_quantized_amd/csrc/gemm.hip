@@ -513,6 +513,188 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
     return hipGetLastError();
 }
 
+// Skinny kernel (M <= 64): bound by streaming the weight from HBM. A
+// workgroup owns 16*FNW weight rows; its KS wavefronts split K between them.
+// Each wavefront issues every load of its K range up front, straight from
+// global memory into VGPRs in the MFMA operand layout (lane l: row l & 15,
+// 16 bytes at offset 16 * (l >> 4) of each 64-byte half of a 128-byte k-slab,
+// so a step reads whole cache lines of 16 rows), widens them and
+// runs the same s4 x s4 MFMAs as the large kernels. The KS partial
+// accumulators are summed through LDS and one wavefront runs the epilogue.
+template <bool S4, int FM, int FNW, int KS, int MAXS, bool OUT_I32>
+__global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
+    const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int steps,
+    void *__restrict__ Y, int64_t ldy) {
+    constexpr int SLAB = 128;  // bytes of each row per k-step: a whole cache line (256 k for s4, 128 k for s8)
+    __shared__ v4i red[KS - 1][FNW][FM][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * 16 * FNW;
+    const int rows_b = min(16 * FNW, N - n0);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(A), (short)0, M * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(B) + (int64_t)n0 * row_bytes, (short)0, rows_b * row_bytes, 0x00020000);
+    const int frow = lane & 15;
+    const int fgrp = lane >> 4;
+    const uint32_t lane_off = (uint32_t)frow * (uint32_t)row_bytes + (uint32_t)(fgrp * 16);
+
+    const int per_wave = (steps + KS - 1) / KS;
+    const int s_begin = wave * per_wave;
+    const int s_end = min(steps, s_begin + per_wave);
+
+    v4i acc[FNW][FM];
+#pragma unroll
+    for (int i = 0; i < FNW; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+
+    // The wavefront's K range is processed in chunks of up to MAXS k-steps;
+    // every load of a chunk is issued before the first one is consumed.
+    for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
+        v4i wv[MAXS][FNW][SLAB / 64], xv[MAXS][FM][SLAB / 64];
+#pragma unroll
+        for (int t = 0; t < MAXS; ++t) {
+            const int s = s0 + t;
+            if (s < s_end) {
+#pragma unroll
+                for (int h = 0; h < SLAB / 64; ++h) {
+#pragma unroll
+                    for (int i = 0; i < FNW; ++i)
+                        wv[t][i][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                            rb, lane_off + (uint32_t)(i * 16) * (uint32_t)row_bytes, s * SLAB + h * 64, 0);
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        xv[t][j][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                            ra, lane_off + (uint32_t)(j * 16) * (uint32_t)row_bytes, s * SLAB + h * 64, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < MAXS; ++t) {
+            if (s0 + t >= s_end) break;
+#pragma unroll
+            for (int h = 0; h < SLAB / 64; ++h) {
+                if constexpr (S4) {
+#pragma unroll
+                    for (int i = 0; i < FNW; ++i) {
+                        const uint4 wp = make_uint4(wv[t][i][h].x, wv[t][i][h].y, wv[t][i][h].z, wv[t][i][h].w);
+                        const v4i wl = widen_lo(wp), wh = widen_hi(wp);
+#pragma unroll
+                        for (int j = 0; j < FM; ++j) {
+                            const uint4 xp =
+                                make_uint4(xv[t][j][h].x, xv[t][j][h].y, xv[t][j][h].z, xv[t][j][h].w);
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, widen_lo(xp), acc[i][j], 0, 0, 0);
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, widen_hi(xp), acc[i][j], 0, 0, 0);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                        for (int j = 0; j < FM; ++j)
+                            acc[i][j] =
+                                __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[t][i][h], xv[t][j][h], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    if (KS > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) red[wave - 1][i][j][lane] = acc[i][j];
+        }
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll 1
+        for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+            for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] += red[w][i][j][lane];
+    }
+
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = j * 16 + frow;
+        if (m >= M) continue;
+        const float sam = OUT_I32 ? 0.0f : sa[m];
+#pragma unroll
+        for (int i = 0; i < FNW; ++i) {
+            const int nb = n0 + i * 16 + 4 * fgrp;
+            if (nb >= N) continue;
+            int a4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a4[r] = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+            if constexpr (OUT_I32) {
+                int32_t *yr = reinterpret_cast<int32_t *>(Y) + (int64_t)m * ldy + nb;
+                if (nb + 3 < N) {
+                    *reinterpret_cast<int4 *>(yr) = make_int4(a4[0], a4[1], a4[2], a4[3]);
+                } else {
+                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = a4[r];
+                }
+            } else {
+                uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + nb;
+                uint16_t o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = nb + r < N ? nb + r : N - 1;
+                    float v = ((float)a4[r] * sam) * sb[n];
+                    if (bias) v = v + bias[n];
+                    o[r] = f32_to_bf16(v);
+                }
+                if (nb + 3 < N) {
+                    *reinterpret_cast<uint2 *>(yr) =
+                        make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+                } else {
+                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = o[r];
+                }
+            }
+        }
+    }
+}
+
+template <bool S4, int FM, int FNW, int KS, int MAXS>
+hipError_t launch_skinny_cfg(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
+                             int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
+                             hipStream_t stream) {
+    const int64_t row_bytes = S4 ? k / 2 : k;
+    const int steps = (int)(row_bytes / 128);
+    dim3 grid((unsigned)((n + 16 * FNW - 1) / (16 * FNW))), block(64 * KS);
+    if (out_i32)
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, true><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy);
+    else
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy);
+    return hipGetLastError();
+}
+
+// KS: enough wavefronts in flight to keep HBM busy (about 2K or more).
+template <bool S4, int FM, int FNW, int MAXS>
+hipError_t launch_skinny_ks(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
+                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+    const int64_t groups = (n + 16 * FNW - 1) / (16 * FNW);
+    if (groups >= 1024)
+        return launch_skinny_cfg<S4, FM, FNW, 2, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    if (groups >= 512)
+        return launch_skinny_cfg<S4, FM, FNW, 4, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    return launch_skinny_cfg<S4, FM, FNW, 8, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+}
+
+template <bool S4>
+hipError_t launch_skinny(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
+                         int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+    // MAXS keeps a chunk's loads within the register budget of 2 waves/SIMD
+    if (m <= 16) return launch_skinny_ks<S4, 1, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    if (m <= 32) return launch_skinny_ks<S4, 2, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    return launch_skinny_ks<S4, 4, 2, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+}
+
 template <bool S4, int BM, int BN, int WAVES_M>
 hipError_t launch_cfg(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                       int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
@@ -534,8 +716,7 @@ hipError_t launch_cfg(const int8_t *a, const int8_t *b, const float *sa, const f
 template <bool S4>
 hipError_t launch_s(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias, int64_t m,
                     int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
-    if (m <= 16) return launch_cfg<S4, 16, 64, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    if (m <= 64) return launch_cfg<S4, 64, 64, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    if (m <= 64) return launch_skinny<S4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
     // large shapes: one 288 x 192 tile per CU when that fills the chip
     const int64_t big_tiles = ((m + 287) / 288) * ((n + 191) / 192);
     if (big_tiles >= 192)
