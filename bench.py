@@ -81,43 +81,62 @@ def cpu_baseline(m: int, k: int, n: int, rows: int, reps: int = 3) -> dict:
     }
 
 
+def _graph_time_us(torch, launches, reps, warm):
+    """Capture `launches` (a list of callables) in one graph; microseconds per launch."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in launches:
+            f()
+    for _ in range(warm):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+
+
 def skinny_sweep(ck, torch, args) -> int:
-    """Memory-bound decode shapes. Each case replays a graph of 32 launches,
-    each on a different weight copy (32 copies exceed the 256 MB Infinity
-    Cache), and reports GB/s on the algorithmic bytes of one launch."""
+    """Memory-bound decode shapes, W4A4 and grouped W4A8. Each case replays a
+    graph of 32 launches, each on a different weight copy (32 copies exceed
+    the 256 MB Infinity Cache), and reports GB/s on the algorithmic bytes of
+    one launch (the activation is quantised once, outside the timing)."""
     dev = torch.device("cuda:0")
     copies = 32
+    reps = max(args.steps // 20, 2)
+    warm = max(args.warmup // 10, 1)
     for n, k in workloads.SKINNY_NK:
         rng = np.random.default_rng(1)
-        wts = []
+        w4, w8g = [], []
         for _ in range(copies):
             w = torch.from_numpy(workloads.make_weight(rng, n, k)).to(dev)
-            wts.append(ck.quantize_weight_convrot(w, 128, 0))
+            w4.append(ck.quantize_weight_convrot(w, 128, 0))
+            w8g.append(ck.quantize_weight_convrot(w, 128, 128))
             del w
         for m in workloads.SKINNY_M:
             x = torch.from_numpy(workloads.make_activations(rng, m, k).view(np.int16)).view(torch.bfloat16).to(dev)
             xq, sx = ck.rotate_quantize_act(x, 128, 4)
+            xq8, sx8 = ck.rotate_quantize_act(x, 128, 8)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for c in range(copies):
-                    ck.linear_w4a4(xq, sx, wts[c][0], wts[c][1], None, out=y)
-            for _ in range(max(args.warmup // 10, 1)):
-                g.replay()
-            torch.cuda.synchronize()
-            reps = max(args.steps // 20, 2)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(reps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / (reps * copies)
+            us = _graph_time_us(torch, [lambda c=c: ck.linear_w4a4(xq, sx, w4[c][0], w4[c][1], None, out=y)
+                                        for c in range(copies)], reps, warm)
             byts = n * k // 2 + 4 * n + m * k // 2 + 4 * m + 2 * m * n
             print(json.dumps({"case": f"w4a4 skinny m={m} n={n} k={k}", "us_per_launch_graph": round(us, 3),
                               "algorithmic_bytes": byts, "GBps": round(byts / us / 1e3, 1),
                               "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
+            ws_bytes = ck.w4a8_workspace_bytes(m, n, k, 0)
+            ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+            us8 = _graph_time_us(torch, [lambda c=c: ck.linear_w4a8_grouped(xq8, sx8, w8g[c][0], w8g[c][1], 128, 0,
+                                                                            out=y, workspace=ws)
+                                         for c in range(copies)], reps, warm)
+            byts8 = n * k // 2 + 4 * n * (k // 128) + m * k + 4 * m + 2 * m * n
+            print(json.dumps({"case": f"w4a8-grouped skinny m={m} n={n} k={k}", "us_per_launch_graph": round(us8, 3),
+                              "algorithmic_bytes": byts8, "GBps": round(byts8 / us8 / 1e3, 1),
+                              "hbm_frac": round(byts8 / us8 / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
     return 0
 
 

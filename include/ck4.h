@@ -168,17 +168,27 @@ ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8
                            void *stream);
 
 /*
- * Grouped W4A8 linear ([PR #97] What this adds, Chunk sizing): for each chunk
- * of `chunk_cols` output columns, decode that slice of the weight into the
- * workspace and run the int8 GEMM writing the chunk's column slice of y
- * through ldy. The result is bit-identical for every chunk width.
- *
- *   chunk_cols  0: the default policy (chunking only when m <= 64; width =
- *               the device L2 size / k rounded down to 128, clamped to
- *               [1024, 4096]); > 0: that width (a multiple of 16);
- *               < 0: one pass over all n.
- *   workspace   device memory of at least ck4_w4a8_workspace_bytes(...) bytes,
- *               16-byte aligned; its contents are scratch.
+ * Grouped W4A8 linear ([PR #97] What this adds, Chunk sizing): y =
+ * bf16(sum_k qx[m,k] w8[n,k] * x_scales[m] * s_row[n]), with w8 and s_row the
+ * decode of ck4_dequant_w4a8_grouped. Three execution paths give bit-identical
+ * results:
+ *   chunk_cols > 0  the pages' chunked path: for each chunk of `chunk_cols`
+ *                   output columns, decode that slice of the weight into the
+ *                   workspace and run the int8 GEMM writing the chunk's
+ *                   column slice of y through ldy (a multiple of 16);
+ *   chunk_cols < 0  one decode pass over all n, then one int8 GEMM;
+ *   chunk_cols == 0 the default policy: for m <= 64 (env
+ *                   CK4_W4A8_CHUNK_MAX_ROWS) and k % 256 == 0, one fused kernel
+ *                   that decodes in registers (no workspace); otherwise chunks
+ *                   of the device L2 size / k rounded down to 128, clamped to
+ *                   [1024, 4096] (env CK4_W4A8_CHUNK_COLS overrides the width)
+ *                   when m <= 64, or a single pass for larger m.
+ *   x_q8, x_scales  from ck4_rotate_quantize_act(bits = 8).
+ *   w_packed, group_scales  from ck4_quantize_weight_convrot(group = g).
+ *   workspace       device memory of at least ck4_w4a8_workspace_bytes(...)
+ *                   bytes (16-byte aligned; may be NULL when that is 0); its
+ *                   contents are scratch.
+ * Unsupported: k % 128 != 0, g not a power of two in [16, 1024].
  */
 size_t ck4_w4a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t chunk_cols);
 ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,

@@ -202,16 +202,20 @@ def w4a8_workspace_bytes(m: int, n: int, k: int, chunk_cols: int = 0) -> int:
 
 def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128, chunk_cols: int = 0,
                         out=None, workspace=None):
-    """Grouped W4A8 linear (decode per column chunk + int8 GEMM) -> bf16 [m, n]."""
+    """Grouped W4A8 linear -> bf16 [m, n].
+
+    chunk_cols > 0: decode per column chunk + int8 GEMM; < 0: one decode pass
+    + one GEMM; 0: the library's policy (the fused kernel for m <= 64).
+    """
     m, k = x_q8.shape
     n = w_packed.shape[0]
     if out is None:
         out = _out_bf16(m, n, x_q8.device)
     need = w4a8_workspace_bytes(m, n, k, chunk_cols)
-    if workspace is None:
+    if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x_q8.device)
     _check("ck4_linear_w4a8_grouped",
            lib().ck4_linear_w4a8_grouped(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales), m, n, k,
                                          group, _ptr(out), out.stride(0), chunk_cols, _ptr(workspace),
-                                         workspace.numel(), _stream(x_q8.device)))
+                                         0 if workspace is None else workspace.numel(), _stream(x_q8.device)))
     return out

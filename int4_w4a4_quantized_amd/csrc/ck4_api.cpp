@@ -211,6 +211,7 @@ ck4_status ck4_dequant_w4a8_grouped(const int8_t *w_packed, const float *group_s
                                                 static_cast<hipStream_t>(stream)));
 }
 
+// Column chunk of the decode + int8 GEMM path; 0 means the fused kernel.
 static int64_t w4a8_chunk(int64_t m, int64_t n, int64_t k, int64_t chunk_cols, int64_t l2_bytes) {
     if (chunk_cols < 0) return n;
     if (chunk_cols > 0) return chunk_cols < n ? chunk_cols : n;
@@ -220,6 +221,8 @@ static int64_t w4a8_chunk(int64_t m, int64_t n, int64_t k, int64_t chunk_cols, i
     const char *e_cols = std::getenv("CK4_W4A8_CHUNK_COLS");
     int64_t c = e_cols ? std::atoll(e_cols) : 0;
     if (c <= 0) {
+        // skinny rows: decode in registers inside the GEMM (no round trip)
+        if (m <= 64 && k % 256 == 0) return 0;
         c = (l2_bytes / k) / 128 * 128;
         if (c < 1024) c = 1024;
         if (c > 4096) c = 4096;
@@ -237,6 +240,7 @@ size_t ck4_w4a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t chunk_c
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices && check_device("ws", &dev) == CK4_OK)
         l2 = g_l2_bytes[dev];
     const int64_t c = w4a8_chunk(m, n, k, chunk_cols, l2);
+    if (c == 0) return 0;
     return (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));
 }
 
@@ -245,25 +249,29 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
                                    uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace, size_t ws_bytes,
                                    void *stream) {
     const char *fn = "ck4_linear_w4a8_grouped";
-    if (!x_q8 || !x_scales || !w_packed || !group_scales || !y || !workspace)
+    if (!x_q8 || !x_scales || !w_packed || !group_scales || !y)
         return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, 8)) return s;
-    if (!aligned(x_q8, 16) || !aligned(w_packed, 16) || !aligned(workspace, 16))
+    if (!aligned(x_q8, 16) || !aligned(w_packed, 16) || (workspace && !aligned(workspace, 16)))
         return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
     if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
     if (!pow2(group) || group < 16 || group > 1024 || k % group != 0)
         return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [16, 1024] dividing k)", fn, group);
     if (chunk_cols > 0 && chunk_cols % 16 != 0)
         return fail(CK4_ERR_INVALID, "%s: chunk_cols=%lld is not a multiple of 16", fn, (long long)chunk_cols);
+    if (chunk_cols != 0 && !workspace)
+        return fail(CK4_ERR_INVALID, "%s: the decode paths (chunk_cols != 0) need a workspace", fn);
     int dev = 0;
     if (ck4_status s = check_device(fn, &dev)) return s;
     const int64_t c = w4a8_chunk(m, n, k, chunk_cols, g_l2_bytes[dev]);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c == 0) return launched(fn, ck4::launch_w4a8_fused(x_q8, x_scales, w_packed, group_scales, m, n, k, group,
+                                                           y, ldy, st));
     const size_t need = (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));
-    if (ws_bytes < need)
-        return fail(CK4_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+    if (!workspace || ws_bytes < need)
+        return fail(CK4_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", fn, workspace ? ws_bytes : 0, need);
     int8_t *w8 = static_cast<int8_t *>(workspace);
     float *srow = reinterpret_cast<float *>(static_cast<char *>(workspace) + align_up(c * k, 256));
-    hipStream_t st = static_cast<hipStream_t>(stream);
     for (int64_t n0 = 0; n0 < n; n0 += c) {
         const int64_t nc = (n - n0) < c ? (n - n0) : c;
         hipError_t e = ck4::launch_w4a8_decode(w_packed, group_scales, k, group, n0, nc, w8, srow, st);

@@ -26,4 +26,10 @@ hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *s
 hipError_t launch_w4a8_decode(const int8_t *w_packed, const float *group_scales, int64_t k, int group,
                               int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream);
 
+// Fused grouped W4A8 linear for m <= 64 (decode in registers + int8 MFMA +
+// epilogue), bit-identical to decode followed by the int8 GEMM.
+hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                             const float *group_scales, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
+                             int64_t ldy, hipStream_t stream);
+
 }  // namespace ck4

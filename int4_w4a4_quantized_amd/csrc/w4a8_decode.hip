@@ -74,3 +74,201 @@ hipError_t launch_w4a8_decode(const int8_t *w_packed, const float *group_scales,
 }
 
 }  // namespace ck4
+
+// ---------------------------------------------------------------------------
+// Fused grouped W4A8 linear for skinny M (M <= 64): the decode above and the
+// rowwise int8 GEMM in one kernel, with the decoded int8 weight never leaving
+// VGPRs. The int8 codes are the same fp32 operations as the decode kernel, so
+// the int32 accumulators, row scales and outputs are identical to decoding
+// first. ([PR #97] What this adds decodes a chunk of columns to an int8
+// buffer that stays in cache for the GEMM; here the "chunk" is one MFMA
+// fragment and the cache is the register file.)
+//
+// Layout: a workgroup owns 16*FNW weight rows; KS wavefronts split K. For
+// v_mfma_i32_16x16x64_i8 lane l holds row l & 15 and 16 consecutive k at
+// offset 16 * (l >> 4) of each 64-k slice: 8 packed weight bytes (one group,
+// since group >= 16) and 16 activation bytes, in the same byte order on both
+// operands. A k-step is four slices, 256 k (one 128-byte line of the packed
+// weight row).
+namespace ck4 {
+namespace {
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Decode 16 int4 codes (two packed words, low nibble first) with multiplier
+// `mult` to 16 int8 codes: clamp(rint(q * mult), -127, 127) in fp32.
+__device__ __forceinline__ v4i_t decode16(uint32_t w0, uint32_t w1, float mult) {
+    uint32_t out[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const uint32_t word = e < 8 ? w0 : w1;
+        const int q = (int)(((word >> (4 * (e & 7))) & 0xFu) ^ 8u) - 8;
+        float t = rintf((float)q * mult);
+        t = fminf(fmaxf(t, -127.0f), 127.0f);
+        out[e >> 2] |= ((uint32_t)(int)t & 0xFFu) << (8 * (e & 3));
+    }
+    return v4i_t{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
+}
+
+template <int FM, int FNW, int KS, int MAXS>
+__global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__restrict__ X, const float *__restrict__ sx,
+                                                           const int8_t *__restrict__ W,
+                                                           const float *__restrict__ gs, int M, int N, int K,
+                                                           int group, uint16_t *__restrict__ Y, int64_t ldy) {
+    __shared__ v4i_t red[KS - 1][FNW][FM][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * 16 * FNW;
+    const int frow = lane & 15;
+    const int fgrp = lane >> 4;
+    const int ng = K / group;
+    const int wrow_bytes = K / 2;
+    const int rows_b = min(16 * FNW, N - n0);
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(X), (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(W) + (int64_t)n0 * wrow_bytes, (short)0, rows_b * wrow_bytes, 0x00020000);
+
+    // Row scale of this lane's weight rows: (max group scale * 7) / 127.
+    float srow[FNW];
+#pragma unroll
+    for (int i = 0; i < FNW; ++i) {
+        const int n = min(n0 + i * 16 + frow, N - 1);
+        float smax = 0.0f;
+        for (int g = 0; g < ng; ++g) smax = fmaxf(smax, gs[(int64_t)n * ng + g]);
+        srow[i] = (smax * 7.0f) / 127.0f;
+    }
+
+    const int steps = K / 256;
+    const int per_wave = (steps + KS - 1) / KS;
+    const int s_begin = wave * per_wave;
+    const int s_end = min(steps, s_begin + per_wave);
+
+    v4i_t acc[FNW][FM];
+#pragma unroll
+    for (int i = 0; i < FNW; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4i_t{0, 0, 0, 0};
+
+    for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
+        uint2 wv[MAXS][FNW][4];
+        v4i_t xv[MAXS][FM][4];
+#pragma unroll
+        for (int t = 0; t < MAXS; ++t) {
+            const int s = s0 + t;
+            if (s < s_end) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+#pragma unroll
+                    for (int i = 0; i < FNW; ++i) {
+                        const uint32_t off = (uint32_t)(i * 16 + frow) * (uint32_t)wrow_bytes + (uint32_t)(8 * fgrp);
+                        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, s * 128 + h * 32, 0);
+                        wv[t][i][h] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+                    }
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        xv[t][j][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                            rx, (uint32_t)(j * 16 + frow) * (uint32_t)K + (uint32_t)(16 * fgrp), s * 256 + h * 64, 0);
+                }
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < MAXS; ++t) {
+            const int s = s0 + t;
+            if (s >= s_end) break;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const int g = (s * 256 + h * 64 + 16 * fgrp) / group;
+#pragma unroll
+                for (int i = 0; i < FNW; ++i) {
+                    const int n = min(n0 + i * 16 + frow, N - 1);
+                    const float mult = srow[i] == 0.0f ? 0.0f : gs[(int64_t)n * ng + g] / srow[i];
+                    const v4i_t w8 = decode16(wv[t][i][h].x, wv[t][i][h].y, mult);
+#pragma unroll
+                    for (int j = 0; j < FM; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    if (KS > 1) {
+        if (wave > 0) {
+#pragma unroll
+            for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) red[wave - 1][i][j][lane] = acc[i][j];
+        }
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll 1
+        for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+            for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j) acc[i][j] += red[w][i][j][lane];
+    }
+
+    // Epilogue: lane holds acc[i][j][r] = y[m][n], m = 16j + (l & 15),
+    // n = n0 + 16i + 4(l >> 4) + r; the weight scale of row n is its s_row,
+    // which lives in the lane that decoded row n: lane (n - n0 - 16i) of the
+    // same 16-lane group, fetched with a cross-lane read.
+#pragma unroll
+    for (int i = 0; i < FNW; ++i) {
+        float sw4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sw4[r] = __shfl(srow[i], 4 * fgrp + r, 64);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = j * 16 + frow;
+            const int nb = n0 + i * 16 + 4 * fgrp;
+            if (m >= M || nb >= N) continue;
+            const float sam = sx[m];
+            uint16_t o[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = bf16_rne(((float)acc[i][j][r] * sam) * sw4[r]);
+            uint16_t *yr = Y + (int64_t)m * ldy + nb;
+            if (nb + 3 < N) {
+                *reinterpret_cast<uint2 *>(yr) =
+                    make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+            } else {
+                for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = o[r];
+            }
+        }
+    }
+}
+
+template <int FM, int FNW, int MAXS>
+hipError_t launch_fused_cfg(const int8_t *x, const float *sx, const int8_t *w, const float *gs, int64_t m, int64_t n,
+                            int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream) {
+    const int64_t groups = (n + 16 * FNW - 1) / (16 * FNW);
+    dim3 grid((unsigned)groups);
+    if (groups >= 1024) {
+        w4a8_fused_kernel<FM, FNW, 2, MAXS><<<grid, dim3(128), 0, stream>>>(x, sx, w, gs, (int)m, (int)n, (int)k, group,
+                                                                        y, ldy);
+    } else if (groups >= 512) {
+        w4a8_fused_kernel<FM, FNW, 4, MAXS><<<grid, dim3(256), 0, stream>>>(x, sx, w, gs, (int)m, (int)n, (int)k, group,
+                                                                        y, ldy);
+    } else {
+        w4a8_fused_kernel<FM, FNW, 8, MAXS><<<grid, dim3(512), 0, stream>>>(x, sx, w, gs, (int)m, (int)n, (int)k, group,
+                                                                        y, ldy);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                             const float *group_scales, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
+                             int64_t ldy, hipStream_t stream) {
+    if (m <= 16) return launch_fused_cfg<1, 1, 2>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+    if (m <= 32) return launch_fused_cfg<2, 1, 2>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+    return launch_fused_cfg<4, 1, 1>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+}
+
+}  // namespace ck4

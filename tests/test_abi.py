@@ -90,7 +90,8 @@ def test_w4a8_validation(L):
     assert d(FAKE, FAKE, 64, 256, 128, 32, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID  # n0 + nc > n
     assert d(FAKE, FAKE, 64, 256, 100, 0, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED
     f = L.ck4_linear_w4a8_grouped
-    assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, 0, NULL, 0, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, 128, NULL, 0, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, -1, NULL, 0, NULL) == ck.CK4_ERR_INVALID
     assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 200, 128, FAKE, 64, 0, FAKE, 1 << 20, NULL) == ck.CK4_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, 24, FAKE, 1 << 20, NULL) == ck.CK4_ERR_INVALID
     l8 = L.ck4_linear_w8a8

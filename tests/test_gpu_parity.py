@@ -205,7 +205,9 @@ def test_w4a8_decode_chunks_bitexact(ck):
 
 
 @pytest.mark.parametrize("m,n,k,chunk", [(8, 1152, 512, 384), (8, 1152, 512, 400), (1, 1152, 512, -1),
-                                         (64, 1500, 1024, 0), (100, 300, 512, 0), (16, 5120, 5120, 0)])
+                                         (64, 1500, 1024, 0), (100, 300, 512, 0), (16, 5120, 5120, 0),
+                                         (3, 1000, 768, 0), (40, 77, 1024, 0), (1, 12288, 3072, 0),
+                                         (64, 130, 384, 0)])
 def test_w4a8_linear_chunked_equals_single_pass_and_oracle(ck, m, n, k, chunk):
     rng = np.random.default_rng(700 + m + n)
     xb = workloads.make_activations(rng, m, k)
@@ -216,6 +218,29 @@ def test_w4a8_linear_chunked_equals_single_pass_and_oracle(ck, m, n, k, chunk):
     y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, 128, -1))
     assert np.array_equal(y, y1)
     assert_bf16_close(y, oracle.linear_w4a8_grouped(xb, wp, gs))
+
+
+@pytest.mark.parametrize("group", [16, 64, 256])
+@pytest.mark.parametrize("m", [1, 24, 64])
+def test_w4a8_fused_matches_chunked_for_all_groups(ck, m, group):
+    # default policy (fused kernel for m <= 64) against an explicit chunked
+    # decode + int8 GEMM, with an all-zero weight row (row scale 0) and a
+    # weight row whose groups all share one scale
+    rng = np.random.default_rng(900 + m + group)
+    n, k = 333, 1536
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    w[7] = 0
+    w[11] = 0.5
+    wp, gs = oracle.quantize_weight_convrot(w, group=group)
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    wpd, gsd = torch.from_numpy(wp).cuda(), torch.from_numpy(gs).cuda()
+    assert ck.w4a8_workspace_bytes(m, n, k, 0) == 0
+    y0 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, group, 0))
+    yc = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, group, 128))
+    assert np.array_equal(y0, yc)
+    assert not y0[:, 7].any()
+    assert_bf16_close(y0, oracle.linear_w4a8_grouped(xb, wp, gs, group))
 
 
 # --------------------------------------------------------------------------
