@@ -9,9 +9,11 @@ before timing (offline weight prep). Workload: 4608 tokens through a 3072 x
 N(0,1) with 1 % outlier channels x20, weights N(0, 0.02).
 
 Prints one JSON line. ``value`` is the layer's int8-op throughput in TOP/s
-(2 M N K per step / step time), ``roofline`` reports the GEMM kernel against
-the int8 dense MFMA peak using HIP-event kernel times taken inside the timed
-region, and ``cpu_baseline`` times the CPU oracle on a bounded row sample.
+(2 M N K per step / step time; the K steps are one HIP graph replay between
+two synchronisations), ``roofline`` reports the GEMM kernel against the int8
+dense MFMA peak using its per-launch time from HIP events around K
+back-to-back launches, and ``cpu_baseline`` times the CPU oracle on the
+workload's rows.
 """
 from __future__ import annotations
 
@@ -184,30 +186,60 @@ def main() -> int:
     sx = torch.empty((m,), dtype=torch.float32, device=dev)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
 
-    def step():
-        ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
-        ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+    # Eager reference output of one step.
+    ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+    ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
 
-    for _ in range(args.warmup):
-        step()
+    # The host launch path (Python + ctypes + HIP) costs about as much as a
+    # step, so the K timed steps are captured in one HIP graph and replayed
+    # once: the kernels then run back to back as a serving loop would issue
+    # them. Warm-up steps are a graph of their own.
+    def capture(n_steps, quant=True, gemm=True):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_steps):
+                if quant:
+                    ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+                if gemm:
+                    ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+        return g
+
+    g_warm = capture(max(args.warmup, 1))
+    g_steps = capture(args.steps)
+    g_gemm_only = capture(args.steps, quant=False)
+    g_quant_only = capture(args.steps, gemm=False)
+    torch.cuda.synchronize()
+    g_warm.replay()
+    torch.cuda.synchronize()
+    # clear the outputs so that the check below sees the timed replay's work
+    xq.zero_()
+    sx.zero_()
+    y.zero_()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        e0, e1, e2 = ev[i]
-        e0.record(stream)
-        ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
-        e1.record(stream)
-        ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
-        e2.record(stream)
+    g_steps.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
+        print("bench.py: graph replay output differs from the eager step", file=sys.stderr)
+        return 1
 
-    quant_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
-    gemm_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    # Per-kernel durations: the same launches, one kernel at a time, back to
+    # back, bracketed by HIP events on the stream they run on.
+    def per_launch_ms(g):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    gemm_ms = per_launch_ms(g_gemm_only)
+    quant_ms = per_launch_ms(g_quant_only)
     ms_per_step = wall * 1e3 / args.steps
     ops = 2.0 * m * n * k
     tops = ops / (ms_per_step * 1e-3) / 1e12
