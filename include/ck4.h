@@ -32,6 +32,13 @@
  *    Nothing is launched when validation fails. ck4_last_error() returns a
  *    thread-local description of the last failure.
  *  - There is no fallback path: an unsupported call fails.
+ *
+ * Citation tags used below (web pages, by title and section):
+ *  [PR #63]  comfy-kitchen "[PR #63] int4_tensorwise: W4A4 layout (+ConvRot)
+ *            with fused CUDA kernels".
+ *  [PR #97]  comfy-kitchen "[PR #97] HIP port of #90: grouped W4A8 over the
+ *            INT8 GEMM".
+ *  [FAST]    "ComfyUI-INT4-Fast" extension listing.
  */
 #ifndef CK4_H
 #define CK4_H

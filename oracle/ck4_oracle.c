@@ -67,8 +67,8 @@ void ck4o_set_num_threads(int n) {
 }
 
 /* ------------------------------------------------------------------------- */
-/* Hadamard rotation ([PR63] "FHT rotation (smem, radix-4)"; [HIPT] "Hadamard
- * ConvRot handling"; [FAST] "Hadamard rotation").                          */
+/* Hadamard rotation ([PR63] Description: the rotation stage of the fused
+ * activation kernel; [HIPT] What it provides; [FAST] Features).           */
 
 /* The normalisation constant of a g-point orthonormal Hadamard transform,
  * rounded once to fp32. */
