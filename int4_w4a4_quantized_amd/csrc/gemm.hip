@@ -31,7 +31,7 @@
 // activation fragment, so each lane's 4 accumulators are 4 consecutive
 // output columns of one row: the epilogue stores 8 contiguous bytes per lane.
 // Workgroup ids are remapped so that each XCD (ids are dealt round-robin to
-// the 8 XCDs) walks a contiguous run of tiles and reuses its L2.
+// the 8 XCDs) owns one rectangular block of tiles and reuses its L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -258,7 +258,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM *
                           amdgpu_waves_per_eu(WPE, WPE))) void
 gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
                 const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes,
-                int ksteps, void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total) {
+                int ksteps, void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m) {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM;
     constexpr int WTN = BN / WGN;
@@ -270,10 +270,23 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
     static_assert(BM % 8 == 0 && BN % 8 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "bad tile");
     __shared__ __attribute__((aligned(1024))) uint4 smem[2 * STAGE / 16];
 
+    // Tile order. Ids are dealt round-robin to the 8 XCDs (id & 7). With
+    // xcd_m > 0 the tile grid is cut into xcd_m x (8 / xcd_m) blocks, one per
+    // XCD, walked row-major inside, so an XCD's L2 holds only its block's A
+    // rows and B rows; otherwise each XCD walks a contiguous run of tiles.
     int tile = blockIdx.x;
-    if ((tiles_total & 7) == 0) tile = (tile & 7) * (tiles_total >> 3) + (tile >> 3);
-    const int tm = tile / tiles_n;
-    const int tn = tile - tm * tiles_n;
+    int tm, tn;
+    if (xcd_m > 0) {
+        const int xcd_n = 8 / xcd_m;
+        const int x = tile & 7, li = tile >> 3;
+        const int bm = (tiles_total / tiles_n) / xcd_m, bn = tiles_n / xcd_n;
+        tm = (x / xcd_n) * bm + li / bn;
+        tn = (x % xcd_n) * bn + li % bn;
+    } else {
+        if ((tiles_total & 7) == 0) tile = (tile & 7) * (tiles_total >> 3) + (tile >> 3);
+        tm = tile / tiles_n;
+        tn = tile - tm * tiles_n;
+    }
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 
@@ -495,6 +508,24 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
     }
 }
 
+// Shape of the per-XCD tile blocks: xcd_m rows of blocks by 8 / xcd_m
+// columns, chosen to minimise the A and B rows one XCD fetches (0: the grid
+// does not split evenly; fall back to contiguous runs).
+int pick_xcd_m(int tiles_m, int tiles_n, int bm, int bn) {
+    int best = 0;
+    long best_rows = 0;
+    for (int xm = 1; xm <= 8; xm *= 2) {
+        const int xn = 8 / xm;
+        if (tiles_m % xm != 0 || tiles_n % xn != 0) continue;
+        const long rows = (long)(tiles_m / xm) * bm + (long)(tiles_n / xn) * bn;
+        if (best == 0 || rows < best_rows) {
+            best = xm;
+            best_rows = rows;
+        }
+    }
+    return best;
+}
+
 template <bool S4, int BM, int BN, int WGM, int WGN, int WPE>
 hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                       int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
@@ -503,13 +534,14 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
     const int tiles_m = (int)((m + BM - 1) / BM);
     const int tiles_n = (int)((n + BN - 1) / BN);
     const int total = tiles_m * tiles_n;
+    const int xcd_m = pick_xcd_m(tiles_m, tiles_n, BM, BN);
     dim3 grid((unsigned)total), block(64 * WGM * WGN);
     if (out_i32)
         gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, true><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m);
     else
         gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m);
     return hipGetLastError();
 }
 

@@ -13,12 +13,15 @@
 //
 // Data layout in registers: each lane owns "chunks" of 16 contiguous elements
 // of the row. Chunk c of a row covers elements [16c, 16c + 16); chunk c is
-// owned by thread c mod blockDim. A Hadamard block of b elements is b/16
-// consecutive chunks, which sit in b/16 consecutive lanes of one wavefront
-// (blockDim is a multiple of 64 and b <= 1024). Butterfly strides 1..8 are
-// inside a lane; stride 16*m pairs lane L with lane L ^ m. The whole row stays
-// in VGPRs between the rotation and the quantisation, so HBM is read once and
-// written once.
+// owned by thread c mod T of the row's T threads. A row of up to 4096
+// elements belongs to one wavefront (T = 64, four rows per workgroup), so its
+// absmax needs no barrier and every row of a 4608-row batch is resident at
+// once; a longer row belongs to a whole workgroup (T = blockDim). A Hadamard
+// block of b elements is b/16 consecutive chunks, which sit in b/16
+// consecutive lanes of one wavefront (T is a multiple of 64 and b <= 1024).
+// Butterfly strides 1..8 are inside a lane; stride 16*m pairs lane L with
+// lane L ^ m. The whole row stays in VGPRs between the rotation and the
+// quantisation, so HBM is read once and written once.
 //
 // Cross-lane butterflies with one instruction per element. A butterfly keeps
 // a + b in the lower lane and a - b in the upper one. Each lane instead keeps
@@ -30,8 +33,8 @@
 // sigma = (-1)^popcount(lane & (b/16 - 1)); it is folded into the final
 // multiply by the normalisation constant, so the rotated values are bitwise
 // those of the plain butterflies (up to the sign of an exact zero). The
-// partner value comes through DPP (strides 16 and 32) or ds_swizzle (64, 128,
-// 256) or ds_bpermute (512).
+// partner value comes through ds_swizzle (strides 16 to 256) or ds_bpermute
+// (512), which use the LDS crossbar and leave the VALU to the arithmetic.
 //
 // The quotient r / s without a divide per element. With y = RN(1/s) computed
 // once per row by the IEEE divide, q0 = RN(r y), e = fma(-q0, s, r) (exact),
@@ -94,16 +97,14 @@ __device__ __forceinline__ void fwht_in_lane(float v[kElems]) {
     }
 }
 
-// The value held by lane L ^ mask.
+// The value held by lane L ^ mask. The exchange goes through the LDS
+// crossbar (ds_swizzle, ds_bpermute) rather than a DPP move, so it costs no
+// VALU instruction: the kernel is bound by VALU issue.
 template <int MASK>
 __device__ __forceinline__ float partner(float x) {
     const int xi = __float_as_int(x);
     int r;
-    if constexpr (MASK == 1) {
-        r = __builtin_amdgcn_mov_dpp(xi, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-    } else if constexpr (MASK == 2) {
-        r = __builtin_amdgcn_mov_dpp(xi, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
-    } else if constexpr (MASK <= 16) {
+    if constexpr (MASK <= 16) {
         r = __builtin_amdgcn_ds_swizzle(xi, 0x1F | (MASK << 10));  // bitmask mode, xor MASK
     } else {
         r = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ MASK) << 2), xi);
@@ -118,14 +119,15 @@ __device__ __forceinline__ void cross_stage(float v[kElems], int lane) {
     for (int i = 0; i < kElems; ++i) v[i] = __builtin_fmaf(partner<MASK>(v[i]), k, v[i]);
 }
 
-// All cross-lane stages for a block of lanes_per_block lanes (ascending mask).
-__device__ __forceinline__ void fwht_cross_lane(float v[kElems], int lane, int lanes_per_block) {
-    if (lanes_per_block > 1) cross_stage<1>(v, lane);
-    if (lanes_per_block > 2) cross_stage<2>(v, lane);
-    if (lanes_per_block > 4) cross_stage<4>(v, lane);
-    if (lanes_per_block > 8) cross_stage<8>(v, lane);
-    if (lanes_per_block > 16) cross_stage<16>(v, lane);
-    if (lanes_per_block > 32) cross_stage<32>(v, lane);
+// All cross-lane stages for a block of LPB lanes (ascending mask).
+template <int LPB>
+__device__ __forceinline__ void fwht_cross_lane(float v[kElems], int lane) {
+    if constexpr (LPB > 1) cross_stage<1>(v, lane);
+    if constexpr (LPB > 2) cross_stage<2>(v, lane);
+    if constexpr (LPB > 4) cross_stage<4>(v, lane);
+    if constexpr (LPB > 8) cross_stage<8>(v, lane);
+    if constexpr (LPB > 16) cross_stage<16>(v, lane);
+    if constexpr (LPB > 32) cross_stage<32>(v, lane);
 }
 
 __device__ __forceinline__ float wave_max(float a) {
@@ -134,36 +136,65 @@ __device__ __forceinline__ float wave_max(float a) {
     return a;
 }
 
-// Integer code of r / s: the bit pattern whose low byte is the int8 code.
+// Integer code of r / s as a bit pattern whose low byte is the code plus
+// BIAS (two's complement). The packed-int4 path uses BIAS = 8, so the low
+// byte is q + 8 in [1, 15] with nothing above bit 3; the int8 path uses 0.
+// Adding 1.5 * 2^23 + BIAS (an even integer, ulp 1 at that magnitude) rounds
+// q1 to the nearest integer, ties to even, exactly as adding 1.5 * 2^23 does.
+template <int BIAS>
 __device__ __forceinline__ uint32_t code_fast(float r, float s, float y) {
     const float q0 = r * y;
     const float e = __builtin_fmaf(-q0, s, r);
     const float q1 = __builtin_fmaf(e, y, q0);
-    return __float_as_uint(q1 + 12582912.0f);  // 1.5 * 2^23
+    return __float_as_uint(q1 + (12582912.0f + (float)BIAS));  // 1.5 * 2^23 + BIAS
 }
 
+template <int BIAS>
 __device__ __forceinline__ uint32_t code_exact(float r, float s, float qmax) {
-    if (s == 0.0f) return 0u;
+    if (s == 0.0f) return (uint32_t)BIAS;
     float t = rintf(r / s);
     t = fminf(fmaxf(t, -qmax), qmax);
-    return (uint32_t)(int)t;
+    return (uint32_t)((int)t + BIAS);
+}
+
+// 8 biased int4 codes (low byte q + 8) -> one word, element 2j in the low
+// nibble of byte j: pairs are joined with one shift-or (bits above 7 are
+// don't-care), the four low bytes gathered with byte permutes, and the bias
+// removed with one XOR ((q + 8) ^ 8 == q & 15 for q in [-8, 7]).
+__device__ __forceinline__ uint32_t pack8_biased(const uint32_t *c) {
+    uint32_t b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) b[t] = (c[2 * t + 1] << 4) | c[2 * t];
+    const uint32_t lo = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);  // [b0.0, b1.0, 0, 0]
+    const uint32_t hi = __builtin_amdgcn_perm(b[3], b[2], 0x04000C0Cu);  // [0, 0, b2.0, b3.0]
+    return (lo | hi) ^ 0x88888888u;
+}
+
+// 4 int8 codes (low bytes) -> one word, byte j = code j.
+__device__ __forceinline__ uint32_t pack4_bytes(const uint32_t *c) {
+    const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x04000C0Cu);
+    return lo | hi;
 }
 
 // out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation.
-template <typename TIn, int OUT, int NCH>
-__global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__restrict__ x, int64_t ldx, int k,
-                                                                  int lanes_per_block, float c, int group,
-                                                                  void *__restrict__ out, int64_t ldo,
-                                                                  float *__restrict__ scales) {
+// WAVE_ROW: each wavefront owns one row (K <= 64 * 16 * NCH), so the row
+// absmax is a wavefront reduction with no LDS and no barrier, and a 256-thread
+// workgroup handles 4 rows; otherwise the workgroup owns one row.
+template <typename TIn, int OUT, int NCH, bool WAVE_ROW, int LPB>
+__global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__restrict__ x, int64_t rows, int64_t ldx,
+                                                                  int k, float c, int group, void *__restrict__ out,
+                                                                  int64_t ldo, float *__restrict__ scales) {
     __shared__ float red[kThreads / 64];
-    const int row = blockIdx.x;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int nthreads = blockDim.x;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = WAVE_ROW ? (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6) : blockIdx.x;
+    if (WAVE_ROW && row >= rows) return;  // whole wavefronts only; this mode has no barrier
+    const int tid = WAVE_ROW ? lane : (int)threadIdx.x;
+    const int nthreads = WAVE_ROW ? 64 : (int)blockDim.x;
     const int nchunks = k / kElems;
     const TIn *xr = x + (int64_t)row * ldx;
     // the sign carried by the cross-lane stages, folded into the scale
-    const float c_lane = (__popc(lane & (lanes_per_block - 1)) & 1) ? -c : c;
+    const float c_lane = (__popc(lane & (LPB - 1)) & 1) ? -c : c;
 
     float v[NCH][kElems];
     float amax = 0.0f;
@@ -173,7 +204,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
         if (ch < nchunks) {
             load_chunk(xr + (int64_t)ch * kElems, v[j]);
             fwht_in_lane(v[j]);
-            fwht_cross_lane(v[j], lane, lanes_per_block);
+            fwht_cross_lane<LPB>(v[j], lane);
 #pragma unroll
             for (int i = 0; i < kElems; ++i) {
                 v[j][i] = v[j][i] * c_lane;
@@ -197,15 +228,18 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
         return;
     } else {
         const float qmax = OUT == 0 ? 7.0f : 127.0f;
+        constexpr int BIAS = OUT == 0 ? 8 : 0;
         float s_row = 0.0f, y_row = 0.0f;
         bool fast_row = false;
         if (group == 0) {
             // absmax over the whole row: wavefront reduction, then across waves.
             amax = wave_max(amax);
-            if (lane == 0) red[tid >> 6] = amax;
-            __syncthreads();
-            amax = red[0];
-            for (int w = 1; w < nthreads / 64; ++w) amax = fmaxf(amax, red[w]);
+            if constexpr (!WAVE_ROW) {
+                if (lane == 0) red[tid >> 6] = amax;
+                __syncthreads();
+                amax = red[0];
+                for (int w = 1; w < nthreads / 64; ++w) amax = fmaxf(amax, red[w]);
+            }
             s_row = amax / qmax;
             fast_row = s_row >= 0x1p-120f && s_row <= 0x1p120f;
             y_row = fast_row ? 1.0f / s_row : 0.0f;
@@ -219,10 +253,10 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             if (group == 0) {
                 if (fast_row) {
 #pragma unroll
-                    for (int i = 0; i < kElems; ++i) code[i] = code_fast(v[j][i], s_row, y_row);
+                    for (int i = 0; i < kElems; ++i) code[i] = code_fast<BIAS>(v[j][i], s_row, y_row);
                 } else {
 #pragma unroll
-                    for (int i = 0; i < kElems; ++i) code[i] = code_exact(v[j][i], s_row, qmax);
+                    for (int i = 0; i < kElems; ++i) code[i] = code_exact<BIAS>(v[j][i], s_row, qmax);
                 }
             } else {
                 // one scale per `group` elements = group/16 consecutive lanes
@@ -235,51 +269,72 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
                 const int lanes_per_group = group / kElems;
                 if ((ch % lanes_per_group) == 0) scales[(int64_t)row * (k / group) + ch / lanes_per_group] = s;
 #pragma unroll
-                for (int i = 0; i < kElems; ++i) code[i] = code_exact(v[j][i], s, qmax);
+                for (int i = 0; i < kElems; ++i) code[i] = code_exact<BIAS>(v[j][i], s, qmax);
             }
             if constexpr (OUT == 0) {
-                uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) w0 |= (code[i] & 0xFu) << (4 * i);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) w1 |= (code[8 + i] & 0xFu) << (4 * i);
+                const uint32_t w0 = pack8_biased(code), w1 = pack8_biased(code + 8);
                 int8_t *o = reinterpret_cast<int8_t *>(out) + (int64_t)row * ldo + (int64_t)ch * (kElems / 2);
                 *reinterpret_cast<uint2 *>(o) = make_uint2(w0, w1);
             } else {
-                uint32_t w[4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    w[d] = 0;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) w[d] |= (code[4 * d + i] & 0xFFu) << (8 * i);
-                }
                 int8_t *o = reinterpret_cast<int8_t *>(out) + (int64_t)row * ldo + (int64_t)ch * kElems;
-                *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+                *reinterpret_cast<uint4 *>(o) =
+                    make_uint4(pack4_bytes(code), pack4_bytes(code + 4), pack4_bytes(code + 8), pack4_bytes(code + 12));
             }
         }
     }
 }
 
-template <typename TIn, int OUT>
-void launch_out(const TIn *x, int nch, dim3 grid, dim3 block, int64_t ldx, int k, int lanes_per_block, float c,
-                int group, void *out, int64_t ldo, float *scales, hipStream_t stream) {
+template <typename TIn, int OUT, bool WAVE_ROW, int LPB>
+void launch_lpb(const TIn *x, int nch, dim3 grid, dim3 block, int64_t rows, int64_t ldx, int k, float c, int group,
+                void *out, int64_t ldo, float *scales, hipStream_t stream) {
     switch (nch) {
     case 1:
-        rotate_quant_kernel<TIn, OUT, 1><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
-                                                                      scales);
+        rotate_quant_kernel<TIn, OUT, 1, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
+                                                                                     ldo, scales);
         break;
     case 2:
-        rotate_quant_kernel<TIn, OUT, 2><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
-                                                                      scales);
+        rotate_quant_kernel<TIn, OUT, 2, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
+                                                                                     ldo, scales);
         break;
     case 3:
-        rotate_quant_kernel<TIn, OUT, 3><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
-                                                                      scales);
+        rotate_quant_kernel<TIn, OUT, 3, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
+                                                                                     ldo, scales);
         break;
     default:
-        rotate_quant_kernel<TIn, OUT, 4><<<grid, block, 0, stream>>>(x, ldx, k, lanes_per_block, c, group, out, ldo,
-                                                                      scales);
+        rotate_quant_kernel<TIn, OUT, 4, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
+                                                                                     ldo, scales);
         break;
+    }
+}
+
+template <typename TIn, int OUT, bool WAVE_ROW>
+void launch_out(const TIn *x, int nch, dim3 grid, dim3 block, int64_t rows, int64_t ldx, int k, int lanes_per_block,
+                float c, int group, void *out, int64_t ldo, float *scales, hipStream_t stream) {
+    switch (lanes_per_block) {
+    case 1: launch_lpb<TIn, OUT, WAVE_ROW, 1>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    case 2: launch_lpb<TIn, OUT, WAVE_ROW, 2>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    case 4: launch_lpb<TIn, OUT, WAVE_ROW, 4>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    case 8: launch_lpb<TIn, OUT, WAVE_ROW, 8>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    case 16: launch_lpb<TIn, OUT, WAVE_ROW, 16>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    case 32: launch_lpb<TIn, OUT, WAVE_ROW, 32>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    default: launch_lpb<TIn, OUT, WAVE_ROW, 64>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    }
+}
+
+template <typename TIn, int OUT>
+void launch_mode(const TIn *x, int nch, bool wave_row, int64_t rows, int64_t ldx, int k, int lanes_per_block, float c,
+                 int group, void *out, int64_t ldo, float *scales, hipStream_t stream) {
+    if (wave_row) {
+        const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), block(kThreads);
+        launch_out<TIn, OUT, true>(x, nch, grid, block, rows, ldx, k, lanes_per_block, c, group, out, ldo, scales,
+                                   stream);
+    } else {
+        const int nchunks = k / kElems;
+        int threads = (nchunks + nch - 1) / nch;
+        threads = (threads + 63) / 64 * 64;
+        const dim3 grid((unsigned)rows), block((unsigned)threads);
+        launch_out<TIn, OUT, false>(x, nch, grid, block, rows, ldx, k, lanes_per_block, c, group, out, ldo, scales,
+                                    stream);
     }
 }
 
@@ -287,18 +342,22 @@ template <typename TIn>
 hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int rot_block, int out_kind, int group,
                         void *out, int64_t ldo, float *scales, hipStream_t stream) {
     const int nchunks = (int)(k / kElems);
-    const int per_thread = (nchunks + kThreads - 1) / kThreads;  // 1..kMaxChunks
-    int threads = (nchunks + per_thread - 1) / per_thread;
-    threads = (threads + 63) / 64 * 64;
+    // a row fits one wavefront when it is at most 64 lanes x kMaxChunks chunks
+    const bool wave_row = nchunks <= 64 * kMaxChunks;
+    const int per_thread = wave_row ? (nchunks + 63) / 64 : (nchunks + kThreads - 1) / kThreads;  // 1..kMaxChunks
     const float c = (float)(1.0 / __builtin_sqrt((double)rot_block));
     const int lanes_per_block = rot_block / kElems;
-    dim3 grid((unsigned)rows), block((unsigned)threads);
     if (out_kind == 0)
-        launch_out<TIn, 0>(x, per_thread, grid, block, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales, stream);
+        launch_mode<TIn, 0>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
+                            stream);
+    else if constexpr (sizeof(TIn) == 4)
+        return hipErrorInvalidValue;  // fp32 rows are weights: packed int4 only
     else if (out_kind == 1)
-        launch_out<TIn, 1>(x, per_thread, grid, block, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales, stream);
+        launch_mode<TIn, 1>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
+                            stream);
     else
-        launch_out<TIn, 2>(x, per_thread, grid, block, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales, stream);
+        launch_mode<TIn, 2>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
+                            stream);
     return hipGetLastError();
 }
 
