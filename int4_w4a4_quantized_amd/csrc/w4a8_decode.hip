@@ -84,12 +84,10 @@ hipError_t launch_w4a8_decode(const int8_t *w_packed, const float *group_scales,
 // buffer that stays in cache for the GEMM; here the "chunk" is one MFMA
 // fragment and the cache is the register file.)
 //
-// Layout: a workgroup owns 16*FNW weight rows; KS wavefronts split K. For
-// v_mfma_i32_16x16x64_i8 lane l holds row l & 15 and 16 consecutive k at
-// offset 16 * (l >> 4) of each 64-k slice: 8 packed weight bytes (one group,
-// since group >= 16) and 16 activation bytes, in the same byte order on both
-// operands. A k-step is four slices, 256 k (one 128-byte line of the packed
-// weight row).
+// A workgroup owns 16*FNW weight rows; KS wavefronts split K and add their
+// int32 partial sums through LDS. The per-code decode costs about five VALU
+// instructions (byte convert, fma, clamp, rounding add, byte gather), since
+// the kernel is bound by VALU issue rather than by the weight stream.
 namespace ck4 {
 namespace {
 
@@ -100,21 +98,57 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// Decode 16 int4 codes (two packed words, low nibble first) with multiplier
-// `mult` to 16 int8 codes: clamp(rint(q * mult), -127, 127) in fp32.
-__device__ __forceinline__ v4i_t decode16(uint32_t w0, uint32_t w1, float mult) {
-    uint32_t out[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const uint32_t word = e < 8 ? w0 : w1;
-        const int q = (int)(((word >> (4 * (e & 7))) & 0xFu) ^ 8u) - 8;
-        float t = rintf((float)q * mult);
-        t = fminf(fmaxf(t, -127.0f), 127.0f);
-        out[e >> 2] |= ((uint32_t)(int)t & 0xFFu) << (8 * (e & 3));
-    }
-    return v4i_t{(int)out[0], (int)out[1], (int)out[2], (int)out[3]};
+// The int8 code of one int4 code: clamp(rint(q * mult), -127, 127), as a bit
+// pattern whose low byte is the code. f = q + 8 (from the XOR-biased nibble)
+// and m8 = -8 * mult, which is exact, so fma(f, mult, m8) is the single
+// rounding of q * mult: the same fp32 value the decode kernel computes.
+// The clamp before rounding equals the clamp after (the bounds are integers),
+// and adding 1.5 * 2^23 rounds to the nearest integer, ties to even.
+__device__ __forceinline__ uint32_t code8(float f, float mult, float m8) {
+    float x = __builtin_fmaf(f, mult, m8);
+    x = fminf(fmaxf(x, -127.0f), 127.0f);
+    return __float_as_uint(x + 12582912.0f);
 }
 
+// Byte B of a word as fp32 in one instruction (the compiler otherwise
+// extracts the byte first).
+template <int B>
+__device__ __forceinline__ float ubyte_f32(uint32_t x) {
+    float f;
+    if constexpr (B == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
+    else if constexpr (B == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
+    else if constexpr (B == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
+    return f;
+}
+
+// One packed word (8 codes, element 2j in the low nibble of byte j) -> the
+// 8 codes as two words of int8, natural order.
+__device__ __forceinline__ uint2 decode8(uint32_t w, float mult, float m8) {
+    const uint32_t u = w ^ 0x88888888u;        // nibble = q + 8, unsigned
+    const uint32_t lo = u & 0x0F0F0F0Fu;       // elements 0, 2, 4, 6
+    const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu; // elements 1, 3, 5, 7
+    uint32_t c[8];
+    c[0] = code8(ubyte_f32<0>(lo), mult, m8);
+    c[1] = code8(ubyte_f32<0>(hi), mult, m8);
+    c[2] = code8(ubyte_f32<1>(lo), mult, m8);
+    c[3] = code8(ubyte_f32<1>(hi), mult, m8);
+    c[4] = code8(ubyte_f32<2>(lo), mult, m8);
+    c[5] = code8(ubyte_f32<2>(hi), mult, m8);
+    c[6] = code8(ubyte_f32<3>(lo), mult, m8);
+    c[7] = code8(ubyte_f32<3>(hi), mult, m8);
+    const uint32_t d0 = __builtin_amdgcn_perm(c[1], c[0], 0x0C0C0400u) | __builtin_amdgcn_perm(c[3], c[2], 0x04000C0Cu);
+    const uint32_t d1 = __builtin_amdgcn_perm(c[5], c[4], 0x0C0C0400u) | __builtin_amdgcn_perm(c[7], c[6], 0x04000C0Cu);
+    return make_uint2(d0, d1);
+}
+
+// Operand layout: a k-step is 256 k. Lane l (row l & 15, part p = l >> 4)
+// owns the 64 contiguous k [256 s + 64 p, 256 s + 64 p + 64) of its weight row
+// and of its activation row; the MFMA of slice h (0..3) takes 16 of them,
+// [.. + 16 h, .. + 16 h + 16), as its 16 bytes. Both operands use the same
+// assignment, so each slice's 64 products are 64 distinct k and the four
+// slices cover the step. A lane's 64 k lie in one weight group when the group
+// is at least 64 wide, which makes the scale division once per step.
 template <int FM, int FNW, int KS, int MAXS>
 __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__restrict__ X, const float *__restrict__ sx,
                                                            const int8_t *__restrict__ W,
@@ -125,22 +159,28 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * 16 * FNW;
     const int frow = lane & 15;
-    const int fgrp = lane >> 4;
+    const int part = lane >> 4;
     const int ng = K / group;
     const int wrow_bytes = K / 2;
     const int rows_b = min(16 * FNW, N - n0);
+    const bool one_group = group >= 64;
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(X), (short)0, M * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t *>(W) + (int64_t)n0 * wrow_bytes, (short)0, rows_b * wrow_bytes, 0x00020000);
 
-    // Row scale of this lane's weight rows: (max group scale * 7) / 127.
+    // Row scale of this lane's weight rows, (max group scale * 7) / 127: the
+    // four lanes of a row split its groups, then combine.
     float srow[FNW];
+    const float *gsr[FNW];
 #pragma unroll
     for (int i = 0; i < FNW; ++i) {
         const int n = min(n0 + i * 16 + frow, N - 1);
+        gsr[i] = gs + (int64_t)n * ng;
         float smax = 0.0f;
-        for (int g = 0; g < ng; ++g) smax = fmaxf(smax, gs[(int64_t)n * ng + g]);
+        for (int g = part; g < ng; g += 4) smax = fmaxf(smax, gsr[i][g]);
+        smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
         srow[i] = (smax * 7.0f) / 127.0f;
     }
 
@@ -156,39 +196,66 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
         for (int j = 0; j < FM; ++j) acc[i][j] = v4i_t{0, 0, 0, 0};
 
     for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
-        uint2 wv[MAXS][FNW][4];
+        // every load of this chunk first: weights, group scales, activations
+        v4i_t wv[MAXS][FNW][2];
+        float gv[MAXS][FNW][4];
         v4i_t xv[MAXS][FM][4];
 #pragma unroll
         for (int t = 0; t < MAXS; ++t) {
             const int s = s0 + t;
             if (s < s_end) {
+                const int kb = s * 256 + part * 64;  // first k of this lane's span
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
+                for (int i = 0; i < FNW; ++i) {
+                    const uint32_t off = (uint32_t)(i * 16 + frow) * (uint32_t)wrow_bytes + (uint32_t)(kb / 2);
+                    wv[t][i][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+                    wv[t][i][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 16, 0);
+                    if (one_group) {
+                        const float g0 = gsr[i][kb / group];
 #pragma unroll
-                    for (int i = 0; i < FNW; ++i) {
-                        const uint32_t off = (uint32_t)(i * 16 + frow) * (uint32_t)wrow_bytes + (uint32_t)(8 * fgrp);
-                        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rw, off, s * 128 + h * 32, 0);
-                        wv[t][i][h] = make_uint2((uint32_t)v[0], (uint32_t)v[1]);
+                        for (int h = 0; h < 4; ++h) gv[t][i][h] = g0;
+                    } else {
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) gv[t][i][h] = gsr[i][(kb + 16 * h) / group];
                     }
+                }
 #pragma unroll
-                    for (int j = 0; j < FM; ++j)
-                        xv[t][j][h] = __builtin_amdgcn_raw_buffer_load_b128(
-                            rx, (uint32_t)(j * 16 + frow) * (uint32_t)K + (uint32_t)(16 * fgrp), s * 256 + h * 64, 0);
+                for (int j = 0; j < FM; ++j) {
+                    const uint32_t off = (uint32_t)(j * 16 + frow) * (uint32_t)K + (uint32_t)kb;
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) xv[t][j][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 16 * h, 0);
                 }
             }
         }
 #pragma unroll
         for (int t = 0; t < MAXS; ++t) {
-            const int s = s0 + t;
-            if (s >= s_end) break;
+            if (s0 + t >= s_end) break;
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                const int g = (s * 256 + h * 64 + 16 * fgrp) / group;
+            for (int i = 0; i < FNW; ++i) {
+                float mult[4], m8[4];
+                if (one_group) {
+                    const float mu = srow[i] == 0.0f ? 0.0f : gv[t][i][0] / srow[i];
 #pragma unroll
-                for (int i = 0; i < FNW; ++i) {
-                    const int n = min(n0 + i * 16 + frow, N - 1);
-                    const float mult = srow[i] == 0.0f ? 0.0f : gs[(int64_t)n * ng + g] / srow[i];
-                    const v4i_t w8 = decode16(wv[t][i][h].x, wv[t][i][h].y, mult);
+                    for (int h = 0; h < 4; ++h) {
+                        mult[h] = mu;
+                        m8[h] = -8.0f * mu;
+                    }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        mult[h] = srow[i] == 0.0f ? 0.0f : gv[t][i][h] / srow[i];
+                        m8[h] = -8.0f * mult[h];
+                    }
+                }
+                const uint32_t words[8] = {(uint32_t)wv[t][i][0][0], (uint32_t)wv[t][i][0][1],
+                                           (uint32_t)wv[t][i][0][2], (uint32_t)wv[t][i][0][3],
+                                           (uint32_t)wv[t][i][1][0], (uint32_t)wv[t][i][1][1],
+                                           (uint32_t)wv[t][i][1][2], (uint32_t)wv[t][i][1][3]};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const uint2 a = decode8(words[2 * h], mult[h], m8[h]);
+                    const uint2 b = decode8(words[2 * h + 1], mult[h], m8[h]);
+                    const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
 #pragma unroll
                     for (int j = 0; j < FM; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
@@ -216,17 +283,16 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
 
     // Epilogue: lane holds acc[i][j][r] = y[m][n], m = 16j + (l & 15),
     // n = n0 + 16i + 4(l >> 4) + r; the weight scale of row n is its s_row,
-    // which lives in the lane that decoded row n: lane (n - n0 - 16i) of the
-    // same 16-lane group, fetched with a cross-lane read.
+    // which lives in lane (n - n0 - 16i) of the same 16-lane group.
 #pragma unroll
     for (int i = 0; i < FNW; ++i) {
         float sw4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sw4[r] = __shfl(srow[i], 4 * fgrp + r, 64);
+        for (int r = 0; r < 4; ++r) sw4[r] = __shfl(srow[i], 4 * part + r, 64);
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int m = j * 16 + frow;
-            const int nb = n0 + i * 16 + 4 * fgrp;
+            const int nb = n0 + i * 16 + 4 * part;
             if (m >= M || nb >= N) continue;
             const float sam = sx[m];
             uint16_t o[4];
