@@ -142,6 +142,93 @@ def skinny_sweep(ck, torch, args) -> int:
     return 0
 
 
+def layer_sweep(ck, torch, args) -> int:
+    """The other layer configurations, each timed as one graph of back-to-back
+    steps: the up and down projections, q/k/v projections sharing one
+    quantised activation against quantising it three times, the rowwise
+    W8A8 layer and the grouped W4A8 layer (int8 activations, M = 4608)."""
+    dev = torch.device("cuda:0")
+    reps = max(args.steps // 4, 10)
+
+    def graph_ms(fn, n_steps):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_steps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n_steps
+
+    def line(case, m, n, k, ms, n_mm=1):
+        ops = 2.0 * m * n * k * n_mm
+        print(json.dumps({"case": case, "m": m, "n": n, "k": k, "ms_per_step": round(ms, 5),
+                          "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+                          "pct_int8_peak": round(100 * ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)}), flush=True)
+
+    def act(lay):
+        return torch.from_numpy(lay.x_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    for name in ("up_3072_12288", "down_12288_3072"):
+        cfg = workloads.WORKLOADS[name]
+        lay = workloads.make_layer(seed=0, **cfg)
+        x = act(lay)
+        wp, ws = ck.quantize_weight_convrot(torch.from_numpy(lay.weights[0]).to(dev), 128, 0)
+        xq = torch.empty((lay.m, lay.k // 2), dtype=torch.int8, device=dev)
+        sx = torch.empty((lay.m,), dtype=torch.float32, device=dev)
+        y = torch.empty((lay.m, lay.n), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+            ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+        line(f"w4a4 layer {name}", lay.m, lay.n, lay.k, graph_ms(step, reps))
+        del x, wp, ws, xq, sx, y, lay
+
+    cfg = workloads.WORKLOADS["qkv_3x3072"]
+    lay = workloads.make_layer(seed=0, **cfg)
+    m, k, n = lay.m, lay.k, lay.n
+    x = act(lay)
+    wts = [ck.quantize_weight_convrot(torch.from_numpy(w).to(dev), 128, 0) for w in lay.weights]
+    xq = torch.empty((m, k // 2), dtype=torch.int8, device=dev)
+    sx = torch.empty((m,), dtype=torch.float32, device=dev)
+    ys = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in wts]
+
+    def qkv_reuse():
+        ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+        for (wp, ws), y in zip(wts, ys):
+            ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+
+    def qkv_separate():
+        for (wp, ws), y in zip(wts, ys):
+            ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+            ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+    line("w4a4 q/k/v, one shared activation quantisation", m, n, k, graph_ms(qkv_reuse, reps), 3)
+    line("w4a4 q/k/v, activation quantised per projection", m, n, k, graph_ms(qkv_separate, reps), 3)
+    del wts, ys
+
+    wd = torch.from_numpy(lay.weights[0]).to(dev)
+    w8, ws8 = ck.quantize_weight_convrot_int8(wd)
+    xq8 = torch.empty((m, k), dtype=torch.int8, device=dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+    def w8a8_step():
+        ck.rotate_quantize_act(x, 128, 8, out=xq8, scales=sx)
+        ck.linear_w8a8(xq8, sx, w8, ws8, None, out=y)
+    line("w8a8 layer square_3072", m, n, k, graph_ms(w8a8_step, reps))
+
+    wg, gs = ck.quantize_weight_convrot(wd, 128, 128)
+    wsp = torch.empty((ck.w4a8_workspace_bytes(m, n, k, 0),), dtype=torch.uint8, device=dev)
+
+    def w4a8_step():
+        ck.rotate_quantize_act(x, 128, 8, out=xq8, scales=sx)
+        ck.linear_w4a8_grouped(xq8, sx, wg, gs, 128, 0, out=y, workspace=wsp)
+    line("w4a8-grouped layer square_3072 (decode + int8 GEMM)", m, n, k, graph_ms(w4a8_step, reps))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +239,8 @@ def main() -> int:
                     help="run only a plain 512 MiB device-to-device copy (scales the HBM byte counters)")
     ap.add_argument("--skinny", action="store_true",
                     help="run the skinny-M sweep (M in 1, 8, 16, 64; N,K = 12288,3072 and 5120,5120) instead")
+    ap.add_argument("--layers", action="store_true",
+                    help="time the other layer configurations (up, down, q/k/v reuse, W8A8, grouped W4A8) instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -173,6 +262,8 @@ def main() -> int:
 
     if args.skinny:
         return skinny_sweep(ck, torch, args)
+    if args.layers:
+        return layer_sweep(ck, torch, args)
 
     cfg = workloads.WORKLOADS["square_3072"]
     m, k, n = cfg["m"], cfg["k"], cfg["n"]

@@ -88,6 +88,22 @@ ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int
                                        int group, int8_t *w_packed, float *w_scales, void *stream);
 
 /*
+ * Offline weight preparation for the rowwise int8 (W8A8) ConvRot linear, the
+ * int8 layout that the int4 layout extends downward ([PR #63] Description;
+ * [FAST] Features: int8 layers in mixed checkpoints).
+ *   w        fp32 [n, ldw], the unrotated weight.
+ *   w_q8     int8 [n, k] (row stride k), codes in [-127, 127].
+ *   w_scales fp32 [n], absmax / 127 of each rotated row.
+ * Same rotation and rounding as ck4_quantize_weight_convrot; an all-zero row
+ * has scale 0 and codes 0. The result feeds ck4_linear_w8a8 together with
+ * ck4_rotate_quantize_act(bits = 8).
+ * Alignment: w and ldw*4 bytes 16-byte aligned; w_q8 16-byte aligned.
+ * Unsupported: k > 16384.
+ */
+ck4_status ck4_quantize_weight_convrot_int8(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                            int8_t *w_q8, float *w_scales, void *stream);
+
+/*
  * Dynamic activation rotation + quantisation, one fused pass per row
  * ([PR #63] Description: fused activation kernel, FHT rotation + rowwise int4
  * quantize + pack; [PR #97] What this adds: the int8 quantiser with

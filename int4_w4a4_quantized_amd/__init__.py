@@ -42,6 +42,7 @@ SIGNATURES = {
     "ck4_status_string": ([_I], ctypes.c_char_p),
     "ck4_last_error": ([], ctypes.c_char_p),
     "ck4_quantize_weight_convrot": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
+    "ck4_quantize_weight_convrot_int8": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
     "ck4_rotate_quantize_act": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "ck4_rotate_act_f32": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_linear_w4a4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
@@ -116,6 +117,18 @@ def quantize_weight_convrot(w: torch.Tensor, rot_block: int = 128, group: int = 
     return wp, ws
 
 
+def quantize_weight_convrot_int8(w: torch.Tensor, rot_block: int = 128):
+    """Offline W8A8 weight prep: fp32 [n, k] -> (int8 codes [n, k], fp32 row scales [n])."""
+    _need(w, torch.float32, "w", 2)
+    n, k = w.shape
+    wq = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    ws = torch.empty((n,), dtype=torch.float32, device=w.device)
+    _check("ck4_quantize_weight_convrot_int8",
+           lib().ck4_quantize_weight_convrot_int8(_ptr(w), n, k, w.stride(0), rot_block, _ptr(wq), _ptr(ws),
+                                                  _stream(w.device)))
+    return wq, ws
+
+
 def rotate_quantize_act(x: torch.Tensor, rot_block: int = 128, bits: int = 4, out=None, scales=None):
     """Dynamic rotate + quantise: bf16 [m, k] -> (int8 [m, k/2] (bits 4) or [m, k] (bits 8), fp32 [m])."""
     _need(x, torch.bfloat16, "x", 2)
@@ -186,6 +199,7 @@ def dequant_w4a8_grouped(w_packed: torch.Tensor, group_scales: torch.Tensor, gro
 
 
 def linear_w8a8(x_q8, x_scales, w8, w_scales, bias=None, out=None):
+    """Rowwise int8 linear from int8 activations and int8 weights -> bf16 [m, n]."""
     m, k = x_q8.shape
     n = w8.shape[0]
     if out is None:
@@ -194,6 +208,12 @@ def linear_w8a8(x_q8, x_scales, w8, w_scales, bias=None, out=None):
            lib().ck4_linear_w8a8(_ptr(x_q8), _ptr(x_scales), _ptr(w8), _ptr(w_scales), _ptr(bias), m, n, k,
                                  _ptr(out), out.stride(0), _stream(x_q8.device)))
     return out
+
+
+def w8a8_linear(x: torch.Tensor, w8: torch.Tensor, w_scales: torch.Tensor, bias=None, rot_block: int = 128):
+    """The whole W8A8 ConvRot layer: rotate + int8-quantise x, then the int8 GEMM + epilogue."""
+    x_q8, sx = rotate_quantize_act(x, rot_block, 8)
+    return linear_w8a8(x_q8, sx, w8, w_scales, bias)
 
 
 def w4a8_workspace_bytes(m: int, n: int, k: int, chunk_cols: int = 0) -> int:

@@ -127,6 +127,21 @@ ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int
                                                   static_cast<hipStream_t>(stream)));
 }
 
+ck4_status ck4_quantize_weight_convrot_int8(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                            int8_t *w_q8, float *w_scales, void *stream) {
+    const char *fn = "ck4_quantize_weight_convrot_int8";
+    if (!w || !w_q8 || !w_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
+    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
+    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (!aligned(w_q8, 16) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
+    if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 1, 0, w_q8, k, w_scales,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 ck4_status ck4_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, int bits,
                                    int8_t *x_q, float *x_scales, void *stream) {
     const char *fn = "ck4_rotate_quantize_act";

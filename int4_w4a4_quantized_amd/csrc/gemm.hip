@@ -724,7 +724,7 @@ hipError_t launch_skinny(const int8_t *a, const int8_t *b, const float *sa, cons
     // MAXS keeps a chunk's loads within the register budget of 2 waves/SIMD
     if (m <= 16) return launch_skinny_ks<S4, 1, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
     if (m <= 32) return launch_skinny_ks<S4, 2, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    return launch_skinny_ks<S4, 4, 2, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+    return launch_skinny_ks<S4, 4, 1, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
 }
 
 template <bool S4, int BM, int BN, int WAVES_M>

@@ -350,11 +350,11 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
     if (out_kind == 0)
         launch_mode<TIn, 0>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
                             stream);
-    else if constexpr (sizeof(TIn) == 4)
-        return hipErrorInvalidValue;  // fp32 rows are weights: packed int4 only
     else if (out_kind == 1)
         launch_mode<TIn, 1>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
                             stream);
+    else if constexpr (sizeof(TIn) == 4)
+        return hipErrorInvalidValue;  // fp32 rows are weights: codes only, no fp32 rotation output
     else
         launch_mode<TIn, 2>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
                             stream);

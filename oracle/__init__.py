@@ -168,6 +168,21 @@ def quantize_weight_convrot(w: np.ndarray, g: int = 128, group: int = 0):
     return packed, (s[:, 0].copy() if group == 0 else s)
 
 
+def quantize_weight_convrot_int8(w: np.ndarray, g: int = 128):
+    """W8A8 weight prep: the fp32 rotation, then rowwise absmax / 127 codes
+    -> (int8 [n, k], fp32 [n]). The int8 layout that the int4 one extends
+    ([PR63] Description)."""
+    return quantize_rows(rotate_f32(w, g), 0, 127)
+
+
+def linear_w8a8(x_bits: np.ndarray, w8: np.ndarray, w_scales: np.ndarray, bias: np.ndarray | None = None,
+                g: int = 128) -> np.ndarray:
+    """y bf16 bits [m, n] of the W8A8 ConvRot linear: int8 activations, int32 GEMM, epilogue."""
+    xq, sx = rotate_quantize_act(x_bits, g, bits=8)
+    acc = gemm_acc(xq, w8, xq.shape[1], bits=8)
+    return epilogue_bf16(acc, sx, w_scales, bias)
+
+
 def rotate_quantize_act(x_bits: np.ndarray, g: int = 128, bits: int = 4):
     """Dynamic activation quantisation -> (packed [m, k/2] or int8 [m, k], fp32 [m])."""
     x = _c(x_bits, np.uint16)

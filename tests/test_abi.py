@@ -79,6 +79,10 @@ def test_rotate_validation(L):
     assert f(FAKE, -1, 256, 256, 128, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
     r = L.ck4_rotate_act_f32
     assert r(FAKE, 4, 256, 256, 128, NULL, NULL) == ck.CK4_ERR_INVALID
+    w8 = L.ck4_quantize_weight_convrot_int8
+    assert w8(FAKE, 4, 256, 256, 128, NULL, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert w8(FAKE, 4, 256, 256, 128, ODD, FAKE, NULL) == ck.CK4_ERR_INVALID  # w_q8 alignment
+    assert w8(FAKE, 4, 384, 384, 256, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % rot_block
     w = L.ck4_quantize_weight_convrot
     assert w(FAKE, 4, 256, 256, 128, 48, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group
     assert w(FAKE, 4, 256, 256, 128, 512, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group > k

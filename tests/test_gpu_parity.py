@@ -244,6 +244,51 @@ def test_w4a8_fused_matches_chunked_for_all_groups(ck, m, group):
 
 
 # --------------------------------------------------------------------------
+# W8A8 rowwise ConvRot linear
+
+
+@pytest.mark.parametrize("n,k,rb", [(64, 256, 128), (257, 3072, 128), (40, 1024, 64), (9, 4096, 256), (3, 12288, 128)])
+def test_w8_weight_quant_bitexact(ck, n, k, rb):
+    rng = np.random.default_rng(1000 + n)
+    w = workloads.make_weight(rng, n, k)
+    w[1] = 0
+    wq, ws = ck.quantize_weight_convrot_int8(torch.from_numpy(w).cuda(), rb)
+    wq_ref, ws_ref = oracle.quantize_weight_convrot_int8(w, rb)
+    assert np.array_equal(host(ws).view(np.uint32), ws_ref.view(np.uint32))
+    assert np.array_equal(host(wq), wq_ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 256, 256), (130, 200, 768), (1, 77, 512), (16, 1000, 3072), (300, 96, 384)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_w8a8_linear(ck, m, n, k, with_bias):
+    rng = np.random.default_rng(1100 + m + n)
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    bias = rng.standard_normal(n).astype(np.float32) if with_bias else None
+    w8, ws = oracle.quantize_weight_convrot_int8(w)
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    y = bf16_host_bits(ck.w8a8_linear(dev_bf16(xb), torch.from_numpy(w8).cuda(), torch.from_numpy(ws).cuda(), bd))
+    ref = oracle.linear_w8a8(xb, w8, ws, bias)
+    if bias is None:
+        assert_bf16_close(y, ref)
+    else:
+        assert_bf16_close(y, ref, atol=2.0 ** -21 * k)
+
+
+def test_w8a8_full_size_square_layer(ck):
+    lay = workloads.make_layer(seed=0, **workloads.WORKLOADS["square_3072"])
+    m, k = lay.m, lay.k
+    w8, ws = ck.quantize_weight_convrot_int8(torch.from_numpy(lay.weights[0]).cuda())
+    w8_ref, ws_ref = oracle.quantize_weight_convrot_int8(lay.weights[0])
+    assert np.array_equal(host(w8), w8_ref) and np.array_equal(host(ws).view(np.uint32), ws_ref.view(np.uint32))
+    y = bf16_host_bits(ck.w8a8_linear(dev_bf16(lay.x_bf16), w8, ws))
+    rows = _sample_rows(m, 30, 2)
+    xq_ref, sx_ref = oracle.rotate_quantize_act(np.ascontiguousarray(lay.x_bf16[rows]), bits=8)
+    acc_ref = oracle.gemm_acc(xq_ref, w8_ref, k, bits=8)
+    assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref, ws_ref))
+
+
+# --------------------------------------------------------------------------
 # Full-size layers, in the launch configuration the benchmark times
 
 

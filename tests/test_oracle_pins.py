@@ -400,3 +400,40 @@ def test_w4a8_linear_close_to_float():
     # W4 weights dominate the error; the pages report 0.02-0.055 relative for
     # their eager W4A8 path against full precision.
     assert rel < 0.15
+
+
+# --------------------------------------------------------------------------
+# W8A8 (the int8 layout the int4 one extends)
+
+
+def test_w8_weight_prep_equals_activation_path_on_bf16_values():
+    # Weights that are exact bf16 values take the same fp32 rotation and the
+    # same absmax/127 quantiser whether they enter as fp32 (weight prep) or
+    # as bf16 (dynamic activation path): two separate oracle code paths.
+    rng = np.random.default_rng(41)
+    xb = workloads.make_activations(rng, 9, 512)
+    w = workloads.bf16_bits_to_f32(xb)
+    q_w, s_w = oracle.quantize_weight_convrot_int8(w)
+    q_x, s_x = oracle.rotate_quantize_act(xb, bits=8)
+    assert np.array_equal(q_w, q_x)
+    assert np.array_equal(s_w.view(np.uint32), s_x.view(np.uint32))
+    assert np.abs(q_w).max() == 127
+
+
+def test_w8a8_linear_within_quantisation_error_of_float():
+    rng = np.random.default_rng(42)
+    m, k, n = 12, 768, 40
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    w8, ws = oracle.quantize_weight_convrot_int8(w)
+    y = oracle.bf16_bits_to_f64(oracle.linear_w8a8(xb, w8, ws))
+    ref = oracle.bf16_bits_to_f64(xb) @ w.astype(np.float64).T
+    # int8 codes: per-element error <= s/2 on both sides; bound the dot product
+    xr = oracle.rotate_f64(oracle.bf16_bits_to_f64(xb))
+    wr = oracle.rotate_f64(w.astype(np.float64))
+    sx = np.abs(xr).max(axis=1) / 127
+    sw = np.abs(wr).max(axis=1) / 127
+    bound = (np.abs(xr).sum(axis=1)[:, None] * sw[None, :] / 2 + sx[:, None] * np.abs(wr).sum(axis=1)[None, :] / 2
+             + k * sx[:, None] * sw[None, :] / 4)
+    err = np.abs(y - ref)
+    assert np.all(err <= bound * 1.01 + np.abs(ref) * 2 ** -7)
