@@ -187,6 +187,23 @@ def layer_sweep(ck, torch, args) -> int:
         line(f"w4a4 layer {name}", lay.m, lay.n, lay.k, graph_ms(step, reps))
         del x, wp, ws, xq, sx, y, lay
 
+    # Weight preparation (offline, HBM-bound): nearest and stochastic rounding
+    # of the up projection's weight, N=12288 x K=3072.
+    cfg = workloads.WORKLOADS["up_3072_12288"]
+    rng = np.random.default_rng(5)
+    wd = torch.from_numpy(workloads.make_weight(rng, cfg["n"], cfg["k"])).to(dev)
+    ud = torch.from_numpy(rng.random((cfg["n"], cfg["k"]), dtype=np.float32)).to(dev)
+    nk, nn = cfg["n"] * cfg["k"], cfg["n"]
+    for case, fn, byts in (
+            ("weight prep, nearest rounding", lambda: ck.quantize_weight_convrot(wd, 128, 0), nk * 4 + nk // 2 + 4 * nn),
+            ("weight prep, stochastic rounding", lambda: ck.quantize_weight_convrot_sr(wd, ud, 128, 0),
+             nk * 8 + nk // 2 + 4 * nn)):
+        ms = graph_ms(fn, 20)
+        print(json.dumps({"case": f"{case} n={cfg['n']} k={cfg['k']}", "ms": round(ms, 5),
+                          "algorithmic_bytes": byts, "GBps": round(byts / (ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(byts / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+    del wd, ud
+
     cfg = workloads.WORKLOADS["qkv_3x3072"]
     lay = workloads.make_layer(seed=0, **cfg)
     m, k, n = lay.m, lay.k, lay.n

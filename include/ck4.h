@@ -39,6 +39,7 @@
  *  [PR #97]  comfy-kitchen "[PR #97] HIP port of #90: grouped W4A8 over the
  *            INT8 GEMM".
  *  [FAST]    "ComfyUI-INT4-Fast" extension listing.
+ *  [HIPT]    "Comfy-INT4-HIPtest" README.
  */
 #ifndef CK4_H
 #define CK4_H
@@ -86,6 +87,22 @@ const char *ck4_last_error(void);
  */
 ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
                                        int group, int8_t *w_packed, float *w_scales, void *stream);
+
+/*
+ * ck4_quantize_weight_convrot with stochastic instead of nearest rounding, for
+ * requantising a weight after a LoRA patch is baked into it ([HIPT] LoRA
+ * modes: "Stochastic").
+ *   u, ldu  fp32 [n, ldu]: one draw in [0, 1) per weight element, supplied
+ *           by the caller (the library has no random number generator).
+ *           Values outside [0, 1) are not checked; the formula below applies.
+ * Each code is clamp(floor(RN(r / s) + u), -7, 7) in fp32, with r the rotated
+ * weight and s its row (group = 0) or group scale, absmax / 7; an all-zero
+ * row or group has scale 0 and codes 0. Other arguments, layouts and errors as
+ * ck4_quantize_weight_convrot; u and ldu*4 bytes 16-byte aligned.
+ */
+ck4_status ck4_quantize_weight_convrot_sr(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                          int group, const float *u, int64_t ldu, int8_t *w_packed, float *w_scales,
+                                          void *stream);
 
 /*
  * Offline weight preparation for the rowwise int8 (W8A8) ConvRot linear, the

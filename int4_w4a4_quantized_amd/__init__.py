@@ -43,6 +43,7 @@ SIGNATURES = {
     "ck4_last_error": ([], ctypes.c_char_p),
     "ck4_quantize_weight_convrot": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "ck4_quantize_weight_convrot_int8": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
+    "ck4_quantize_weight_convrot_sr": ([_P, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _P, _P], _I),
     "ck4_rotate_quantize_act": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "ck4_rotate_act_f32": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_linear_w4a4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
@@ -114,6 +115,19 @@ def quantize_weight_convrot(w: torch.Tensor, rot_block: int = 128, group: int = 
     _check("ck4_quantize_weight_convrot",
            lib().ck4_quantize_weight_convrot(_ptr(w), n, k, w.stride(0), rot_block, group, _ptr(wp), _ptr(ws),
                                              _stream(w.device)))
+    return wp, ws
+
+
+def quantize_weight_convrot_sr(w: torch.Tensor, u: torch.Tensor, rot_block: int = 128, group: int = 0):
+    """Weight prep with stochastic rounding; u fp32 [n, k] holds one draw in [0, 1) per element."""
+    _need(w, torch.float32, "w", 2)
+    _need(u, torch.float32, "u", 2)
+    n, k = w.shape
+    wp = torch.empty((n, k // 2), dtype=torch.int8, device=w.device)
+    ws = torch.empty((n,) if group == 0 else (n, k // group), dtype=torch.float32, device=w.device)
+    _check("ck4_quantize_weight_convrot_sr",
+           lib().ck4_quantize_weight_convrot_sr(_ptr(w), n, k, w.stride(0), rot_block, group, _ptr(u), u.stride(0),
+                                                _ptr(wp), _ptr(ws), _stream(w.device)))
     return wp, ws
 
 

@@ -127,6 +127,26 @@ ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int
                                                   static_cast<hipStream_t>(stream)));
 }
 
+ck4_status ck4_quantize_weight_convrot_sr(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                          int group, const float *u, int64_t ldu, int8_t *w_packed, float *w_scales,
+                                          void *stream) {
+    const char *fn = "ck4_quantize_weight_convrot_sr";
+    if (!w || !u || !w_packed || !w_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
+    if (ldw < k || ldu < k) return fail(CK4_ERR_INVALID, "%s: ldw or ldu < k", fn);
+    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (!aligned(u, 16) || (ldu * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: u/ldu not 16-byte aligned", fn);
+    if (!aligned(w_packed, 8) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
+    if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (group != 0 && (!pow2(group) || group < 16 || group > 1024 || k % group != 0))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need 0 or a power of two in [16, 1024] dividing k)", fn,
+                    group);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2, w_scales,
+                                                  static_cast<hipStream_t>(stream), u, ldu));
+}
+
 ck4_status ck4_quantize_weight_convrot_int8(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
                                             int8_t *w_q8, float *w_scales, void *stream) {
     const char *fn = "ck4_quantize_weight_convrot_int8";

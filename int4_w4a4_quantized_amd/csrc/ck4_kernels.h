@@ -11,9 +11,11 @@ namespace ck4 {
 //   in_kind   0: bf16 input, 1: fp32 input
 //   out_kind  0: packed int4 (+ scales), 1: int8 codes (+ scales), 2: fp32 rotation
 //   group     0: one scale per row; > 0: one scale per `group` elements (int4 only)
+//   u, ldu    fp32 input only: if u is not null, stochastic rounding with the
+//             draw u[row * ldu + col] in [0, 1) for each element
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
-                               int out_kind, int group, void *out, int64_t ldo, float *scales,
-                               hipStream_t stream);
+                               int out_kind, int group, void *out, int64_t ldo, float *scales, hipStream_t stream,
+                               const float *u = nullptr, int64_t ldu = 0);
 
 // Integer GEMM acc[m, n] = sum_k a[m, k] b[n, k] on int8 MFMA, with a rank-one
 // bf16 epilogue (out_i32 == false) or an int32 store (out_i32 == true).

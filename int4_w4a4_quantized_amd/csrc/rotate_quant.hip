@@ -157,6 +157,17 @@ __device__ __forceinline__ uint32_t code_exact(float r, float s, float qmax) {
     return (uint32_t)((int)t + BIAS);
 }
 
+// Stochastic rounding with a caller-supplied draw uv in [0, 1):
+// clamp(floor(RN(r / s) + uv), -qmax, qmax) in fp32, biased like code_exact.
+template <int BIAS>
+__device__ __forceinline__ uint32_t code_sr(float r, float s, float uv, float qmax) {
+    if (s == 0.0f) return (uint32_t)BIAS;
+    const float x = r / s;
+    float t = floorf(x + uv);
+    t = fminf(fmaxf(t, -qmax), qmax);
+    return (uint32_t)((int)t + BIAS);
+}
+
 // 8 biased int4 codes (low byte q + 8) -> one word, element 2j in the low
 // nibble of byte j: pairs are joined with one shift-or (bits above 7 are
 // don't-care), the four low bytes gathered with byte permutes, and the bias
@@ -184,7 +195,8 @@ __device__ __forceinline__ uint32_t pack4_bytes(const uint32_t *c) {
 template <typename TIn, int OUT, int NCH, bool WAVE_ROW, int LPB>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__restrict__ x, int64_t rows, int64_t ldx,
                                                                   int k, float c, int group, void *__restrict__ out,
-                                                                  int64_t ldo, float *__restrict__ scales) {
+                                                                  int64_t ldo, float *__restrict__ scales,
+                                                                  const float *__restrict__ u, int64_t ldu) {
     __shared__ float red[kThreads / 64];
     const int lane = threadIdx.x & 63;
     const int64_t row = WAVE_ROW ? (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6) : blockIdx.x;
@@ -250,7 +262,24 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             const int ch = tid + j * nthreads;
             if (ch >= nchunks) continue;
             uint32_t code[kElems];
-            if (group == 0) {
+            // stochastic rounding (weights only): one draw per element
+            float uv[kElems];
+            const bool sr = sizeof(TIn) == 4 && u != nullptr;
+            if (sr) {
+                const float4 *up = reinterpret_cast<const float4 *>(u + row * ldu + (int64_t)ch * kElems);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float4 t = up[i];
+                    uv[4 * i] = t.x;
+                    uv[4 * i + 1] = t.y;
+                    uv[4 * i + 2] = t.z;
+                    uv[4 * i + 3] = t.w;
+                }
+            }
+            if (group == 0 && sr) {
+#pragma unroll
+                for (int i = 0; i < kElems; ++i) code[i] = code_sr<BIAS>(v[j][i], s_row, uv[i], qmax);
+            } else if (group == 0) {
                 if (fast_row) {
 #pragma unroll
                     for (int i = 0; i < kElems; ++i) code[i] = code_fast<BIAS>(v[j][i], s_row, y_row);
@@ -268,8 +297,13 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
                 const float s = gmax / qmax;
                 const int lanes_per_group = group / kElems;
                 if ((ch % lanes_per_group) == 0) scales[(int64_t)row * (k / group) + ch / lanes_per_group] = s;
+                if (sr) {
 #pragma unroll
-                for (int i = 0; i < kElems; ++i) code[i] = code_exact<BIAS>(v[j][i], s, qmax);
+                    for (int i = 0; i < kElems; ++i) code[i] = code_sr<BIAS>(v[j][i], s, uv[i], qmax);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kElems; ++i) code[i] = code_exact<BIAS>(v[j][i], s, qmax);
+                }
             }
             if constexpr (OUT == 0) {
                 const uint32_t w0 = pack8_biased(code), w1 = pack8_biased(code + 8);
@@ -286,61 +320,62 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
 
 template <typename TIn, int OUT, bool WAVE_ROW, int LPB>
 void launch_lpb(const TIn *x, int nch, dim3 grid, dim3 block, int64_t rows, int64_t ldx, int k, float c, int group,
-                void *out, int64_t ldo, float *scales, hipStream_t stream) {
+                void *out, int64_t ldo, float *scales, const float *u, int64_t ldu, hipStream_t stream) {
     switch (nch) {
     case 1:
         rotate_quant_kernel<TIn, OUT, 1, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales);
+                                                                                     ldo, scales, u, ldu);
         break;
     case 2:
         rotate_quant_kernel<TIn, OUT, 2, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales);
+                                                                                     ldo, scales, u, ldu);
         break;
     case 3:
         rotate_quant_kernel<TIn, OUT, 3, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales);
+                                                                                     ldo, scales, u, ldu);
         break;
     default:
         rotate_quant_kernel<TIn, OUT, 4, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales);
+                                                                                     ldo, scales, u, ldu);
         break;
     }
 }
 
 template <typename TIn, int OUT, bool WAVE_ROW>
 void launch_out(const TIn *x, int nch, dim3 grid, dim3 block, int64_t rows, int64_t ldx, int k, int lanes_per_block,
-                float c, int group, void *out, int64_t ldo, float *scales, hipStream_t stream) {
+                float c, int group, void *out, int64_t ldo, float *scales, const float *u, int64_t ldu,
+                hipStream_t stream) {
     switch (lanes_per_block) {
-    case 1: launch_lpb<TIn, OUT, WAVE_ROW, 1>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
-    case 2: launch_lpb<TIn, OUT, WAVE_ROW, 2>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
-    case 4: launch_lpb<TIn, OUT, WAVE_ROW, 4>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
-    case 8: launch_lpb<TIn, OUT, WAVE_ROW, 8>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
-    case 16: launch_lpb<TIn, OUT, WAVE_ROW, 16>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
-    case 32: launch_lpb<TIn, OUT, WAVE_ROW, 32>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
-    default: launch_lpb<TIn, OUT, WAVE_ROW, 64>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, stream); break;
+    case 1: launch_lpb<TIn, OUT, WAVE_ROW, 1>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
+    case 2: launch_lpb<TIn, OUT, WAVE_ROW, 2>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
+    case 4: launch_lpb<TIn, OUT, WAVE_ROW, 4>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
+    case 8: launch_lpb<TIn, OUT, WAVE_ROW, 8>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
+    case 16: launch_lpb<TIn, OUT, WAVE_ROW, 16>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
+    case 32: launch_lpb<TIn, OUT, WAVE_ROW, 32>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
+    default: launch_lpb<TIn, OUT, WAVE_ROW, 64>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
     }
 }
 
 template <typename TIn, int OUT>
 void launch_mode(const TIn *x, int nch, bool wave_row, int64_t rows, int64_t ldx, int k, int lanes_per_block, float c,
-                 int group, void *out, int64_t ldo, float *scales, hipStream_t stream) {
+                 int group, void *out, int64_t ldo, float *scales, const float *u, int64_t ldu, hipStream_t stream) {
     if (wave_row) {
         const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), block(kThreads);
         launch_out<TIn, OUT, true>(x, nch, grid, block, rows, ldx, k, lanes_per_block, c, group, out, ldo, scales,
-                                   stream);
+                                   u, ldu, stream);
     } else {
         const int nchunks = k / kElems;
         int threads = (nchunks + nch - 1) / nch;
         threads = (threads + 63) / 64 * 64;
         const dim3 grid((unsigned)rows), block((unsigned)threads);
         launch_out<TIn, OUT, false>(x, nch, grid, block, rows, ldx, k, lanes_per_block, c, group, out, ldo, scales,
-                                    stream);
+                                    u, ldu, stream);
     }
 }
 
 template <typename TIn>
 hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int rot_block, int out_kind, int group,
-                        void *out, int64_t ldo, float *scales, hipStream_t stream) {
+                        void *out, int64_t ldo, float *scales, const float *u, int64_t ldu, hipStream_t stream) {
     const int nchunks = (int)(k / kElems);
     // a row fits one wavefront when it is at most 64 lanes x kMaxChunks chunks
     const bool wave_row = nchunks <= 64 * kMaxChunks;
@@ -349,28 +384,28 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
     const int lanes_per_block = rot_block / kElems;
     if (out_kind == 0)
         launch_mode<TIn, 0>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
-                            stream);
+                            u, ldu, stream);
     else if (out_kind == 1)
         launch_mode<TIn, 1>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
-                            stream);
+                            u, ldu, stream);
     else if constexpr (sizeof(TIn) == 4)
         return hipErrorInvalidValue;  // fp32 rows are weights: codes only, no fp32 rotation output
     else
         launch_mode<TIn, 2>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
-                            stream);
+                            u, ldu, stream);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
-                               int out_kind, int group, void *out, int64_t ldo, float *scales,
-                               hipStream_t stream) {
+                               int out_kind, int group, void *out, int64_t ldo, float *scales, hipStream_t stream,
+                               const float *u, int64_t ldu) {
     if (in_kind == 0)
         return launch_typed(static_cast<const uint16_t *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo,
-                            scales, stream);
-    return launch_typed(static_cast<const float *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo, scales,
-                        stream);
+                            scales, nullptr, 0, stream);
+    return launch_typed(static_cast<const float *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo, scales, u,
+                        ldu, stream);
 }
 
 }  // namespace ck4

@@ -53,6 +53,8 @@ def lib():
             "ck4o_rotate_rows_bf16": ([P, I64, I64, I64, I, P], None),
             "ck4o_rotate_rows_f64": ([P, I64, I64, I, P], None),
             "ck4o_quantize_rows": ([P, I64, I64, I, I, P, P], None),
+            "ck4o_quantize_rows_sr": ([P, P, I64, I64, I64, I, I, P, P], None),
+            "ck4o_quantize_weight_convrot_sr": ([P, I64, I64, I64, I, I, P, I64, P, P], None),
             "ck4o_pack_int4": ([P, I64, P], None),
             "ck4o_unpack_int4": ([P, I64, P], None),
             "ck4o_quantize_weight_convrot": ([P, I64, I64, I64, I, I, P, P], None),
@@ -181,6 +183,30 @@ def linear_w8a8(x_bits: np.ndarray, w8: np.ndarray, w_scales: np.ndarray, bias: 
     xq, sx = rotate_quantize_act(x_bits, g, bits=8)
     acc = gemm_acc(xq, w8, xq.shape[1], bits=8)
     return epilogue_bf16(acc, sx, w_scales, bias)
+
+
+def quantize_rows_sr(r: np.ndarray, u: np.ndarray, group: int = 0, qmax: int = 7):
+    """Stochastic-rounding quantisation with caller-supplied u in [0, 1)."""
+    r = _c(r, np.float32)
+    u = _c(u, np.float32)
+    m, k = r.shape
+    q = np.empty((m, k), np.int8)
+    ng = 1 if group == 0 else k // group
+    s = np.empty((m, ng), np.float32)
+    lib().ck4o_quantize_rows_sr(_p(r), _p(u), k, m, k, group, qmax, _p(q), _p(s))
+    return q, (s[:, 0].copy() if group == 0 else s)
+
+
+def quantize_weight_convrot_sr(w: np.ndarray, u: np.ndarray, g: int = 128, group: int = 0):
+    """Weight prep with stochastic rounding -> (packed int8 [n, k/2], fp32 scales)."""
+    w = _c(w, np.float32)
+    u = _c(u, np.float32)
+    n, k = w.shape
+    packed = np.empty((n, k // 2), np.int8)
+    ng = 1 if group == 0 else k // group
+    s = np.empty((n, ng), np.float32)
+    lib().ck4o_quantize_weight_convrot_sr(_p(w), n, k, k, g, group, _p(u), k, _p(packed), _p(s))
+    return packed, (s[:, 0].copy() if group == 0 else s)
 
 
 def rotate_quantize_act(x_bits: np.ndarray, g: int = 128, bits: int = 4):

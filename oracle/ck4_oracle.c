@@ -189,6 +189,46 @@ void ck4o_quantize_rows(const float *r, int64_t m, int64_t k, int group, int qma
     }
 }
 
+/* Stochastic-rounding quantisation ([HIPT] LoRA modes, "Stochastic": LoRA
+ * patches are baked into the weight with stochastic instead of nearest
+ * rounding, so small updates survive in expectation). Reading: the scale and
+ * the all-zero case are those of ck4o_quantize_rows; each element draws one
+ * u in [0, 1) (supplied by the caller, u[row * ldu + col]) and
+ *   t = RN(RN(v / s) + u)   (fp32),   q = clamp(floor(t), -qmax, qmax),
+ * so q is floor(v/s) or floor(v/s) + 1 with E[q] = v/s up to fp32 rounding. */
+void ck4o_quantize_rows_sr(const float *r, const float *u, int64_t ldu, int64_t m, int64_t k, int group, int qmax,
+                           int8_t *q, float *scales) {
+    const int64_t gs = group > 0 ? group : k;
+    const int64_t ng = k / gs;
+    const float fq = (float)qmax;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < m; row++) {
+        for (int64_t gi = 0; gi < ng; gi++) {
+            const float *v = r + row * k + gi * gs;
+            const float *uv = u + row * ldu + gi * gs;
+            int8_t *out = q + row * k + gi * gs;
+            float amax = 0.0f;
+            for (int64_t j = 0; j < gs; j++) {
+                float a = fabsf(v[j]);
+                if (a > amax) amax = a;
+            }
+            float s = amax / fq;
+            scales[row * ng + gi] = s;
+            for (int64_t j = 0; j < gs; j++) {
+                if (s == 0.0f) {
+                    out[j] = 0;
+                    continue;
+                }
+                float x = v[j] / s;
+                float t = floorf(x + uv[j]);
+                if (t > fq) t = fq;
+                if (t < -fq) t = -fq;
+                out[j] = (int8_t)t;
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------- */
 /* Low-nibble-first packing of signed int4 pairs ([PR63]: "packed signed int4
  * pairs (low-nibble-first, [N, K/2] int8 container)"; exact round trip). */
@@ -223,6 +263,18 @@ void ck4o_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int64_t 
     int8_t *q = (int8_t *)malloc((size_t)(n * k));
     ck4o_rotate_rows_f32(w, n, k, ldw, g, r);
     ck4o_quantize_rows(r, n, k, group, 7, q, scales);
+    ck4o_pack_int4(q, n * k, packed);
+    free(q);
+    free(r);
+}
+
+/* The weight preparation above with stochastic rounding (u fp32 [n, ldu]). */
+void ck4o_quantize_weight_convrot_sr(const float *w, int64_t n, int64_t k, int64_t ldw, int g, int group,
+                                     const float *u, int64_t ldu, int8_t *packed, float *scales) {
+    float *r = (float *)malloc((size_t)(n * k) * sizeof(float));
+    int8_t *q = (int8_t *)malloc((size_t)(n * k));
+    ck4o_rotate_rows_f32(w, n, k, ldw, g, r);
+    ck4o_quantize_rows_sr(r, u, ldu, n, k, group, 7, q, scales);
     ck4o_pack_int4(q, n * k, packed);
     free(q);
     free(r);

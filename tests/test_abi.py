@@ -79,6 +79,11 @@ def test_rotate_validation(L):
     assert f(FAKE, -1, 256, 256, 128, 4, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
     r = L.ck4_rotate_act_f32
     assert r(FAKE, 4, 256, 256, 128, NULL, NULL) == ck.CK4_ERR_INVALID
+    sr = L.ck4_quantize_weight_convrot_sr
+    assert sr(FAKE, 4, 256, 256, 128, 0, NULL, 256, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID  # u null
+    assert sr(FAKE, 4, 256, 256, 128, 0, ODD, 256, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID  # u alignment
+    assert sr(FAKE, 4, 256, 256, 128, 0, FAKE, 200, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID  # ldu < k
+    assert sr(FAKE, 4, 256, 256, 128, 48, FAKE, 256, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group
     w8 = L.ck4_quantize_weight_convrot_int8
     assert w8(FAKE, 4, 256, 256, 128, NULL, FAKE, NULL) == ck.CK4_ERR_INVALID
     assert w8(FAKE, 4, 256, 256, 128, ODD, FAKE, NULL) == ck.CK4_ERR_INVALID  # w_q8 alignment

@@ -244,6 +244,33 @@ def test_w4a8_fused_matches_chunked_for_all_groups(ck, m, group):
 
 
 # --------------------------------------------------------------------------
+# Stochastic-rounding weight requantisation
+
+
+@pytest.mark.parametrize("n,k,group", [(64, 256, 0), (257, 3072, 0), (33, 1024, 128), (12, 4096, 64), (5, 12288, 0)])
+def test_sr_weight_quant_bitexact(ck, n, k, group):
+    rng = np.random.default_rng(1200 + n)
+    w = workloads.make_weight(rng, n, k)
+    w[2] = 0
+    u = rng.random((n, k), dtype=np.float32)
+    u[0, :8] = [0.0, 0.5, 0.99999994, 0.25, 0.0, 0.75, 0.5, 0.0]
+    wp, ws = ck.quantize_weight_convrot_sr(torch.from_numpy(w).cuda(), torch.from_numpy(u).cuda(), 128, group)
+    wp_ref, ws_ref = oracle.quantize_weight_convrot_sr(w, u, group=group)
+    assert np.array_equal(host(ws).view(np.uint32), ws_ref.view(np.uint32))
+    assert np.array_equal(host(wp), wp_ref)
+
+
+def test_sr_weight_quant_row_stride(ck):
+    rng = np.random.default_rng(1300)
+    n, k = 40, 768
+    w = workloads.make_weight(rng, n, k)
+    u_wide = rng.random((n, k + 64), dtype=np.float32)
+    wp, ws = ck.quantize_weight_convrot_sr(torch.from_numpy(w).cuda(), torch.from_numpy(u_wide).cuda()[:, :k])
+    wp_ref, ws_ref = oracle.quantize_weight_convrot_sr(w, np.ascontiguousarray(u_wide[:, :k]))
+    assert np.array_equal(host(wp), wp_ref)
+
+
+# --------------------------------------------------------------------------
 # W8A8 rowwise ConvRot linear
 
 

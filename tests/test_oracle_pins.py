@@ -437,3 +437,57 @@ def test_w8a8_linear_within_quantisation_error_of_float():
              + k * sx[:, None] * sw[None, :] / 4)
     err = np.abs(y - ref)
     assert np.all(err <= bound * 1.01 + np.abs(ref) * 2 ** -7)
+
+
+# --------------------------------------------------------------------------
+# Stochastic-rounding requantisation (u supplied by the caller)
+
+
+def _quotients(r, s):
+    """fp32 r / s per row; 0 for the all-zero rows (s == 0)."""
+    sd = np.where(s == 0, np.float32(1), s).astype(np.float32)
+    return np.where(s[:, None] == 0, np.float32(0), r.astype(np.float32) / sd[:, None]).astype(np.float32)
+
+
+def test_sr_with_u_zero_is_floor_and_half_is_round_half_up():
+    rng = np.random.default_rng(51)
+    r = (rng.standard_normal((6, 256)) * 3).astype(np.float32)
+    r[2] = 0
+    q_near, s = oracle.quantize_rows(r)
+    x = _quotients(r, s)
+    q0, s0 = oracle.quantize_rows_sr(r, np.zeros_like(r))
+    assert np.array_equal(s0.view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(q0, np.clip(np.floor(x), -7, 7).astype(np.int8))
+    qh, _ = oracle.quantize_rows_sr(r, np.full_like(r, 0.5))
+    assert np.array_equal(qh, np.clip(np.floor(x + np.float32(0.5)), -7, 7).astype(np.int8))
+    assert not q0[2].any() and not qh[2].any()
+
+
+def test_sr_codes_are_floor_or_ceil_and_unbiased():
+    rng = np.random.default_rng(52)
+    r = (rng.standard_normal((1, 128)) * 2).astype(np.float32)
+    _, s = oracle.quantize_rows(r)
+    x = _quotients(r, s)[0]
+    draws = 4000
+    rr = np.repeat(r, draws, axis=0)
+    u = rng.random(rr.shape, dtype=np.float32)
+    q, _ = oracle.quantize_rows_sr(rr, u)
+    fl = np.floor(x)
+    assert np.all((q == fl) | (q == fl + 1))
+    # E[q] = x: each code is a Bernoulli(frac(x)) step above floor(x)
+    p = x - fl
+    sigma = np.sqrt(np.maximum(p * (1 - p), 1e-12) / draws)
+    assert np.all(np.abs(q.mean(axis=0) - x) <= 5 * sigma + 1e-6)
+
+
+def test_sr_weight_prep_matches_nearest_scales_and_packs():
+    rng = np.random.default_rng(53)
+    w = workloads.make_weight(rng, 17, 512)
+    w[4] = 0
+    u = rng.random(w.shape, dtype=np.float32)
+    for group in (0, 128):
+        wp, ws = oracle.quantize_weight_convrot_sr(w, u, group=group)
+        _, ws_near = oracle.quantize_weight_convrot(w, group=group)
+        assert np.array_equal(ws.view(np.uint32), ws_near.view(np.uint32))
+        q = oracle.unpack_int4(wp)
+        assert np.abs(q).max() <= 7 and not q[4].any()
