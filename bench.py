@@ -113,11 +113,12 @@ def skinny_sweep(ck, torch, args) -> int:
     warm = max(args.warmup // 10, 1)
     for n, k in workloads.SKINNY_NK:
         rng = np.random.default_rng(1)
-        w4, w8g = [], []
+        w4, w8g, w8e = [], [], []
         for _ in range(copies):
             w = torch.from_numpy(workloads.make_weight(rng, n, k)).to(dev)
             w4.append(ck.quantize_weight_convrot(w, 128, 0))
             w8g.append(ck.quantize_weight_convrot(w, 128, 128))
+            w8e.append(ck.quantize_weight_convrot_e4m3(w, 128, 128))
             del w
         for m in workloads.SKINNY_M:
             x = torch.from_numpy(workloads.make_activations(rng, m, k).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -139,6 +140,14 @@ def skinny_sweep(ck, torch, args) -> int:
             print(json.dumps({"case": f"w4a8-grouped skinny m={m} n={n} k={k}", "us_per_launch_graph": round(us8, 3),
                               "algorithmic_bytes": byts8, "GBps": round(byts8 / us8 / 1e3, 1),
                               "hbm_frac": round(byts8 / us8 / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
+            use = _graph_time_us(torch, [lambda c=c: ck.linear_w4a8_grouped(xq8, sx8, w8e[c][0], w8e[c][1], 128, 0,
+                                                                            out=y, workspace=ws)
+                                         for c in range(copies)], reps, warm)
+            byte8 = n * k // 2 + n * (k // 128) + m * k + 4 * m + 2 * m * n
+            print(json.dumps({"case": f"w4a8-grouped-e4m3-scales skinny m={m} n={n} k={k}",
+                              "us_per_launch_graph": round(use, 3), "algorithmic_bytes": byte8,
+                              "GBps": round(byte8 / use / 1e3, 1),
+                              "hbm_frac": round(byte8 / use / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
     return 0
 
 

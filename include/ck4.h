@@ -236,6 +236,32 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
                                    uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace,
                                    size_t ws_bytes, void *stream);
 
+
+/*
+ * Grouped W4A8 with FP8 E4M3 group scales ([PR #97] What this adds: group
+ * scales in fp32 or e4m3, one decode for both). E4M3 is the OCP format: sign,
+ * 4 exponent bits (bias 7), 3 mantissa bits, largest 448, no infinities.
+ *
+ * ck4_quantize_weight_convrot_e4m3: as ck4_quantize_weight_convrot with
+ *   group > 0, except that each group scale absmax / 7 is rounded to E4M3
+ *   (nearest, ties to even, saturating at 448), stored as one byte in
+ *   group_scales uint8 [n, k/group], and the group's codes are
+ *   clamp(rint(r / s8), -7, 7) against the value s8 that byte decodes to
+ *   (a byte that decodes to 0 gives codes 0).
+ * ck4_dequant_w4a8_grouped_e4m3, ck4_linear_w4a8_grouped_e4m3: as the fp32
+ *   versions; each scale byte decodes exactly to fp32 first, so the decode
+ *   and the linear are those of the decoded fp32 scales, bit for bit.
+ */
+ck4_status ck4_quantize_weight_convrot_e4m3(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                            int group, int8_t *w_packed, uint8_t *group_scales, void *stream);
+ck4_status ck4_dequant_w4a8_grouped_e4m3(const int8_t *w_packed, const uint8_t *group_scales, int64_t n, int64_t k,
+                                         int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales,
+                                         void *stream);
+ck4_status ck4_linear_w4a8_grouped_e4m3(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                        const uint8_t *group_scales, int64_t m, int64_t n, int64_t k, int group,
+                                        uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace,
+                                        size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,10 @@ SIGNATURES = {
     "ck4_linear_w8a8": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_w4a8_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
     "ck4_linear_w4a8_grouped": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t, _P], _I),
+    "ck4_quantize_weight_convrot_e4m3": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
+    "ck4_dequant_w4a8_grouped_e4m3": ([_P, _P, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
+    "ck4_linear_w4a8_grouped_e4m3": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t,
+                                      _P], _I),
 }
 
 
@@ -131,6 +135,18 @@ def quantize_weight_convrot_sr(w: torch.Tensor, u: torch.Tensor, rot_block: int 
     return wp, ws
 
 
+def quantize_weight_convrot_e4m3(w: torch.Tensor, rot_block: int = 128, group: int = 128):
+    """Grouped weight prep with E4M3 group scales -> (int8 [n, k/2], uint8 E4M3 bytes [n, k/group])."""
+    _need(w, torch.float32, "w", 2)
+    n, k = w.shape
+    wp = torch.empty((n, k // 2), dtype=torch.int8, device=w.device)
+    gs = torch.empty((n, k // group), dtype=torch.uint8, device=w.device)
+    _check("ck4_quantize_weight_convrot_e4m3",
+           lib().ck4_quantize_weight_convrot_e4m3(_ptr(w), n, k, w.stride(0), rot_block, group, _ptr(wp), _ptr(gs),
+                                                  _stream(w.device)))
+    return wp, gs
+
+
 def quantize_weight_convrot_int8(w: torch.Tensor, rot_block: int = 128):
     """Offline W8A8 weight prep: fp32 [n, k] -> (int8 codes [n, k], fp32 row scales [n])."""
     _need(w, torch.float32, "w", 2)
@@ -200,15 +216,18 @@ def w4a4_linear(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
 
 def dequant_w4a8_grouped(w_packed: torch.Tensor, group_scales: torch.Tensor, group: int = 128, n0: int = 0,
                          nc: int | None = None):
-    """Grouped int4 -> int8 decode of weight rows [n0, n0+nc) -> (int8 [nc, k], fp32 [nc])."""
+    """Grouped int4 -> int8 decode of weight rows [n0, n0+nc) -> (int8 [nc, k], fp32 [nc]).
+
+    group_scales: fp32, or uint8 holding E4M3 bytes.
+    """
     n, k = w_packed.shape[0], w_packed.shape[1] * 2
     if nc is None:
         nc = n - n0
     w8 = torch.empty((nc, k), dtype=torch.int8, device=w_packed.device)
     sr = torch.empty((nc,), dtype=torch.float32, device=w_packed.device)
-    _check("ck4_dequant_w4a8_grouped",
-           lib().ck4_dequant_w4a8_grouped(_ptr(w_packed), _ptr(group_scales), n, k, group, n0, nc, _ptr(w8),
-                                          _ptr(sr), _stream(w_packed.device)))
+    name = "ck4_dequant_w4a8_grouped_e4m3" if group_scales.dtype == torch.uint8 else "ck4_dequant_w4a8_grouped"
+    _check(name, getattr(lib(), name)(_ptr(w_packed), _ptr(group_scales), n, k, group, n0, nc, _ptr(w8), _ptr(sr),
+                                      _stream(w_packed.device)))
     return w8, sr
 
 
@@ -240,6 +259,7 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
 
     chunk_cols > 0: decode per column chunk + int8 GEMM; < 0: one decode pass
     + one GEMM; 0: the library's policy (the fused kernel for m <= 64).
+    group_scales: fp32, or uint8 holding E4M3 bytes.
     """
     m, k = x_q8.shape
     n = w_packed.shape[0]
@@ -248,8 +268,8 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
     need = w4a8_workspace_bytes(m, n, k, chunk_cols)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x_q8.device)
-    _check("ck4_linear_w4a8_grouped",
-           lib().ck4_linear_w4a8_grouped(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales), m, n, k,
-                                         group, _ptr(out), out.stride(0), chunk_cols, _ptr(workspace),
-                                         0 if workspace is None else workspace.numel(), _stream(x_q8.device)))
+    name = "ck4_linear_w4a8_grouped_e4m3" if group_scales.dtype == torch.uint8 else "ck4_linear_w4a8_grouped"
+    _check(name, getattr(lib(), name)(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales), m, n, k,
+                                      group, _ptr(out), out.stride(0), chunk_cols, _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(), _stream(x_q8.device)))
     return out

@@ -144,7 +144,25 @@ ck4_status ck4_quantize_weight_convrot_sr(const float *w, int64_t n, int64_t k, 
                     group);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2, w_scales,
-                                                  static_cast<hipStream_t>(stream), u, ldu));
+                                                  static_cast<hipStream_t>(stream), ck4::WeightOpts{u, ldu, false}));
+}
+
+ck4_status ck4_quantize_weight_convrot_e4m3(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                            int group, int8_t *w_packed, uint8_t *group_scales, void *stream) {
+    const char *fn = "ck4_quantize_weight_convrot_e4m3";
+    if (!w || !w_packed || !group_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
+    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
+    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (!aligned(w_packed, 8)) return fail(CK4_ERR_INVALID, "%s: w_packed misaligned", fn);
+    if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (!pow2(group) || group < 16 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [16, 1024] dividing k)", fn, group);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2,
+                                                  reinterpret_cast<float *>(group_scales),
+                                                  static_cast<hipStream_t>(stream), ck4::WeightOpts{nullptr, 0, true}));
 }
 
 ck4_status ck4_quantize_weight_convrot_int8(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
@@ -229,10 +247,12 @@ ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8
                       stream);
 }
 
-ck4_status ck4_dequant_w4a8_grouped(const int8_t *w_packed, const float *group_scales, int64_t n, int64_t k,
-                                    int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales,
-                                    void *stream) {
-    const char *fn = "ck4_dequant_w4a8_grouped";
+}  // extern "C"
+
+namespace {
+
+ck4_status dequant_w4a8(const char *fn, const int8_t *w_packed, const void *group_scales, bool e4m3, int64_t n,
+                        int64_t k, int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales, void *stream) {
     if (!w_packed || !group_scales || !w8 || !row_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0 || k <= 0 || nc <= 0) return fail(CK4_ERR_INVALID, "%s: n, k, nc must be positive", fn);
     if (n0 < 0 || n0 + nc > n) return fail(CK4_ERR_INVALID, "%s: rows [n0, n0+nc) outside [0, n)", fn);
@@ -242,8 +262,26 @@ ck4_status ck4_dequant_w4a8_grouped(const int8_t *w_packed, const float *group_s
         return fail(CK4_ERR_INVALID, "%s: w_packed / w8 not 16-byte aligned", fn);
     if (nc > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: nc too large", fn);
     if (ck4_status s = check_device(fn)) return s;
-    return launched(fn, ck4::launch_w4a8_decode(w_packed, group_scales, k, group, n0, nc, w8, row_scales,
+    return launched(fn, ck4::launch_w4a8_decode(w_packed, group_scales, e4m3, k, group, n0, nc, w8, row_scales,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+ck4_status ck4_dequant_w4a8_grouped(const int8_t *w_packed, const float *group_scales, int64_t n, int64_t k,
+                                    int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales,
+                                    void *stream) {
+    return dequant_w4a8("ck4_dequant_w4a8_grouped", w_packed, group_scales, false, n, k, group, n0, nc, w8,
+                        row_scales, stream);
+}
+
+ck4_status ck4_dequant_w4a8_grouped_e4m3(const int8_t *w_packed, const uint8_t *group_scales, int64_t n, int64_t k,
+                                         int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales,
+                                         void *stream) {
+    return dequant_w4a8("ck4_dequant_w4a8_grouped_e4m3", w_packed, group_scales, true, n, k, group, n0, nc, w8,
+                        row_scales, stream);
 }
 
 // Column chunk of the decode + int8 GEMM path; 0 means the fused kernel.
@@ -279,11 +317,13 @@ size_t ck4_w4a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t chunk_c
     return (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));
 }
 
-ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
-                                   const float *group_scales, int64_t m, int64_t n, int64_t k, int group,
-                                   uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace, size_t ws_bytes,
-                                   void *stream) {
-    const char *fn = "ck4_linear_w4a8_grouped";
+}  // extern "C"
+
+namespace {
+
+ck4_status linear_w4a8(const char *fn, const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                       const void *group_scales, bool e4m3, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
+                       int64_t ldy, int64_t chunk_cols, void *workspace, size_t ws_bytes, void *stream) {
     if (!x_q8 || !x_scales || !w_packed || !group_scales || !y)
         return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, 8)) return s;
@@ -300,8 +340,8 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
     if (ck4_status s = check_device(fn, &dev)) return s;
     const int64_t c = w4a8_chunk(m, n, k, chunk_cols, g_l2_bytes[dev]);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (c == 0) return launched(fn, ck4::launch_w4a8_fused(x_q8, x_scales, w_packed, group_scales, m, n, k, group,
-                                                           y, ldy, st));
+    if (c == 0) return launched(fn, ck4::launch_w4a8_fused(x_q8, x_scales, w_packed, group_scales, e4m3, m, n, k,
+                                                           group, y, ldy, st));
     const size_t need = (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));
     if (!workspace || ws_bytes < need)
         return fail(CK4_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", fn, workspace ? ws_bytes : 0, need);
@@ -309,12 +349,32 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
     float *srow = reinterpret_cast<float *>(static_cast<char *>(workspace) + align_up(c * k, 256));
     for (int64_t n0 = 0; n0 < n; n0 += c) {
         const int64_t nc = (n - n0) < c ? (n - n0) : c;
-        hipError_t e = ck4::launch_w4a8_decode(w_packed, group_scales, k, group, n0, nc, w8, srow, st);
+        hipError_t e = ck4::launch_w4a8_decode(w_packed, group_scales, e4m3, k, group, n0, nc, w8, srow, st);
         if (e != hipSuccess) return launched(fn, e);
         e = ck4::launch_gemm(false, x_q8, w8, x_scales, srow, nullptr, m, nc, k, false, y + n0, ldy, st);
         if (e != hipSuccess) return launched(fn, e);
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                   const float *group_scales, int64_t m, int64_t n, int64_t k, int group,
+                                   uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace, size_t ws_bytes,
+                                   void *stream) {
+    return linear_w4a8("ck4_linear_w4a8_grouped", x_q8, x_scales, w_packed, group_scales, false, m, n, k, group, y,
+                       ldy, chunk_cols, workspace, ws_bytes, stream);
+}
+
+ck4_status ck4_linear_w4a8_grouped_e4m3(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                        const uint8_t *group_scales, int64_t m, int64_t n, int64_t k, int group,
+                                        uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace,
+                                        size_t ws_bytes, void *stream) {
+    return linear_w4a8("ck4_linear_w4a8_grouped_e4m3", x_q8, x_scales, w_packed, group_scales, true, m, n, k, group,
+                       y, ldy, chunk_cols, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

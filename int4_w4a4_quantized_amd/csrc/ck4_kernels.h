@@ -7,15 +7,25 @@
 
 namespace ck4 {
 
-// Rotation + quantisation of rows (one workgroup per row).
+// Options of the weight path (fp32 input) of launch_rotate_quant.
+//   u, ldu      if u is not null: stochastic rounding with the draw
+//               u[row * ldu + col] in [0, 1) for each element
+//   scale_e4m3  grouped int4 only: group scales are stored as E4M3 bytes and
+//               the codes use the decoded scale
+struct WeightOpts {
+    const float *u = nullptr;
+    int64_t ldu = 0;
+    bool scale_e4m3 = false;
+};
+
+// Rotation + quantisation of rows (one wavefront or one workgroup per row).
 //   in_kind   0: bf16 input, 1: fp32 input
 //   out_kind  0: packed int4 (+ scales), 1: int8 codes (+ scales), 2: fp32 rotation
 //   group     0: one scale per row; > 0: one scale per `group` elements (int4 only)
-//   u, ldu    fp32 input only: if u is not null, stochastic rounding with the
-//             draw u[row * ldu + col] in [0, 1) for each element
+//   scales    fp32, or E4M3 bytes when wo.scale_e4m3
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
                                int out_kind, int group, void *out, int64_t ldo, float *scales, hipStream_t stream,
-                               const float *u = nullptr, int64_t ldu = 0);
+                               WeightOpts wo = WeightOpts{});
 
 // Integer GEMM acc[m, n] = sum_k a[m, k] b[n, k] on int8 MFMA, with a rank-one
 // bf16 epilogue (out_i32 == false) or an int32 store (out_i32 == true).
@@ -24,14 +34,15 @@ hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *s
                        const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
                        hipStream_t stream);
 
-// Grouped int4 -> int8 decode of weight rows [n0, n0 + nc).
-hipError_t launch_w4a8_decode(const int8_t *w_packed, const float *group_scales, int64_t k, int group,
+// Grouped int4 -> int8 decode of weight rows [n0, n0 + nc). group_scales are
+// fp32, or E4M3 bytes when scale_e4m3.
+hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, bool scale_e4m3, int64_t k, int group,
                               int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream);
 
 // Fused grouped W4A8 linear for m <= 64 (decode in registers + int8 MFMA +
 // epilogue), bit-identical to decode followed by the int8 GEMM.
 hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
-                             const float *group_scales, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
-                             int64_t ldy, hipStream_t stream);
+                             const void *group_scales, bool scale_e4m3, int64_t m, int64_t n, int64_t k, int group,
+                             uint16_t *y, int64_t ldy, hipStream_t stream);
 
 }  // namespace ck4

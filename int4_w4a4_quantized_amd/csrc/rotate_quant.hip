@@ -50,6 +50,7 @@
 #include <stdint.h>
 
 #include "ck4_kernels.h"
+#include "fp8_e4m3.h"
 
 namespace ck4 {
 namespace {
@@ -196,7 +197,7 @@ template <typename TIn, int OUT, int NCH, bool WAVE_ROW, int LPB>
 __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__restrict__ x, int64_t rows, int64_t ldx,
                                                                   int k, float c, int group, void *__restrict__ out,
                                                                   int64_t ldo, float *__restrict__ scales,
-                                                                  const float *__restrict__ u, int64_t ldu) {
+                                                                  WeightOpts wo) {
     __shared__ float red[kThreads / 64];
     const int lane = threadIdx.x & 63;
     const int64_t row = WAVE_ROW ? (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6) : blockIdx.x;
@@ -264,9 +265,9 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             uint32_t code[kElems];
             // stochastic rounding (weights only): one draw per element
             float uv[kElems];
-            const bool sr = sizeof(TIn) == 4 && u != nullptr;
+            const bool sr = sizeof(TIn) == 4 && wo.u != nullptr;
             if (sr) {
-                const float4 *up = reinterpret_cast<const float4 *>(u + row * ldu + (int64_t)ch * kElems);
+                const float4 *up = reinterpret_cast<const float4 *>(wo.u + row * wo.ldu + (int64_t)ch * kElems);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float4 t = up[i];
@@ -294,9 +295,17 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
 #pragma unroll
                 for (int i = 0; i < kElems; ++i) gmax = fmaxf(gmax, fabsf(v[j][i]));
                 for (int off = 1; off < group / kElems; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
-                const float s = gmax / qmax;
+                float s = gmax / qmax;
                 const int lanes_per_group = group / kElems;
-                if ((ch % lanes_per_group) == 0) scales[(int64_t)row * (k / group) + ch / lanes_per_group] = s;
+                const int64_t si = (int64_t)row * (k / group) + ch / lanes_per_group;
+                if (sizeof(TIn) == 4 && wo.scale_e4m3) {
+                    // the scale is stored as E4M3 and the codes use its decoded value
+                    const uint32_t b = e4m3_encode(s);
+                    s = e4m3_decode(b);
+                    if ((ch % lanes_per_group) == 0) reinterpret_cast<uint8_t *>(scales)[si] = (uint8_t)b;
+                } else if ((ch % lanes_per_group) == 0) {
+                    scales[si] = s;
+                }
                 if (sr) {
 #pragma unroll
                     for (int i = 0; i < kElems; ++i) code[i] = code_sr<BIAS>(v[j][i], s, uv[i], qmax);
@@ -320,62 +329,61 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
 
 template <typename TIn, int OUT, bool WAVE_ROW, int LPB>
 void launch_lpb(const TIn *x, int nch, dim3 grid, dim3 block, int64_t rows, int64_t ldx, int k, float c, int group,
-                void *out, int64_t ldo, float *scales, const float *u, int64_t ldu, hipStream_t stream) {
+                void *out, int64_t ldo, float *scales, WeightOpts wo, hipStream_t stream) {
     switch (nch) {
     case 1:
         rotate_quant_kernel<TIn, OUT, 1, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales, u, ldu);
+                                                                                     ldo, scales, wo);
         break;
     case 2:
         rotate_quant_kernel<TIn, OUT, 2, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales, u, ldu);
+                                                                                     ldo, scales, wo);
         break;
     case 3:
         rotate_quant_kernel<TIn, OUT, 3, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales, u, ldu);
+                                                                                     ldo, scales, wo);
         break;
     default:
         rotate_quant_kernel<TIn, OUT, 4, WAVE_ROW, LPB><<<grid, block, 0, stream>>>(x, rows, ldx, k, c, group, out,
-                                                                                     ldo, scales, u, ldu);
+                                                                                     ldo, scales, wo);
         break;
     }
 }
 
 template <typename TIn, int OUT, bool WAVE_ROW>
 void launch_out(const TIn *x, int nch, dim3 grid, dim3 block, int64_t rows, int64_t ldx, int k, int lanes_per_block,
-                float c, int group, void *out, int64_t ldo, float *scales, const float *u, int64_t ldu,
-                hipStream_t stream) {
+                float c, int group, void *out, int64_t ldo, float *scales, WeightOpts wo, hipStream_t stream) {
     switch (lanes_per_block) {
-    case 1: launch_lpb<TIn, OUT, WAVE_ROW, 1>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
-    case 2: launch_lpb<TIn, OUT, WAVE_ROW, 2>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
-    case 4: launch_lpb<TIn, OUT, WAVE_ROW, 4>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
-    case 8: launch_lpb<TIn, OUT, WAVE_ROW, 8>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
-    case 16: launch_lpb<TIn, OUT, WAVE_ROW, 16>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
-    case 32: launch_lpb<TIn, OUT, WAVE_ROW, 32>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
-    default: launch_lpb<TIn, OUT, WAVE_ROW, 64>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, u, ldu, stream); break;
+    case 1: launch_lpb<TIn, OUT, WAVE_ROW, 1>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, wo, stream); break;
+    case 2: launch_lpb<TIn, OUT, WAVE_ROW, 2>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, wo, stream); break;
+    case 4: launch_lpb<TIn, OUT, WAVE_ROW, 4>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, wo, stream); break;
+    case 8: launch_lpb<TIn, OUT, WAVE_ROW, 8>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, wo, stream); break;
+    case 16: launch_lpb<TIn, OUT, WAVE_ROW, 16>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, wo, stream); break;
+    case 32: launch_lpb<TIn, OUT, WAVE_ROW, 32>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, wo, stream); break;
+    default: launch_lpb<TIn, OUT, WAVE_ROW, 64>(x, nch, grid, block, rows, ldx, k, c, group, out, ldo, scales, wo, stream); break;
     }
 }
 
 template <typename TIn, int OUT>
 void launch_mode(const TIn *x, int nch, bool wave_row, int64_t rows, int64_t ldx, int k, int lanes_per_block, float c,
-                 int group, void *out, int64_t ldo, float *scales, const float *u, int64_t ldu, hipStream_t stream) {
+                 int group, void *out, int64_t ldo, float *scales, WeightOpts wo, hipStream_t stream) {
     if (wave_row) {
         const dim3 grid((unsigned)((rows + kThreads / 64 - 1) / (kThreads / 64))), block(kThreads);
         launch_out<TIn, OUT, true>(x, nch, grid, block, rows, ldx, k, lanes_per_block, c, group, out, ldo, scales,
-                                   u, ldu, stream);
+                                   wo, stream);
     } else {
         const int nchunks = k / kElems;
         int threads = (nchunks + nch - 1) / nch;
         threads = (threads + 63) / 64 * 64;
         const dim3 grid((unsigned)rows), block((unsigned)threads);
         launch_out<TIn, OUT, false>(x, nch, grid, block, rows, ldx, k, lanes_per_block, c, group, out, ldo, scales,
-                                    u, ldu, stream);
+                                    wo, stream);
     }
 }
 
 template <typename TIn>
 hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int rot_block, int out_kind, int group,
-                        void *out, int64_t ldo, float *scales, const float *u, int64_t ldu, hipStream_t stream) {
+                        void *out, int64_t ldo, float *scales, WeightOpts wo, hipStream_t stream) {
     const int nchunks = (int)(k / kElems);
     // a row fits one wavefront when it is at most 64 lanes x kMaxChunks chunks
     const bool wave_row = nchunks <= 64 * kMaxChunks;
@@ -384,15 +392,15 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
     const int lanes_per_block = rot_block / kElems;
     if (out_kind == 0)
         launch_mode<TIn, 0>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
-                            u, ldu, stream);
+                            wo, stream);
     else if (out_kind == 1)
         launch_mode<TIn, 1>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
-                            u, ldu, stream);
+                            wo, stream);
     else if constexpr (sizeof(TIn) == 4)
         return hipErrorInvalidValue;  // fp32 rows are weights: codes only, no fp32 rotation output
     else
         launch_mode<TIn, 2>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
-                            u, ldu, stream);
+                            wo, stream);
     return hipGetLastError();
 }
 
@@ -400,12 +408,12 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
 
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
                                int out_kind, int group, void *out, int64_t ldo, float *scales, hipStream_t stream,
-                               const float *u, int64_t ldu) {
+                               WeightOpts wo) {
     if (in_kind == 0)
         return launch_typed(static_cast<const uint16_t *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo,
-                            scales, nullptr, 0, stream);
-    return launch_typed(static_cast<const float *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo, scales, u,
-                        ldu, stream);
+                            scales, WeightOpts{}, stream);
+    return launch_typed(static_cast<const float *>(x), rows, k, ldx, rot_block, out_kind, group, out, ldo, scales, wo,
+                        stream);
 }
 
 }  // namespace ck4

@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include "ck4_kernels.h"
+#include "fp8_e4m3.h"
 
 namespace ck4 {
 namespace {
@@ -24,8 +25,9 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ int sext4(uint32_t nib) { return (int)(nib ^ 8u) - 8; }
 
+template <bool E4M3>
 __global__ __launch_bounds__(kThreads) void w4a8_decode_kernel(const int8_t *__restrict__ wp,
-                                                               const float *__restrict__ gs, int k, int group,
+                                                               const void *__restrict__ gs, int k, int group,
                                                                int64_t n0, int8_t *__restrict__ w8,
                                                                float *__restrict__ row_scales) {
     __shared__ float red[kThreads / 64];
@@ -33,10 +35,10 @@ __global__ __launch_bounds__(kThreads) void w4a8_decode_kernel(const int8_t *__r
     const int64_t row = n0 + i;
     const int tid = threadIdx.x;
     const int ng = k / group;
-    const float *sg = gs + row * ng;
+    auto sg = [&](int g) { return load_scale<E4M3>(gs, row * ng + g); };
 
     float smax = 0.0f;
-    for (int g = tid; g < ng; g += kThreads) smax = fmaxf(smax, sg[g]);
+    for (int g = tid; g < ng; g += kThreads) smax = fmaxf(smax, sg(g));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
     if ((tid & 63) == 0) red[tid >> 6] = smax;
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kThreads) void w4a8_decode_kernel(const int8_t *__r
     const int8_t *src = wp + row * (int64_t)(k / 2);
     int8_t *dst = w8 + (int64_t)i * k;
     for (int ch = tid; ch < nchunks; ch += kThreads) {
-        const float mult = srow == 0.0f ? 0.0f : sg[(ch * 16) / group] / srow;
+        const float mult = srow == 0.0f ? 0.0f : sg((ch * 16) / group) / srow;
         const uint2 p = *reinterpret_cast<const uint2 *>(src + ch * 8);
         const uint32_t words[2] = {p.x, p.y};
         uint32_t out[4] = {0, 0, 0, 0};
@@ -66,10 +68,14 @@ __global__ __launch_bounds__(kThreads) void w4a8_decode_kernel(const int8_t *__r
 
 }  // namespace
 
-hipError_t launch_w4a8_decode(const int8_t *w_packed, const float *group_scales, int64_t k, int group,
+hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, bool scale_e4m3, int64_t k, int group,
                               int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream) {
-    w4a8_decode_kernel<<<dim3((unsigned)nc), dim3(kThreads), 0, stream>>>(w_packed, group_scales, (int)k, group,
-                                                                          n0, w8, row_scales);
+    if (scale_e4m3)
+        w4a8_decode_kernel<true><<<dim3((unsigned)nc), dim3(kThreads), 0, stream>>>(w_packed, group_scales, (int)k,
+                                                                                    group, n0, w8, row_scales);
+    else
+        w4a8_decode_kernel<false><<<dim3((unsigned)nc), dim3(kThreads), 0, stream>>>(w_packed, group_scales, (int)k,
+                                                                                     group, n0, w8, row_scales);
     return hipGetLastError();
 }
 
@@ -149,10 +155,10 @@ __device__ __forceinline__ uint2 decode8(uint32_t w, float mult, float m8) {
 // assignment, so each slice's 64 products are 64 distinct k and the four
 // slices cover the step. A lane's 64 k lie in one weight group when the group
 // is at least 64 wide, which makes the scale division once per step.
-template <int FM, int FNW, int KS, int MAXS>
+template <int FM, int FNW, int KS, int MAXS, bool E4M3>
 __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__restrict__ X, const float *__restrict__ sx,
                                                            const int8_t *__restrict__ W,
-                                                           const float *__restrict__ gs, int M, int N, int K,
+                                                           const void *__restrict__ gs, int M, int N, int K,
                                                            int group, uint16_t *__restrict__ Y, int64_t ldy) {
     __shared__ v4i_t red[KS - 1][FNW][FM][64];
     const int lane = threadIdx.x & 63;
@@ -172,13 +178,13 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
     // Row scale of this lane's weight rows, (max group scale * 7) / 127: the
     // four lanes of a row split its groups, then combine.
     float srow[FNW];
-    const float *gsr[FNW];
+    int64_t gsr[FNW];  // index of the row's first group scale
 #pragma unroll
     for (int i = 0; i < FNW; ++i) {
         const int n = min(n0 + i * 16 + frow, N - 1);
-        gsr[i] = gs + (int64_t)n * ng;
+        gsr[i] = (int64_t)n * ng;
         float smax = 0.0f;
-        for (int g = part; g < ng; g += 4) smax = fmaxf(smax, gsr[i][g]);
+        for (int g = part; g < ng; g += 4) smax = fmaxf(smax, load_scale<E4M3>(gs, gsr[i] + g));
         smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
         smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
         srow[i] = (smax * 7.0f) / 127.0f;
@@ -211,12 +217,12 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
                     wv[t][i][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
                     wv[t][i][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 16, 0);
                     if (one_group) {
-                        const float g0 = gsr[i][kb / group];
+                        const float g0 = load_scale<E4M3>(gs, gsr[i] + kb / group);
 #pragma unroll
                         for (int h = 0; h < 4; ++h) gv[t][i][h] = g0;
                     } else {
 #pragma unroll
-                        for (int h = 0; h < 4; ++h) gv[t][i][h] = gsr[i][(kb + 16 * h) / group];
+                        for (int h = 0; h < 4; ++h) gv[t][i][h] = load_scale<E4M3>(gs, gsr[i] + (kb + 16 * h) / group);
                     }
                 }
 #pragma unroll
@@ -309,32 +315,42 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
     }
 }
 
-template <int FM, int FNW, int MAXS>
-hipError_t launch_fused_cfg(const int8_t *x, const float *sx, const int8_t *w, const float *gs, int64_t m, int64_t n,
+template <int FM, int FNW, int MAXS, bool E4M3>
+hipError_t launch_fused_cfg(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
                             int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream) {
     const int64_t groups = (n + 16 * FNW - 1) / (16 * FNW);
     dim3 grid((unsigned)groups);
     if (groups >= 1024) {
-        w4a8_fused_kernel<FM, FNW, 2, MAXS><<<grid, dim3(128), 0, stream>>>(x, sx, w, gs, (int)m, (int)n, (int)k, group,
-                                                                        y, ldy);
+        w4a8_fused_kernel<FM, FNW, 2, MAXS, E4M3><<<grid, dim3(128), 0, stream>>>(x, sx, w, gs, (int)m, (int)n,
+                                                                                (int)k, group, y, ldy);
     } else if (groups >= 512) {
-        w4a8_fused_kernel<FM, FNW, 4, MAXS><<<grid, dim3(256), 0, stream>>>(x, sx, w, gs, (int)m, (int)n, (int)k, group,
-                                                                        y, ldy);
+        w4a8_fused_kernel<FM, FNW, 4, MAXS, E4M3><<<grid, dim3(256), 0, stream>>>(x, sx, w, gs, (int)m, (int)n,
+                                                                                (int)k, group, y, ldy);
     } else {
-        w4a8_fused_kernel<FM, FNW, 8, MAXS><<<grid, dim3(512), 0, stream>>>(x, sx, w, gs, (int)m, (int)n, (int)k, group,
-                                                                        y, ldy);
+        w4a8_fused_kernel<FM, FNW, 8, MAXS, E4M3><<<grid, dim3(512), 0, stream>>>(x, sx, w, gs, (int)m, (int)n,
+                                                                                (int)k, group, y, ldy);
     }
     return hipGetLastError();
+}
+
+template <bool E4M3>
+hipError_t launch_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed, const void *group_scales,
+                        int64_t m, int64_t n, int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream) {
+    if (m <= 16)
+        return launch_fused_cfg<1, 1, 2, E4M3>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+    if (m <= 32)
+        return launch_fused_cfg<2, 1, 2, E4M3>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+    return launch_fused_cfg<4, 1, 1, E4M3>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
 }
 
 }  // namespace
 
 hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
-                             const float *group_scales, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
-                             int64_t ldy, hipStream_t stream) {
-    if (m <= 16) return launch_fused_cfg<1, 1, 2>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
-    if (m <= 32) return launch_fused_cfg<2, 1, 2>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
-    return launch_fused_cfg<4, 1, 1>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+                             const void *group_scales, bool scale_e4m3, int64_t m, int64_t n, int64_t k, int group,
+                             uint16_t *y, int64_t ldy, hipStream_t stream) {
+    if (scale_e4m3)
+        return launch_fused<true>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+    return launch_fused<false>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
 }
 
 }  // namespace ck4

@@ -54,6 +54,9 @@ def lib():
             "ck4o_rotate_rows_f64": ([P, I64, I64, I, P], None),
             "ck4o_quantize_rows": ([P, I64, I64, I, I, P, P], None),
             "ck4o_quantize_rows_sr": ([P, P, I64, I64, I64, I, I, P, P], None),
+            "ck4o_e4m3_decode": ([ctypes.c_uint8], ctypes.c_float),
+            "ck4o_e4m3_encode": ([ctypes.c_float], ctypes.c_uint8),
+            "ck4o_quantize_weight_convrot_e4m3": ([P, I64, I64, I64, I, I, P, P], None),
             "ck4o_quantize_weight_convrot_sr": ([P, I64, I64, I64, I, I, P, I64, P, P], None),
             "ck4o_pack_int4": ([P, I64, P], None),
             "ck4o_unpack_int4": ([P, I64, P], None),
@@ -207,6 +210,35 @@ def quantize_weight_convrot_sr(w: np.ndarray, u: np.ndarray, g: int = 128, group
     s = np.empty((n, ng), np.float32)
     lib().ck4o_quantize_weight_convrot_sr(_p(w), n, k, k, g, group, _p(u), k, _p(packed), _p(s))
     return packed, (s[:, 0].copy() if group == 0 else s)
+
+
+def e4m3_decode(b) -> np.ndarray:
+    """fp32 values of E4M3 bytes."""
+    b = np.asarray(b, np.uint8)
+    return np.array([lib().ck4o_e4m3_decode(int(v)) for v in b.ravel()], np.float32).reshape(b.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """E4M3 bytes of fp32 values (nearest, ties to even, saturating at 448)."""
+    x = np.asarray(x, np.float32)
+    return np.array([lib().ck4o_e4m3_encode(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def quantize_weight_convrot_e4m3(w: np.ndarray, g: int = 128, group: int = 128):
+    """Grouped weight prep with e4m3 group scales -> (packed int8 [n, k/2], uint8 [n, k/group])."""
+    w = _c(w, np.float32)
+    n, k = w.shape
+    packed = np.empty((n, k // 2), np.int8)
+    s8 = np.empty((n, k // group), np.uint8)
+    lib().ck4o_quantize_weight_convrot_e4m3(_p(w), n, k, k, g, group, _p(packed), _p(s8))
+    return packed, s8
+
+
+def linear_w4a8_grouped_e4m3(x_bits: np.ndarray, w_packed: np.ndarray, scales8: np.ndarray,
+                             group: int = 128, g: int = 128) -> np.ndarray:
+    """Grouped W4A8 linear with e4m3 group scales: the scales decode exactly to
+    fp32, then the same decode, int8 GEMM and epilogue as fp32 scales."""
+    return linear_w4a8_grouped(x_bits, w_packed, e4m3_decode(scales8), group, g)
 
 
 def rotate_quantize_act(x_bits: np.ndarray, g: int = 128, bits: int = 4):

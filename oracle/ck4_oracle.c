@@ -229,6 +229,40 @@ void ck4o_quantize_rows_sr(const float *r, const float *u, int64_t ldu, int64_t 
     }
 }
 
+/* FP8 E4M3 group scales ([PR97] What this adds: fp32 or e4m3 group scales).
+ * The OCP E4M3 format: sign, 4 exponent bits (bias 7), 3 mantissa bits, no
+ * infinities, S.1111.111 is NaN; normals (1 + m/8) 2^(e-7), e = 1..15,
+ * largest 448; subnormals (m/8) 2^-6. Reading for encoding (the pages name
+ * only the format): round to nearest, ties to even, computed in double;
+ * magnitudes at or above 448 saturate to 448. */
+float ck4o_e4m3_decode(uint8_t b) {
+    const int e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return (float)((b & 0x80) ? -v : v);
+}
+
+uint8_t ck4o_e4m3_encode(float xf) {
+    const double x = fabs((double)xf);
+    const uint8_t sign = signbit(xf) ? 0x80 : 0x00;
+    if (!(x < 448.0)) return sign | 0x7E;
+    if (x < ldexp(1.0, -6)) {                 /* subnormal: a multiple of 2^-9 */
+        const double m = nearbyint(x * 512.0); /* ties to even; 8 is the least normal */
+        return sign | (uint8_t)m;
+    }
+    int ex;
+    frexp(x, &ex);                 /* x = f 2^ex, f in [0.5, 1) */
+    int e = ex - 1;                /* x = F 2^e, F in [1, 2) */
+    double mm = nearbyint((ldexp(x, -e) - 1.0) * 8.0);
+    if (mm == 8.0) {
+        mm = 0.0;
+        e += 1;
+    }
+    const int be = e + 7;
+    if (be > 15 || (be == 15 && mm == 7.0)) return sign | 0x7E;
+    return sign | (uint8_t)((be << 3) | (int)mm);
+}
+
 /* ------------------------------------------------------------------------- */
 /* Low-nibble-first packing of signed int4 pairs ([PR63]: "packed signed int4
  * pairs (low-nibble-first, [N, K/2] int8 container)"; exact round trip). */
@@ -275,6 +309,46 @@ void ck4o_quantize_weight_convrot_sr(const float *w, int64_t n, int64_t k, int64
     int8_t *q = (int8_t *)malloc((size_t)(n * k));
     ck4o_rotate_rows_f32(w, n, k, ldw, g, r);
     ck4o_quantize_rows_sr(r, u, ldu, n, k, group, 7, q, scales);
+    ck4o_pack_int4(q, n * k, packed);
+    free(q);
+    free(r);
+}
+
+/* Grouped weight quantisation with e4m3 group scales: the fp32 group scale
+ * absmax / 7 is rounded to e4m3, and the codes are taken against the value
+ * that byte decodes to, clamp(rint(v / s8), -7, 7) (a scale that decodes to
+ * 0 gives codes 0). */
+void ck4o_quantize_weight_convrot_e4m3(const float *w, int64_t n, int64_t k, int64_t ldw, int g, int group,
+                                       int8_t *packed, uint8_t *scales8) {
+    float *r = (float *)malloc((size_t)(n * k) * sizeof(float));
+    int8_t *q = (int8_t *)malloc((size_t)(n * k));
+    ck4o_rotate_rows_f32(w, n, k, ldw, g, r);
+    const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < n; row++) {
+        for (int64_t gi = 0; gi < ng; gi++) {
+            const float *v = r + row * k + gi * group;
+            int8_t *out = q + row * k + gi * group;
+            float amax = 0.0f;
+            for (int64_t j = 0; j < group; j++) {
+                float a = fabsf(v[j]);
+                if (a > amax) amax = a;
+            }
+            const uint8_t b = ck4o_e4m3_encode(amax / 7.0f);
+            scales8[row * ng + gi] = b;
+            const float s = ck4o_e4m3_decode(b);
+            for (int64_t j = 0; j < group; j++) {
+                if (s == 0.0f) {
+                    out[j] = 0;
+                    continue;
+                }
+                float t = rintf(v[j] / s);
+                if (t > 7.0f) t = 7.0f;
+                if (t < -7.0f) t = -7.0f;
+                out[j] = (int8_t)t;
+            }
+        }
+    }
     ck4o_pack_int4(q, n * k, packed);
     free(q);
     free(r);

@@ -103,6 +103,13 @@ def test_w4a8_validation(L):
     assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, -1, NULL, 0, NULL) == ck.CK4_ERR_INVALID
     assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 200, 128, FAKE, 64, 0, FAKE, 1 << 20, NULL) == ck.CK4_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, 8, 64, 256, 128, FAKE, 64, 24, FAKE, 1 << 20, NULL) == ck.CK4_ERR_INVALID
+    e = L.ck4_quantize_weight_convrot_e4m3
+    assert e(FAKE, 4, 256, 256, 128, 0, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group 0 has no group scales
+    assert e(FAKE, 4, 256, 256, 128, 128, FAKE, NULL, NULL) == ck.CK4_ERR_INVALID
+    de = L.ck4_dequant_w4a8_grouped_e4m3
+    assert de(FAKE, FAKE, 64, 256, 128, 32, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    fe = L.ck4_linear_w4a8_grouped_e4m3
+    assert fe(FAKE, FAKE, FAKE, FAKE, 8, 64, 200, 128, FAKE, 64, 0, FAKE, 1 << 20, NULL) == ck.CK4_ERR_UNSUPPORTED
     l8 = L.ck4_linear_w8a8
     assert l8(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 192, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
 

@@ -244,6 +244,47 @@ def test_w4a8_fused_matches_chunked_for_all_groups(ck, m, group):
 
 
 # --------------------------------------------------------------------------
+# Grouped W4A8 with E4M3 group scales
+
+
+def _e4m3_weight(rng, n, k):
+    w = workloads.make_weight(rng, n, k)
+    w[1] = 0
+    w[2] *= 1e-6      # group scales in the E4M3 subnormal range
+    w[3] *= 3e4       # group scales above 448: saturate
+    return w
+
+
+@pytest.mark.parametrize("n,k,group", [(64, 256, 128), (40, 1024, 16), (33, 3072, 64), (20, 2048, 256)])
+def test_e4m3_weight_prep_and_decode_bitexact(ck, n, k, group):
+    rng = np.random.default_rng(1400 + n)
+    w = _e4m3_weight(rng, n, k)
+    wp, s8 = ck.quantize_weight_convrot_e4m3(torch.from_numpy(w).cuda(), 128, group)
+    wp_ref, s8_ref = oracle.quantize_weight_convrot_e4m3(w, group=group)
+    assert np.array_equal(host(s8), s8_ref)
+    assert np.array_equal(host(wp), wp_ref)
+    w8, sr = ck.dequant_w4a8_grouped(wp, s8, group)
+    w8_ref, sr_ref = oracle.decode_w4a8(wp_ref, oracle.e4m3_decode(s8_ref), group)
+    assert np.array_equal(host(sr).view(np.uint32), sr_ref.view(np.uint32))
+    assert np.array_equal(host(w8), w8_ref)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1000, 768), (16, 5120, 5120), (64, 130, 1024), (100, 300, 512)])
+def test_e4m3_linear_fused_chunked_single_equal_and_match_oracle(ck, m, n, k):
+    rng = np.random.default_rng(1500 + m)
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    wp_ref, s8_ref = oracle.quantize_weight_convrot_e4m3(w)
+    wpd, s8d = torch.from_numpy(wp_ref).cuda(), torch.from_numpy(s8_ref).cuda()
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    y0 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, s8d, 128, 0))
+    y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, s8d, 128, -1))
+    yc = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, s8d, 128, 256))
+    assert np.array_equal(y0, y1) and np.array_equal(y0, yc)
+    assert_bf16_close(y0, oracle.linear_w4a8_grouped_e4m3(xb, wp_ref, s8_ref))
+
+
+# --------------------------------------------------------------------------
 # Stochastic-rounding weight requantisation
 
 

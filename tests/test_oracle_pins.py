@@ -491,3 +491,61 @@ def test_sr_weight_prep_matches_nearest_scales_and_packs():
         assert np.array_equal(ws.view(np.uint32), ws_near.view(np.uint32))
         q = oracle.unpack_int4(wp)
         assert np.abs(q).max() <= 7 and not q[4].any()
+
+
+# --------------------------------------------------------------------------
+# E4M3 group scales (OCP FP8 E4M3: bias 7, largest 448, no infinities)
+
+
+def test_e4m3_decode_anchor_values_and_structure():
+    d = oracle.e4m3_decode(np.arange(256, dtype=np.uint8)).astype(np.float64)
+    assert d[0x7E] == 448.0 and d[0x08] == 2.0 ** -6 and d[0x01] == 2.0 ** -9
+    assert d[0x07] == 0.875 * 2.0 ** -6 and d[0x38] == 1.0 and d[0x00] == 0.0
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF])
+    pos = d[:0x7F]
+    assert np.all(np.diff(pos) > 0)                      # strictly increasing codes
+    assert np.array_equal(d[0x80:0xFF], -pos)            # sign bit
+    for e in range(1, 16):                               # spacing 2^(e-10) inside binade e
+        codes = [(e << 3) | m for m in range(8) if (e << 3) | m < 0x7F]
+        assert np.all(np.diff(d[codes]) == 2.0 ** (e - 10))
+
+
+def test_e4m3_encode_is_nearest_ties_even_saturating():
+    vals = oracle.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    rng = np.random.default_rng(61)
+    x = np.concatenate([rng.random(300) * 460, 2.0 ** rng.uniform(-12, 9, 300)]).astype(np.float32)
+    b = oracle.e4m3_encode(x)
+    got = oracle.e4m3_decode(b).astype(np.float64)
+    best = np.min(np.abs(x.astype(np.float64)[:, None] - vals[None, :]), axis=1)
+    inside = x.astype(np.float64) < 448
+    assert np.all(np.abs(x.astype(np.float64) - got)[inside] == best[inside])
+    assert np.all(b[~inside] == 0x7E)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    exact = mids.astype(np.float64) == (vals[:-1] + vals[1:]) / 2
+    bm = oracle.e4m3_encode(mids[exact])
+    assert np.all(bm % 2 == 0)                           # ties go to the even code
+    assert np.array_equal(oracle.e4m3_encode(vals.astype(np.float32)), np.arange(0x7F, dtype=np.uint8))
+    assert oracle.e4m3_encode(np.float32(1e6)) == 0x7E and oracle.e4m3_encode(np.float32(-1.0)) == 0xB8
+
+
+def test_e4m3_weight_prep_rounds_fp32_scales_and_bounds_codes():
+    rng = np.random.default_rng(62)
+    w = workloads.make_weight(rng, 9, 1024)
+    w[3] = 0
+    w[4] *= 1e-6          # scales in the subnormal range
+    for group in (32, 128):
+        wp, s8 = oracle.quantize_weight_convrot_e4m3(w, group=group)
+        _, s32 = oracle.quantize_weight_convrot(w, group=group)
+        assert np.array_equal(s8, oracle.e4m3_encode(s32))
+        sd = oracle.e4m3_decode(s8).astype(np.float64)
+        q = oracle.unpack_int4(wp).astype(np.float64).reshape(9, -1, group)
+        r = oracle.rotate_f32(w).astype(np.float64).reshape(9, -1, group)
+        ok = sd > 0
+        sdb = np.broadcast_to(sd[..., None], r.shape)
+        okb = np.broadcast_to(ok[..., None], r.shape)
+        err = np.abs(r - q * sdb)
+        unclipped = np.abs(r) <= 7 * sdb
+        sel = okb & unclipped
+        assert np.all(err[sel] <= sdb[sel] / 2 * (1 + 2 ** -20))   # nearest code against the decoded scale
+        assert np.all(np.abs(q[okb & ~unclipped]) == 7)           # beyond 7 s8: clamped
+        assert not q[~okb].any() and not q[3].any()
