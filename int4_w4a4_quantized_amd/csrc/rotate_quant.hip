@@ -1,10 +1,11 @@
 // Fused ConvRot rotation + symmetric quantisation + packing, one row per
-// workgroup, for gfx950.
+// wavefront (or per workgroup for long rows), for gfx950.
 //
 // What it computes ("[PR #63] int4_tensorwise: W4A4 layout (+ConvRot) with
-// fused CUDA kernels", Description: fused activation kernel = FHT rotation +
-// rowwise int4 quantize + pack in one pass; weights are packed signed int4
-// pairs, low nibble first, with one fp32 scale per row):
+// fused CUDA kernels", Description: the activation kernel rotates, takes the
+// row scale, quantises to int4 and packs in a single pass; weights are stored
+// as int4 code pairs, the even element in the low nibble, with one fp32 scale
+// per row):
 //   r = x * blockdiag(H_b, ..., H_b) * fp32(1/sqrt(b))     (fp32, b = rot_block)
 //   s = absmax(r) / qmax                                  (fp32 divide)
 //   q = clamp(rint(r / s), -qmax, qmax)                    (fp32 quotient, ties to even)

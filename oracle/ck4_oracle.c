@@ -264,8 +264,9 @@ uint8_t ck4o_e4m3_encode(float xf) {
 }
 
 /* ------------------------------------------------------------------------- */
-/* Low-nibble-first packing of signed int4 pairs ([PR63]: "packed signed int4
- * pairs (low-nibble-first, [N, K/2] int8 container)"; exact round trip). */
+/* Packing of signed int4 pairs into bytes, the even element in the low nibble
+ * ([PR63] Description: the weight layout is [N, K/2] bytes of code pairs);
+ * unpacking is its exact inverse. */
 
 void ck4o_pack_int4(const int8_t *q, int64_t count, int8_t *packed) {
     for (int64_t j = 0; j < count / 2; j++) {
@@ -354,8 +355,9 @@ void ck4o_quantize_weight_convrot_e4m3(const float *w, int64_t n, int64_t k, int
     free(r);
 }
 
-/* Activation path ([PR63]: "activations are rotated + quantized to int4
- * dynamically"): bf16 x [m, ldx] -> rotate -> per-row quantise.
+/* Activation path ([PR63] Description: activations are rotated and quantised
+ * to int4 at run time, inside the kernel): bf16 x [m, ldx] -> rotate ->
+ * per-row quantise.
  * bits == 4: out is packed int8 [m, k/2], codes in [-7, 7].
  * bits == 8: out is int8 [m, k], codes in [-127, 127]. scales fp32 [m]. */
 void ck4o_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int g, int bits,
@@ -425,8 +427,8 @@ uint16_t ck4o_f64_to_bf16(double v) {
     return out;
 }
 
-/* Rank-one epilogue ([PR63]: "per-row/per-col scales factor out of the K
- * loop"): y[i, j] = bf16(acc[i, j] * sx[i] * sw[j] (+ bias[j])), evaluated in
+/* Rank-one epilogue ([PR63] Description: the row and column scales do not
+ * depend on k, so they are applied once after the integer sum): y[i, j] = bf16(acc[i, j] * sx[i] * sw[j] (+ bias[j])), evaluated in
  * fp64. y is bf16 bits with row stride ldy. bias may be NULL. */
 void ck4o_epilogue_bf16(const int32_t *acc, const float *sx, const float *sw, const float *bias,
                         int64_t m, int64_t n, int64_t ldy, uint16_t *y) {
