@@ -252,6 +252,44 @@ def layer_sweep(ck, torch, args) -> int:
         ck.rotate_quantize_act(x, 128, 8, out=xq8, scales=sx)
         ck.linear_w4a8_grouped(xq8, sx, wg, gs, 128, 0, out=y, workspace=wsp)
     line("w4a8-grouped layer square_3072 (decode + int8 GEMM)", m, n, k, graph_ms(w4a8_step, reps))
+    del w8, ws8, xq8, wg, gs, wsp
+
+    # Dynamic LoRA on the square layer: the rotated down projection, then the
+    # GEMM with the up projection fused into its epilogue.
+    wp, ws = ck.quantize_weight_convrot(wd, 128, 0)
+
+    def base_gemm():
+        ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+    ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+    base_ms = graph_ms(base_gemm, reps)
+    for rank in (32, 128):
+        a, b = workloads.make_lora(np.random.default_rng(70 + rank), rank, k, n)
+        a_rot = ck.lora_prepare_down(torch.from_numpy(a).to(dev))
+        bd = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+        t = torch.empty((m, rank), dtype=torch.bfloat16, device=dev)
+
+        def down():
+            ck.lora_down(x, a_rot, 0.5, 128, out=t)
+
+        def lora_gemm():
+            ck.linear_w4a4_lora(xq, sx, wp, ws, t, bd, None, out=y)
+
+        def lora_step():
+            ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
+            ck.lora_down(x, a_rot, 0.5, 128, out=t)
+            ck.linear_w4a4_lora(xq, sx, wp, ws, t, bd, None, out=y)
+        d_ms = graph_ms(down, reps)
+        byts = m * k * 2 + rank * k * 2 + m * rank * 2
+        print(json.dumps({"case": f"lora down projection m={m} k={k} rank={rank}", "ms": round(d_ms, 5),
+                          "algorithmic_bytes": byts, "GBps": round(byts / (d_ms * 1e-3) / 1e9, 1),
+                          "hbm_frac": round(byts / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          "bf16_TFLOPs": round(2.0 * m * k * rank / (d_ms * 1e-3) / 1e12, 1)}), flush=True)
+        g_ms = graph_ms(lora_gemm, reps)
+        print(json.dumps({"case": f"w4a4 GEMM + fused lora up projection rank={rank}", "ms": round(g_ms, 5),
+                          "base_gemm_ms": round(base_ms, 5), "epilogue_overhead_ms": round(g_ms - base_ms, 5)}),
+              flush=True)
+        line(f"w4a4 layer square_3072 + dynamic lora rank={rank}", m, n, k, graph_ms(lora_step, reps))
+        del a_rot, bd, t
     return 0
 
 

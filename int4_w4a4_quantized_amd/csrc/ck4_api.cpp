@@ -214,7 +214,7 @@ ck4_status ck4_rotate_act_f32(const uint16_t *x, int64_t m, int64_t k, int64_t l
 
 static ck4_status gemm_entry(const char *fn, bool s4, const int8_t *a, const float *sa, const int8_t *b,
                              const float *sb, const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32,
-                             void *y, int64_t ldy, void *stream) {
+                             void *y, int64_t ldy, void *stream, ck4::LoraUp lora = ck4::LoraUp{}) {
     if (!a || !b || !y || (!out_i32 && (!sa || !sb))) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, out_i32 ? 16 : 8)) return s;
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
@@ -224,7 +224,7 @@ static ck4_status gemm_entry(const char *fn, bool s4, const int8_t *a, const flo
                     (long long)step_k);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_gemm(s4, a, b, sa, sb, bias, m, n, k, out_i32, y, ldy,
-                                         static_cast<hipStream_t>(stream)));
+                                         static_cast<hipStream_t>(stream), lora));
 }
 
 ck4_status ck4_linear_w4a4(const int8_t *x_q, const float *x_scales, const int8_t *w_packed, const float *w_scales,
@@ -375,6 +375,67 @@ ck4_status ck4_linear_w4a8_grouped_e4m3(const int8_t *x_q8, const float *x_scale
                                         size_t ws_bytes, void *stream) {
     return linear_w4a8("ck4_linear_w4a8_grouped_e4m3", x_q8, x_scales, w_packed, group_scales, true, m, n, k, group,
                        y, ldy, chunk_cols, workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+bool lora_rank_ok(int64_t rank) { return rank == 32 || rank == 64 || rank == 128 || rank == 256; }
+
+}  // namespace
+
+extern "C" {
+
+ck4_status ck4_lora_prepare_down(const float *a, int64_t rank, int64_t k, int64_t lda, int rot_block,
+                                 uint16_t *a_rot, void *stream) {
+    const char *fn = "ck4_lora_prepare_down";
+    if (!a || !a_rot) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (rank <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: rank and k must be positive", fn);
+    if (lda < k) return fail(CK4_ERR_INVALID, "%s: lda < k", fn);
+    if (!aligned(a, 16) || (lda * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: a/lda not 16-byte aligned", fn);
+    if (!aligned(a_rot, 16)) return fail(CK4_ERR_INVALID, "%s: a_rot not 16-byte aligned", fn);
+    if (!lora_rank_ok(rank))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
+    if (rot_block > 256) return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d > 256", fn, rot_block);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(a, 1, rank, k, lda, rot_block, 3, 0, a_rot, k, nullptr,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, const uint16_t *a_rot,
+                         int64_t rank, float alpha, uint16_t *t, void *stream) {
+    const char *fn = "ck4_lora_down";
+    if (!x || !a_rot || !t) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (m <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m and k must be positive", fn);
+    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
+    if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: x/ldx not 16-byte aligned", fn);
+    if (!aligned(a_rot, 16) || !aligned(t, 16)) return fail(CK4_ERR_INVALID, "%s: a_rot or t misaligned", fn);
+    if (m > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m too large", fn);
+    if (!lora_rank_ok(rank))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
+    if (rot_block > 256) return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d > 256", fn, rot_block);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    const int64_t chunk = rot_block < 128 ? 128 : rot_block;
+    if (k % chunk != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of %lld", fn, (long long)k, (long long)chunk);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_lora_down(x, m, k, ldx, rot_block, a_rot, rank, alpha, t,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_linear_w4a4_lora(const int8_t *x_q, const float *x_scales, const int8_t *w_packed,
+                                const float *w_scales, const float *bias, const uint16_t *t, const uint16_t *b_up,
+                                int64_t rank, int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy,
+                                void *stream) {
+    const char *fn = "ck4_linear_w4a4_lora";
+    if (!t || !b_up) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (!aligned(t, 16) || !aligned(b_up, 16)) return fail(CK4_ERR_INVALID, "%s: t or b_up misaligned", fn);
+    if (!lora_rank_ok(rank))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
+    return gemm_entry(fn, true, x_q, x_scales, w_packed, w_scales, bias, m, n, k, false, y, ldy, stream,
+                      ck4::LoraUp{t, b_up, (int)rank});
 }
 
 }  // extern "C"

@@ -21,18 +21,38 @@ struct WeightOpts {
 // Rotation + quantisation of rows (one wavefront or one workgroup per row).
 //   in_kind   0: bf16 input, 1: fp32 input
 //   out_kind  0: packed int4 (+ scales), 1: int8 codes (+ scales), 2: fp32 rotation
+//             (bf16 input only), 3: the rotation rounded to bf16
 //   group     0: one scale per row; > 0: one scale per `group` elements (int4 only)
 //   scales    fp32, or E4M3 bytes when wo.scale_e4m3
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
                                int out_kind, int group, void *out, int64_t ldo, float *scales, hipStream_t stream,
                                WeightOpts wo = WeightOpts{});
 
+// LoRA up-projection added in the bf16 epilogue of launch_gemm: t is the
+// bf16 down-projected activation [m, rank], b the bf16 up-projection
+// [n, rank], both row-major and 16-byte aligned; rank is a multiple of 32
+// (0 or t == nullptr: no LoRA term).
+struct LoraUp {
+    const uint16_t *t = nullptr;
+    const uint16_t *b = nullptr;
+    int rank = 0;
+};
+
 // Integer GEMM acc[m, n] = sum_k a[m, k] b[n, k] on int8 MFMA, with a rank-one
 // bf16 epilogue (out_i32 == false) or an int32 store (out_i32 == true).
 //   s4 true:  a, b packed int4 [rows, k/2]; false: int8 codes [rows, k].
+//   lora      bf16 epilogue only: y += t b^T before the rounding
 hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *sa, const float *sb,
                        const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
-                       hipStream_t stream);
+                       hipStream_t stream, LoraUp lora = LoraUp{});
+
+// LoRA down-projection in the rotated basis: t[m, j] = bf16(alpha *
+// sum_k bf16(rotate(x)[m, k]) a_rot[j, k]) with fp32 accumulation, x bf16
+// [m, k] (row stride ldx), a_rot bf16 [rank, k], t bf16 [m, rank].
+// rank in {32, 64, 128, 256}; rot_block in {16, ..., 256}; k a multiple of
+// max(128, rot_block).
+hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, const uint16_t *a_rot,
+                            int64_t rank, float alpha, uint16_t *t, hipStream_t stream);
 
 // Grouped int4 -> int8 decode of weight rows [n0, n0 + nc). group_scales are
 // fp32, or E4M3 bytes when scale_e4m3.

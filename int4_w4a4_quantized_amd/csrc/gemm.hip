@@ -22,16 +22,18 @@
 //    by both operands leaves every dot product unchanged ([PR #63]: both
 //    operands share the fragment k-permutation).
 //
-// Tiling: a workgroup of 256 threads (4 wavefronts) computes a BM x BN tile
-// of y. Each K step stages 128 bytes of every row of both operands in LDS
-// (256 int4 or 128 int8 values), double buffered with one barrier per step.
-// Rows are stored as 8 chunks of 16 bytes with the chunk index XORed with
-// (row & 7), so the 16 rows read by one fragment load land on distinct banks.
-// The MFMA's first operand is the weight fragment and its second the
-// activation fragment, so each lane's 4 accumulators are 4 consecutive
-// output columns of one row: the epilogue stores 8 contiguous bytes per lane.
-// Workgroup ids are remapped so that each XCD (ids are dealt round-robin to
-// the 8 XCDs) owns one rectangular block of tiles and reuses its L2.
+// Two kernels: a large-tile kernel that stages both operands in LDS (M > 64)
+// and a skinny kernel that streams the weight straight into registers
+// (M <= 64). In both, the MFMA's first operand is the weight fragment and its
+// second the activation fragment, so each lane's 4 accumulators are 4
+// consecutive output columns of one row.
+//
+// Optional LoRA up-projection (dynamic LoRA, "Comfy-INT4-HIPtest" README, LoRA
+// modes): with t = the bf16 down-projected activation [M, R] and b = the bf16
+// up-projection [N, R], the epilogue adds sum_j t[m, j] b[n, j] to the fp32
+// value of y before the bf16 rounding, with v_mfma_f32_16x16x32_bf16 whose
+// fragment layout matches the int8 one (first operand b rows, second t rows),
+// so the sum accumulates straight onto the lane's 4 outputs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,10 +43,10 @@ namespace ck4 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kRowBytes = 128;          // bytes of each row per K step
-constexpr int kChunks = kRowBytes / 16;  // 16-byte chunks per row per step
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ v4i as_v4i(uint4 u) {
     v4i r;
@@ -64,184 +66,39 @@ __device__ __forceinline__ v4i widen_lo(uint4 p) {
                              (p.w << 4) & 0xF0F0F0F0u));
 }
 
-__device__ __forceinline__ int lds_index(int row, int chunk) { return row * kChunks + (chunk ^ (row & 7)); }
-
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     __bf16 h = (__bf16)f;
     return __builtin_bit_cast(uint16_t, h);
 }
 
-template <bool S4, int BM, int BN, int WAVES_M, bool OUT_I32>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B,
-                                                        const float *__restrict__ sa, const float *__restrict__ sb,
-                                                        const float *__restrict__ bias, int M, int N,
-                                                        int64_t row_bytes, int ksteps, void *__restrict__ Y,
-                                                        int64_t ldy, int tiles_n, int tiles_total) {
-    constexpr int WAVES_N = 4 / WAVES_M;
-    constexpr int WTM = BM / WAVES_M;
-    constexpr int WTN = BN / WAVES_N;
-    constexpr int FM = WTM / 16;
-    constexpr int FN = WTN / 16;
-    constexpr int ROWS = BM + BN;
-    constexpr int TOTAL_CHUNKS = ROWS * kChunks;
-    constexpr int LOADS = (TOTAL_CHUNKS + kThreads - 1) / kThreads;
-    static_assert(FM >= 1 && FN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "bad tile");
-
-    __shared__ uint4 lds[2][TOTAL_CHUNKS];
-
-    int tile = blockIdx.x;
-    if ((tiles_total & 7) == 0) tile = (tile & 7) * (tiles_total >> 3) + (tile >> 3);
-    const int tm = tile / tiles_n;
-    const int tn = tile - tm * tiles_n;
-    const int m0 = tm * BM;
-    const int n0 = tn * BN;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave / WAVES_N;
-    const int wn = wave - wm * WAVES_N;
-
-    // Global -> LDS staging: chunk q = tid + i * 256 is row q / 8, chunk q % 8.
-    const int8_t *gp[LOADS];
-    bool gv[LOADS];
-    int lo[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int q = tid + i * kThreads;
-        const int r = q / kChunks;
-        const int c = q % kChunks;
-        bool valid = q < TOTAL_CHUNKS;
-        const int8_t *base = A;
-        if (r < BM) {
-            const int gr = m0 + r;
-            valid = valid && gr < M;
-            base = A + (int64_t)(valid ? gr : 0) * row_bytes;
-        } else {
-            const int gr = n0 + (r - BM);
-            valid = valid && gr < N;
-            base = B + (int64_t)(valid ? gr : 0) * row_bytes;
-        }
-        gp[i] = base + c * 16;
-        gv[i] = valid;
-        lo[i] = q < TOTAL_CHUNKS ? lds_index(r, c) : 0;
-    }
-
-    uint4 pre[LOADS];
-    auto gload = [&](int step) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            pre[i] = gv[i] ? *reinterpret_cast<const uint4 *>(gp[i] + (int64_t)step * kRowBytes)
-                           : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            if (tid + i * kThreads < TOTAL_CHUNKS) lds[buf][lo[i]] = pre[i];
-        }
-    };
-
-    v4i acc[FN][FM];
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
+// y[i][j] += the LoRA term of output fragment (i, j): 16 columns from
+// nbase + 16 i by 16 rows from mbase + 16 j, in the int8 accumulator layout
+// (lane l: row l & 15, columns 4 (l >> 4) .. + 3). Each 32-wide slice of the
+// rank is one v_mfma_f32_16x16x32_bf16 per fragment, first operand 16 rows of
+// b, second 16 rows of t, both read straight from global memory (lane l: row
+// l & 15, the 8 values at 8 (l >> 4) of the slice). Rows past M or N read the
+// last valid row; their results are never stored. The whole wavefront runs it.
+template <int FN, int FM>
+__device__ __forceinline__ void lora_up(v4f (&y)[FN][FM], const LoraUp lo, int nbase, int mbase, int N, int M,
+                                        int lane) {
     const int frow = lane & 15;
-    const int fgrp = lane >> 4;
-    for (int s = 0; s < ksteps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < ksteps) gload(s + 1);
-        const uint4 *As = lds[buf];
-        const uint4 *Bs = lds[buf] + BM * kChunks;
+    const int koff = 8 * (lane >> 4);
+    const uint16_t *bp[FN];
+    const uint16_t *tp[FM];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int c = half * 4 + fgrp;
-            uint4 xa[FM], wb[FN];
+    for (int i = 0; i < FN; ++i) bp[i] = lo.b + (int64_t)min(nbase + i * 16 + frow, N - 1) * lo.rank + koff;
 #pragma unroll
-            for (int j = 0; j < FM; ++j) {
-                const int r = wm * WTM + j * 16 + frow;
-                xa[j] = As[lds_index(r, c)];
-            }
+    for (int j = 0; j < FM; ++j) tp[j] = lo.t + (int64_t)min(mbase + j * 16 + frow, M - 1) * lo.rank + koff;
+    for (int kk = 0; kk < lo.rank; kk += 32) {
+        v8bf bf[FN], tf[FM];
 #pragma unroll
-            for (int i = 0; i < FN; ++i) {
-                const int r = wn * WTN + i * 16 + frow;
-                wb[i] = Bs[lds_index(r, c)];
-            }
-            if constexpr (S4) {
-                v4i xl[FM], xh[FM];
+        for (int i = 0; i < FN; ++i) bf[i] = *reinterpret_cast<const v8bf *>(bp[i] + kk);
 #pragma unroll
-                for (int j = 0; j < FM; ++j) {
-                    xl[j] = widen_lo(xa[j]);
-                    xh[j] = widen_hi(xa[j]);
-                }
+        for (int j = 0; j < FM; ++j) tf[j] = *reinterpret_cast<const v8bf *>(tp[j] + kk);
 #pragma unroll
-                for (int i = 0; i < FN; ++i) {
-                    const v4i wl = widen_lo(wb[i]);
-                    const v4i wh = widen_hi(wb[i]);
+        for (int i = 0; i < FN; ++i)
 #pragma unroll
-                    for (int j = 0; j < FM; ++j) {
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, xl[j], acc[i][j], 0, 0, 0);
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, xh[j], acc[i][j], 0, 0, 0);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < FN; ++i)
-#pragma unroll
-                    for (int j = 0; j < FM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(wb[i]), as_v4i(xa[j]),
-                                                                          acc[i][j], 0, 0, 0);
-            }
-        }
-        if (s + 1 < ksteps) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // Epilogue. Lane holds acc[i][j][r] = y[m][n] with
-    //   m = m0 + wm*WTM + j*16 + (lane & 15), n = n0 + wn*WTN + i*16 + 4*(lane >> 4) + r.
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * WTM + j * 16 + frow;
-        if (m >= M) continue;
-        const float sam = OUT_I32 ? 0.0f : sa[m];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-            const int nb = n0 + wn * WTN + i * 16 + 4 * fgrp;
-            if (nb >= N) continue;
-            int a4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a4[r] = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-            if constexpr (OUT_I32) {
-                int32_t *yr = reinterpret_cast<int32_t *>(Y) + (int64_t)m * ldy + nb;
-                if (nb + 3 < N) {
-                    *reinterpret_cast<int4 *>(yr) = make_int4(a4[0], a4[1], a4[2], a4[3]);
-                } else {
-                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = a4[r];
-                }
-            } else {
-                uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + nb;
-                uint16_t o[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int n = nb + r < N ? nb + r : N - 1;
-                    float v = ((float)a4[r] * sam) * sb[n];
-                    if (bias) v = v + bias[n];
-                    o[r] = f32_to_bf16(v);
-                }
-                if (nb + 3 < N) {
-                    *reinterpret_cast<uint2 *>(yr) =
-                        make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-                } else {
-                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = o[r];
-                }
-            }
-        }
+            for (int j = 0; j < FM; ++j) y[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], tf[j], y[i][j], 0, 0, 0);
     }
 }
 
@@ -253,12 +110,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const int8_t *__restrict
 // stage s and land while stage s is multiplied. Within a stage, the fragments
 // are read from LDS per 64-byte half; two wavefronts per SIMD hide the LDS
 // latency of one behind the MFMAs of the other.
-template <bool S4, int BM, int BN, int WGM, int WGN, int WPE, bool OUT_I32>
+template <bool S4, int BM, int BN, int WGM, int WGN, int WPE, bool OUT_I32, bool LORA>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WPE, WPE))) void
 gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
                 const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes,
-                int ksteps, void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m) {
+                int ksteps, void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m,
+                LoraUp lora) {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM;
     constexpr int WTN = BN / WGN;
@@ -464,9 +322,26 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
         // Rank-one epilogue, staged through LDS so that the tile leaves as
         // whole rows: y = bf16((acc * sa[m]) * sb[n] (+ bias[n])) into a
         // [BM][BN + 8] bf16 tile, then 16-byte row-contiguous stores.
+        // With LoRA, the fp32 values of the whole wave tile are formed first and
+        // the up-projection accumulates onto them on the matrix cores.
         constexpr int LD = BN + 8;
         static_assert(BM * LD * 2 <= 2 * STAGE, "output tile does not fit in LDS");
         uint16_t *tile_lds = reinterpret_cast<uint16_t *>(smem);
+        v4f yv[LORA ? FN : 1][LORA ? FM : 1];
+        if constexpr (LORA) {
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int a = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+                        float v = ((float)a * sa_r[j]) * sb_r[i][r];
+                        if (bias) v = v + bias[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
+                        yv[i][j][r] = v;
+                    }
+            lora_up<FN, FM>(yv, lora, n0 + wn * WTN, m0 + wm * WTM, N, M, lane);
+        }
         __syncthreads();  // every wave has finished reading the last stage
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
@@ -477,10 +352,14 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
                 uint16_t o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int a = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
-                    float v = ((float)a * sa_r[j]) * sb_r[i][r];
-                    if (bias) v = v + bias[min(n0 + nl + r, N - 1)];
-                    o[r] = f32_to_bf16(v);
+                    if constexpr (LORA) {
+                        o[r] = f32_to_bf16(yv[i][j][r]);
+                    } else {
+                        const int a = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+                        float v = ((float)a * sa_r[j]) * sb_r[i][r];
+                        if (bias) v = v + bias[min(n0 + nl + r, N - 1)];
+                        o[r] = f32_to_bf16(v);
+                    }
                 }
                 *reinterpret_cast<uint2 *>(tile_lds + ml * LD + nl) =
                     make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
@@ -528,7 +407,8 @@ int pick_xcd_m(int tiles_m, int tiles_n, int bm, int bn) {
 
 template <bool S4, int BM, int BN, int WGM, int WGN, int WPE>
 hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
-                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                      LoraUp lora) {
     const int64_t row_bytes = S4 ? k / 2 : k;
     const int ksteps = (int)(row_bytes / kRowBytes);
     const int tiles_m = (int)((m + BM - 1) / BM);
@@ -537,11 +417,14 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
     const int xcd_m = pick_xcd_m(tiles_m, tiles_n, BM, BN);
     dim3 grid((unsigned)total), block(64 * WGM * WGN);
     if (out_i32)
-        gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, true><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m);
+        gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, true, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m, lora);
+    else if (lora.rank > 0)
+        gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, false, true><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m, lora);
     else
-        gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m);
+        gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, false, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m, lora);
     return hipGetLastError();
 }
 
@@ -553,11 +436,11 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
 // so a step reads whole cache lines of 16 rows), widens them and
 // runs the same s4 x s4 MFMAs as the large kernels. The KS partial
 // accumulators are summed through LDS and one wavefront runs the epilogue.
-template <bool S4, int FM, int FNW, int KS, int MAXS, bool OUT_I32>
+template <bool S4, int FM, int FNW, int KS, int MAXS, bool OUT_I32, bool LORA>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
     const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int steps,
-    void *__restrict__ Y, int64_t ldy) {
+    void *__restrict__ Y, int64_t ldy, LoraUp lora) {
     constexpr int SLAB = 128;  // bytes of each row per k-step: a whole cache line (256 k for s4, 128 k for s8)
     __shared__ v4i red[KS - 1][FNW][FM][64];
     const int lane = threadIdx.x & 63;
@@ -650,6 +533,28 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
                 for (int j = 0; j < FM; ++j) acc[i][j] += red[w][i][j][lane];
     }
 
+    // With LoRA, every fragment's fp32 values are formed first (clamped rows,
+    // so the whole wavefront runs the up-projection MFMAs) and the stores below
+    // round them.
+    v4f yv[LORA ? FNW : 1][LORA ? FM : 1];
+    if constexpr (LORA) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const float sam = sa[min(j * 16 + frow, M - 1)];
+#pragma unroll
+            for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int n = min(n0 + i * 16 + 4 * fgrp + r, N - 1);
+                    const int a = S4 ? (acc[i][j][r] >> 8) : acc[i][j][r];
+                    float v = ((float)a * sam) * sb[n];
+                    if (bias) v = v + bias[n];
+                    yv[i][j][r] = v;
+                }
+        }
+        lora_up<FNW, FM>(yv, lora, n0, 0, N, M, lane);
+    }
+
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
         const int m = j * 16 + frow;
@@ -674,10 +579,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
                 uint16_t o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int n = nb + r < N ? nb + r : N - 1;
-                    float v = ((float)a4[r] * sam) * sb[n];
-                    if (bias) v = v + bias[n];
-                    o[r] = f32_to_bf16(v);
+                    if constexpr (LORA) {
+                        o[r] = f32_to_bf16(yv[i][j][r]);
+                    } else {
+                        const int n = nb + r < N ? nb + r : N - 1;
+                        float v = ((float)a4[r] * sam) * sb[n];
+                        if (bias) v = v + bias[n];
+                        o[r] = f32_to_bf16(v);
+                    }
                 }
                 if (nb + 3 < N) {
                     *reinterpret_cast<uint2 *>(yr) =
@@ -693,76 +602,65 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
 template <bool S4, int FM, int FNW, int KS, int MAXS>
 hipError_t launch_skinny_cfg(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                              int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
-                             hipStream_t stream) {
+                             hipStream_t stream, LoraUp lora) {
     const int64_t row_bytes = S4 ? k / 2 : k;
     const int steps = (int)(row_bytes / 128);
     dim3 grid((unsigned)((n + 16 * FNW - 1) / (16 * FNW))), block(64 * KS);
     if (out_i32)
-        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, true><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy);
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, true, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
+    else if (lora.rank > 0)
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, false, true><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
     else
-        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy);
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, false, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
     return hipGetLastError();
 }
 
 // KS: enough wavefronts in flight to keep HBM busy (about 2K or more).
 template <bool S4, int FM, int FNW, int MAXS>
 hipError_t launch_skinny_ks(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
-                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                         LoraUp lora) {
     const int64_t groups = (n + 16 * FNW - 1) / (16 * FNW);
     if (groups >= 1024)
-        return launch_skinny_cfg<S4, FM, FNW, 2, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+        return launch_skinny_cfg<S4, FM, FNW, 2, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     if (groups >= 512)
-        return launch_skinny_cfg<S4, FM, FNW, 4, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    return launch_skinny_cfg<S4, FM, FNW, 8, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+        return launch_skinny_cfg<S4, FM, FNW, 4, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_skinny_cfg<S4, FM, FNW, 8, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 template <bool S4>
 hipError_t launch_skinny(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
-                         int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+                         int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                         LoraUp lora) {
     // MAXS keeps a chunk's loads within the register budget of 2 waves/SIMD
-    if (m <= 16) return launch_skinny_ks<S4, 1, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    if (m <= 32) return launch_skinny_ks<S4, 2, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    return launch_skinny_ks<S4, 4, 1, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-}
-
-template <bool S4, int BM, int BN, int WAVES_M>
-hipError_t launch_cfg(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
-                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
-    const int64_t row_bytes = S4 ? k / 2 : k;
-    const int ksteps = (int)(row_bytes / kRowBytes);
-    const int tiles_m = (int)((m + BM - 1) / BM);
-    const int tiles_n = (int)((n + BN - 1) / BN);
-    const int total = tiles_m * tiles_n;
-    dim3 grid((unsigned)total), block(kThreads);
-    if (out_i32)
-        gemm_kernel<S4, BM, BN, WAVES_M, true><<<grid, block, 0, stream>>>(a, b, sa, sb, bias, (int)m, (int)n,
-                                                                          row_bytes, ksteps, y, ldy, tiles_n, total);
-    else
-        gemm_kernel<S4, BM, BN, WAVES_M, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, row_bytes, ksteps, y, ldy, tiles_n, total);
-    return hipGetLastError();
+    if (m <= 16) return launch_skinny_ks<S4, 1, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    if (m <= 32) return launch_skinny_ks<S4, 2, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_skinny_ks<S4, 4, 1, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 template <bool S4>
 hipError_t launch_s(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias, int64_t m,
-                    int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
-    if (m <= 64) return launch_skinny<S4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+                    int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                    LoraUp lora) {
+    if (m <= 64) return launch_skinny<S4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     // large shapes: one 288 x 192 tile per CU when that fills the chip
     const int64_t big_tiles = ((m + 287) / 288) * ((n + 191) / 192);
     if (big_tiles >= 192)
-        return launch_big<S4, 288, 192, 2, 4, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    return launch_big<S4, 128, 128, 2, 2, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+        return launch_big<S4, 288, 192, 2, 4, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_big<S4, 128, 128, 2, 2, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *sa, const float *sb,
                        const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
-                       hipStream_t stream) {
-    if (s4) return launch_s<true>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
-    return launch_s<false>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+                       hipStream_t stream, LoraUp lora) {
+    if (out_i32 || lora.t == nullptr) lora.rank = 0;
+    if (s4) return launch_s<true>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_s<false>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 }  // namespace ck4

@@ -52,85 +52,15 @@
 
 #include "ck4_kernels.h"
 #include "fp8_e4m3.h"
+#include "fwht.h"
 
 namespace ck4 {
 namespace {
 
-constexpr int kElems = 16;     // contiguous elements per chunk
 constexpr int kMaxChunks = 4;  // chunks per thread: k <= 16 * 256 * 4 = 16384
 constexpr int kThreads = 256;
 // The kernel is instantiated per chunks-per-thread count NCH (1..4), so a row
 // of K <= 4096 keeps 16 values per lane in VGPRs and the occupancy stays high.
-
-__device__ __forceinline__ void load_chunk(const uint16_t *p, float v[kElems]) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-    uint4 a = q[0], b = q[1];
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-}
-
-__device__ __forceinline__ void load_chunk(const float *p, float v[kElems]) {
-    const float4 *q = reinterpret_cast<const float4 *>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float4 t = q[i];
-        v[4 * i] = t.x;
-        v[4 * i + 1] = t.y;
-        v[4 * i + 2] = t.z;
-        v[4 * i + 3] = t.w;
-    }
-}
-
-// Butterflies with stride 1, 2, 4, 8 inside the chunk (ascending).
-__device__ __forceinline__ void fwht_in_lane(float v[kElems]) {
-#pragma unroll
-    for (int h = 1; h < kElems; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < kElems; ++i) {
-            if (i & h) continue;
-            float a = v[i], b = v[i + h];
-            v[i] = a + b;
-            v[i + h] = a - b;
-        }
-    }
-}
-
-// The value held by lane L ^ mask. The exchange goes through the LDS
-// crossbar (ds_swizzle, ds_bpermute) rather than a DPP move, so it costs no
-// VALU instruction: the kernel is bound by VALU issue.
-template <int MASK>
-__device__ __forceinline__ float partner(float x) {
-    const int xi = __float_as_int(x);
-    int r;
-    if constexpr (MASK <= 16) {
-        r = __builtin_amdgcn_ds_swizzle(xi, 0x1F | (MASK << 10));  // bitmask mode, xor MASK
-    } else {
-        r = __builtin_amdgcn_ds_bpermute((int)((__lane_id() ^ MASK) << 2), xi);
-    }
-    return __int_as_float(r);
-}
-
-template <int MASK>
-__device__ __forceinline__ void cross_stage(float v[kElems], int lane) {
-    const float k = (lane & MASK) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < kElems; ++i) v[i] = __builtin_fmaf(partner<MASK>(v[i]), k, v[i]);
-}
-
-// All cross-lane stages for a block of LPB lanes (ascending mask).
-template <int LPB>
-__device__ __forceinline__ void fwht_cross_lane(float v[kElems], int lane) {
-    if constexpr (LPB > 1) cross_stage<1>(v, lane);
-    if constexpr (LPB > 2) cross_stage<2>(v, lane);
-    if constexpr (LPB > 4) cross_stage<4>(v, lane);
-    if constexpr (LPB > 8) cross_stage<8>(v, lane);
-    if constexpr (LPB > 16) cross_stage<16>(v, lane);
-    if constexpr (LPB > 32) cross_stage<32>(v, lane);
-}
 
 __device__ __forceinline__ float wave_max(float a) {
 #pragma unroll
@@ -190,7 +120,7 @@ __device__ __forceinline__ uint32_t pack4_bytes(const uint32_t *c) {
     return lo | hi;
 }
 
-// out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation.
+// out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation, 3 bf16 rotation.
 // WAVE_ROW: each wavefront owns one row (K <= 64 * 16 * NCH), so the row
 // absmax is a wavefront reduction with no LDS and no barrier, and a 256-thread
 // workgroup handles 4 rows; otherwise the workgroup owns one row.
@@ -237,6 +167,24 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     d[i] = make_float4(v[j][4 * i], v[j][4 * i + 1], v[j][4 * i + 2], v[j][4 * i + 3]);
+            }
+        }
+        return;
+    } else if constexpr (OUT == 3) {
+        // the rotation rounded once to bf16, nearest even
+        uint16_t *o = reinterpret_cast<uint16_t *>(out) + (int64_t)row * ldo;
+#pragma unroll
+        for (int j = 0; j < NCH; ++j) {
+            const int ch = tid + j * nthreads;
+            if (ch < nchunks) {
+                uint32_t wds[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    wds[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][2 * i]) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][2 * i + 1]) << 16);
+                uint4 *d = reinterpret_cast<uint4 *>(o + (int64_t)ch * kElems);
+                d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+                d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
             }
         }
         return;
@@ -397,8 +345,11 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
     else if (out_kind == 1)
         launch_mode<TIn, 1>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
                             wo, stream);
+    else if (out_kind == 3)
+        launch_mode<TIn, 3>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
+                            wo, stream);
     else if constexpr (sizeof(TIn) == 4)
-        return hipErrorInvalidValue;  // fp32 rows are weights: codes only, no fp32 rotation output
+        return hipErrorInvalidValue;  // fp32 rows: codes or the bf16 rotation only
     else
         launch_mode<TIn, 2>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
                             wo, stream);

@@ -64,6 +64,7 @@ def lib():
             "ck4o_rotate_quantize_act": ([P, I64, I64, I64, I, I, P, P], None),
             "ck4o_gemm_acc": ([P, P, I64, I64, I64, I, P], None),
             "ck4o_f64_to_bf16": ([ctypes.c_double], ctypes.c_uint16),
+            "ck4o_f64_to_bf16_array": ([P, I64, P], None),
             "ck4o_epilogue_bf16": ([P, P, P, P, I64, I64, I64, P], None),
             "ck4o_linear_w4a4": ([P, P, P, P, I64, I64, I64, I, P], None),
             "ck4o_decode_w4a8": ([P, P, I64, I64, I, I64, I64, P, P], None),
@@ -316,3 +317,56 @@ def linear_w4a8_grouped(x_bits: np.ndarray, w_packed: np.ndarray, group_scales: 
 
 def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def to_bf16(v: np.ndarray) -> np.ndarray:
+    """Round fp64 (or fp32, converted exactly) values once to bf16, nearest even -> uint16 bits."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, np.uint16)
+    lib().ck4o_f64_to_bf16_array(_p(v), v.size, _p(out))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Dynamic LoRA ("Comfy-INT4-HIPtest" README, "LoRA modes": the Dynamic mode
+# keeps the LoRA factors apart and adds their product at inference;
+# "ComfyUI-INT4-Fast", "Features": the down projection is rotated with the
+# same Hadamard blocks so that it matches the rotated activation). With the
+# orthonormal block rotation R, x A^T = (x R)(A R)^T: the down projection
+# consumes the activation's rotation. Readings (the pages give no arithmetic):
+# A R is rounded to bf16 once at preparation; the rotated activation is
+# rounded to bf16 before the product; t = alpha * (x R)(A R)^T is rounded to
+# bf16; the up projection t B^T is added to the layer's value before its one
+# bf16 rounding. Products and sums here are fp64 over those bf16 values.
+
+
+def lora_prepare_down(a: np.ndarray, g: int = 128) -> np.ndarray:
+    """bf16 bits of A R: each fp32 row of the down projection rotated like a weight row."""
+    return to_bf16(rotate_f32(a, g))
+
+
+def lora_down(x_bits: np.ndarray, a_rot_bits: np.ndarray, alpha: float, g: int = 128) -> np.ndarray:
+    """t = bf16(alpha * bf16(x R) (A R)^T) -> bf16 bits [m, rank]; x R is the quantiser's fp32 rotation."""
+    xr = bf16_bits_to_f64(to_bf16(rotate_bf16(x_bits, g)))
+    ar = bf16_bits_to_f64(a_rot_bits)
+    return to_bf16(float(alpha) * (xr @ ar.T))
+
+
+def epilogue_lora(acc: np.ndarray, sx: np.ndarray, sw: np.ndarray, t_bits: np.ndarray, b_bits: np.ndarray,
+                  bias: np.ndarray | None = None) -> np.ndarray:
+    """y = bf16(acc sx sw (+ bias) + t B^T), fp64 -> bf16 bits [m, n]."""
+    v = _c(acc, np.int32).astype(np.float64) * _c(sx, np.float32).astype(np.float64)[:, None]
+    v = v * _c(sw, np.float32).astype(np.float64)[None, :]
+    if bias is not None:
+        v = v + _c(bias, np.float32).astype(np.float64)[None, :]
+    v = v + bf16_bits_to_f64(t_bits) @ bf16_bits_to_f64(b_bits).T
+    return to_bf16(v)
+
+
+def linear_w4a4_lora(x_bits: np.ndarray, w_packed: np.ndarray, w_scales: np.ndarray, a_rot_bits: np.ndarray,
+                     b_bits: np.ndarray, alpha: float, bias: np.ndarray | None = None, g: int = 128) -> np.ndarray:
+    """The W4A4 ConvRot layer plus a dynamic LoRA -> bf16 bits [m, n]."""
+    xq, sx = rotate_quantize_act(x_bits, g, bits=4)
+    acc = gemm_acc(xq, w_packed, xq.shape[1] * 2)
+    t = lora_down(x_bits, a_rot_bits, alpha, g)
+    return epilogue_lora(acc, sx, w_scales, t, b_bits, bias)

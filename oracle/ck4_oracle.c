@@ -36,6 +36,9 @@
  *  - Grouped W4A8 decode: s_row = (max_g s_g * 7) / 127, w8 = clamp(rint(q *
  *    (s_g / s_row)), -127, 127), all fp32; an all-zero row gives s_row = 0,
  *    w8 = 0.
+ *  - Dynamic LoRA ([HIPT] "LoRA modes", [FAST] "Features"): stated in the
+ *    Python layer of the oracle (oracle/__init__.py), in fp64 over the bf16
+ *    operands, with this file's rotation and bf16 rounding.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  * No FMA contraction and no reassociation, so every fp32 operation below is
@@ -425,6 +428,12 @@ uint16_t ck4o_f64_to_bf16(double v) {
     uint16_t out = (uint16_t)(u >> 16);
     if (signbit(v)) out |= 0x8000;
     return out;
+}
+
+/* Element-wise single rounding of fp64 values to bf16 bits. */
+void ck4o_f64_to_bf16_array(const double *v, int64_t count, uint16_t *out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < count; i++) out[i] = ck4o_f64_to_bf16(v[i]);
 }
 
 /* Rank-one epilogue ([PR63] Description: the row and column scales do not

@@ -114,6 +114,29 @@ def test_w4a8_validation(L):
     assert l8(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 192, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
 
 
+def test_lora_validation(L):
+    p = L.ck4_lora_prepare_down
+    assert p(NULL, 32, 256, 256, 128, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert p(FAKE, 32, 256, 200, 128, FAKE, NULL) == ck.CK4_ERR_INVALID  # lda < k
+    assert p(FAKE, 32, 256, 256, 128, ODD, NULL) == ck.CK4_ERR_INVALID  # a_rot alignment
+    assert p(FAKE, 48, 256, 256, 128, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rank
+    assert p(FAKE, 32, 512, 512, 512, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rot_block > 256
+    d = L.ck4_lora_down
+    assert d(FAKE, 8, 256, 256, 128, FAKE, 32, 1.0, NULL, NULL) == ck.CK4_ERR_INVALID
+    assert d(FAKE, 0, 256, 256, 128, FAKE, 32, 1.0, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert d(FAKE, 8, 256, 256, 128, FAKE, 32, 1.0, ODD, NULL) == ck.CK4_ERR_INVALID  # t alignment
+    assert d(FAKE, 8, 256, 252, 128, FAKE, 32, 1.0, FAKE, NULL) == ck.CK4_ERR_INVALID  # ldx < k
+    assert d(FAKE, 8, 320, 320, 64, FAKE, 32, 1.0, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 128
+    assert d(FAKE, 8, 256, 256, 128, FAKE, 96, 1.0, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rank
+    assert d(FAKE, 8, 1024, 1024, 512, FAKE, 32, 1.0, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rot_block
+    f = L.ck4_linear_w4a4_lora
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE, 32, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, ODD, 32, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 16, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 32, 8, 8, 384, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 32, 8, 8, 256, FAKE, 4, NULL) == ck.CK4_ERR_INVALID
+
+
 def test_no_cpu_fallback_without_library(tmp_path, monkeypatch):
     # The binding must fail loudly, not compute elsewhere, when the library is absent.
     monkeypatch.setattr(ck, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -403,3 +403,149 @@ def test_skinny_layers(ck, m, n, k):
     xq8, sx8 = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
     y8 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx8, torch.from_numpy(wpg).cuda(), torch.from_numpy(gs).cuda()))
     assert_bf16_close(y8, oracle.linear_w4a8_grouped(xb, wpg, gs))
+
+
+# --------------------------------------------------------------------------
+# Dynamic LoRA: rotated down projection, up projection fused in the epilogue.
+# Bars: A R is bit-exact (same fp32 rotation, one RNE rounding); t is within
+# one bf16 rounding step (2^-7 relative) plus the fp32 accumulation bound
+# (K + 16) 2^-24 alpha sum |bf16(xR)| |A R| of the exact value; y is within
+# the suite's 1e-2 relative plus the fp32 epilogue's rounding of both summands
+# (the fp32 base value, 2^-21 of it, and the rank + 8 fp32 additions of the
+# LoRA sum).
+
+
+def f64_of(bits):
+    return workloads.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+@pytest.mark.parametrize("rank,k,rb", [(32, 256, 128), (64, 3072, 128), (128, 1024, 16), (256, 2048, 256),
+                                       (32, 16384, 128), (64, 512, 64), (128, 512, 32)])
+def test_lora_prepare_down_bitexact(ck, rank, k, rb):
+    a, _ = workloads.make_lora(np.random.default_rng(900 + rank + k), rank, k, 1)
+    got = bf16_host_bits(ck.lora_prepare_down(torch.from_numpy(a).cuda(), rb))
+    assert np.array_equal(got, oracle.lora_prepare_down(a, rb))
+
+
+def _t_atol(xb, a_rot, alpha, rb):
+    xr = np.abs(f64_of(oracle.to_bf16(oracle.rotate_bf16(xb, rb))))
+    return abs(alpha) * (xb.shape[1] + 16) * 2.0 ** -24 * (xr @ np.abs(f64_of(a_rot)).T)
+
+
+def _assert_t_close(got_bits, ref_bits, atol):
+    g, r = f64_of(got_bits), f64_of(ref_bits)
+    bad = np.abs(g - r) > 2.0 ** -7 * 1.01 * np.abs(r) + 1.01 * atol
+    assert not bad.any(), f"{bad.sum()} of {bad.size} outside; first at {np.argwhere(bad)[0]}"
+
+
+@pytest.mark.parametrize("m,k,rb,rank", [(1, 256, 128, 32), (16, 3072, 128, 64), (17, 1024, 16, 128),
+                                         (33, 2048, 256, 256), (100, 512, 64, 32), (130, 384, 128, 64),
+                                         (5, 16384, 128, 128), (64, 5120, 128, 128), (47, 1280, 32, 256)])
+def test_lora_down(ck, m, k, rb, rank):
+    rng = np.random.default_rng(910 + m + rank)
+    xb = workloads.make_activations(rng, m, k)
+    xb[m // 2] = 0
+    a, _ = workloads.make_lora(rng, rank, k, 1)
+    a_rot = oracle.lora_prepare_down(a, rb)
+    alpha = 0.625
+    t = bf16_host_bits(ck.lora_down(dev_bf16(xb), dev_bf16(a_rot), alpha, rb))
+    assert not f64_of(t[m // 2]).any()
+    _assert_t_close(t, oracle.lora_down(xb, a_rot, alpha, rb), _t_atol(xb, a_rot, alpha, rb))
+
+
+def test_lora_down_row_stride(ck):
+    m, k, rank = 40, 1024, 64
+    rng = np.random.default_rng(919)
+    wide = workloads.make_activations(rng, m, k + 256)
+    a, _ = workloads.make_lora(rng, rank, k, 1)
+    a_rot = oracle.lora_prepare_down(a)
+    t = bf16_host_bits(ck.lora_down(dev_bf16(wide)[:, :k], dev_bf16(a_rot), 1.0))
+    xb = np.ascontiguousarray(wide[:, :k])
+    _assert_t_close(t, oracle.lora_down(xb, a_rot, 1.0), _t_atol(xb, a_rot, 1.0, 128))
+
+
+def _lora_atol(acc, sx, ws, bias, t_bits, b_bits, rank):
+    base = np.abs(acc.astype(np.float64) * sx.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :])
+    if bias is not None:
+        base = base + np.abs(bias.astype(np.float64))[None, :]
+    lora = np.abs(f64_of(t_bits)) @ np.abs(f64_of(b_bits)).T
+    return 2.0 ** -21 * base + (rank + 8) * 2.0 ** -24 * (base + lora)
+
+
+@pytest.mark.parametrize("m,n,k,rank", [(1, 77, 256, 32), (16, 300, 512, 64), (33, 130, 1024, 128),
+                                        (64, 1000, 768, 256), (65, 200, 512, 32), (130, 257, 768, 64),
+                                        (300, 96, 1280, 128), (1000, 520, 512, 256)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear_w4a4_lora_epilogue(ck, m, n, k, rank, with_bias):
+    _, xq, sx, wp, ws = _quantised_pair(m, n, k, 920 + m + n)
+    rng = np.random.default_rng(930 + rank)
+    t = workloads.f32_to_bf16_bits(rng.normal(0.0, 2.0, (m, rank)).astype(np.float32))
+    _, b = workloads.make_lora(rng, rank, k, n)
+    bias = rng.standard_normal(n).astype(np.float32) if with_bias else None
+    y = ck.linear_w4a4_lora(torch.from_numpy(xq).cuda(), torch.from_numpy(sx).cuda(), torch.from_numpy(wp).cuda(),
+                            torch.from_numpy(ws).cuda(), dev_bf16(t), dev_bf16(b),
+                            None if bias is None else torch.from_numpy(bias).cuda())
+    acc = oracle.gemm_acc(xq, wp, k)
+    y_ref = oracle.epilogue_lora(acc, sx, ws, t, b, bias)
+    assert_bf16_close(bf16_host_bits(y), y_ref, atol=_lora_atol(acc, sx, ws, bias, t, b, rank))
+
+
+@pytest.mark.parametrize("m,n,k", [(8, 300, 512), (500, 200, 768)])
+def test_lora_with_zero_t_is_plain_linear_bitwise(ck, m, n, k):
+    _, xq, sx, wp, ws = _quantised_pair(m, n, k, 940 + m)
+    _, b = workloads.make_lora(np.random.default_rng(941), 64, k, n)
+    bias = np.random.default_rng(942).standard_normal(n).astype(np.float32)
+    dq = [torch.from_numpy(v).cuda() for v in (xq, sx, wp, ws)]
+    bd = torch.from_numpy(bias).cuda()
+    y0 = bf16_host_bits(ck.linear_w4a4(*dq, bd))
+    t0 = torch.zeros((m, 64), dtype=torch.bfloat16, device="cuda")
+    y1 = bf16_host_bits(ck.linear_w4a4_lora(*dq, t0, dev_bf16(b), bd))
+    assert np.array_equal(y0, y1)
+
+
+@pytest.mark.parametrize("m,n,k,rank,rb", [(1, 3072, 3072, 128, 128), (64, 512, 1024, 64, 64),
+                                           (200, 384, 2048, 32, 256), (97, 1000, 512, 256, 16)])
+def test_w4a4_lora_layer_end_to_end(ck, m, n, k, rank, rb):
+    lay = workloads.make_layer(m, k, n, seed=950 + m)
+    a, b = workloads.make_lora(np.random.default_rng(951 + m), rank, k, n)
+    alpha = 0.5
+    wp, ws = oracle.quantize_weight_convrot(lay.weights[0], rb)
+    a_rot = oracle.lora_prepare_down(a, rb)
+    y = ck.w4a4_lora_linear(dev_bf16(lay.x_bf16), torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda(),
+                            dev_bf16(a_rot), dev_bf16(b), alpha, None, rb)
+    y_ref = oracle.linear_w4a4_lora(lay.x_bf16, wp, ws, a_rot, b, alpha, g=rb)
+    xq, sx = oracle.rotate_quantize_act(lay.x_bf16, rb)
+    acc = oracle.gemm_acc(xq, wp, k)
+    t_ref = oracle.lora_down(lay.x_bf16, a_rot, alpha, rb)
+    # t may differ from the oracle's by its own bound; carry that through B
+    dt = 2.0 ** -7 * 1.01 * np.abs(f64_of(t_ref)) + 1.01 * _t_atol(lay.x_bf16, a_rot, alpha, rb)
+    atol = _lora_atol(acc, sx, ws, None, t_ref, b, rank) + dt @ np.abs(f64_of(b)).T
+    assert_bf16_close(bf16_host_bits(y), y_ref, atol=atol)
+
+
+def test_full_size_square_layer_with_lora(ck):
+    cfg = workloads.WORKLOADS["square_3072"]
+    lay = workloads.make_layer(seed=0, **cfg)
+    m, k, n = lay.m, lay.k, lay.n
+    rank, alpha = 128, 0.5
+    a, b = workloads.make_lora(np.random.default_rng(960), rank, k, n)
+    wp, ws = oracle.quantize_weight_convrot(lay.weights[0])
+    a_rot = oracle.lora_prepare_down(a)
+    a_rot_d = ck.lora_prepare_down(torch.from_numpy(a).cuda())
+    assert np.array_equal(bf16_host_bits(a_rot_d), a_rot)
+    xd = dev_bf16(lay.x_bf16)
+    xq, sx = ck.rotate_quantize_act(xd, 128, 4)
+    t = ck.lora_down(xd, a_rot_d, alpha)
+    y = bf16_host_bits(ck.linear_w4a4_lora(xq, sx, torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda(), t,
+                                           dev_bf16(b)))
+    rows = _sample_rows(m, 30, 2)
+    xr = np.ascontiguousarray(lay.x_bf16[rows])
+    t_ref = oracle.lora_down(xr, a_rot, alpha)
+    _assert_t_close(bf16_host_bits(t)[rows], t_ref, _t_atol(xr, a_rot, alpha, 128))
+    xq_ref, sx_ref = oracle.rotate_quantize_act(xr)
+    acc = oracle.gemm_acc(xq_ref, wp, k)
+    # the up projection is checked on the device's own t
+    t_dev = bf16_host_bits(t)[rows]
+    y_ref = oracle.epilogue_lora(acc, sx_ref, ws, t_dev, b)
+    assert_bf16_close(y[rows], y_ref, atol=_lora_atol(acc, sx_ref, ws, None, t_dev, b, rank))
+

@@ -549,3 +549,125 @@ def test_e4m3_weight_prep_rounds_fp32_scales_and_bounds_codes():
         assert np.all(err[sel] <= sdb[sel] / 2 * (1 + 2 ** -20))   # nearest code against the decoded scale
         assert np.all(np.abs(q[okb & ~unclipped]) == 7)           # beyond 7 s8: clamped
         assert not q[~okb].any() and not q[3].any()
+
+
+# --------------------------------------------------------------------------
+# Dynamic LoRA: the down projection is rotated like the weights, so that
+# x A^T = (x R)(A R)^T for the orthonormal block rotation R.
+
+
+def _rot_err_f32(v, g=128):
+    """Per-element bound on |fp32 rotation - exact rotation| (the bound pinned above)."""
+    v = np.abs(np.asarray(v, np.float64))
+    m, k = v.shape
+    blk = v.reshape(m, k // g, g).sum(axis=2, keepdims=True)
+    e = (math.log2(g) + 2) * 2.0 ** -24 * blk / math.sqrt(g) * 1.01
+    return np.broadcast_to(e, (m, k // g, g)).reshape(m, k)
+
+
+def _bf16(bits):
+    return workloads.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def test_lora_prepare_down_is_rotation_rounded_once():
+    rng = np.random.default_rng(40)
+    a, _ = workloads.make_lora(rng, 32, 512, 8)
+    got = _bf16(oracle.lora_prepare_down(a))
+    exact = oracle.rotate_f64(a.astype(np.float64))
+    e32 = _rot_err_f32(a)
+    # bf16 keeps 8 significant bits: one rounding is within 2^-8 relative
+    bound = 2.0 ** -8 * (np.abs(exact) + e32) + e32
+    assert np.all(np.abs(got - exact) <= bound)
+    # the rows keep their inner products (R is orthonormal), up to the bf16 rounding
+    gram = got @ got.T
+    ref = a.astype(np.float64) @ a.astype(np.float64).T
+    assert np.all(np.abs(gram - ref) <= 2.0 ** -6.9 * (np.abs(got) @ np.abs(got).T))
+    # the bound is not vacuous: an unrotated A is far outside it
+    assert np.any(np.abs(_bf16(oracle.to_bf16(a)) - exact) > bound)
+
+
+def test_lora_down_equals_unrotated_product_within_rounding():
+    lay = workloads.make_layer(24, 512, 8, seed=41)
+    a, _ = workloads.make_lora(np.random.default_rng(42), 64, 512, 8)
+    alpha = 0.75
+    t = _bf16(oracle.lora_down(lay.x_bf16, oracle.lora_prepare_down(a), alpha))
+    x = _bf16(lay.x_bf16)
+    ref = alpha * x @ a.astype(np.float64).T
+    rx = np.abs(oracle.rotate_f64(x))
+    ra = np.abs(oracle.rotate_f64(a.astype(np.float64)))
+    # each operand is the fp32 rotation rounded once to bf16 (2^-8 relative),
+    # then t itself is rounded once
+    ex = _rot_err_f32(x) * (1 + 2.0 ** -7) + 2.0 ** -8 * rx
+    ea = _rot_err_f32(a) * (1 + 2.0 ** -7) + 2.0 ** -8 * ra
+    prod_err = ex @ ra.T + rx @ ea.T + ex @ ea.T
+    bound = alpha * prod_err * 1.001 + 2.0 ** -8 * np.abs(t) * 1.001
+    assert np.all(np.abs(t - ref) <= bound)
+    assert np.median(np.abs(t - ref) / bound) < 0.2
+    # a down projection left unrotated (a plausible slip) breaks the bound
+    xr = _bf16(oracle.to_bf16(oracle.rotate_bf16(lay.x_bf16)))
+    t_bad = _bf16(oracle.to_bf16(alpha * xr @ _bf16(oracle.to_bf16(a)).T))
+    assert np.any(np.abs(t_bad - ref) > bound)
+
+
+def test_lora_zero_alpha_is_plain_linear():
+    lay = workloads.make_layer(9, 256, 40, seed=43)
+    a, b = workloads.make_lora(np.random.default_rng(44), 32, 256, 40)
+    wp, ws = oracle.quantize_weight_convrot(lay.weights[0])
+    a_rot = oracle.lora_prepare_down(a)
+    assert np.all(_bf16(oracle.lora_down(lay.x_bf16, a_rot, 0.0)) == 0)
+    y0 = oracle.linear_w4a4_lora(lay.x_bf16, wp, ws, a_rot, b, 0.0)
+    assert np.array_equal(y0, oracle.linear_w4a4(lay.x_bf16, wp, ws))
+
+
+def test_lora_up_adds_rank_terms_exactly():
+    m, n, k, rank = 10, 24, 256, 32
+    lay = workloads.make_layer(m, k, n, seed=45)
+    wp, ws = oracle.quantize_weight_convrot(lay.weights[0])
+    xq, sx = oracle.rotate_quantize_act(lay.x_bf16)
+    acc = oracle.gemm_acc(xq, wp, k)
+    rng = np.random.default_rng(46)
+    # t[:, 0] = 2^e_m (exact in bf16), b[:, 0] = c_n; column 7 of t is noise
+    # whose b column is zero; every other entry is zero
+    e = rng.integers(-3, 4, m)
+    t = np.zeros((m, rank), np.uint16)
+    t[:, 0] = workloads.f32_to_bf16_bits(np.ldexp(np.ones(m, np.float32), e))
+    t[:, 7] = workloads.f32_to_bf16_bits(rng.standard_normal(m).astype(np.float32))
+    b = np.zeros((n, rank), np.uint16)
+    c = workloads.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32))
+    b[:, 0] = c
+    y = oracle.epilogue_lora(acc, sx, ws, t, b)
+    cf = workloads.bf16_bits_to_f32(c)
+    for i in range(m):
+        for j in range(n):
+            exact = (Fraction(int(acc[i, j])) * Fraction(float(sx[i])) * Fraction(float(ws[j]))
+                     + Fraction(2) ** int(e[i]) * Fraction(float(cf[j])))
+            got = Fraction(_bf16_value(int(y[i, j])))
+            if exact == 0:
+                assert got == 0
+                continue
+            ulp = Fraction(2) ** (math.frexp(float(exact))[1] - 8)
+            assert abs(got - exact) <= ulp / 2
+    # with t = e_0 for every row the LoRA term is a column bias: same rounding as the plain epilogue
+    t1 = np.zeros((m, rank), np.uint16)
+    t1[:, 0] = 0x3F80
+    assert np.array_equal(oracle.epilogue_lora(acc, sx, ws, t1, b), oracle.epilogue_bf16(acc, sx, ws, cf))
+
+
+def test_lora_layer_is_base_layer_plus_float_lora():
+    m, n, k, rank = 16, 40, 512, 64
+    lay = workloads.make_layer(m, k, n, seed=47)
+    a, b = workloads.make_lora(np.random.default_rng(48), rank, k, n)
+    alpha = 0.5
+    wp, ws = oracle.quantize_weight_convrot(lay.weights[0])
+    a_rot = oracle.lora_prepare_down(a)
+    y = _bf16(oracle.linear_w4a4_lora(lay.x_bf16, wp, ws, a_rot, b, alpha))
+    y0 = _bf16(oracle.linear_w4a4(lay.x_bf16, wp, ws))
+    x = _bf16(lay.x_bf16)
+    bf = _bf16(b)
+    ref_t = alpha * x @ a.astype(np.float64).T
+    t = _bf16(oracle.lora_down(lay.x_bf16, a_rot, alpha))
+    # |t - ref_t| is pinned above; measure it here and carry it through B
+    dt = np.abs(t - ref_t)
+    bound = 2.0 ** -8 * (np.abs(y) + np.abs(y0)) + dt @ np.abs(bf).T * 1.001 + 2.0 ** -20
+    assert np.all(np.abs((y - y0) - ref_t @ bf.T) <= bound)
+

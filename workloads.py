@@ -12,7 +12,10 @@ transformer's hidden states and linear weights):
   Hadamard rotation exists to spread out (comfy-kitchen PR #63 "int4_tensorwise:
   W4A4 layout (+ConvRot)", Description; runcomfy ComfyUI-INT4-Fast page, "How
   ComfyUI-INT4-Fast Works"); rounded to bf16 with round-to-nearest-even;
-* weights ``W``: ``[N, K]`` fp32 drawn from N(0, 0.02).
+* weights ``W``: ``[N, K]`` fp32 drawn from N(0, 0.02);
+* LoRA factors (dynamic LoRA): down ``A`` ``[rank, K]`` fp32 and up ``B``
+  ``[N, rank]`` rounded to bf16, both drawn from N(0, 0.02), so that the LoRA
+  term is a visible fraction of the layer's output.
 
 Draw order for one seed: outlier channel indices, then ``x``, then each weight
 in turn. The same host arrays feed the oracle and the GPU, so the two sides
@@ -63,6 +66,16 @@ def make_activations(rng: np.random.Generator, m: int, k: int, idx: np.ndarray |
 def make_weight(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
     """fp32 ``[n, k]`` drawn from N(0, 0.02)."""
     return rng.normal(0.0, WEIGHT_STD, (n, k)).astype(np.float32)
+
+
+LORA_STD = 0.02
+
+
+def make_lora(rng: np.random.Generator, rank: int, k: int, n: int):
+    """LoRA factors: (down fp32 ``[rank, k]``, up bf16 bit patterns ``uint16 [n, rank]``)."""
+    a = rng.normal(0.0, LORA_STD, (rank, k)).astype(np.float32)
+    b = f32_to_bf16_bits(rng.normal(0.0, LORA_STD, (n, rank)).astype(np.float32))
+    return a, b
 
 
 @dataclass
