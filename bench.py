@@ -265,8 +265,8 @@ def layer_sweep(ck, torch, args) -> int:
     for rank in (32, 128):
         a, b = workloads.make_lora(np.random.default_rng(70 + rank), rank, k, n)
         a_rot = ck.lora_prepare_down(torch.from_numpy(a).to(dev))
-        bd = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
-        t = torch.empty((m, rank), dtype=torch.bfloat16, device=dev)
+        bd = ck.lora_prepare_up(torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev))
+        t = torch.empty(((m + 15) // 16 * 16, rank), dtype=torch.bfloat16, device=dev)
 
         def down():
             ck.lora_down(x, a_rot, 0.5, 128, out=t)

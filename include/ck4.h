@@ -268,39 +268,54 @@ ck4_status ck4_linear_w4a8_grouped_e4m3(const int8_t *x_q8, const float *x_scale
  * Dynamic LoRA patching rotates the LoRA down projection with the same
  * Hadamard blocks, so that it stays coherent with the rotated activation).
  * For a LoRA y += alpha * (x A^T) B^T with A fp32 [rank, k] (down) and
- * B [n, rank] (up), the orthonormal rotation R of the quantiser gives
- * x A^T = (x R)(A R)^T, so the down projection runs on the activation the
- * quantiser rotates anyway:
- *   ck4_lora_prepare_down  a_rot = bf16(A R): each row of a (fp32, row
- *       stride lda) rotated with the weight path's fp32 butterflies and
- *       rounded to bf16 (nearest even); a_rot bf16 [rank, k] contiguous.
- *       Once per LoRA, like the weight preparation.
- *   ck4_lora_down  t[m, j] = bf16(alpha * sum_k bf16((x R)[m, k]) a_rot[j, k]),
- *       with x R the fp32 rotation of ck4_rotate_act_f32 (bit for bit),
- *       products and sums in fp32; x bf16 [m, ldx]; t bf16 [m, rank]
- *       contiguous.
+ * B bf16 [n, rank] (up), the orthonormal rotation R of the quantiser gives
+ * x A^T = (x R)(A R)^T, so the down projection runs on the rotated
+ * activation.
+ *
+ * Fragment order. The LoRA operands live in device memory in the register
+ * order of the bf16 matrix instructions, so that every wavefront load is one
+ * contiguous 1 KB: a bf16 matrix Z [rows, cols] (cols a multiple of 32, rows
+ * rounded up to a multiple of 16) is stored as 16-row x 32-column tiles of
+ * 512 values, tile (r / 16, c / 32) at element offset
+ * ((r / 16) * (cols / 32) + c / 32) * 512, and element (i, c) of a tile at
+ * (16 * ((c >> 2) & 3) + i) * 8 + 4 * (c >> 4) + (c & 3).
+ *
+ *   ck4_lora_prepare_down  a_pack = bf16(A R) in fragment order ([rank, k],
+ *       rank * k values): each row of a (fp32, row stride lda) rotated with
+ *       the weight path's fp32 butterflies and rounded to bf16 (nearest
+ *       even). Once per LoRA, like the weight preparation.
+ *   ck4_lora_prepare_up  b_pack = b in fragment order ([n, rank] padded to
+ *       n16 = 16 * ceil(n / 16) rows with zeros: n16 * rank values); b bf16
+ *       [n, ldb] holds the up matrix, already scaled as the caller wants.
+ *   ck4_lora_down  t_pack = t in fragment order ([m, rank] as 16 * ceil(m / 16)
+ *       rows: rows >= m of the last block hold unspecified values), with
+ *       t[m, j] = bf16(alpha * sum_k bf16((x R)[m, k]) (A R)[j, k]); x R is
+ *       the product of x with the +-1 Hadamard blocks accumulated in fp32 and
+ *       scaled by fp32(1 / sqrt(rot_block)) (the rotation of
+ *       ck4_rotate_act_f32 up to fp32 rounding order); products and sums in
+ *       fp32; x bf16 [m, ldx].
  *   ck4_linear_w4a4_lora  ck4_linear_w4a4 with the up projection fused into
  *       its epilogue: y = bf16(acc * x_scales[m] * w_scales[n] (+ bias[n])
- *       + sum_j t[m, j] b_up[n, j]); the fp32 value of the base layer and
- *       the LoRA sum are added in fp32 before the one bf16 rounding.
- *       b_up bf16 [n, rank] contiguous (the up matrix, already scaled as the
- *       caller wants; alpha lives in ck4_lora_down).
+ *       + sum_j t[m, j] b[n, j]); the fp32 value of the base layer and the
+ *       LoRA sum are added in fp32 before the one bf16 rounding.
  * Several LoRAs active at once are one LoRA of their summed ranks: stack
  * their scaled down rows and up columns (zero rows and columns pad the stack
  * to a supported rank and add nothing).
- * rank: 32, 64, 128 or 256. Alignment: x, ldx*2, a_rot, t, b_up 16 bytes.
- * Unsupported: rot_block above 256 for the LoRA calls; k not a multiple of
- * max(128, rot_block) for ck4_lora_down; otherwise as ck4_rotate_act_f32 and
- * ck4_linear_w4a4.
+ * rank: 32, 64, 128 or 256. Alignment: x, ldx*2, a_pack, b_pack, t_pack
+ * 16 bytes; a and lda*4 16 bytes; b, ldb*2 8 bytes.
+ * Unsupported: rot_block above 256; k not a multiple of max(128, rot_block)
+ * for ck4_lora_down; otherwise as ck4_rotate_act_f32 and ck4_linear_w4a4.
  */
 ck4_status ck4_lora_prepare_down(const float *a, int64_t rank, int64_t k, int64_t lda, int rot_block,
-                                 uint16_t *a_rot, void *stream);
-ck4_status ck4_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, const uint16_t *a_rot,
-                         int64_t rank, float alpha, uint16_t *t, void *stream);
+                                 uint16_t *a_pack, void *stream);
+ck4_status ck4_lora_prepare_up(const uint16_t *b, int64_t n, int64_t rank, int64_t ldb, uint16_t *b_pack,
+                               void *stream);
+ck4_status ck4_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, const uint16_t *a_pack,
+                         int64_t rank, float alpha, uint16_t *t_pack, void *stream);
 ck4_status ck4_linear_w4a4_lora(const int8_t *x_q, const float *x_scales, const int8_t *w_packed,
-                                const float *w_scales, const float *bias, const uint16_t *t, const uint16_t *b_up,
-                                int64_t rank, int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy,
-                                void *stream);
+                                const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k, uint16_t *y,
+                                int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,7 @@ SIGNATURES = {
     "ck4_linear_w4a8_grouped_e4m3": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t,
                                       _P], _I),
     "ck4_lora_prepare_down": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
+    "ck4_lora_prepare_up": ([_P, _I64, _I64, _I64, _P, _P], _I),
     "ck4_lora_down": ([_P, _I64, _I64, _I64, _I, _P, _I64, ctypes.c_float, _P, _P], _I),
     "ck4_linear_w4a4_lora": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _I),
 }
@@ -278,61 +279,77 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
     return out
 
 
+def _rows16(n: int) -> int:
+    return (n + 15) // 16 * 16
+
+
 def lora_prepare_down(a: torch.Tensor, rot_block: int = 128):
-    """Rotated LoRA down projection: fp32 A [rank, k] -> bf16 A R [rank, k]."""
+    """Rotated LoRA down projection: fp32 A [rank, k] -> bf16 A R [rank, k] in MFMA fragment order."""
     _need(a, torch.float32, "a", 2)
     rank, k = a.shape
-    a_rot = torch.empty((rank, k), dtype=torch.bfloat16, device=a.device)
+    a_pack = torch.empty((rank, k), dtype=torch.bfloat16, device=a.device)
     _check("ck4_lora_prepare_down",
-           lib().ck4_lora_prepare_down(_ptr(a), rank, k, a.stride(0), rot_block, _ptr(a_rot), _stream(a.device)))
-    return a_rot
+           lib().ck4_lora_prepare_down(_ptr(a), rank, k, a.stride(0), rot_block, _ptr(a_pack), _stream(a.device)))
+    return a_pack
 
 
-def lora_down(x: torch.Tensor, a_rot: torch.Tensor, alpha: float = 1.0, rot_block: int = 128, out=None):
-    """t = bf16(alpha * bf16(x R) a_rot^T): bf16 x [m, k], bf16 a_rot [rank, k] -> bf16 t [m, rank]."""
+def lora_prepare_up(b: torch.Tensor):
+    """LoRA up projection: bf16 B [n, rank] -> fragment order [16 * ceil(n / 16), rank] (zero padding rows)."""
+    _need(b, torch.bfloat16, "b", 2)
+    n, rank = b.shape
+    b_pack = torch.empty((_rows16(n), rank), dtype=torch.bfloat16, device=b.device)
+    _check("ck4_lora_prepare_up",
+           lib().ck4_lora_prepare_up(_ptr(b), n, rank, b.stride(0), _ptr(b_pack), _stream(b.device)))
+    return b_pack
+
+
+def lora_down(x: torch.Tensor, a_pack: torch.Tensor, alpha: float = 1.0, rot_block: int = 128, out=None):
+    """t = bf16(alpha * bf16(x R) (A R)^T) in fragment order [16 * ceil(m / 16), rank], from bf16 x [m, k]."""
     _need(x, torch.bfloat16, "x", 2)
-    _need(a_rot, torch.bfloat16, "a_rot", 2)
+    _need(a_pack, torch.bfloat16, "a_pack", 2)
     m, k = x.shape
-    rank = a_rot.shape[0]
-    if a_rot.shape[1] != k or not a_rot.is_contiguous():
-        raise ValueError("a_rot must be a contiguous [rank, k] tensor")
+    rank = a_pack.shape[0]
+    if a_pack.shape[1] != k or not a_pack.is_contiguous():
+        raise ValueError("a_pack must be a contiguous [rank, k] tensor")
     if out is None:
-        out = torch.empty((m, rank), dtype=torch.bfloat16, device=x.device)
+        out = torch.empty((_rows16(m), rank), dtype=torch.bfloat16, device=x.device)
     _need(out, torch.bfloat16, "out", 2)
-    if tuple(out.shape) != (m, rank) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous [m, rank] tensor")
+    if tuple(out.shape) != (_rows16(m), rank) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [16 * ceil(m / 16), rank] tensor")
     _check("ck4_lora_down",
-           lib().ck4_lora_down(_ptr(x), m, k, x.stride(0), rot_block, _ptr(a_rot), rank, float(alpha), _ptr(out),
+           lib().ck4_lora_down(_ptr(x), m, k, x.stride(0), rot_block, _ptr(a_pack), rank, float(alpha), _ptr(out),
                                _stream(x.device)))
     return out
 
 
 def linear_w4a4_lora(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
-                     t: torch.Tensor, b_up: torch.Tensor, bias: torch.Tensor | None = None,
+                     t_pack: torch.Tensor, b_pack: torch.Tensor, bias: torch.Tensor | None = None,
                      out: torch.Tensor | None = None):
-    """W4A4 linear with the LoRA up projection in its epilogue: y = base + t b_up^T, bf16 [m, n]."""
+    """W4A4 linear with the LoRA up projection in its epilogue: y = base + t B^T, bf16 [m, n].
+
+    t_pack from lora_down, b_pack from lora_prepare_up (both in fragment order)."""
     m, k = x_q.shape[0], x_q.shape[1] * 2
     n = w_packed.shape[0]
-    _need(t, torch.bfloat16, "t", 2)
-    _need(b_up, torch.bfloat16, "b_up", 2)
-    rank = t.shape[1]
-    if t.shape[0] != m or not t.is_contiguous():
-        raise ValueError("t must be a contiguous [m, rank] tensor")
-    if tuple(b_up.shape) != (n, rank) or not b_up.is_contiguous():
-        raise ValueError("b_up must be a contiguous [n, rank] tensor")
+    _need(t_pack, torch.bfloat16, "t_pack", 2)
+    _need(b_pack, torch.bfloat16, "b_pack", 2)
+    rank = t_pack.shape[1]
+    if tuple(t_pack.shape) != (_rows16(m), rank) or not t_pack.is_contiguous():
+        raise ValueError("t_pack must be a contiguous [16 * ceil(m / 16), rank] tensor")
+    if tuple(b_pack.shape) != (_rows16(n), rank) or not b_pack.is_contiguous():
+        raise ValueError("b_pack must be a contiguous [16 * ceil(n / 16), rank] tensor")
     if out is None:
         out = _out_bf16(m, n, x_q.device)
     _need(out, torch.bfloat16, "out", 2)
     _check("ck4_linear_w4a4_lora",
-           lib().ck4_linear_w4a4_lora(_ptr(x_q), _ptr(x_scales), _ptr(w_packed), _ptr(w_scales), _ptr(bias), _ptr(t),
-                                      _ptr(b_up), rank, m, n, k, _ptr(out), out.stride(0), _stream(x_q.device)))
+           lib().ck4_linear_w4a4_lora(_ptr(x_q), _ptr(x_scales), _ptr(w_packed), _ptr(w_scales), _ptr(bias),
+                                      _ptr(t_pack), _ptr(b_pack), rank, m, n, k, _ptr(out), out.stride(0),
+                                      _stream(x_q.device)))
     return out
 
 
-def w4a4_lora_linear(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, a_rot: torch.Tensor,
-                     b_up: torch.Tensor, alpha: float = 1.0, bias=None, rot_block: int = 128):
+def w4a4_lora_linear(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, a_pack: torch.Tensor,
+                     b_pack: torch.Tensor, alpha: float = 1.0, bias=None, rot_block: int = 128):
     """The whole layer with a dynamic LoRA: quantise x, down-project its rotation, GEMM + fused up projection."""
     x_q, sx = rotate_quantize_act(x, rot_block, 4)
-    t = lora_down(x, a_rot, alpha, rot_block)
-    return linear_w4a4_lora(x_q, sx, w_packed, w_scales, t, b_up, bias)
-
+    t = lora_down(x, a_pack, alpha, rot_block)
+    return linear_w4a4_lora(x_q, sx, w_packed, w_scales, t, b_pack, bias)

@@ -388,30 +388,48 @@ bool lora_rank_ok(int64_t rank) { return rank == 32 || rank == 64 || rank == 128
 extern "C" {
 
 ck4_status ck4_lora_prepare_down(const float *a, int64_t rank, int64_t k, int64_t lda, int rot_block,
-                                 uint16_t *a_rot, void *stream) {
+                                 uint16_t *a_pack, void *stream) {
     const char *fn = "ck4_lora_prepare_down";
-    if (!a || !a_rot) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (!a || !a_pack) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (rank <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: rank and k must be positive", fn);
     if (lda < k) return fail(CK4_ERR_INVALID, "%s: lda < k", fn);
     if (!aligned(a, 16) || (lda * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: a/lda not 16-byte aligned", fn);
-    if (!aligned(a_rot, 16)) return fail(CK4_ERR_INVALID, "%s: a_rot not 16-byte aligned", fn);
+    if (!aligned(a_pack, 16)) return fail(CK4_ERR_INVALID, "%s: a_pack not 16-byte aligned", fn);
     if (!lora_rank_ok(rank))
         return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
     if (rot_block > 256) return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d > 256", fn, rot_block);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (k % 32 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 32", fn, (long long)k);
     if (ck4_status s = check_device(fn)) return s;
-    return launched(fn, ck4::launch_rotate_quant(a, 1, rank, k, lda, rot_block, 3, 0, a_rot, k, nullptr,
+    return launched(fn, ck4::launch_rotate_quant(a, 1, rank, k, lda, rot_block, 3, 0, a_pack, k, nullptr,
                                                   static_cast<hipStream_t>(stream)));
 }
 
-ck4_status ck4_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, const uint16_t *a_rot,
-                         int64_t rank, float alpha, uint16_t *t, void *stream) {
+ck4_status ck4_lora_prepare_up(const uint16_t *b, int64_t n, int64_t rank, int64_t ldb, uint16_t *b_pack,
+                               void *stream) {
+    const char *fn = "ck4_lora_prepare_up";
+    if (!b || !b_pack) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (n <= 0) return fail(CK4_ERR_INVALID, "%s: n must be positive", fn);
+    if (ldb < rank) return fail(CK4_ERR_INVALID, "%s: ldb < rank", fn);
+    if (!aligned(b, 8) || (ldb * 2) % 8 != 0) return fail(CK4_ERR_INVALID, "%s: b/ldb not 8-byte aligned", fn);
+    if (!aligned(b_pack, 16)) return fail(CK4_ERR_INVALID, "%s: b_pack not 16-byte aligned", fn);
+    if (!lora_rank_ok(rank))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
+    if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_lora_pack(b, n, rank, ldb, b_pack, static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, const uint16_t *a_pack,
+                         int64_t rank, float alpha, uint16_t *t_pack, void *stream) {
+    const uint16_t *a_rot = a_pack;
+    uint16_t *t = t_pack;
     const char *fn = "ck4_lora_down";
     if (!x || !a_rot || !t) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (m <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m and k must be positive", fn);
     if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
     if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: x/ldx not 16-byte aligned", fn);
-    if (!aligned(a_rot, 16) || !aligned(t, 16)) return fail(CK4_ERR_INVALID, "%s: a_rot or t misaligned", fn);
+    if (!aligned(a_rot, 16) || !aligned(t, 16)) return fail(CK4_ERR_INVALID, "%s: a_pack or t_pack misaligned", fn);
     if (m > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m too large", fn);
     if (!lora_rank_ok(rank))
         return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
@@ -426,12 +444,13 @@ ck4_status ck4_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, i
 }
 
 ck4_status ck4_linear_w4a4_lora(const int8_t *x_q, const float *x_scales, const int8_t *w_packed,
-                                const float *w_scales, const float *bias, const uint16_t *t, const uint16_t *b_up,
-                                int64_t rank, int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy,
-                                void *stream) {
+                                const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k, uint16_t *y,
+                                int64_t ldy, void *stream) {
     const char *fn = "ck4_linear_w4a4_lora";
+    const uint16_t *t = t_pack, *b_up = b_pack;
     if (!t || !b_up) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
-    if (!aligned(t, 16) || !aligned(b_up, 16)) return fail(CK4_ERR_INVALID, "%s: t or b_up misaligned", fn);
+    if (!aligned(t, 16) || !aligned(b_up, 16)) return fail(CK4_ERR_INVALID, "%s: t_pack or b_pack misaligned", fn);
     if (!lora_rank_ok(rank))
         return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
     return gemm_entry(fn, true, x_q, x_scales, w_packed, w_scales, bias, m, n, k, false, y, ldy, stream,

@@ -21,17 +21,23 @@ struct WeightOpts {
 // Rotation + quantisation of rows (one wavefront or one workgroup per row).
 //   in_kind   0: bf16 input, 1: fp32 input
 //   out_kind  0: packed int4 (+ scales), 1: int8 codes (+ scales), 2: fp32 rotation
-//             (bf16 input only), 3: the rotation rounded to bf16
+//             (bf16 input only), 3: the rotation rounded to bf16, in MFMA fragment
+//             order (rows a multiple of 16, k a multiple of 32; ldo unused)
 //   group     0: one scale per row; > 0: one scale per `group` elements (int4 only)
 //   scales    fp32, or E4M3 bytes when wo.scale_e4m3
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
                                int out_kind, int group, void *out, int64_t ldo, float *scales, hipStream_t stream,
                                WeightOpts wo = WeightOpts{});
 
+// MFMA fragment order of a bf16 matrix [rows, cols] (rows padded with whole
+// 16-row blocks, cols a multiple of 32): 16-row x 32-column tiles of 512
+// values, tile (r / 16, c / 32) at ((r / 16) * (cols / 32) + c / 32) * 512,
+// element (i, c) of a tile at (16 ((c >> 2) & 3) + i) * 8 + 4 (c >> 4) + (c & 3).
+//
 // LoRA up-projection added in the bf16 epilogue of launch_gemm: t is the
 // bf16 down-projected activation [m, rank], b the bf16 up-projection
-// [n, rank], both row-major and 16-byte aligned; rank is a multiple of 32
-// (0 or t == nullptr: no LoRA term).
+// [n, rank], both in fragment order and 16-byte aligned; rank is a multiple
+// of 32 (0 or t == nullptr: no LoRA term).
 struct LoraUp {
     const uint16_t *t = nullptr;
     const uint16_t *b = nullptr;
@@ -46,9 +52,16 @@ hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *s
                        const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
                        hipStream_t stream, LoraUp lora = LoraUp{});
 
+// b (bf16 [n, rank], row stride ldb) to fragment order, zero rows padding n
+// to a multiple of 16.
+hipError_t launch_lora_pack(const uint16_t *b, int64_t n, int64_t rank, int64_t ldb, uint16_t *out,
+                            hipStream_t stream);
+
 // LoRA down-projection in the rotated basis: t[m, j] = bf16(alpha *
-// sum_k bf16(rotate(x)[m, k]) a_rot[j, k]) with fp32 accumulation, x bf16
-// [m, k] (row stride ldx), a_rot bf16 [rank, k], t bf16 [m, rank].
+// sum_k bf16(rotate(x)[m, k]) a_rot[j, k]) with fp32 accumulation (the
+// rotation too runs on the bf16 matrix cores, accumulating in fp32), x bf16
+// [m, k] (row stride ldx), a_rot bf16 [rank, k] and t bf16 [m, rank] in
+// fragment order (t: whole 16-row blocks).
 // rank in {32, 64, 128, 256}; rot_block in {16, ..., 256}; k a multiple of
 // max(128, rot_block).
 hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block, const uint16_t *a_rot,

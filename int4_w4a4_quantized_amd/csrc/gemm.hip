@@ -30,10 +30,11 @@
 //
 // Optional LoRA up-projection (dynamic LoRA, "Comfy-INT4-HIPtest" README, LoRA
 // modes): with t = the bf16 down-projected activation [M, R] and b = the bf16
-// up-projection [N, R], the epilogue adds sum_j t[m, j] b[n, j] to the fp32
-// value of y before the bf16 rounding, with v_mfma_f32_16x16x32_bf16 whose
-// fragment layout matches the int8 one (first operand b rows, second t rows),
-// so the sum accumulates straight onto the lane's 4 outputs.
+// up-projection [N, R], both in MFMA fragment order, the epilogue adds
+// sum_j t[m, j] b[n, j] to the fp32 value of y before the bf16 rounding, with
+// v_mfma_f32_16x16x32_bf16 whose result layout matches the int8 one (first
+// operand b rows, second t rows), so the sum accumulates straight onto the
+// lane's 4 outputs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,29 +73,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 }
 
 // y[i][j] += the LoRA term of output fragment (i, j): 16 columns from
-// nbase + 16 i by 16 rows from mbase + 16 j, in the int8 accumulator layout
-// (lane l: row l & 15, columns 4 (l >> 4) .. + 3). Each 32-wide slice of the
-// rank is one v_mfma_f32_16x16x32_bf16 per fragment, first operand 16 rows of
-// b, second 16 rows of t, both read straight from global memory (lane l: row
-// l & 15, the 8 values at 8 (l >> 4) of the slice). Rows past M or N read the
-// last valid row; their results are never stored. The whole wavefront runs it.
+// nbase + 16 i by 16 rows from mbase + 16 j (both multiples of 16), in the
+// int8 accumulator layout (lane l: row l & 15, columns 4 (l >> 4) .. + 3).
+// t and b are in MFMA fragment order (16-row x 32-column tiles of 512
+// values in operand register order, tile (r / 16, c / 32) at
+// ((r / 16) * (rank / 32) + c / 32) * 512), so each operand register is one
+// contiguous 1 KB wavefront load: lane l reads the 16 bytes at 16 l. Each
+// 32-wide slice of the rank is one v_mfma_f32_16x16x32_bf16 per fragment,
+// first operand a tile of b, second a tile of t. Row blocks past the last
+// one read the last one; their results are never stored. The whole
+// wavefront runs it.
 template <int FN, int FM>
 __device__ __forceinline__ void lora_up(v4f (&y)[FN][FM], const LoraUp lo, int nbase, int mbase, int N, int M,
                                         int lane) {
-    const int frow = lane & 15;
-    const int koff = 8 * (lane >> 4);
+    const int tq = lo.rank / 32;
+    const int nb_last = (N + 15) / 16 - 1, mb_last = (M + 15) / 16 - 1;
     const uint16_t *bp[FN];
     const uint16_t *tp[FM];
 #pragma unroll
-    for (int i = 0; i < FN; ++i) bp[i] = lo.b + (int64_t)min(nbase + i * 16 + frow, N - 1) * lo.rank + koff;
+    for (int i = 0; i < FN; ++i) bp[i] = lo.b + (int64_t)min(nbase / 16 + i, nb_last) * tq * 512 + lane * 8;
 #pragma unroll
-    for (int j = 0; j < FM; ++j) tp[j] = lo.t + (int64_t)min(mbase + j * 16 + frow, M - 1) * lo.rank + koff;
-    for (int kk = 0; kk < lo.rank; kk += 32) {
+    for (int j = 0; j < FM; ++j) tp[j] = lo.t + (int64_t)min(mbase / 16 + j, mb_last) * tq * 512 + lane * 8;
+    for (int kk = 0; kk < tq; ++kk) {
         v8bf bf[FN], tf[FM];
 #pragma unroll
-        for (int i = 0; i < FN; ++i) bf[i] = *reinterpret_cast<const v8bf *>(bp[i] + kk);
+        for (int i = 0; i < FN; ++i) bf[i] = *reinterpret_cast<const v8bf *>(bp[i] + kk * 512);
 #pragma unroll
-        for (int j = 0; j < FM; ++j) tf[j] = *reinterpret_cast<const v8bf *>(tp[j] + kk);
+        for (int j = 0; j < FM; ++j) tf[j] = *reinterpret_cast<const v8bf *>(tp[j] + kk * 512);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -102,14 +107,6 @@ __device__ __forceinline__ void lora_up(v4f (&y)[FN][FM], const LoraUp lo, int n
     }
 }
 
-// Large-tile kernel: BM x BN tile, WGM x WGN wavefronts, one workgroup per CU.
-// Operands are staged global -> LDS with buffer_load ... lds (no VGPR round
-// trip); the buffer range of each operand ends at the last valid row of the
-// tile, so rows past M or N read as zeros. Two LDS stages of 128 bytes per
-// row; the loads for stage s+1 are issued right after the barrier that opens
-// stage s and land while stage s is multiplied. Within a stage, the fragments
-// are read from LDS per 64-byte half; two wavefronts per SIMD hide the LDS
-// latency of one behind the MFMAs of the other.
 template <bool S4, int BM, int BN, int WGM, int WGN, int WPE, bool OUT_I32, bool LORA>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WPE, WPE))) void

@@ -120,7 +120,7 @@ __device__ __forceinline__ uint32_t pack4_bytes(const uint32_t *c) {
     return lo | hi;
 }
 
-// out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation, 3 bf16 rotation.
+// out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation, 3 bf16 rotation in MFMA fragment order.
 // WAVE_ROW: each wavefront owns one row (K <= 64 * 16 * NCH), so the row
 // absmax is a wavefront reduction with no LDS and no barrier, and a 256-thread
 // workgroup handles 4 rows; otherwise the workgroup owns one row.
@@ -171,20 +171,25 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
         }
         return;
     } else if constexpr (OUT == 3) {
-        // the rotation rounded once to bf16, nearest even
-        uint16_t *o = reinterpret_cast<uint16_t *>(out) + (int64_t)row * ldo;
+        // the rotation rounded once to bf16 (nearest even), stored in MFMA
+        // fragment order: 16-row x 32-column tiles of 512 values, tile
+        // (row / 16, col / 32) at ((row / 16) * (k / 32) + col / 32) * 512,
+        // element (i, c) of a tile at (16 ((c >> 2) & 3) + i) * 8 + 4 (c >> 4) + (c & 3).
+        // A 16-value chunk is half a tile row: four runs of 4 values, 8 bytes each.
+        uint16_t *o = reinterpret_cast<uint16_t *>(out) + ((row >> 4) * (int64_t)(k / 32)) * 512 + (row & 15) * 8;
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
             const int ch = tid + j * nthreads;
             if (ch < nchunks) {
-                uint32_t wds[8];
+                uint16_t *tile = o + (int64_t)(ch >> 1) * 512 + 4 * (ch & 1);
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    wds[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][2 * i]) |
-                             ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][2 * i + 1]) << 16);
-                uint4 *d = reinterpret_cast<uint4 *>(o + (int64_t)ch * kElems);
-                d[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
-                d[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t lo = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][4 * q]) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][4 * q + 1]) << 16);
+                    const uint32_t hi = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][4 * q + 2]) |
+                                        ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)v[j][4 * q + 3]) << 16);
+                    *reinterpret_cast<uint2 *>(tile + 16 * q * 8) = make_uint2(lo, hi);
+                }
             }
         }
         return;

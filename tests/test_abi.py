@@ -8,6 +8,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import int4_w4a4_quantized_amd as ck
@@ -129,6 +131,12 @@ def test_lora_validation(L):
     assert d(FAKE, 8, 320, 320, 64, FAKE, 32, 1.0, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 128
     assert d(FAKE, 8, 256, 256, 128, FAKE, 96, 1.0, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rank
     assert d(FAKE, 8, 1024, 1024, 512, FAKE, 32, 1.0, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rot_block
+    u = L.ck4_lora_prepare_up
+    assert u(NULL, 40, 32, 32, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert u(FAKE, 40, 32, 16, FAKE, NULL) == ck.CK4_ERR_INVALID  # ldb < rank
+    assert u(FAKE, 40, 32, 32, ODD, NULL) == ck.CK4_ERR_INVALID  # b_pack alignment
+    assert u(FAKE, 40, 48, 48, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # rank
+    assert p(FAKE, 32, 272, 272, 16, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 32
     f = L.ck4_linear_w4a4_lora
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE, 32, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, ODD, 32, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
@@ -143,3 +151,18 @@ def test_no_cpu_fallback_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ck, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         ck.lib()
+
+
+def test_fragment_order_helper_is_the_documented_permutation():
+    import frag_layout
+    for rows, cols in ((16, 32), (40, 64), (1, 256), (33, 3072)):
+        off = frag_layout.offsets(frag_layout.rows16(rows), cols)
+        assert np.array_equal(np.sort(off.reshape(-1)), np.arange(off.size))
+        z = np.random.default_rng(rows).integers(0, 65535, (rows, cols), dtype=np.uint16)
+        assert np.array_equal(frag_layout.unpack(frag_layout.pack(z), rows), z)
+    # a tile holds, at lane l = 16 g + i, slots 0-3 = columns 4 g .. 4 g + 3 and
+    # slots 4-7 = columns 16 + 4 g .. of row i
+    z = np.arange(16 * 32, dtype=np.uint16).reshape(16, 32)
+    t = frag_layout.pack(z).reshape(64, 8)
+    assert list(t[16 * 2 + 5]) == [5 * 32 + c for c in (8, 9, 10, 11, 24, 25, 26, 27)]
+

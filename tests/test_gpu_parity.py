@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import frag_layout
 import oracle
 import workloads
 
@@ -407,12 +408,17 @@ def test_skinny_layers(ck, m, n, k):
 
 # --------------------------------------------------------------------------
 # Dynamic LoRA: rotated down projection, up projection fused in the epilogue.
-# Bars: A R is bit-exact (same fp32 rotation, one RNE rounding); t is within
-# one bf16 rounding step (2^-7 relative) plus the fp32 accumulation bound
-# (K + 16) 2^-24 alpha sum |bf16(xR)| |A R| of the exact value; y is within
-# the suite's 1e-2 relative plus the fp32 epilogue's rounding of both summands
-# (the fp32 base value, 2^-21 of it, and the rank + 8 fp32 additions of the
-# LoRA sum).
+# Bars: A R is bit-exact (same fp32 rotation, one RNE rounding). t is within
+# one bf16 rounding step (2^-7 relative) of the oracle's, plus the fp32
+# accumulation bound (K + 16) 2^-24 alpha sum |bf16(xR)| |A R|, plus the
+# elements of x R that may round to a different bf16 on the two sides: the
+# kernel accumulates x H on the matrix cores, the oracle with butterflies,
+# both in fp32, so an element whose exact value lies within the fp32 error
+# bound (b + 2) 2^-24 sum_block |x| / sqrt(b) of a bf16 rounding boundary may
+# round either way; each such element adds its two roundings' distance times
+# |A R|. y is within the suite's 1e-2 relative plus the fp32 epilogue's
+# rounding of both summands (the fp32 base value, 2^-21 of it, and the
+# rank + 8 fp32 additions of the LoRA sum).
 
 
 def f64_of(bits):
@@ -424,12 +430,33 @@ def f64_of(bits):
 def test_lora_prepare_down_bitexact(ck, rank, k, rb):
     a, _ = workloads.make_lora(np.random.default_rng(900 + rank + k), rank, k, 1)
     got = bf16_host_bits(ck.lora_prepare_down(torch.from_numpy(a).cuda(), rb))
-    assert np.array_equal(got, oracle.lora_prepare_down(a, rb))
+    assert np.array_equal(frag_layout.unpack(got, rank), oracle.lora_prepare_down(a, rb))
+
+
+@pytest.mark.parametrize("n,rank", [(1, 32), (40, 64), (3072, 128), (1000, 256), (17, 32)])
+def test_lora_prepare_up_is_fragment_order(ck, n, rank):
+    rng = np.random.default_rng(905 + n)
+    wide = workloads.f32_to_bf16_bits(rng.standard_normal((n, rank + 8)).astype(np.float32))
+    got = bf16_host_bits(ck.lora_prepare_up(dev_bf16(wide)[:, :rank]))
+    assert np.array_equal(got, frag_layout.pack(np.ascontiguousarray(wide[:, :rank])))
+
+
+def _lora_down_dev(ck, xd, a_rot, alpha, rb, m):
+    """Runs the device down projection from the oracle's A R (packed on the host); returns t [m, rank]."""
+    t_pack = ck.lora_down(xd, dev_bf16(frag_layout.pack(a_rot)), alpha, rb)
+    return frag_layout.unpack(bf16_host_bits(t_pack), m)
 
 
 def _t_atol(xb, a_rot, alpha, rb):
-    xr = np.abs(f64_of(oracle.to_bf16(oracle.rotate_bf16(xb, rb))))
-    return abs(alpha) * (xb.shape[1] + 16) * 2.0 ** -24 * (xr @ np.abs(f64_of(a_rot)).T)
+    x = f64_of(xb)
+    m, k = x.shape
+    exact = oracle.rotate_f64(x, rb)
+    blk = np.abs(x).reshape(m, k // rb, rb).sum(axis=2, keepdims=True)
+    e = np.broadcast_to((rb + 2) * 2.0 ** -24 * blk / np.sqrt(rb) * 1.01, (m, k // rb, rb)).reshape(m, k)
+    step = np.abs(f64_of(oracle.to_bf16(exact + e)) - f64_of(oracle.to_bf16(exact - e)))
+    ar = np.abs(f64_of(a_rot)).T
+    xr = np.abs(f64_of(oracle.to_bf16(oracle.rotate_bf16(xb, rb)))) + step
+    return abs(alpha) * ((k + 16) * 2.0 ** -24 * (xr @ ar) + step @ ar)
 
 
 def _assert_t_close(got_bits, ref_bits, atol):
@@ -448,7 +475,7 @@ def test_lora_down(ck, m, k, rb, rank):
     a, _ = workloads.make_lora(rng, rank, k, 1)
     a_rot = oracle.lora_prepare_down(a, rb)
     alpha = 0.625
-    t = bf16_host_bits(ck.lora_down(dev_bf16(xb), dev_bf16(a_rot), alpha, rb))
+    t = _lora_down_dev(ck, dev_bf16(xb), a_rot, alpha, rb, m)
     assert not f64_of(t[m // 2]).any()
     _assert_t_close(t, oracle.lora_down(xb, a_rot, alpha, rb), _t_atol(xb, a_rot, alpha, rb))
 
@@ -459,7 +486,7 @@ def test_lora_down_row_stride(ck):
     wide = workloads.make_activations(rng, m, k + 256)
     a, _ = workloads.make_lora(rng, rank, k, 1)
     a_rot = oracle.lora_prepare_down(a)
-    t = bf16_host_bits(ck.lora_down(dev_bf16(wide)[:, :k], dev_bf16(a_rot), 1.0))
+    t = _lora_down_dev(ck, dev_bf16(wide)[:, :k], a_rot, 1.0, 128, m)
     xb = np.ascontiguousarray(wide[:, :k])
     _assert_t_close(t, oracle.lora_down(xb, a_rot, 1.0), _t_atol(xb, a_rot, 1.0, 128))
 
@@ -483,7 +510,7 @@ def test_linear_w4a4_lora_epilogue(ck, m, n, k, rank, with_bias):
     _, b = workloads.make_lora(rng, rank, k, n)
     bias = rng.standard_normal(n).astype(np.float32) if with_bias else None
     y = ck.linear_w4a4_lora(torch.from_numpy(xq).cuda(), torch.from_numpy(sx).cuda(), torch.from_numpy(wp).cuda(),
-                            torch.from_numpy(ws).cuda(), dev_bf16(t), dev_bf16(b),
+                            torch.from_numpy(ws).cuda(), dev_bf16(frag_layout.pack(t)), dev_bf16(frag_layout.pack(b)),
                             None if bias is None else torch.from_numpy(bias).cuda())
     acc = oracle.gemm_acc(xq, wp, k)
     y_ref = oracle.epilogue_lora(acc, sx, ws, t, b, bias)
@@ -498,8 +525,8 @@ def test_lora_with_zero_t_is_plain_linear_bitwise(ck, m, n, k):
     dq = [torch.from_numpy(v).cuda() for v in (xq, sx, wp, ws)]
     bd = torch.from_numpy(bias).cuda()
     y0 = bf16_host_bits(ck.linear_w4a4(*dq, bd))
-    t0 = torch.zeros((m, 64), dtype=torch.bfloat16, device="cuda")
-    y1 = bf16_host_bits(ck.linear_w4a4_lora(*dq, t0, dev_bf16(b), bd))
+    t0 = torch.zeros((frag_layout.rows16(m), 64), dtype=torch.bfloat16, device="cuda")
+    y1 = bf16_host_bits(ck.linear_w4a4_lora(*dq, t0, dev_bf16(frag_layout.pack(b)), bd))
     assert np.array_equal(y0, y1)
 
 
@@ -512,7 +539,7 @@ def test_w4a4_lora_layer_end_to_end(ck, m, n, k, rank, rb):
     wp, ws = oracle.quantize_weight_convrot(lay.weights[0], rb)
     a_rot = oracle.lora_prepare_down(a, rb)
     y = ck.w4a4_lora_linear(dev_bf16(lay.x_bf16), torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda(),
-                            dev_bf16(a_rot), dev_bf16(b), alpha, None, rb)
+                            dev_bf16(frag_layout.pack(a_rot)), ck.lora_prepare_up(dev_bf16(b)), alpha, None, rb)
     y_ref = oracle.linear_w4a4_lora(lay.x_bf16, wp, ws, a_rot, b, alpha, g=rb)
     xq, sx = oracle.rotate_quantize_act(lay.x_bf16, rb)
     acc = oracle.gemm_acc(xq, wp, k)
@@ -532,20 +559,21 @@ def test_full_size_square_layer_with_lora(ck):
     wp, ws = oracle.quantize_weight_convrot(lay.weights[0])
     a_rot = oracle.lora_prepare_down(a)
     a_rot_d = ck.lora_prepare_down(torch.from_numpy(a).cuda())
-    assert np.array_equal(bf16_host_bits(a_rot_d), a_rot)
+    assert np.array_equal(frag_layout.unpack(bf16_host_bits(a_rot_d), rank), a_rot)
     xd = dev_bf16(lay.x_bf16)
     xq, sx = ck.rotate_quantize_act(xd, 128, 4)
     t = ck.lora_down(xd, a_rot_d, alpha)
     y = bf16_host_bits(ck.linear_w4a4_lora(xq, sx, torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda(), t,
-                                           dev_bf16(b)))
+                                           ck.lora_prepare_up(dev_bf16(b))))
+    t_all = frag_layout.unpack(bf16_host_bits(t), m)
     rows = _sample_rows(m, 30, 2)
     xr = np.ascontiguousarray(lay.x_bf16[rows])
     t_ref = oracle.lora_down(xr, a_rot, alpha)
-    _assert_t_close(bf16_host_bits(t)[rows], t_ref, _t_atol(xr, a_rot, alpha, 128))
+    _assert_t_close(t_all[rows], t_ref, _t_atol(xr, a_rot, alpha, 128))
     xq_ref, sx_ref = oracle.rotate_quantize_act(xr)
     acc = oracle.gemm_acc(xq_ref, wp, k)
     # the up projection is checked on the device's own t
-    t_dev = bf16_host_bits(t)[rows]
+    t_dev = t_all[rows]
     y_ref = oracle.epilogue_lora(acc, sx_ref, ws, t_dev, b)
     assert_bf16_close(y[rows], y_ref, atol=_lora_atol(acc, sx_ref, ws, None, t_dev, b, rank))
 
