@@ -252,10 +252,44 @@ def layer_sweep(ck, torch, args) -> int:
         ck.rotate_quantize_act(x, 128, 8, out=xq8, scales=sx)
         ck.linear_w4a8_grouped(xq8, sx, wg, gs, 128, 0, out=y, workspace=wsp)
     line("w4a8-grouped layer square_3072 (decode + int8 GEMM)", m, n, k, graph_ms(w4a8_step, reps))
-    del w8, ws8, xq8, wg, gs, wsp
+    del w8, ws8, xq8, wg, gs, wsp, wd, lay, x, xq, sx, y
+    return lora_sweep(ck, torch, args)
 
-    # Dynamic LoRA on the square layer: the rotated down projection, then the
-    # GEMM with the up projection fused into its epilogue.
+
+def lora_sweep(ck, torch, args) -> int:
+    """Dynamic LoRA on the square layer (M = 4608, K = N = 3072): the rotated
+    down projection, the GEMM with the up projection fused into its epilogue,
+    and the whole layer with both, at ranks 32 and 128."""
+    dev = torch.device("cuda:0")
+    reps = max(args.steps // 4, 10)
+    cfg = workloads.WORKLOADS["square_3072"]
+    lay = workloads.make_layer(seed=0, **cfg)
+    m, k, n = lay.m, lay.k, lay.n
+    x = torch.from_numpy(lay.x_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
+    wd = torch.from_numpy(lay.weights[0]).to(dev)
+    xq = torch.empty((m, k // 2), dtype=torch.int8, device=dev)
+    sx = torch.empty((m,), dtype=torch.float32, device=dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+
+    def graph_ms(fn, n_steps):
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_steps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n_steps
+
+    def line(case, ms):
+        ops = 2.0 * m * n * k
+        print(json.dumps({"case": case, "m": m, "n": n, "k": k, "ms_per_step": round(ms, 5),
+                          "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+                          "pct_int8_peak": round(100 * ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)}), flush=True)
+
     wp, ws = ck.quantize_weight_convrot(wd, 128, 0)
 
     def base_gemm():
@@ -288,7 +322,7 @@ def layer_sweep(ck, torch, args) -> int:
         print(json.dumps({"case": f"w4a4 GEMM + fused lora up projection rank={rank}", "ms": round(g_ms, 5),
                           "base_gemm_ms": round(base_ms, 5), "epilogue_overhead_ms": round(g_ms - base_ms, 5)}),
               flush=True)
-        line(f"w4a4 layer square_3072 + dynamic lora rank={rank}", m, n, k, graph_ms(lora_step, reps))
+        line(f"w4a4 layer square_3072 + dynamic lora rank={rank}", graph_ms(lora_step, reps))
         del a_rot, bd, t
     return 0
 
@@ -303,6 +337,8 @@ def main() -> int:
                     help="run only a plain 512 MiB device-to-device copy (scales the HBM byte counters)")
     ap.add_argument("--skinny", action="store_true",
                     help="run the skinny-M sweep (M in 1, 8, 16, 64; N,K = 12288,3072 and 5120,5120) instead")
+    ap.add_argument("--lora", action="store_true",
+                    help="time the dynamic LoRA down projection, fused up projection and layer")
     ap.add_argument("--layers", action="store_true",
                     help="time the other layer configurations (up, down, q/k/v reuse, W8A8, grouped W4A8) instead")
     args = ap.parse_args()
@@ -326,6 +362,8 @@ def main() -> int:
 
     if args.skinny:
         return skinny_sweep(ck, torch, args)
+    if args.lora:
+        return lora_sweep(ck, torch, args)
     if args.layers:
         return layer_sweep(ck, torch, args)
 
