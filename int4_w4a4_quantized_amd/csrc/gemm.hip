@@ -170,10 +170,12 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
             if (q < NINSTR) {
                 const bool is_a = q < BM / 8;
                 const int qr = is_a ? q : q - BM / 8;
-                // per-lane part in the VGPR offset, per-instruction part in soffset
+                // the row (lane and instruction parts) in the VGPR offset, which the
+                // descriptor's range check covers, so rows past M or N read as zeros;
+                // the k offset within the row in soffset
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    is_a ? ra : rb, (__attribute__((address_space(3))) void *)(base + q * 1024), 16, lane_off,
-                    (uint32_t)(qr * 8) * (uint32_t)row_bytes + (uint32_t)(s * kRowBytes), 0, 0);
+                    is_a ? ra : rb, (__attribute__((address_space(3))) void *)(base + q * 1024), 16,
+                    lane_off + (uint32_t)(qr * 8) * (uint32_t)row_bytes, (uint32_t)(s * kRowBytes), 0, 0);
             }
         }
     };
@@ -426,20 +428,38 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
 }
 
 // Skinny kernel (M <= 64): bound by streaming the weight from HBM. A
-// workgroup owns 16*FNW weight rows; its KS wavefronts split K between them.
-// Each wavefront issues every load of its K range up front, straight from
-// global memory into VGPRs in the MFMA operand layout (lane l: row l & 15,
-// 16 bytes at offset 16 * (l >> 4) of each 64-byte half of a 128-byte k-slab,
-// so a step reads whole cache lines of 16 rows), widens them and
-// runs the same s4 x s4 MFMAs as the large kernels. The KS partial
-// accumulators are summed through LDS and one wavefront runs the epilogue.
-template <bool S4, int FM, int FNW, int KS, int MAXS, bool OUT_I32, bool LORA>
+// workgroup owns 16*FNW weight rows; its KS wavefronts split K between them,
+// up to MAXS k-steps (128 bytes of every row each) in flight per wavefront.
+// Two ways to bring a step in:
+//  * direct (LDS_STAGE false): every load of a chunk straight from global
+//    memory into VGPRs in the MFMA operand layout (lane l: row l & 15, 16
+//    bytes at 16 (l >> 4) of each 64-byte half), so compute starts as soon as
+//    the first step lands and no LDS limits residency;
+//  * staged (LDS_STAGE true, used when the activation has 64 rows and its
+//    fragments are four of every five loads): the 16*FNW weight rows and
+//    16*FM activation rows of each step are copied global -> LDS with
+//    buffer_load ... lds into the wavefront's own slots, 8 rows x 128 bytes
+//    per instruction, and the fragments are read from LDS. The copies are
+//    coalesced (each group of four lanes reads one 64-byte segment), whereas
+//    the direct loads put four rows in each group of four lanes, which costs
+//    the address unit about four times the cycles per load. As in the large
+//    kernel the 16-byte chunk index is XORed with (row & 7), so a fragment read
+//    hits 16 distinct banks.
+// Rows past M or N read as zeros (range-checked vector offsets). The KS
+// partial accumulators are summed through LDS and one wavefront runs the
+// epilogue.
+template <bool S4, int FM, int FNW, int KS, int MAXS, bool LDS_STAGE, bool OUT_I32, bool LORA>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
     const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int steps,
     void *__restrict__ Y, int64_t ldy, LoraUp lora) {
-    constexpr int SLAB = 128;  // bytes of each row per k-step: a whole cache line (256 k for s4, 128 k for s8)
-    __shared__ v4i red[KS - 1][FNW][FM][64];
+    constexpr int SLAB = 128;  // bytes of each row per k-step: 256 k for s4, 128 k for s8
+    constexpr int ROWS = 16 * (FNW + FM);  // staged rows per step: weights, then activations
+    constexpr int SLOT = ROWS * SLAB;
+    constexpr int NINS = ROWS / 8;  // copy instructions per step, 8 rows x 128 bytes each
+    constexpr int RING = LDS_STAGE ? KS * MAXS * SLOT : 0;
+    constexpr int RED = (KS - 1) * FNW * FM * 64 * 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[RING > RED ? RING : RED];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * 16 * FNW;
@@ -450,7 +470,12 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
         const_cast<int8_t *>(B) + (int64_t)n0 * row_bytes, (short)0, rows_b * row_bytes, 0x00020000);
     const int frow = lane & 15;
     const int fgrp = lane >> 4;
+    // direct loads: lane l reads row l & 15, 16 bytes at 16 (l >> 4) of each 64-byte half
     const uint32_t lane_off = (uint32_t)frow * (uint32_t)row_bytes + (uint32_t)(fgrp * 16);
+    // copy lane: row 8q + (l >> 3) of the step's rows, logical chunk (l & 7) ^ (row & 7)
+    const int crow = lane >> 3;
+    const uint32_t c_off = (uint32_t)(((lane & 7) ^ crow) * 16);
+    uint8_t *ring = lds + wave * MAXS * SLOT;
 
     const int per_wave = (steps + KS - 1) / KS;
     const int s_begin = wave * per_wave;
@@ -462,63 +487,120 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    // The wavefront's K range is processed in chunks of up to MAXS k-steps;
-    // every load of a chunk is issued before the first one is consumed.
-    for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
-        v4i wv[MAXS][FNW][SLAB / 64], xv[MAXS][FM][SLAB / 64];
-#pragma unroll
-        for (int t = 0; t < MAXS; ++t) {
-            const int s = s0 + t;
-            if (s < s_end) {
-#pragma unroll
+    if constexpr (LDS_STAGE) {
+        for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
+            // the previous chunk's fragment reads have completed before its slots are overwritten
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    #pragma unroll
+            for (int t = 0; t < MAXS; ++t) {
+                const int s = s0 + t;
+                if (s < s_end) {
+    #pragma unroll
+                    for (int q = 0; q < NINS; ++q) {
+                        const bool is_w = q < 2 * FNW;
+                        const int r = (is_w ? q : q - 2 * FNW) * 8 + crow;  // row within weights / activations
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                            is_w ? rb : ra, (__attribute__((address_space(3))) void *)(ring + t * SLOT + q * 1024), 16,
+                            (uint32_t)r * (uint32_t)row_bytes + (uint32_t)(s * SLAB) + c_off, 0, 0, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wavefront's copies have landed
+            asm volatile("" ::: "memory");        // and no LDS read moves above that wait
+    #pragma unroll
+            for (int t = 0; t < MAXS; ++t) {
+                if (s0 + t >= s_end) break;
+                const uint8_t *slot = ring + t * SLOT;
+    #pragma unroll
                 for (int h = 0; h < SLAB / 64; ++h) {
-#pragma unroll
+                    const int coff = ((4 * h + fgrp) ^ (frow & 7)) * 16;
+                    uint4 wv[FNW], xv[FM];
+    #pragma unroll
                     for (int i = 0; i < FNW; ++i)
-                        wv[t][i][h] = __builtin_amdgcn_raw_buffer_load_b128(
-                            rb, lane_off + (uint32_t)(i * 16) * (uint32_t)row_bytes, s * SLAB + h * 64, 0);
-#pragma unroll
+                        wv[i] = *reinterpret_cast<const uint4 *>(slot + (i * 16 + frow) * SLAB + coff);
+    #pragma unroll
                     for (int j = 0; j < FM; ++j)
-                        xv[t][j][h] = __builtin_amdgcn_raw_buffer_load_b128(
-                            ra, lane_off + (uint32_t)(j * 16) * (uint32_t)row_bytes, s * SLAB + h * 64, 0);
+                        xv[j] = *reinterpret_cast<const uint4 *>(slot + (16 * FNW + j * 16 + frow) * SLAB + coff);
+                    if constexpr (S4) {
+    #pragma unroll
+                        for (int i = 0; i < FNW; ++i) {
+                            const v4i wl = widen_lo(wv[i]), wh = widen_hi(wv[i]);
+    #pragma unroll
+                            for (int j = 0; j < FM; ++j) {
+                                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, widen_lo(xv[j]), acc[i][j], 0, 0, 0);
+                                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, widen_hi(xv[j]), acc[i][j], 0, 0, 0);
+                            }
+                        }
+                    } else {
+    #pragma unroll
+                        for (int i = 0; i < FNW; ++i)
+    #pragma unroll
+                            for (int j = 0; j < FM; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(as_v4i(wv[i]), as_v4i(xv[j]), acc[i][j],
+                                                                                  0, 0, 0);
+                    }
                 }
             }
         }
-#pragma unroll
-        for (int t = 0; t < MAXS; ++t) {
-            if (s0 + t >= s_end) break;
-#pragma unroll
-            for (int h = 0; h < SLAB / 64; ++h) {
-                if constexpr (S4) {
-#pragma unroll
-                    for (int i = 0; i < FNW; ++i) {
-                        const uint4 wp = make_uint4(wv[t][i][h].x, wv[t][i][h].y, wv[t][i][h].z, wv[t][i][h].w);
-                        const v4i wl = widen_lo(wp), wh = widen_hi(wp);
-#pragma unroll
-                        for (int j = 0; j < FM; ++j) {
-                            const uint4 xp =
-                                make_uint4(xv[t][j][h].x, xv[t][j][h].y, xv[t][j][h].z, xv[t][j][h].w);
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, widen_lo(xp), acc[i][j], 0, 0, 0);
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, widen_hi(xp), acc[i][j], 0, 0, 0);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < FNW; ++i)
-#pragma unroll
+    } else {
+        for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
+            v4i wv[MAXS][FNW][SLAB / 64], xv[MAXS][FM][SLAB / 64];
+    #pragma unroll
+            for (int t = 0; t < MAXS; ++t) {
+                const int s = s0 + t;
+                if (s < s_end) {
+    #pragma unroll
+                    for (int h = 0; h < SLAB / 64; ++h) {
+    #pragma unroll
+                        for (int i = 0; i < FNW; ++i)
+                            wv[t][i][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                                rb, lane_off + (uint32_t)(i * 16) * (uint32_t)row_bytes, s * SLAB + h * 64, 0);
+    #pragma unroll
                         for (int j = 0; j < FM; ++j)
-                            acc[i][j] =
-                                __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[t][i][h], xv[t][j][h], acc[i][j], 0, 0, 0);
+                            xv[t][j][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                                ra, lane_off + (uint32_t)(j * 16) * (uint32_t)row_bytes, s * SLAB + h * 64, 0);
+                    }
+                }
+            }
+    #pragma unroll
+            for (int t = 0; t < MAXS; ++t) {
+                if (s0 + t >= s_end) break;
+    #pragma unroll
+                for (int h = 0; h < SLAB / 64; ++h) {
+                    if constexpr (S4) {
+    #pragma unroll
+                        for (int i = 0; i < FNW; ++i) {
+                            const uint4 wp = make_uint4(wv[t][i][h].x, wv[t][i][h].y, wv[t][i][h].z, wv[t][i][h].w);
+                            const v4i wl = widen_lo(wp), wh = widen_hi(wp);
+    #pragma unroll
+                            for (int j = 0; j < FM; ++j) {
+                                const uint4 xp =
+                                    make_uint4(xv[t][j][h].x, xv[t][j][h].y, xv[t][j][h].z, xv[t][j][h].w);
+                                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, widen_lo(xp), acc[i][j], 0, 0, 0);
+                                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, widen_hi(xp), acc[i][j], 0, 0, 0);
+                            }
+                        }
+                    } else {
+    #pragma unroll
+                        for (int i = 0; i < FNW; ++i)
+    #pragma unroll
+                            for (int j = 0; j < FM; ++j)
+                                acc[i][j] =
+                                    __builtin_amdgcn_mfma_i32_16x16x64_i8(wv[t][i][h], xv[t][j][h], acc[i][j], 0, 0, 0);
+                    }
                 }
             }
         }
     }
 
+    v4i *red = reinterpret_cast<v4i *>(lds);  // [KS - 1][FNW][FM][64], over the copy slots
     if (KS > 1) {
+        __syncthreads();  // every wavefront is done with its copy slots
         if (wave > 0) {
 #pragma unroll
             for (int i = 0; i < FNW; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) red[wave - 1][i][j][lane] = acc[i][j];
+                for (int j = 0; j < FM; ++j) red[(((wave - 1) * FNW + i) * FM + j) * 64 + lane] = acc[i][j];
         }
         __syncthreads();
         if (wave > 0) return;
@@ -527,7 +609,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
 #pragma unroll
             for (int i = 0; i < FNW; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] += red[w][i][j][lane];
+                for (int j = 0; j < FM; ++j) acc[i][j] += red[((w * FNW + i) * FM + j) * 64 + lane];
     }
 
     // With LoRA, every fragment's fp32 values are formed first (clamped rows,
@@ -596,46 +678,64 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
     }
 }
 
-template <bool S4, int FM, int FNW, int KS, int MAXS>
+// MAXS: k-steps in flight per wavefront. Direct loads: 4, or 2 with a 64-row
+// activation (the VGPR budget of 2 waves per SIMD). Staged: 1 to 4, about
+// 20 KB of copy slots per wavefront, so that a CU's 160 KB of LDS holds eight
+// wavefronts, and at most 128 KB per workgroup.
+template <int FM, int FNW, int KS, bool LDS_STAGE>
+constexpr int skinny_maxs() {
+    if constexpr (!LDS_STAGE) {
+        return FM >= 4 ? 2 : 4;
+    } else {
+        constexpr int slot = 16 * (FNW + FM) * 128;
+        constexpr int m1 = (20 * 1024) / slot;
+        constexpr int m2 = (128 * 1024) / (KS * slot);
+        constexpr int m = m1 < m2 ? m1 : m2;
+        return m < 1 ? 1 : (m > 4 ? 4 : m);
+    }
+}
+
+template <bool S4, int FM, int FNW, int KS>
 hipError_t launch_skinny_cfg(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                              int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
                              hipStream_t stream, LoraUp lora) {
+    constexpr bool STG = FM >= 4;
+    constexpr int MAXS = skinny_maxs<FM, FNW, KS, STG>();
     const int64_t row_bytes = S4 ? k / 2 : k;
     const int steps = (int)(row_bytes / 128);
     dim3 grid((unsigned)((n + 16 * FNW - 1) / (16 * FNW))), block(64 * KS);
     if (out_i32)
-        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, true, false><<<grid, block, 0, stream>>>(
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, STG, true, false><<<grid, block, 0, stream>>>(
             a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
     else if (lora.rank > 0)
-        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, false, true><<<grid, block, 0, stream>>>(
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, STG, false, true><<<grid, block, 0, stream>>>(
             a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
     else
-        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, false, false><<<grid, block, 0, stream>>>(
+        gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, STG, false, false><<<grid, block, 0, stream>>>(
             a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
     return hipGetLastError();
 }
 
 // KS: enough wavefronts in flight to keep HBM busy (about 2K or more).
-template <bool S4, int FM, int FNW, int MAXS>
+template <bool S4, int FM, int FNW>
 hipError_t launch_skinny_ks(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                             int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
-                         LoraUp lora) {
+                            LoraUp lora) {
     const int64_t groups = (n + 16 * FNW - 1) / (16 * FNW);
     if (groups >= 1024)
-        return launch_skinny_cfg<S4, FM, FNW, 2, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+        return launch_skinny_cfg<S4, FM, FNW, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     if (groups >= 512)
-        return launch_skinny_cfg<S4, FM, FNW, 4, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
-    return launch_skinny_cfg<S4, FM, FNW, 8, MAXS>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+        return launch_skinny_cfg<S4, FM, FNW, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_skinny_cfg<S4, FM, FNW, 8>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 template <bool S4>
 hipError_t launch_skinny(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                          int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                          LoraUp lora) {
-    // MAXS keeps a chunk's loads within the register budget of 2 waves/SIMD
-    if (m <= 16) return launch_skinny_ks<S4, 1, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
-    if (m <= 32) return launch_skinny_ks<S4, 2, 1, 4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
-    return launch_skinny_ks<S4, 4, 1, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    if (m <= 16) return launch_skinny_ks<S4, 1, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    if (m <= 32) return launch_skinny_ks<S4, 2, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_skinny_ks<S4, 4, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 template <bool S4>
