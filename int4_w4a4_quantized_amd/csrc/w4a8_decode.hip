@@ -148,6 +148,46 @@ __device__ __forceinline__ uint2 decode8(uint32_t w, float mult, float m8) {
     return make_uint2(d0, d1);
 }
 
+// Table decode for a lane whose 64 codes share one multiplier. The int8 code
+// of nibble u (two's complement q = u or u - 16) is the same function of q for
+// all of them, so the 16 codes are formed once with the same fp32 steps as
+// code8 (RN(q * mult), clamp, round) and looked up per code with v_perm. By
+// symmetry (RN, the clamp and ties-to-even rounding are odd functions) only
+// q = 0..8 are evaluated; code(-q) is the negation, formed on the magic-add
+// bit pattern as 2 * 0x4B400000 - bits. Table words: T0 = codes of q = 0..7
+// (bytes 0..7 of {t.y, t.x}), T1 = codes of q = -8..-1 (bytes of {t.w, t.z}).
+__device__ __forceinline__ uint4 code_table(float mult) {
+    uint32_t r[9];
+#pragma unroll
+    for (int q = 0; q <= 8; ++q)
+        r[q] = __float_as_uint(fminf(fmaxf((float)q * mult, -127.0f), 127.0f) + 12582912.0f);
+    uint32_t n[9];
+#pragma unroll
+    for (int q = 1; q <= 8; ++q) n[q] = 2u * 0x4B400000u - r[q];
+    auto pack4 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+        return __builtin_amdgcn_perm(b, a, 0x0C0C0400u) | __builtin_amdgcn_perm(d, c, 0x04000C0Cu);
+    };
+    return make_uint4(pack4(r[0], r[1], r[2], r[3]), pack4(r[4], r[5], r[6], r[7]), pack4(n[8], n[7], n[6], n[5]),
+                      pack4(n[4], n[3], n[2], n[1]));
+}
+
+// Four nibble bytes (0..15 each) -> their four codes: one v_perm per half of
+// the table, and a byte mask from bit 3 (selector 0x0C gives 0x00, 0x0D 0xFF).
+__device__ __forceinline__ uint32_t lookup4(uint32_t nib, uint4 tab) {
+    const uint32_t sel = nib & 0x07070707u;
+    const uint32_t a = __builtin_amdgcn_perm(tab.y, tab.x, sel);
+    const uint32_t b = __builtin_amdgcn_perm(tab.w, tab.z, sel);
+    const uint32_t mask = __builtin_amdgcn_perm(0u, 0u, ((nib >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+    return (b & mask) | (a & ~mask);
+}
+
+// One packed word (8 codes) -> two words of int8 codes in natural order, as decode8.
+__device__ __forceinline__ uint2 decode8_table(uint32_t w, uint4 tab) {
+    const uint32_t lo = lookup4(w & 0x0F0F0F0Fu, tab);         // elements 0, 2, 4, 6
+    const uint32_t hi = lookup4((w >> 4) & 0x0F0F0F0Fu, tab);  // elements 1, 3, 5, 7
+    return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+}
+
 // Operand layout: a k-step is 256 k. Lane l (row l & 15, part p = l >> 4)
 // owns the 64 contiguous k [256 s + 64 p, 256 s + 64 p + 64) of its weight row
 // and of its activation row; the MFMA of slice h (0..3) takes 16 of them,
@@ -238,25 +278,32 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
             if (s0 + t >= s_end) break;
 #pragma unroll
             for (int i = 0; i < FNW; ++i) {
-                float mult[4], m8[4];
-                if (one_group) {
-                    const float mu = srow[i] == 0.0f ? 0.0f : gv[t][i][0] / srow[i];
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        mult[h] = mu;
-                        m8[h] = -8.0f * mu;
-                    }
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        mult[h] = srow[i] == 0.0f ? 0.0f : gv[t][i][h] / srow[i];
-                        m8[h] = -8.0f * mult[h];
-                    }
-                }
                 const uint32_t words[8] = {(uint32_t)wv[t][i][0][0], (uint32_t)wv[t][i][0][1],
                                            (uint32_t)wv[t][i][0][2], (uint32_t)wv[t][i][0][3],
                                            (uint32_t)wv[t][i][1][0], (uint32_t)wv[t][i][1][1],
                                            (uint32_t)wv[t][i][1][2], (uint32_t)wv[t][i][1][3]};
+                if (one_group) {
+                    // one multiplier for the lane's 64 codes: table decode
+                    const float mu = srow[i] == 0.0f ? 0.0f : gv[t][i][0] / srow[i];
+                    const uint4 tab = code_table(mu);
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const uint2 a = decode8_table(words[2 * h], tab);
+                        const uint2 b = decode8_table(words[2 * h + 1], tab);
+                        const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
+#pragma unroll
+                        for (int j = 0; j < FM; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
+                    }
+                    continue;
+                }
+                // groups narrower than 64: a multiplier per 16 codes, per-code decode
+                float mult[4], m8[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    mult[h] = srow[i] == 0.0f ? 0.0f : gv[t][i][h] / srow[i];
+                    m8[h] = -8.0f * mult[h];
+                }
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
                     const uint2 a = decode8(words[2 * h], mult[h], m8[h]);

@@ -577,3 +577,60 @@ def test_full_size_square_layer_with_lora(ck):
     y_ref = oracle.epilogue_lora(acc, sx_ref, ws, t_dev, b)
     assert_bf16_close(y[rows], y_ref, atol=_lora_atol(acc, sx_ref, ws, None, t_dev, b, rank))
 
+
+
+# --------------------------------------------------------------------------
+# Graph capture: every path launches only kernels (no memset or allocation
+# nodes), so a captured graph replays to the eager result, bit for bit, on
+# every replay, with unrelated eager work and synchronisations in between.
+
+
+def test_graph_replays_match_eager(ck):
+    m, n, k, rank = 200, 520, 1024, 64
+    lay = workloads.make_layer(m, k, n, seed=970)
+    a, b = workloads.make_lora(np.random.default_rng(971), rank, k, n)
+    xd = dev_bf16(lay.x_bf16)
+    wd = torch.from_numpy(lay.weights[0]).cuda()
+    wp, ws = ck.quantize_weight_convrot(wd, 128, 0)
+    wg, gs = ck.quantize_weight_convrot(wd, 128, 128)
+    a_pack = ck.lora_prepare_down(torch.from_numpy(a).cuda())
+    b_pack = ck.lora_prepare_up(dev_bf16(b))
+    xs = xd[:8]  # a skinny batch for the fused W4A8 kernel
+    xq = torch.empty((m, k // 2), dtype=torch.int8, device="cuda")
+    sx = torch.empty((m,), dtype=torch.float32, device="cuda")
+    xq8 = torch.empty((8, k), dtype=torch.int8, device="cuda")
+    sx8 = torch.empty((8,), dtype=torch.float32, device="cuda")
+    t = torch.empty((frag_layout.rows16(m), rank), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    yl = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    y8 = torch.empty((8, n), dtype=torch.bfloat16, device="cuda")
+    y8c = torch.empty((8, 528), dtype=torch.bfloat16, device="cuda")[:, :n]  # the chunked path needs ldy % 16 == 0
+    wsp = torch.empty((ck.w4a8_workspace_bytes(8, n, k, 256),), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ck.rotate_quantize_act(xd, 128, 4, out=xq, scales=sx)
+        ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+        ck.lora_down(xd, a_pack, 0.5, 128, out=t)
+        ck.linear_w4a4_lora(xq, sx, wp, ws, t, b_pack, None, out=yl)
+        ck.rotate_quantize_act(xs, 128, 8, out=xq8, scales=sx8)
+        ck.linear_w4a8_grouped(xq8, sx8, wg, gs, 128, 0, out=y8)
+        ck.linear_w4a8_grouped(xq8, sx8, wg, gs, 128, 256, out=y8c, workspace=wsp)
+
+    outs = (xq, sx, t, y, yl, y8, y8c)
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.zero_()
+        junk = torch.randn(4096, device="cuda").sum()  # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8)), f"replay {rep} differs"
+        del junk
