@@ -18,6 +18,8 @@ workload's rows.
 from __future__ import annotations
 
 import argparse
+import ctypes
+import statistics
 import hashlib
 import json
 import os
@@ -83,8 +85,34 @@ def cpu_baseline(m: int, k: int, n: int, rows: int, reps: int = 3) -> dict:
     }
 
 
-def _graph_time_us(torch, launches, reps, warm):
-    """Capture `launches` (a list of callables) in one graph; microseconds per launch."""
+def _max_sclk_mhz():
+    """The device's peak engine clock in MHz as the HIP runtime reports it
+    (hipDeviceGetAttribute with hipDeviceAttributeClockRate, which is 5 in
+    hip_runtime_api.h's enum and is given in kHz); None if the query fails."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0) != 0 or khz.value <= 0:
+            return None
+        return khz.value // 1000
+    except OSError:
+        return None
+
+
+def _device_peaks(torch, mhz) -> dict:
+    """The int8 peak from the device: CUs x 8192 int8 ops per clock per CU
+    (v_mfma_i32_16x16x64_i8: 32768 ops per 16 cycles on each of 4 SIMDs) x
+    the maximum engine clock."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return {"cus": cus, "max_sclk_mhz": mhz,
+            "int8_dense_tops": None if mhz is None else round(cus * 8192 * mhz * 1e6 / 1e12, 1),
+            "used_peak_tops": INT8_PEAK_TOPS}
+
+
+def _graph_time_us(torch, launches, reps, warm, batches=5):
+    """Capture `launches` (a list of callables) in one graph; microseconds per
+    launch as (min, median) over `batches` batches of `reps` replays, each batch
+    bracketed by HIP events (the pages time min of 5 x 100 iterations)."""
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -93,13 +121,27 @@ def _graph_time_us(torch, launches, reps, warm):
     for _ in range(warm):
         g.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / (reps * len(launches))
+    times = []
+    for _ in range(batches):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / (reps * len(launches)))
+    return min(times), statistics.median(times)
+
+
+def _skinny_line(case, us, hot_us, byts):
+    """One skinny case: HBM figure (32 weight copies, min and median of 5
+    batches) and the labelled hot-cache figure (one copy, cached)."""
+    mn, md = us
+    return json.dumps({"case": case, "us_per_launch_graph": round(md, 3), "us_min": round(mn, 3),
+                       "algorithmic_bytes": byts, "GBps": round(byts / md / 1e3, 1),
+                       "hbm_frac": round(byts / md / 1e3 / HBM_PEAK_GBS, 4),
+                       "GBps_min_time": round(byts / mn / 1e3, 1),
+                       "hot_cache_us": round(hot_us[1], 3), "hot_cache_GBps": round(byts / hot_us[1] / 1e3, 1)})
 
 
 def _clock_warmup(torch, fn, seconds: float = 0.25) -> None:
@@ -125,6 +167,7 @@ def skinny_sweep(ck, torch, args) -> int:
     copies = 32
     reps = max(args.steps // 20, 2)
     warm = max(args.warmup // 10, 1)
+    nb = max(args.batches, 1)
     for n, k in workloads.SKINNY_NK:
         rng = np.random.default_rng(1)
         w4, w8g, w8e = [], [], []
@@ -140,29 +183,24 @@ def skinny_sweep(ck, torch, args) -> int:
             xq8, sx8 = ck.rotate_quantize_act(x, 128, 8)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             _clock_warmup(torch, lambda: ck.linear_w4a4(xq, sx, w4[0][0], w4[0][1], None, out=y), 0.1)
-            us = _graph_time_us(torch, [lambda c=c: ck.linear_w4a4(xq, sx, w4[c][0], w4[c][1], None, out=y)
-                                        for c in range(copies)], reps, warm)
+            def w4a4(c):
+                return lambda: ck.linear_w4a4(xq, sx, w4[c][0], w4[c][1], None, out=y)
+            cold = [w4a4(c) for c in range(copies)]
+            hot = [w4a4(0) for _ in range(copies)]
             byts = n * k // 2 + 4 * n + m * k // 2 + 4 * m + 2 * m * n
-            print(json.dumps({"case": f"w4a4 skinny m={m} n={n} k={k}", "us_per_launch_graph": round(us, 3),
-                              "algorithmic_bytes": byts, "GBps": round(byts / us / 1e3, 1),
-                              "hbm_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
+            print(_skinny_line(f"w4a4 skinny m={m} n={n} k={k}", _graph_time_us(torch, cold, reps, warm, nb),
+                               _graph_time_us(torch, hot, reps, warm, nb), byts), flush=True)
             ws_bytes = ck.w4a8_workspace_bytes(m, n, k, 0)
             ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
-            us8 = _graph_time_us(torch, [lambda c=c: ck.linear_w4a8_grouped(xq8, sx8, w8g[c][0], w8g[c][1], 128, 0,
-                                                                            out=y, workspace=ws)
-                                         for c in range(copies)], reps, warm)
-            byts8 = n * k // 2 + 4 * n * (k // 128) + m * k + 4 * m + 2 * m * n
-            print(json.dumps({"case": f"w4a8-grouped skinny m={m} n={n} k={k}", "us_per_launch_graph": round(us8, 3),
-                              "algorithmic_bytes": byts8, "GBps": round(byts8 / us8 / 1e3, 1),
-                              "hbm_frac": round(byts8 / us8 / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
-            use = _graph_time_us(torch, [lambda c=c: ck.linear_w4a8_grouped(xq8, sx8, w8e[c][0], w8e[c][1], 128, 0,
-                                                                            out=y, workspace=ws)
-                                         for c in range(copies)], reps, warm)
-            byte8 = n * k // 2 + n * (k // 128) + m * k + 4 * m + 2 * m * n
-            print(json.dumps({"case": f"w4a8-grouped-e4m3-scales skinny m={m} n={n} k={k}",
-                              "us_per_launch_graph": round(use, 3), "algorithmic_bytes": byte8,
-                              "GBps": round(byte8 / use / 1e3, 1),
-                              "hbm_frac": round(byte8 / use / 1e3 / HBM_PEAK_GBS, 4)}), flush=True)
+            for label, wl, byt in (
+                    ("w4a8-grouped", w8g, n * k // 2 + 4 * n * (k // 128) + m * k + 4 * m + 2 * m * n),
+                    ("w4a8-grouped-e4m3-scales", w8e, n * k // 2 + n * (k // 128) + m * k + 4 * m + 2 * m * n)):
+                def w4a8(c, wl=wl):
+                    return lambda: ck.linear_w4a8_grouped(xq8, sx8, wl[c][0], wl[c][1], 128, 0, out=y, workspace=ws)
+                print(_skinny_line(f"{label} skinny m={m} n={n} k={k}",
+                                   _graph_time_us(torch, [w4a8(c) for c in range(copies)], reps, warm, nb),
+                                   _graph_time_us(torch, [w4a8(0) for _ in range(copies)], reps, warm, nb), byt),
+                      flush=True)
     return 0
 
 
@@ -357,6 +395,8 @@ def main() -> int:
                     help="run only a plain 512 MiB device-to-device copy (scales the HBM byte counters)")
     ap.add_argument("--skinny", action="store_true",
                     help="run the skinny-M sweep (M in 1, 8, 16, 64; N,K = 12288,3072 and 5120,5120) instead")
+    ap.add_argument("--batches", type=int, default=5,
+                    help="timed batches per skinny case (min and median are reported)")
     ap.add_argument("--lora", action="store_true",
                     help="time the dynamic LoRA down projection, fused up projection and layer")
     ap.add_argument("--layers", action="store_true",
@@ -387,6 +427,7 @@ def main() -> int:
     if args.layers:
         return layer_sweep(ck, torch, args)
 
+    sclk_mhz = _max_sclk_mhz()
     cfg = workloads.WORKLOADS["square_3072"]
     m, k, n = cfg["m"], cfg["k"], cfg["n"]
     lay = workloads.make_layer(m, k, n, seed=0)
@@ -453,6 +494,18 @@ def main() -> int:
 
     gemm_ms = per_launch_ms(g_gemm_only)
     quant_ms = per_launch_ms(g_quant_only)
+
+    # Spread: min and median over 5 graphs of 100 layer steps (the pages time
+    # min of 5 x 100 iterations); reported beside the contract's single timing.
+    g_100 = capture(100)
+    spread = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g_100.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        spread.append(e0.elapsed_time(e1) / 100)
     ms_per_step = wall * 1e3 / args.steps
     ops = 2.0 * m * n * k
     tops = ops / (ms_per_step * 1e-3) / 1e12
@@ -495,6 +548,9 @@ def main() -> int:
             "gemm_ms": round(gemm_ms, 5),
             "gemm_TOPS": round(gemm_tops, 2),
         },
+        "spread": {"batches": 5, "steps_per_batch": 100, "ms_per_step_min": round(min(spread), 5),
+                   "ms_per_step_median": round(statistics.median(spread), 5)},
+        "peaks": _device_peaks(torch, sclk_mhz),
         "context": {"L4_ms_per_layer_same_shape": 0.54, "note": "another machine's number; context only"},
     }
     if args.cpu_rows > 0:
