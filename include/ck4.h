@@ -75,7 +75,8 @@ const char *ck4_last_error(void);
  *   group    0: one scale per output row (W4A4 layout), w_scales is fp32 [n].
  *            g > 0: one scale per contiguous group of g elements along K
  *            (grouped W4A8 layout), w_scales is fp32 [n, k/g]; g must be a
- *            power of two in [16, 1024] dividing k.
+ *            power of two in [4, 1024] dividing k ([PR #97] Testing: group sizes
+ *            4 to 64 are decoded bit-exactly).
  *   w_packed int8 [n, k/2] (row stride k/2): codes in [-7, 7], element 2j of a
  *            row in the low nibble of byte j, element 2j+1 in the high nibble.
  * Each row is rotated in fp32 (butterfly strides ascending, then one multiply
@@ -190,7 +191,7 @@ ck4_status ck4_gemm_w4a4_acc_i32(const int8_t *x_q, const int8_t *w_packed, int6
  * s_row = (max_j s[row, j] * 7) / 127, w8 = clamp(rint(q * (s[row, j] / s_row)), -127, 127),
  * all fp32; an all-zero row gives s_row = 0 and w8 = 0.
  * Alignment: w_packed and w8 16-byte aligned. Unsupported: g not a power of two in
- * [16, 1024].
+ * [4, 1024].
  */
 ck4_status ck4_dequant_w4a8_grouped(const int8_t *w_packed, const float *group_scales, int64_t n, int64_t k,
                                     int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales,
@@ -228,7 +229,7 @@ ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8
  *   workspace       device memory of at least ck4_w4a8_workspace_bytes(...)
  *                   bytes (16-byte aligned; may be NULL when that is 0); its
  *                   contents are scratch.
- * Unsupported: k % 128 != 0, g not a power of two in [16, 1024].
+ * Unsupported: k % 128 != 0, g not a power of two in [4, 1024].
  */
 size_t ck4_w4a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t chunk_cols);
 ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
@@ -261,6 +262,47 @@ ck4_status ck4_linear_w4a8_grouped_e4m3(const int8_t *x_q8, const float *x_scale
                                         const uint8_t *group_scales, int64_t m, int64_t n, int64_t k, int group,
                                         uint16_t *y, int64_t ldy, int64_t chunk_cols, void *workspace,
                                         size_t ws_bytes, void *stream);
+
+/*
+ * Grouped W4A8 with a frozen 16-entry codebook ([PR #97] What this adds: an
+ * optional codebook staged for the decode; On #96: a frozen codebook lookup
+ * table, and a decode that is bit exact with a pinned codebook). The pages
+ * give neither the codebook's values nor how codes map through it; these
+ * calls take the plain reading: the 4-bit code u (0..15, as stored, low
+ * nibble first) stands for codebook[u] times the group scale.
+ *
+ *   codebook     HOST pointer to 16 fp32 entries, read during the call and
+ *                copied into the kernel arguments; every entry finite and
+ *                cmax = max |codebook[u]| in [2^-64, 2^64], else
+ *                CK4_ERR_INVALID. The same 16 values must be passed to the
+ *                decode and the linear as to the preparation.
+ *   scale_e4m3   0: group_scales fp32 [n, k/g]; 1: E4M3 bytes [n, k/g] (as
+ *                ck4_quantize_weight_convrot_e4m3).
+ *
+ * ck4_quantize_weight_convrot_codebook: rotation as ck4_quantize_weight_convrot;
+ *   per group s = absmax / cmax (fp32 divide; with scale_e4m3 rounded to
+ *   E4M3 and the decoded byte used), t = r / s (fp32 divide; t = 0 when
+ *   s == 0), and u = the index minimising the fp32 value |t - codebook[u]|,
+ *   the lowest such index on ties.
+ * ck4_dequant_w4a8_codebook: s_row = (max_j s[row, j] * cmax) / 127,
+ *   w8 = clamp(rint(codebook[u] * (s[row, j] / s_row)), -127, 127), all fp32;
+ *   an all-zero row decodes to zeros. Rows, chunks and layouts as
+ *   ck4_dequant_w4a8_grouped.
+ * ck4_linear_w4a8_codebook: as ck4_linear_w4a8_grouped on that decode (same
+ *   three execution paths, bit-identical).
+ * Group g: a power of two in [4, 1024] dividing k. Other arguments, alignment
+ * and errors as the fp32-scale calls.
+ */
+ck4_status ck4_quantize_weight_convrot_codebook(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                                int group, const float *codebook, int scale_e4m3, int8_t *w_packed,
+                                                void *group_scales, void *stream);
+ck4_status ck4_dequant_w4a8_codebook(const int8_t *w_packed, const void *group_scales, int scale_e4m3,
+                                     const float *codebook, int64_t n, int64_t k, int group, int64_t n0, int64_t nc,
+                                     int8_t *w8, float *row_scales, void *stream);
+ck4_status ck4_linear_w4a8_codebook(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                    const void *group_scales, int scale_e4m3, const float *codebook, int64_t m,
+                                    int64_t n, int64_t k, int group, uint16_t *y, int64_t ldy, int64_t chunk_cols,
+                                    void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Dynamic LoRA side path ([HIPT] LoRA modes: the Dynamic mode keeps the LoRA

@@ -36,6 +36,7 @@ _lib = None
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I = ctypes.c_int
+_PF = ctypes.POINTER(ctypes.c_float)  # host float array
 
 SIGNATURES = {
     "ck4_version": ([], ctypes.c_char_p),
@@ -56,6 +57,10 @@ SIGNATURES = {
     "ck4_dequant_w4a8_grouped_e4m3": ([_P, _P, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
     "ck4_linear_w4a8_grouped_e4m3": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t,
                                       _P], _I),
+    "ck4_quantize_weight_convrot_codebook": ([_P, _I64, _I64, _I64, _I, _I, _PF, _I, _P, _P, _P], _I),
+    "ck4_dequant_w4a8_codebook": ([_P, _P, _I, _PF, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
+    "ck4_linear_w4a8_codebook": ([_P, _P, _P, _P, _I, _PF, _I64, _I64, _I64, _I, _P, _I64, _I64, _P,
+                                  ctypes.c_size_t, _P], _I),
     "ck4_lora_prepare_down": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_lora_prepare_up": ([_P, _I64, _I64, _I64, _P, _P], _I),
     "ck4_lora_down": ([_P, _I64, _I64, _I64, _I, _P, _I64, ctypes.c_float, _P, _P], _I),
@@ -151,6 +156,33 @@ def quantize_weight_convrot_e4m3(w: torch.Tensor, rot_block: int = 128, group: i
     return wp, gs
 
 
+def _codebook(codebook):
+    """16 codebook entries (list, numpy array or CPU tensor) -> a host float[16]."""
+    if isinstance(codebook, torch.Tensor):
+        if codebook.device.type != "cpu":
+            raise ValueError("the codebook is a host array of 16 floats")
+        codebook = codebook.tolist()
+    vals = [float(v) for v in (codebook.tolist() if hasattr(codebook, "tolist") else codebook)]
+    if len(vals) != 16:
+        raise ValueError(f"the codebook has 16 entries, got {len(vals)}")
+    return (ctypes.c_float * 16)(*vals)
+
+
+def quantize_weight_convrot_codebook(w: torch.Tensor, codebook, rot_block: int = 128, group: int = 128,
+                                     scale_e4m3: bool = False):
+    """Grouped weight prep against a frozen 16-entry codebook -> (int8 [n, k/2]
+    packed indices, group scales fp32 [n, k/group] or uint8 E4M3 bytes)."""
+    _need(w, torch.float32, "w", 2)
+    n, k = w.shape
+    wp = torch.empty((n, k // 2), dtype=torch.int8, device=w.device)
+    gs = torch.empty((n, k // group), dtype=torch.uint8 if scale_e4m3 else torch.float32, device=w.device)
+    _check("ck4_quantize_weight_convrot_codebook",
+           lib().ck4_quantize_weight_convrot_codebook(_ptr(w), n, k, w.stride(0), rot_block, group,
+                                                      _codebook(codebook), int(bool(scale_e4m3)), _ptr(wp), _ptr(gs),
+                                                      _stream(w.device)))
+    return wp, gs
+
+
 def quantize_weight_convrot_int8(w: torch.Tensor, rot_block: int = 128):
     """Offline W8A8 weight prep: fp32 [n, k] -> (int8 codes [n, k], fp32 row scales [n])."""
     _need(w, torch.float32, "w", 2)
@@ -219,17 +251,24 @@ def w4a4_linear(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
 
 
 def dequant_w4a8_grouped(w_packed: torch.Tensor, group_scales: torch.Tensor, group: int = 128, n0: int = 0,
-                         nc: int | None = None):
+                         nc: int | None = None, codebook=None):
     """Grouped int4 -> int8 decode of weight rows [n0, n0+nc) -> (int8 [nc, k], fp32 [nc]).
 
-    group_scales: fp32, or uint8 holding E4M3 bytes.
+    group_scales: fp32, or uint8 holding E4M3 bytes. codebook: the 16 host
+    entries the weight was prepared with, or None for plain int4 codes.
     """
     n, k = w_packed.shape[0], w_packed.shape[1] * 2
     if nc is None:
         nc = n - n0
     w8 = torch.empty((nc, k), dtype=torch.int8, device=w_packed.device)
     sr = torch.empty((nc,), dtype=torch.float32, device=w_packed.device)
-    name = "ck4_dequant_w4a8_grouped_e4m3" if group_scales.dtype == torch.uint8 else "ck4_dequant_w4a8_grouped"
+    e4m3 = group_scales.dtype == torch.uint8
+    if codebook is not None:
+        _check("ck4_dequant_w4a8_codebook",
+               lib().ck4_dequant_w4a8_codebook(_ptr(w_packed), _ptr(group_scales), int(e4m3), _codebook(codebook), n,
+                                               k, group, n0, nc, _ptr(w8), _ptr(sr), _stream(w_packed.device)))
+        return w8, sr
+    name = "ck4_dequant_w4a8_grouped_e4m3" if e4m3 else "ck4_dequant_w4a8_grouped"
     _check(name, getattr(lib(), name)(_ptr(w_packed), _ptr(group_scales), n, k, group, n0, nc, _ptr(w8), _ptr(sr),
                                       _stream(w_packed.device)))
     return w8, sr
@@ -258,12 +297,13 @@ def w4a8_workspace_bytes(m: int, n: int, k: int, chunk_cols: int = 0) -> int:
 
 
 def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128, chunk_cols: int = 0,
-                        out=None, workspace=None):
+                        out=None, workspace=None, codebook=None):
     """Grouped W4A8 linear -> bf16 [m, n].
 
     chunk_cols > 0: decode per column chunk + int8 GEMM; < 0: one decode pass
     + one GEMM; 0: the library's policy (the fused kernel for m <= 64).
-    group_scales: fp32, or uint8 holding E4M3 bytes.
+    group_scales: fp32, or uint8 holding E4M3 bytes. codebook: the 16 host
+    entries the weight was prepared with, or None.
     """
     m, k = x_q8.shape
     n = w_packed.shape[0]
@@ -272,7 +312,15 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
     need = w4a8_workspace_bytes(m, n, k, chunk_cols)
     if workspace is None and need > 0:
         workspace = torch.empty((need,), dtype=torch.uint8, device=x_q8.device)
-    name = "ck4_linear_w4a8_grouped_e4m3" if group_scales.dtype == torch.uint8 else "ck4_linear_w4a8_grouped"
+    e4m3 = group_scales.dtype == torch.uint8
+    if codebook is not None:
+        _check("ck4_linear_w4a8_codebook",
+               lib().ck4_linear_w4a8_codebook(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales),
+                                              int(e4m3), _codebook(codebook), m, n, k, group, _ptr(out),
+                                              out.stride(0), chunk_cols, _ptr(workspace),
+                                              0 if workspace is None else workspace.numel(), _stream(x_q8.device)))
+        return out
+    name = "ck4_linear_w4a8_grouped_e4m3" if e4m3 else "ck4_linear_w4a8_grouped"
     _check(name, getattr(lib(), name)(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales), m, n, k,
                                       group, _ptr(out), out.stride(0), chunk_cols, _ptr(workspace),
                                       0 if workspace is None else workspace.numel(), _stream(x_q8.device)))

@@ -3,6 +3,7 @@
 // rejected call launches nothing.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -36,6 +37,22 @@ ck4_status ok() {
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// A host codebook of 16 fp32 entries -> the kernels' by-value copy.
+ck4_status make_codebook(const char *fn, const float *codebook, ck4::Codebook *cb) {
+    if (!codebook) return fail(CK4_ERR_INVALID, "%s: null codebook", fn);
+    float cmax = 0.0f;
+    for (int u = 0; u < 16; ++u) {
+        if (!std::isfinite(codebook[u])) return fail(CK4_ERR_INVALID, "%s: codebook[%d] is not finite", fn, u);
+        cb->v[u] = codebook[u];
+        cmax = std::fabs(codebook[u]) > cmax ? std::fabs(codebook[u]) : cmax;
+    }
+    if (!(cmax >= 0x1p-64f && cmax <= 0x1p64f))
+        return fail(CK4_ERR_INVALID, "%s: max |codebook| = %g is outside [2^-64, 2^64]", fn, (double)cmax);
+    cb->cmax = cmax;
+    cb->on = true;
+    return CK4_OK;
+}
 
 constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once[kMaxDevices];
@@ -72,7 +89,7 @@ constexpr int64_t kMaxRows = 0x7FFFFFFF;
 
 ck4_status check_rot(const char *fn, int64_t k, int rot_block) {
     if (!pow2(rot_block) || rot_block < 16 || rot_block > 1024)
-        return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d (need a power of two in [16, 1024])", fn, rot_block);
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d (need a power of two in [4, 1024])", fn, rot_block);
     if (k % rot_block != 0)
         return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of rot_block=%d", fn, (long long)k,
                     rot_block);
@@ -119,8 +136,8 @@ ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int
     if (!aligned(w_packed, 8) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
-    if (group != 0 && (!pow2(group) || group < 16 || group > 1024 || k % group != 0))
-        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need 0 or a power of two in [16, 1024] dividing k)", fn,
+    if (group != 0 && (!pow2(group) || group < 4 || group > 1024 || k % group != 0))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need 0 or a power of two in [4, 1024] dividing k)", fn,
                     group);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2, w_scales,
@@ -139,8 +156,8 @@ ck4_status ck4_quantize_weight_convrot_sr(const float *w, int64_t n, int64_t k, 
     if (!aligned(w_packed, 8) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
-    if (group != 0 && (!pow2(group) || group < 16 || group > 1024 || k % group != 0))
-        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need 0 or a power of two in [16, 1024] dividing k)", fn,
+    if (group != 0 && (!pow2(group) || group < 4 || group > 1024 || k % group != 0))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need 0 or a power of two in [4, 1024] dividing k)", fn,
                     group);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2, w_scales,
@@ -157,12 +174,34 @@ ck4_status ck4_quantize_weight_convrot_e4m3(const float *w, int64_t n, int64_t k
     if (!aligned(w_packed, 8)) return fail(CK4_ERR_INVALID, "%s: w_packed misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
-    if (!pow2(group) || group < 16 || group > 1024 || k % group != 0)
-        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [16, 1024] dividing k)", fn, group);
+    if (!pow2(group) || group < 4 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [4, 1024] dividing k)", fn, group);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2,
                                                   reinterpret_cast<float *>(group_scales),
                                                   static_cast<hipStream_t>(stream), ck4::WeightOpts{nullptr, 0, true}));
+}
+
+ck4_status ck4_quantize_weight_convrot_codebook(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                                int group, const float *codebook, int scale_e4m3, int8_t *w_packed,
+                                                void *group_scales, void *stream) {
+    const char *fn = "ck4_quantize_weight_convrot_codebook";
+    if (!w || !w_packed || !group_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    ck4::WeightOpts wo{nullptr, 0, scale_e4m3 != 0};
+    if (ck4_status s = make_codebook(fn, codebook, &wo.cb)) return s;
+    if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
+    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
+    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (!aligned(w_packed, 8) || (!scale_e4m3 && !aligned(group_scales, 4)))
+        return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
+    if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (!pow2(group) || group < 4 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [4, 1024] dividing k)", fn, group);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(w, 1, n, k, ldw, rot_block, 0, group, w_packed, k / 2,
+                                                  static_cast<float *>(group_scales),
+                                                  static_cast<hipStream_t>(stream), wo));
 }
 
 ck4_status ck4_quantize_weight_convrot_int8(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
@@ -252,18 +291,19 @@ ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8
 namespace {
 
 ck4_status dequant_w4a8(const char *fn, const int8_t *w_packed, const void *group_scales, bool e4m3, int64_t n,
-                        int64_t k, int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales, void *stream) {
+                        int64_t k, int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales, void *stream,
+                        const ck4::Codebook &cb = ck4::Codebook{}) {
     if (!w_packed || !group_scales || !w8 || !row_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0 || k <= 0 || nc <= 0) return fail(CK4_ERR_INVALID, "%s: n, k, nc must be positive", fn);
     if (n0 < 0 || n0 + nc > n) return fail(CK4_ERR_INVALID, "%s: rows [n0, n0+nc) outside [0, n)", fn);
-    if (!pow2(group) || group < 16 || group > 1024 || k % group != 0)
-        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [16, 1024] dividing k)", fn, group);
+    if (!pow2(group) || group < 4 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [4, 1024] dividing k)", fn, group);
     if (!aligned(w_packed, 16) || !aligned(w8, 16) || (k / 2) % 8 != 0)
         return fail(CK4_ERR_INVALID, "%s: w_packed / w8 not 16-byte aligned", fn);
     if (nc > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: nc too large", fn);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_w4a8_decode(w_packed, group_scales, e4m3, k, group, n0, nc, w8, row_scales,
-                                                static_cast<hipStream_t>(stream)));
+                                                static_cast<hipStream_t>(stream), cb));
 }
 
 }  // namespace
@@ -282,6 +322,16 @@ ck4_status ck4_dequant_w4a8_grouped_e4m3(const int8_t *w_packed, const uint8_t *
                                          void *stream) {
     return dequant_w4a8("ck4_dequant_w4a8_grouped_e4m3", w_packed, group_scales, true, n, k, group, n0, nc, w8,
                         row_scales, stream);
+}
+
+ck4_status ck4_dequant_w4a8_codebook(const int8_t *w_packed, const void *group_scales, int scale_e4m3,
+                                     const float *codebook, int64_t n, int64_t k, int group, int64_t n0, int64_t nc,
+                                     int8_t *w8, float *row_scales, void *stream) {
+    const char *fn = "ck4_dequant_w4a8_codebook";
+    ck4::Codebook cb;
+    if (ck4_status s = make_codebook(fn, codebook, &cb)) return s;
+    return dequant_w4a8(fn, w_packed, group_scales, scale_e4m3 != 0, n, k, group, n0, nc, w8, row_scales, stream,
+                        cb);
 }
 
 // Column chunk of the decode + int8 GEMM path; 0 means the fused kernel.
@@ -323,15 +373,16 @@ namespace {
 
 ck4_status linear_w4a8(const char *fn, const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
                        const void *group_scales, bool e4m3, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
-                       int64_t ldy, int64_t chunk_cols, void *workspace, size_t ws_bytes, void *stream) {
+                       int64_t ldy, int64_t chunk_cols, void *workspace, size_t ws_bytes, void *stream,
+                       const ck4::Codebook &cb = ck4::Codebook{}) {
     if (!x_q8 || !x_scales || !w_packed || !group_scales || !y)
         return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, 8)) return s;
     if (!aligned(x_q8, 16) || !aligned(w_packed, 16) || (workspace && !aligned(workspace, 16)))
         return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
     if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
-    if (!pow2(group) || group < 16 || group > 1024 || k % group != 0)
-        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [16, 1024] dividing k)", fn, group);
+    if (!pow2(group) || group < 4 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [4, 1024] dividing k)", fn, group);
     if (chunk_cols > 0 && chunk_cols % 16 != 0)
         return fail(CK4_ERR_INVALID, "%s: chunk_cols=%lld is not a multiple of 16", fn, (long long)chunk_cols);
     if (chunk_cols != 0 && !workspace)
@@ -341,7 +392,7 @@ ck4_status linear_w4a8(const char *fn, const int8_t *x_q8, const float *x_scales
     const int64_t c = w4a8_chunk(m, n, k, chunk_cols, g_l2_bytes[dev]);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (c == 0) return launched(fn, ck4::launch_w4a8_fused(x_q8, x_scales, w_packed, group_scales, e4m3, m, n, k,
-                                                           group, y, ldy, st));
+                                                           group, y, ldy, st, cb));
     const size_t need = (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));
     if (!workspace || ws_bytes < need)
         return fail(CK4_ERR_INVALID, "%s: workspace %zu bytes < %zu needed", fn, workspace ? ws_bytes : 0, need);
@@ -349,7 +400,7 @@ ck4_status linear_w4a8(const char *fn, const int8_t *x_q8, const float *x_scales
     float *srow = reinterpret_cast<float *>(static_cast<char *>(workspace) + align_up(c * k, 256));
     for (int64_t n0 = 0; n0 < n; n0 += c) {
         const int64_t nc = (n - n0) < c ? (n - n0) : c;
-        hipError_t e = ck4::launch_w4a8_decode(w_packed, group_scales, e4m3, k, group, n0, nc, w8, srow, st);
+        hipError_t e = ck4::launch_w4a8_decode(w_packed, group_scales, e4m3, k, group, n0, nc, w8, srow, st, cb);
         if (e != hipSuccess) return launched(fn, e);
         e = ck4::launch_gemm(false, x_q8, w8, x_scales, srow, nullptr, m, nc, k, false, y + n0, ldy, st);
         if (e != hipSuccess) return launched(fn, e);
@@ -375,6 +426,17 @@ ck4_status ck4_linear_w4a8_grouped_e4m3(const int8_t *x_q8, const float *x_scale
                                         size_t ws_bytes, void *stream) {
     return linear_w4a8("ck4_linear_w4a8_grouped_e4m3", x_q8, x_scales, w_packed, group_scales, true, m, n, k, group,
                        y, ldy, chunk_cols, workspace, ws_bytes, stream);
+}
+
+ck4_status ck4_linear_w4a8_codebook(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                    const void *group_scales, int scale_e4m3, const float *codebook, int64_t m,
+                                    int64_t n, int64_t k, int group, uint16_t *y, int64_t ldy, int64_t chunk_cols,
+                                    void *workspace, size_t ws_bytes, void *stream) {
+    const char *fn = "ck4_linear_w4a8_codebook";
+    ck4::Codebook cb;
+    if (ck4_status s = make_codebook(fn, codebook, &cb)) return s;
+    return linear_w4a8(fn, x_q8, x_scales, w_packed, group_scales, scale_e4m3 != 0, m, n, k, group, y, ldy,
+                       chunk_cols, workspace, ws_bytes, stream, cb);
 }
 
 }  // extern "C"

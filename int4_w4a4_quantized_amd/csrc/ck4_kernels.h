@@ -7,15 +7,29 @@
 
 namespace ck4 {
 
+// A frozen 16-entry codebook of the grouped int4 weight, passed by value
+// (it travels in the kernel arguments, so every wavefront reads it from
+// scalar registers): code u stands for the value v[u] times the group scale.
+// cmax = max |v[u]| > 0 takes the place of 7 in the scale formulas.
+struct Codebook {
+    float v[16] = {};
+    float cmax = 0.0f;
+    bool on = false;
+};
+
 // Options of the weight path (fp32 input) of launch_rotate_quant.
 //   u, ldu      if u is not null: stochastic rounding with the draw
 //               u[row * ldu + col] in [0, 1) for each element
 //   scale_e4m3  grouped int4 only: group scales are stored as E4M3 bytes and
 //               the codes use the decoded scale
+//   cb          grouped int4 only: if cb.on, each code is the index of the
+//               codebook entry nearest to r / s (ties to the lower index),
+//               with s = absmax / cb.cmax
 struct WeightOpts {
     const float *u = nullptr;
     int64_t ldu = 0;
     bool scale_e4m3 = false;
+    Codebook cb = Codebook{};
 };
 
 // Rotation + quantisation of rows (one wavefront or one workgroup per row).
@@ -68,14 +82,16 @@ hipError_t launch_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx
                             int64_t rank, float alpha, uint16_t *t, hipStream_t stream);
 
 // Grouped int4 -> int8 decode of weight rows [n0, n0 + nc). group_scales are
-// fp32, or E4M3 bytes when scale_e4m3.
+// fp32, or E4M3 bytes when scale_e4m3; group is a power of two >= 4; with
+// cb.on the codes index the codebook instead of standing for q = -8..7.
 hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, bool scale_e4m3, int64_t k, int group,
-                              int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream);
+                              int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream,
+                              const Codebook &cb = Codebook{});
 
-// Fused grouped W4A8 linear for m <= 64 (decode in registers + int8 MFMA +
-// epilogue), bit-identical to decode followed by the int8 GEMM.
+// Fused grouped W4A8 linear for m <= 64 and k % 256 == 0 (decode in registers
+// + int8 MFMA + epilogue), bit-identical to decode followed by the int8 GEMM.
 hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
                              const void *group_scales, bool scale_e4m3, int64_t m, int64_t n, int64_t k, int group,
-                             uint16_t *y, int64_t ldy, hipStream_t stream);
+                             uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb = Codebook{});
 
 }  // namespace ck4

@@ -100,6 +100,41 @@ __device__ __forceinline__ uint32_t code_sr(float r, float s, float uv, float qm
     return (uint32_t)((int)t + BIAS);
 }
 
+// Codebook code of r / s, biased like code_exact<8> (the low byte is u ^ 8,
+// so pack8_biased stores the index u): the entry u nearest to t = r / s
+// (IEEE quotient; t = 0 when s == 0) by the fp32 distance |t - v[u]|, the
+// lowest index among equal distances.
+__device__ __forceinline__ uint32_t code_codebook(float r, float s, const Codebook &cb) {
+    const float t = s == 0.0f ? 0.0f : r / s;
+    float best = fabsf(t - cb.v[0]);
+    uint32_t u = 0;
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+        const float d = fabsf(t - cb.v[i]);
+        if (d < best) {
+            best = d;
+            u = (uint32_t)i;
+        }
+    }
+    return u ^ 8u;
+}
+
+// Scale of one weight group: absmax / qdiv, or its E4M3 rounding (stored as
+// a byte, and the decoded value is what the codes use). Stored by the caller's
+// `store` flag at scales[si].
+__device__ __forceinline__ float group_scale(float gmax, float qdiv, bool e4m3, bool store, float *scales,
+                                             int64_t si) {
+    float s = gmax / qdiv;
+    if (e4m3) {
+        const uint32_t b = e4m3_encode(s);
+        s = e4m3_decode(b);
+        if (store) reinterpret_cast<uint8_t *>(scales)[si] = (uint8_t)b;
+    } else if (store) {
+        scales[si] = s;
+    }
+    return s;
+}
+
 // 8 biased int4 codes (low byte q + 8) -> one word, element 2j in the low
 // nibble of byte j: pairs are joined with one shift-or (bits above 7 are
 // don't-care), the four low bytes gathered with byte permutes, and the bias
@@ -242,30 +277,54 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
 #pragma unroll
                     for (int i = 0; i < kElems; ++i) code[i] = code_exact<BIAS>(v[j][i], s_row, qmax);
                 }
-            } else {
-                // one scale per `group` elements = group/16 consecutive lanes
-                // (offline weight preparation: the IEEE divide throughout)
-                float gmax = 0.0f;
+            } else if constexpr (sizeof(TIn) == 4) {
+                // Grouped weight codes (offline preparation: the IEEE divide
+                // throughout). sv[i] is the scale of element i of the chunk.
+                const float qdiv = wo.cb.on ? wo.cb.cmax : qmax;
+                const int64_t gbase = (int64_t)row * (k / group);
+                float sv[kElems];
+                if (group >= kElems) {
+                    // one scale per `group` elements = group/16 consecutive lanes
+                    float gmax = 0.0f;
 #pragma unroll
-                for (int i = 0; i < kElems; ++i) gmax = fmaxf(gmax, fabsf(v[j][i]));
-                for (int off = 1; off < group / kElems; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
-                float s = gmax / qmax;
-                const int lanes_per_group = group / kElems;
-                const int64_t si = (int64_t)row * (k / group) + ch / lanes_per_group;
-                if (sizeof(TIn) == 4 && wo.scale_e4m3) {
-                    // the scale is stored as E4M3 and the codes use its decoded value
-                    const uint32_t b = e4m3_encode(s);
-                    s = e4m3_decode(b);
-                    if ((ch % lanes_per_group) == 0) reinterpret_cast<uint8_t *>(scales)[si] = (uint8_t)b;
-                } else if ((ch % lanes_per_group) == 0) {
-                    scales[si] = s;
+                    for (int i = 0; i < kElems; ++i) gmax = fmaxf(gmax, fabsf(v[j][i]));
+                    for (int off = 1; off < group / kElems; off <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, off, 64));
+                    const int lanes_per_group = group / kElems;
+                    const float sg = group_scale(gmax, qdiv, wo.scale_e4m3, (ch % lanes_per_group) == 0, scales,
+                                                 gbase + ch / lanes_per_group);
+#pragma unroll
+                    for (int i = 0; i < kElems; ++i) sv[i] = sg;
+                } else {
+                    // groups of 4 or 8 inside the chunk: absmax of each run of 4
+                    float gm[kElems / 4];
+#pragma unroll
+                    for (int sb = 0; sb < kElems / 4; ++sb) {
+                        gm[sb] = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) gm[sb] = fmaxf(gm[sb], fabsf(v[j][4 * sb + i]));
+                    }
+                    const int per_chunk = kElems / group;
+#pragma unroll
+                    for (int sb = 0; sb < kElems / 4; ++sb) {
+                        // group 8: run sb joins its partner sb ^ 1
+                        const float gmax = group == 8 ? fmaxf(gm[sb], gm[sb ^ 1]) : gm[sb];
+                        const int gi = group == 8 ? sb >> 1 : sb;
+                        const bool first = group == 8 ? (sb & 1) == 0 : true;
+                        const float sg = group_scale(gmax, qdiv, wo.scale_e4m3, first, scales,
+                                                     gbase + (int64_t)ch * per_chunk + gi);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sv[4 * sb + i] = sg;
+                    }
                 }
-                if (sr) {
+                if (wo.cb.on) {
 #pragma unroll
-                    for (int i = 0; i < kElems; ++i) code[i] = code_sr<BIAS>(v[j][i], s, uv[i], qmax);
+                    for (int i = 0; i < kElems; ++i) code[i] = code_codebook(v[j][i], sv[i], wo.cb);
+                } else if (sr) {
+#pragma unroll
+                    for (int i = 0; i < kElems; ++i) code[i] = code_sr<BIAS>(v[j][i], sv[i], uv[i], qmax);
                 } else {
 #pragma unroll
-                    for (int i = 0; i < kElems; ++i) code[i] = code_exact<BIAS>(v[j][i], s, qmax);
+                    for (int i = 0; i < kElems; ++i) code[i] = code_exact<BIAS>(v[j][i], sv[i], qmax);
                 }
             }
             if constexpr (OUT == 0) {

@@ -1,14 +1,17 @@
 // Grouped int4 -> int8 weight decode for gfx950.
 //
 // What it computes ("[PR #97] HIP port of #90: grouped W4A8 over the INT8
-// GEMM", What this adds: int4 codes with per-group fp32 scales are decoded to
-// int8 codes that the rowwise int8 GEMM consumes, one lane turning 8 packed
-// bytes into 16 int8 with one 16-byte store; Chunk sizing: rows [n0, n0+nc)
-// at a time). The int8 GEMM applies one scale per row in its epilogue, so the
-// decode re-expresses the group scales against a row scale:
-//   s_row = (max_g s[row, g] * 7) / 127
-//   w8    = clamp(rint(q * (s[row, g] / s_row)), -127, 127)      (all fp32)
-// An all-zero row (s_row == 0) decodes to zeros.
+// GEMM", What this adds: int4 codes with per-group fp32 or e4m3 scales are
+// decoded to int8 codes that the rowwise int8 GEMM consumes, one lane turning
+// 8 packed bytes into 16 int8 with one 16-byte store, optionally through a
+// codebook staged in LDS; Chunk sizing: rows [n0, n0+nc) at a time). The int8
+// GEMM applies one scale per row in its epilogue, so the decode re-expresses
+// the group scales against a row scale:
+//   s_row = (max_g s[row, g] * c) / 127
+//   w8    = clamp(rint(val(u) * (s[row, g] / s_row)), -127, 127)      (all fp32)
+// where u is the 4-bit code, val(u) = q (u as a two's-complement int4) and
+// c = 7, or with a codebook val(u) = cb[u] and c = max |cb|. An all-zero row
+// (s_row == 0) decodes to zeros. Groups are powers of two from 4 up.
 //
 // One workgroup per output row: the row scale is a workgroup max-reduction
 // over that row's group scales, then each lane decodes 16-element chunks.
@@ -25,40 +28,52 @@ constexpr int kThreads = 256;
 
 __device__ __forceinline__ int sext4(uint32_t nib) { return (int)(nib ^ 8u) - 8; }
 
-template <bool E4M3>
+template <bool E4M3, bool CB>
 __global__ __launch_bounds__(kThreads) void w4a8_decode_kernel(const int8_t *__restrict__ wp,
                                                                const void *__restrict__ gs, int k, int group,
                                                                int64_t n0, int8_t *__restrict__ w8,
-                                                               float *__restrict__ row_scales) {
+                                                               float *__restrict__ row_scales, Codebook cb) {
     __shared__ float red[kThreads / 64];
+    __shared__ float lut[16];
     const int i = blockIdx.x;
     const int64_t row = n0 + i;
     const int tid = threadIdx.x;
     const int ng = k / group;
     auto sg = [&](int g) { return load_scale<E4M3>(gs, row * ng + g); };
+    if (CB && tid < 16) lut[tid] = cb.v[tid];
 
     float smax = 0.0f;
     for (int g = tid; g < ng; g += kThreads) smax = fmaxf(smax, sg(g));
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
     if ((tid & 63) == 0) red[tid >> 6] = smax;
-    __syncthreads();
+    __syncthreads();  // also publishes the codebook
     smax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float srow = (smax * 7.0f) / 127.0f;
+    const float srow = (smax * (CB ? cb.cmax : 7.0f)) / 127.0f;
     if (tid == 0) row_scales[i] = srow;
 
     const int nchunks = k / 16;
     const int8_t *src = wp + row * (int64_t)(k / 2);
     int8_t *dst = w8 + (int64_t)i * k;
     for (int ch = tid; ch < nchunks; ch += kThreads) {
-        const float mult = srow == 0.0f ? 0.0f : sg((ch * 16) / group) / srow;
+        // multipliers of the chunk's groups: one for groups of 16 and wider,
+        // else one per run of 4 elements (groups of 4 or 8)
+        float mult[4];
+        mult[0] = srow == 0.0f ? 0.0f : sg((ch * 16) / group) / srow;
+        if (group >= 16) {
+            mult[1] = mult[2] = mult[3] = mult[0];
+        } else {
+#pragma unroll
+            for (int r = 1; r < 4; ++r) mult[r] = srow == 0.0f ? 0.0f : sg((ch * 16 + 4 * r) / group) / srow;
+        }
         const uint2 p = *reinterpret_cast<const uint2 *>(src + ch * 8);
         const uint32_t words[2] = {p.x, p.y};
         uint32_t out[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int q = sext4((words[e >> 3] >> (4 * (e & 7))) & 0xFu);
-            float t = rintf((float)q * mult);
+            const uint32_t u = (words[e >> 3] >> (4 * (e & 7))) & 0xFu;
+            const float val = CB ? lut[u] : (float)sext4(u);
+            float t = rintf(val * mult[e >> 2]);
             t = fminf(fmaxf(t, -127.0f), 127.0f);
             out[e >> 2] |= ((uint32_t)(int)t & 0xFFu) << (8 * (e & 3));
         }
@@ -66,16 +81,26 @@ __global__ __launch_bounds__(kThreads) void w4a8_decode_kernel(const int8_t *__r
     }
 }
 
+template <bool E4M3>
+void launch_decode_typed(const int8_t *w_packed, const void *group_scales, int64_t k, int group, int64_t n0,
+                         int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream, const Codebook &cb) {
+    if (cb.on)
+        w4a8_decode_kernel<E4M3, true><<<dim3((unsigned)nc), dim3(kThreads), 0, stream>>>(
+            w_packed, group_scales, (int)k, group, n0, w8, row_scales, cb);
+    else
+        w4a8_decode_kernel<E4M3, false><<<dim3((unsigned)nc), dim3(kThreads), 0, stream>>>(
+            w_packed, group_scales, (int)k, group, n0, w8, row_scales, cb);
+}
+
 }  // namespace
 
 hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, bool scale_e4m3, int64_t k, int group,
-                              int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream) {
+                              int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream,
+                              const Codebook &cb) {
     if (scale_e4m3)
-        w4a8_decode_kernel<true><<<dim3((unsigned)nc), dim3(kThreads), 0, stream>>>(w_packed, group_scales, (int)k,
-                                                                                    group, n0, w8, row_scales);
+        launch_decode_typed<true>(w_packed, group_scales, k, group, n0, nc, w8, row_scales, stream, cb);
     else
-        w4a8_decode_kernel<false><<<dim3((unsigned)nc), dim3(kThreads), 0, stream>>>(w_packed, group_scales, (int)k,
-                                                                                     group, n0, w8, row_scales);
+        launch_decode_typed<false>(w_packed, group_scales, k, group, n0, nc, w8, row_scales, stream, cb);
     return hipGetLastError();
 }
 
@@ -188,6 +213,51 @@ __device__ __forceinline__ uint2 decode8_table(uint32_t w, uint4 tab) {
     return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
 }
 
+// decode8 with the first four codes (bytes 0-1) under one multiplier and the
+// last four (bytes 2-3) under another: a word that spans two groups of 4.
+__device__ __forceinline__ uint2 decode8_2(uint32_t w, float ma, float m8a, float mb, float m8b) {
+    const uint32_t u = w ^ 0x88888888u;
+    const uint32_t lo = u & 0x0F0F0F0Fu;
+    const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;
+    uint32_t c[8];
+    c[0] = code8(ubyte_f32<0>(lo), ma, m8a);
+    c[1] = code8(ubyte_f32<0>(hi), ma, m8a);
+    c[2] = code8(ubyte_f32<1>(lo), ma, m8a);
+    c[3] = code8(ubyte_f32<1>(hi), ma, m8a);
+    c[4] = code8(ubyte_f32<2>(lo), mb, m8b);
+    c[5] = code8(ubyte_f32<2>(hi), mb, m8b);
+    c[6] = code8(ubyte_f32<3>(lo), mb, m8b);
+    c[7] = code8(ubyte_f32<3>(hi), mb, m8b);
+    const uint32_t d0 = __builtin_amdgcn_perm(c[1], c[0], 0x0C0C0400u) | __builtin_amdgcn_perm(c[3], c[2], 0x04000C0Cu);
+    const uint32_t d1 = __builtin_amdgcn_perm(c[5], c[4], 0x0C0C0400u) | __builtin_amdgcn_perm(c[7], c[6], 0x04000C0Cu);
+    return make_uint2(d0, d1);
+}
+
+// Codebook table for one multiplier: byte u = clamp(rint(RN(cb[u] * mult)),
+// -127, 127), the same fp32 steps as the decode kernel, all 16 entries
+// evaluated (a codebook has no symmetry to exploit). The entries come from
+// the kernel arguments, i.e. scalar registers.
+__device__ __forceinline__ uint4 code_table_cb(float mult, const Codebook &cb) {
+    uint32_t r[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+        r[u] = __float_as_uint(fminf(fmaxf(cb.v[u] * mult, -127.0f), 127.0f) + 12582912.0f);
+    auto pack4 = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+        return __builtin_amdgcn_perm(b, a, 0x0C0C0400u) | __builtin_amdgcn_perm(d, c, 0x04000C0Cu);
+    };
+    return make_uint4(pack4(r[0], r[1], r[2], r[3]), pack4(r[4], r[5], r[6], r[7]), pack4(r[8], r[9], r[10], r[11]),
+                      pack4(r[12], r[13], r[14], r[15]));
+}
+
+// decode8_table with elements 0-3 (bytes 0-1) looked up in ta and elements
+// 4-7 (bytes 2-3) in tb.
+__device__ __forceinline__ uint2 decode8_table2(uint32_t w, uint4 ta, uint4 tb) {
+    const uint32_t ln = w & 0x0F0F0F0Fu, hn = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t lo = __builtin_amdgcn_perm(lookup4(ln, tb), lookup4(ln, ta), 0x07060100u);
+    const uint32_t hi = __builtin_amdgcn_perm(lookup4(hn, tb), lookup4(hn, ta), 0x07060100u);
+    return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
+}
+
 // Operand layout: a k-step is 256 k. Lane l (row l & 15, part p = l >> 4)
 // owns the 64 contiguous k [256 s + 64 p, 256 s + 64 p + 64) of its weight row
 // and of its activation row; the MFMA of slice h (0..3) takes 16 of them,
@@ -195,11 +265,16 @@ __device__ __forceinline__ uint2 decode8_table(uint32_t w, uint4 tab) {
 // assignment, so each slice's 64 products are 64 distinct k and the four
 // slices cover the step. A lane's 64 k lie in one weight group when the group
 // is at least 64 wide, which makes the scale division once per step.
-template <int FM, int FNW, int KS, int MAXS, bool E4M3>
+// SG = 0 for groups of 16 and wider; SG = 8 or 4 for those narrow groups
+// (a multiplier per 8-code word, or per half word). CB: codes index the
+// codebook cb.
+template <int FM, int FNW, int KS, int MAXS, bool E4M3, int SG, bool CB>
 __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__restrict__ X, const float *__restrict__ sx,
                                                            const int8_t *__restrict__ W,
                                                            const void *__restrict__ gs, int M, int N, int K,
-                                                           int group, uint16_t *__restrict__ Y, int64_t ldy) {
+                                                           int group, uint16_t *__restrict__ Y, int64_t ldy,
+                                                           Codebook cb) {
+    constexpr int NGV = SG == 0 ? 4 : 64 / SG;  // group scales per lane and k-step
     __shared__ v4i_t red[KS - 1][FNW][FM][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -227,7 +302,7 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
         for (int g = part; g < ng; g += 4) smax = fmaxf(smax, load_scale<E4M3>(gs, gsr[i] + g));
         smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
         smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-        srow[i] = (smax * 7.0f) / 127.0f;
+        srow[i] = (smax * (CB ? cb.cmax : 7.0f)) / 127.0f;
     }
 
     const int steps = K / 256;
@@ -244,7 +319,7 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
     for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
         // every load of this chunk first: weights, group scales, activations
         v4i_t wv[MAXS][FNW][2];
-        float gv[MAXS][FNW][4];
+        float gv[MAXS][FNW][NGV];
         v4i_t xv[MAXS][FM][4];
 #pragma unroll
         for (int t = 0; t < MAXS; ++t) {
@@ -256,7 +331,10 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
                     const uint32_t off = (uint32_t)(i * 16 + frow) * (uint32_t)wrow_bytes + (uint32_t)(kb / 2);
                     wv[t][i][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
                     wv[t][i][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 16, 0);
-                    if (one_group) {
+                    if constexpr (SG != 0) {
+#pragma unroll
+                        for (int c = 0; c < NGV; ++c) gv[t][i][c] = load_scale<E4M3>(gs, gsr[i] + kb / SG + c);
+                    } else if (one_group) {
                         const float g0 = load_scale<E4M3>(gs, gsr[i] + kb / group);
 #pragma unroll
                         for (int h = 0; h < 4; ++h) gv[t][i][h] = g0;
@@ -282,10 +360,38 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
                                            (uint32_t)wv[t][i][0][2], (uint32_t)wv[t][i][0][3],
                                            (uint32_t)wv[t][i][1][0], (uint32_t)wv[t][i][1][1],
                                            (uint32_t)wv[t][i][1][2], (uint32_t)wv[t][i][1][3]};
+                if constexpr (SG != 0) {
+                    // groups of 8 or 4: a multiplier per word or per half word
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        uint2 d[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int wi = 2 * h + e;
+                            const int ga = SG == 8 ? wi : 2 * wi, gb = SG == 8 ? wi : 2 * wi + 1;
+                            const float ma = srow[i] == 0.0f ? 0.0f : gv[t][i][ga] / srow[i];
+                            const float mb = SG == 8 ? ma : (srow[i] == 0.0f ? 0.0f : gv[t][i][gb] / srow[i]);
+                            if constexpr (CB) {
+                                const uint4 ta = code_table_cb(ma, cb);
+                                d[e] = SG == 8 ? decode8_table(words[wi], ta)
+                                               : decode8_table2(words[wi], ta, code_table_cb(mb, cb));
+                            } else {
+                                d[e] = decode8_2(words[wi], ma, -8.0f * ma, mb, -8.0f * mb);
+                            }
+                        }
+                        const v4i_t w8 = v4i_t{(int)d[0].x, (int)d[0].y, (int)d[1].x, (int)d[1].y};
+#pragma unroll
+                        for (int j = 0; j < FM; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
+                    }
+                    continue;
+                }
                 if (one_group) {
                     // one multiplier for the lane's 64 codes: table decode
                     const float mu = srow[i] == 0.0f ? 0.0f : gv[t][i][0] / srow[i];
-                    const uint4 tab = code_table(mu);
+                    uint4 tab;
+                    if constexpr (CB) tab = code_table_cb(mu, cb);
+                    else tab = code_table(mu);
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
                         const uint2 a = decode8_table(words[2 * h], tab);
@@ -297,7 +403,21 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
                     }
                     continue;
                 }
-                // groups narrower than 64: a multiplier per 16 codes, per-code decode
+                // groups of 16 and 32: a multiplier per 16 codes
+                if constexpr (CB) {
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        const uint4 tab = code_table_cb(srow[i] == 0.0f ? 0.0f : gv[t][i][h] / srow[i], cb);
+                        const uint2 a = decode8_table(words[2 * h], tab);
+                        const uint2 b = decode8_table(words[2 * h + 1], tab);
+                        const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
+#pragma unroll
+                        for (int j = 0; j < FM; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
+                    }
+                    continue;
+                }
+                // per-code decode
                 float mult[4], m8[4];
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
@@ -362,42 +482,72 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
     }
 }
 
-template <int FM, int FNW, int MAXS, bool E4M3>
+template <int FM, int FNW, int MAXS, bool E4M3, int SG, bool CB>
 hipError_t launch_fused_cfg(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
-                            int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream) {
+                            int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
     const int64_t groups = (n + 16 * FNW - 1) / (16 * FNW);
     dim3 grid((unsigned)groups);
-    if (groups >= 1024) {
-        w4a8_fused_kernel<FM, FNW, 2, MAXS, E4M3><<<grid, dim3(128), 0, stream>>>(x, sx, w, gs, (int)m, (int)n,
-                                                                                (int)k, group, y, ldy);
+    if constexpr (SG != 0 || CB) {
+        // narrow groups and codebooks: one K split (4 wavefronts) for every width
+        w4a8_fused_kernel<FM, FNW, 4, MAXS, E4M3, SG, CB><<<grid, dim3(256), 0, stream>>>(
+            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
+    } else if (groups >= 1024) {
+        w4a8_fused_kernel<FM, FNW, 2, MAXS, E4M3, 0, false><<<grid, dim3(128), 0, stream>>>(
+            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
     } else if (groups >= 512) {
-        w4a8_fused_kernel<FM, FNW, 4, MAXS, E4M3><<<grid, dim3(256), 0, stream>>>(x, sx, w, gs, (int)m, (int)n,
-                                                                                (int)k, group, y, ldy);
+        w4a8_fused_kernel<FM, FNW, 4, MAXS, E4M3, 0, false><<<grid, dim3(256), 0, stream>>>(
+            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
     } else {
-        w4a8_fused_kernel<FM, FNW, 8, MAXS, E4M3><<<grid, dim3(512), 0, stream>>>(x, sx, w, gs, (int)m, (int)n,
-                                                                                (int)k, group, y, ldy);
+        w4a8_fused_kernel<FM, FNW, 8, MAXS, E4M3, 0, false><<<grid, dim3(512), 0, stream>>>(
+            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
     }
     return hipGetLastError();
 }
 
-template <bool E4M3>
+template <bool E4M3, int SG, bool CB>
 hipError_t launch_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed, const void *group_scales,
-                        int64_t m, int64_t n, int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream) {
+                        int64_t m, int64_t n, int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream,
+                        const Codebook &cb) {
     if (m <= 16)
-        return launch_fused_cfg<1, 1, 2, E4M3>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+        return launch_fused_cfg<1, 1, 2, E4M3, SG, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
+                                                        stream, cb);
     if (m <= 32)
-        return launch_fused_cfg<2, 1, 2, E4M3>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
-    return launch_fused_cfg<4, 1, 1, E4M3>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+        return launch_fused_cfg<2, 1, 2, E4M3, SG, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
+                                                        stream, cb);
+    return launch_fused_cfg<4, 1, 1, E4M3, SG, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
+                                                    stream, cb);
+}
+
+template <bool E4M3, bool CB>
+hipError_t launch_fused_groups(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                               const void *group_scales, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
+                               int64_t ldy, hipStream_t stream, const Codebook &cb) {
+    if (group == 4)
+        return launch_fused<E4M3, 4, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
+    if (group == 8)
+        return launch_fused<E4M3, 8, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
+    return launch_fused<E4M3, 0, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
+}
+
+template <bool E4M3>
+hipError_t launch_fused_cb(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed, const void *group_scales,
+                           int64_t m, int64_t n, int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream,
+                           const Codebook &cb) {
+    if (cb.on)
+        return launch_fused_groups<E4M3, true>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream,
+                                               cb);
+    return launch_fused_groups<E4M3, false>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream,
+                                            cb);
 }
 
 }  // namespace
 
 hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
                              const void *group_scales, bool scale_e4m3, int64_t m, int64_t n, int64_t k, int group,
-                             uint16_t *y, int64_t ldy, hipStream_t stream) {
+                             uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
     if (scale_e4m3)
-        return launch_fused<true>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
-    return launch_fused<false>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream);
+        return launch_fused_cb<true>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
+    return launch_fused_cb<false>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
 }
 
 }  // namespace ck4

@@ -68,6 +68,8 @@ def lib():
             "ck4o_epilogue_bf16": ([P, P, P, P, I64, I64, I64, P], None),
             "ck4o_linear_w4a4": ([P, P, P, P, I64, I64, I64, I, P], None),
             "ck4o_decode_w4a8": ([P, P, I64, I64, I, I64, I64, P, P], None),
+            "ck4o_quantize_weight_convrot_codebook": ([P, I64, I64, I64, I, I, P, I, P, P], None),
+            "ck4o_decode_w4a8_codebook": ([P, P, P, I64, I64, I, I64, I64, P, P], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -310,6 +312,47 @@ def linear_w4a8_grouped(x_bits: np.ndarray, w_packed: np.ndarray, group_scales: 
                         group: int = 128, g: int = 128) -> np.ndarray:
     """Grouped W4A8 linear: decode, int8 activations, int8 GEMM, epilogue."""
     w8, srow = decode_w4a8(w_packed, group_scales, group)
+    xq, sx = rotate_quantize_act(x_bits, g, bits=8)
+    acc = gemm_acc(xq, w8, xq.shape[1], bits=8)
+    return epilogue_bf16(acc, sx, srow)
+
+
+def quantize_weight_convrot_codebook(w: np.ndarray, codebook, g: int = 128, group: int = 128,
+                                     e4m3: bool = False):
+    """Grouped weight prep against a 16-entry codebook -> (packed indices int8
+    [n, k/2], group scales fp32 [n, k/group] or e4m3 uint8 [n, k/group])."""
+    w = _c(w, np.float32)
+    cb = _c(codebook, np.float32)
+    assert cb.shape == (16,)
+    n, k = w.shape
+    packed = np.empty((n, k // 2), np.int8)
+    scales = np.empty((n, k // group), np.uint8 if e4m3 else np.float32)
+    lib().ck4o_quantize_weight_convrot_codebook(_p(w), n, k, k, g, group, _p(cb), int(bool(e4m3)), _p(packed),
+                                                _p(scales))
+    return packed, scales
+
+
+def decode_w4a8_codebook(w_packed: np.ndarray, group_scales: np.ndarray, codebook, group: int = 128,
+                         n0: int = 0, nc: int | None = None):
+    """Codebook decode of rows [n0, n0+nc) -> (int8 [nc, k], fp32 [nc]); e4m3
+    scale bytes decode exactly to fp32 first."""
+    wp = _c(w_packed, np.int8)
+    n, k = wp.shape[0], wp.shape[1] * 2
+    gs = np.asarray(group_scales)
+    gs = e4m3_decode(gs) if gs.dtype == np.uint8 else _c(gs, np.float32)
+    cb = _c(codebook, np.float32)
+    if nc is None:
+        nc = n - n0
+    w8 = np.empty((nc, k), np.int8)
+    sr = np.empty((nc,), np.float32)
+    lib().ck4o_decode_w4a8_codebook(_p(wp), _p(gs), _p(cb), n, k, group, n0, nc, _p(w8), _p(sr))
+    return w8, sr
+
+
+def linear_w4a8_codebook(x_bits: np.ndarray, w_packed: np.ndarray, group_scales: np.ndarray, codebook,
+                         group: int = 128, g: int = 128) -> np.ndarray:
+    """Codebook W4A8 linear: codebook decode, int8 activations, int8 GEMM, epilogue."""
+    w8, srow = decode_w4a8_codebook(w_packed, group_scales, codebook, group)
     xq, sx = rotate_quantize_act(x_bits, g, bits=8)
     acc = gemm_acc(xq, w8, xq.shape[1], bits=8)
     return epilogue_bf16(acc, sx, srow)

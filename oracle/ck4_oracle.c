@@ -36,6 +36,12 @@
  *  - Grouped W4A8 decode: s_row = (max_g s_g * 7) / 127, w8 = clamp(rint(q *
  *    (s_g / s_row)), -127, 127), all fp32; an all-zero row gives s_row = 0,
  *    w8 = 0.
+ *  - Codebook ([PR97] "What this adds", "On #96"; the pages give no values
+ *    and no mapping): the 4-bit code u (0..15, as stored) stands for cb[u]
+ *    times the group scale, cmax = max |cb[u]|. Preparation: s = absmax /
+ *    cmax, t = v / s (t = 0 when s = 0), u = the index of the smallest fp32
+ *    |t - cb[u]|, the lowest index on ties. Decode: s_row = (max_g s_g *
+ *    cmax) / 127, w8 = clamp(rint(cb[u] * (s_g / s_row)), -127, 127).
  *  - Dynamic LoRA ([HIPT] "LoRA modes", [FAST] "Features"): stated in the
  *    Python layer of the oracle (oracle/__init__.py), in fp64 over the bf16
  *    operands, with this file's rotation and bf16 rounding.
@@ -490,6 +496,104 @@ void ck4o_decode_w4a8(const int8_t *w_packed, const float *group_scales, int64_t
                 uint8_t byte = (uint8_t)w_packed[row * (k / 2) + kk / 2];
                 int8_t qv = sext4((kk & 1) ? (byte >> 4) : (byte & 0x0F));
                 float t = rintf((float)qv * mult);
+                if (t > 127.0f) t = 127.0f;
+                if (t < -127.0f) t = -127.0f;
+                w8[i * k + kk] = (int8_t)t;
+            }
+        }
+    }
+}
+
+/* ---- Codebook variant of the grouped W4A8 weight ([PR97] "What this adds":
+ * an optional codebook for the decode; "On #96": a frozen codebook lookup
+ * table). cb holds 16 fp32 entries; cmax = max |cb[u]| (assumed > 0). */
+
+static float codebook_cmax(const float *cb) {
+    float c = 0.0f;
+    for (int u = 0; u < 16; u++)
+        if (fabsf(cb[u]) > c) c = fabsf(cb[u]);
+    return c;
+}
+
+/* Index of the entry nearest to t by the fp32 distance |t - cb[u]|, the
+ * lowest index among equal distances. */
+static int codebook_nearest(float t, const float *cb) {
+    int best = 0;
+    float bd = fabsf(t - cb[0]);
+    for (int u = 1; u < 16; u++) {
+        float d = fabsf(t - cb[u]);
+        if (d < bd) {
+            bd = d;
+            best = u;
+        }
+    }
+    return best;
+}
+
+/* Rotate the rows in fp32, then for each group of `group` elements along K:
+ * s = absmax / cmax (with e4m3 != 0 rounded to e4m3: the byte is stored and
+ * its decoded value used), t = v / s (0 when s = 0), code = nearest entry.
+ * packed int8 [n, k/2] holds the indices, even k in the low nibble; scales
+ * is fp32 [n, k/group] or, with e4m3, uint8 [n, k/group]. */
+void ck4o_quantize_weight_convrot_codebook(const float *w, int64_t n, int64_t k, int64_t ldw, int g, int group,
+                                           const float *cb, int e4m3, int8_t *packed, void *scales) {
+    float *r = (float *)malloc((size_t)(n * k) * sizeof(float));
+    int8_t *u = (int8_t *)malloc((size_t)(n * k));
+    ck4o_rotate_rows_f32(w, n, k, ldw, g, r);
+    const float cmax = codebook_cmax(cb);
+    const int64_t ng = k / group;
+#pragma omp parallel for schedule(static)
+    for (int64_t row = 0; row < n; row++) {
+        for (int64_t gi = 0; gi < ng; gi++) {
+            const float *v = r + row * k + gi * group;
+            int8_t *out = u + row * k + gi * group;
+            float amax = 0.0f;
+            for (int64_t j = 0; j < group; j++) {
+                float a = fabsf(v[j]);
+                if (a > amax) amax = a;
+            }
+            float s = amax / cmax;
+            if (e4m3) {
+                const uint8_t b = ck4o_e4m3_encode(s);
+                ((uint8_t *)scales)[row * ng + gi] = b;
+                s = ck4o_e4m3_decode(b);
+            } else {
+                ((float *)scales)[row * ng + gi] = s;
+            }
+            for (int64_t j = 0; j < group; j++) {
+                const float t = s == 0.0f ? 0.0f : v[j] / s;
+                out[j] = (int8_t)codebook_nearest(t, cb);
+            }
+        }
+    }
+    ck4o_pack_int4(u, n * k, packed);
+    free(u);
+    free(r);
+}
+
+/* Decode of rows [n0, n0 + nc) of a codebook weight with fp32 group scales:
+ * s_row = (max_g s_g * cmax) / 127, w8 = clamp(rint(cb[u] * (s_g / s_row)),
+ * -127, 127), all fp32; an all-zero row gives s_row = 0 and w8 = 0. */
+void ck4o_decode_w4a8_codebook(const int8_t *w_packed, const float *group_scales, const float *cb, int64_t n,
+                               int64_t k, int group, int64_t n0, int64_t nc, int8_t *w8, float *row_scales) {
+    (void)n;
+    const float cmax = codebook_cmax(cb);
+    const int64_t ng = k / group;
+    for (int64_t i = 0; i < nc; i++) {
+        const int64_t row = n0 + i;
+        const float *sg = group_scales + row * ng;
+        float smax = 0.0f;
+        for (int64_t gi = 0; gi < ng; gi++)
+            if (sg[gi] > smax) smax = sg[gi];
+        const float srow = (smax * cmax) / 127.0f;
+        row_scales[i] = srow;
+        for (int64_t gi = 0; gi < ng; gi++) {
+            const float mult = srow == 0.0f ? 0.0f : sg[gi] / srow;
+            for (int64_t j = 0; j < group; j++) {
+                const int64_t kk = gi * group + j;
+                const uint8_t byte = (uint8_t)w_packed[row * (k / 2) + kk / 2];
+                const unsigned code = (kk & 1) ? (byte >> 4) : (byte & 0x0F);
+                float t = rintf(cb[code] * mult);
                 if (t > 127.0f) t = 127.0f;
                 if (t < -127.0f) t = -127.0f;
                 w8[i * k + kk] = (int8_t)t;

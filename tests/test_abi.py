@@ -116,6 +116,32 @@ def test_w4a8_validation(L):
     assert l8(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 192, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
 
 
+def test_codebook_validation(L):
+    cb = (ctypes.c_float * 16)(*[float(i - 8) / 8 for i in range(16)])
+    zero = (ctypes.c_float * 16)()
+    bad = (ctypes.c_float * 16)(*([0.5] * 15 + [float("nan")]))
+    q = L.ck4_quantize_weight_convrot_codebook
+    assert q(FAKE, 4, 256, 256, 128, 128, NULL, 0, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert "codebook" in last(L)
+    assert q(FAKE, 4, 256, 256, 128, 128, zero, 0, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert q(FAKE, 4, 256, 256, 128, 128, bad, 0, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert "not finite" in last(L)
+    assert q(FAKE, 4, 256, 256, 128, 2, cb, 0, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group < 4
+    assert q(FAKE, 4, 256, 256, 128, 0, cb, 0, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # no group scales
+    odd2 = ctypes.c_void_p((1 << 20) + 2)
+    assert q(FAKE, 4, 256, 256, 128, 128, cb, 0, FAKE, odd2, NULL) == ck.CK4_ERR_INVALID   # fp32 scales misaligned
+    d = L.ck4_dequant_w4a8_codebook
+    assert d(FAKE, FAKE, 0, NULL, 64, 256, 128, 0, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert d(FAKE, FAKE, 0, cb, 64, 256, 128, 32, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID  # n0 + nc > n
+    f = L.ck4_linear_w4a8_codebook
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, zero, 8, 64, 256, 128, FAKE, 64, 0, FAKE, 1 << 20, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, cb, 8, 64, 256, 2, FAKE, 64, 0, FAKE, 1 << 20, NULL) == ck.CK4_ERR_UNSUPPORTED
+    w = L.ck4_quantize_weight_convrot
+    assert w(FAKE, 4, 256, 256, 128, 2, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # group 2
+    with pytest.raises(ValueError):
+        ck._codebook([1.0] * 15)
+
+
 def test_lora_validation(L):
     p = L.ck4_lora_prepare_down
     assert p(NULL, 32, 256, 256, 128, FAKE, NULL) == ck.CK4_ERR_INVALID

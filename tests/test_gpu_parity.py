@@ -98,6 +98,7 @@ def test_activation_quant_bitexact(ck, m, k, rb, bits):
     (64, 256, 128, 0), (17, 384, 128, 0), (300, 3072, 128, 0), (5, 12288, 128, 0),
     (33, 1024, 64, 0), (40, 2048, 256, 0), (64, 512, 128, 128), (37, 3072, 128, 128),
     (16, 1024, 128, 16), (16, 1024, 128, 32), (16, 1024, 128, 64), (16, 1024, 128, 256), (8, 5120, 128, 128),
+    (16, 1024, 128, 4), (16, 1024, 128, 8), (5, 3072, 128, 4), (9, 12288, 128, 8), (33, 256, 16, 4),
 ])
 def test_weight_quant_bitexact(ck, n, k, rb, group):
     rng = np.random.default_rng(300 + n)
@@ -181,7 +182,8 @@ def test_repeatable_bitwise(ck):
 
 
 @pytest.mark.parametrize("n,k,group", [(64, 256, 128), (1152, 512, 128), (100, 3072, 128), (48, 1024, 16),
-                                       (48, 1024, 32), (48, 1024, 64), (48, 2048, 256)])
+                                       (48, 1024, 32), (48, 1024, 64), (48, 2048, 256), (48, 1024, 4),
+                                       (48, 1024, 8), (7, 5120, 4)])
 def test_w4a8_decode_bitexact(ck, n, k, group):
     rng = np.random.default_rng(600 + n)
     w = workloads.make_weight(rng, n, k)
@@ -221,7 +223,7 @@ def test_w4a8_linear_chunked_equals_single_pass_and_oracle(ck, m, n, k, chunk):
     assert_bf16_close(y, oracle.linear_w4a8_grouped(xb, wp, gs))
 
 
-@pytest.mark.parametrize("group", [16, 64, 256])
+@pytest.mark.parametrize("group", [4, 8, 16, 64, 256])
 @pytest.mark.parametrize("m", [1, 24, 64])
 def test_w4a8_fused_matches_chunked_for_all_groups(ck, m, group):
     # default policy (fused kernel for m <= 64) against an explicit chunked
@@ -256,7 +258,8 @@ def _e4m3_weight(rng, n, k):
     return w
 
 
-@pytest.mark.parametrize("n,k,group", [(64, 256, 128), (40, 1024, 16), (33, 3072, 64), (20, 2048, 256)])
+@pytest.mark.parametrize("n,k,group", [(64, 256, 128), (40, 1024, 16), (33, 3072, 64), (20, 2048, 256),
+                                       (40, 1024, 4), (40, 1024, 8)])
 def test_e4m3_weight_prep_and_decode_bitexact(ck, n, k, group):
     rng = np.random.default_rng(1400 + n)
     w = _e4m3_weight(rng, n, k)
@@ -286,10 +289,89 @@ def test_e4m3_linear_fused_chunked_single_equal_and_match_oracle(ck, m, n, k):
 
 
 # --------------------------------------------------------------------------
+# Grouped W4A8 with a frozen 16-entry codebook
+
+# an unordered table with a repeated entry, a zero and an asymmetric range
+CB_ODD = np.array([0.9, -0.2, 0.05, 0.5, -1.3, 0.0, 0.3, -0.6, 1.1, -0.05, 0.7, 0.5, -0.9, 0.15, -0.35, 0.2],
+                  np.float32)
+
+
+def _codebooks():
+    return {"normal": workloads.make_codebook(), "odd": CB_ODD}
+
+
+@pytest.mark.parametrize("cbname", ["normal", "odd"])
+@pytest.mark.parametrize("e4m3", [False, True])
+@pytest.mark.parametrize("n,k,group", [(64, 256, 128), (40, 1024, 4), (40, 1024, 8), (33, 3072, 16),
+                                       (17, 2048, 64), (9, 12288, 256)])
+def test_codebook_weight_prep_and_decode_bitexact(ck, cbname, e4m3, n, k, group):
+    cb = _codebooks()[cbname]
+    rng = np.random.default_rng(1600 + n + group)
+    w = _e4m3_weight(rng, n, k) if e4m3 else workloads.make_weight(rng, n, k)
+    w[0] = 0
+    wp, gs = ck.quantize_weight_convrot_codebook(torch.from_numpy(w).cuda(), cb, 128, group, e4m3)
+    wp_ref, gs_ref = oracle.quantize_weight_convrot_codebook(w, cb, group=group, e4m3=e4m3)
+    assert np.array_equal(host(gs).view(np.uint8), gs_ref.view(np.uint8))
+    assert np.array_equal(host(wp), wp_ref)
+    w8, sr = ck.dequant_w4a8_grouped(wp, gs, group, codebook=cb)
+    w8_ref, sr_ref = oracle.decode_w4a8_codebook(wp_ref, gs_ref, cb, group)
+    assert np.array_equal(host(sr).view(np.uint32), sr_ref.view(np.uint32))
+    assert np.array_equal(host(w8), w8_ref)
+    # a chunk of rows decodes to the same bits
+    n0, nc = n // 3, n - n // 3
+    w8c, src = ck.dequant_w4a8_grouped(wp, gs, group, n0, nc, codebook=cb)
+    assert np.array_equal(host(w8c), w8_ref[n0:]) and np.array_equal(host(src), sr_ref[n0:])
+
+
+@pytest.mark.parametrize("cbname", ["normal", "odd"])
+@pytest.mark.parametrize("e4m3", [False, True])
+@pytest.mark.parametrize("m,n,k,group", [(1, 1000, 768, 128), (16, 333, 1536, 4), (24, 333, 1536, 8),
+                                         (64, 130, 1024, 32), (40, 77, 1024, 256), (100, 300, 512, 64)])
+def test_codebook_linear_paths_equal_and_match_oracle(ck, cbname, e4m3, m, n, k, group):
+    cb = _codebooks()[cbname]
+    rng = np.random.default_rng(1700 + m + group)
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    w[7] = 0
+    wp_ref, gs_ref = oracle.quantize_weight_convrot_codebook(w, cb, group=group, e4m3=e4m3)
+    wpd, gsd = torch.from_numpy(wp_ref).cuda(), torch.from_numpy(gs_ref).cuda()
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    y0 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, group, 0, codebook=cb))
+    y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, group, -1, codebook=cb))
+    yc = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, group, 128, codebook=cb))
+    assert np.array_equal(y0, y1) and np.array_equal(y0, yc)
+    assert not y0[:, 7].any()
+    assert_bf16_close(y0, oracle.linear_w4a8_codebook(xb, wp_ref, gs_ref, cb, group))
+
+
+def test_codebook_skinny_full_size(ck):
+    # decode shape at full size: N=12288, K=3072, one token, group 128, through
+    # the fused kernel (default policy) and the single-pass decode; the oracle
+    # checks a sample of output columns through the decoded int8 weight.
+    cb = workloads.make_codebook()
+    rng = np.random.default_rng(1800)
+    n, k = 12288, 3072
+    xb = workloads.make_activations(rng, 1, k)
+    w = workloads.make_weight(rng, n, k)
+    wp, gs = ck.quantize_weight_convrot_codebook(torch.from_numpy(w).cuda(), cb, 128, 128)
+    wp_ref, gs_ref = oracle.quantize_weight_convrot_codebook(w, cb, group=128)
+    assert np.array_equal(host(wp), wp_ref) and np.array_equal(host(gs), gs_ref)
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    y0 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wp, gs, 128, 0, codebook=cb))
+    y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wp, gs, 128, -1, codebook=cb))
+    assert np.array_equal(y0, y1)
+    cols = np.random.default_rng(1801).choice(n, 256, replace=False)
+    cols.sort()
+    ref = oracle.linear_w4a8_codebook(xb, wp_ref[cols], gs_ref[cols], cb, 128)
+    assert_bf16_close(y0[:, cols], ref)
+
+
+# --------------------------------------------------------------------------
 # Stochastic-rounding weight requantisation
 
 
-@pytest.mark.parametrize("n,k,group", [(64, 256, 0), (257, 3072, 0), (33, 1024, 128), (12, 4096, 64), (5, 12288, 0)])
+@pytest.mark.parametrize("n,k,group", [(64, 256, 0), (257, 3072, 0), (33, 1024, 128), (12, 4096, 64), (5, 12288, 0),
+                                       (33, 1024, 4), (12, 2048, 8)])
 def test_sr_weight_quant_bitexact(ck, n, k, group):
     rng = np.random.default_rng(1200 + n)
     w = workloads.make_weight(rng, n, k)

@@ -207,15 +207,16 @@ def test_quantiser_monotone_and_power_of_two_invariant():
     assert np.array_equal(s2, s * np.float32(2.0 ** 13))
 
 
-def test_grouped_quantiser_per_group():
+@pytest.mark.parametrize("G", [4, 8, 128])
+def test_grouped_quantiser_per_group(G):
     rng = np.random.default_rng(9)
     r = rng.standard_normal((4, 512)).astype(np.float32)
     r[:, 130] = 40.0
-    q, s = oracle.quantize_rows(r, 128, 7)
-    assert s.shape == (4, 4)
-    for gi in range(4):
-        qg, sg = oracle.quantize_rows(np.ascontiguousarray(r[:, gi * 128:(gi + 1) * 128]), 0, 7)
-        assert np.array_equal(q[:, gi * 128:(gi + 1) * 128], qg)
+    q, s = oracle.quantize_rows(r, G, 7)
+    assert s.shape == (4, 512 // G)
+    for gi in range(512 // G):
+        qg, sg = oracle.quantize_rows(np.ascontiguousarray(r[:, gi * G:(gi + 1) * G]), 0, 7)
+        assert np.array_equal(q[:, gi * G:(gi + 1) * G], qg)
         assert np.array_equal(s[:, gi], sg)
 
 
@@ -348,9 +349,11 @@ def test_linear_within_quantisation_error_bound_of_float():
 # Grouped W4A8 decode
 
 
-def test_w4a8_decode_invariants():
+@pytest.mark.parametrize("G", [4, 8, 16, 32, 64, 128])
+def test_w4a8_decode_invariants(G):
+    # the pages test the decode over group sizes 4 to 64 ([PR97] Testing)
     rng = np.random.default_rng(14)
-    n, k, G = 64, 512, 128
+    n, k = 64, 512
     w = workloads.make_weight(rng, n, k)
     w[:, 3] *= 30
     wp, gs = oracle.quantize_weight_convrot(w, group=G)
@@ -549,6 +552,131 @@ def test_e4m3_weight_prep_rounds_fp32_scales_and_bounds_codes():
         assert np.all(err[sel] <= sdb[sel] / 2 * (1 + 2 ** -20))   # nearest code against the decoded scale
         assert np.all(np.abs(q[okb & ~unclipped]) == 7)           # beyond 7 s8: clamped
         assert not q[~okb].any() and not q[3].any()
+
+
+# --------------------------------------------------------------------------
+# Codebook W4A8 ([PR97] What this adds, On #96): code u stands for cb[u]
+# times the group scale; prep picks the nearest entry, decode re-expresses
+# cb[u] * s_g against the row scale max_g s_g * cmax / 127.
+
+# The uniform int4 levels as a codebook: u -> q for u < 8, u - 16 above,
+# with the unused -8 replaced by -7 so that cmax = 7 as in the int4 path.
+CB_UNIFORM = np.array([0, 1, 2, 3, 4, 5, 6, 7, -7, -7, -6, -5, -4, -3, -2, -1], np.float32)
+
+
+@pytest.mark.parametrize("G", [4, 8, 16, 32, 64, 128])
+@pytest.mark.parametrize("e4m3", [False, True])
+def test_codebook_of_uniform_levels_is_the_int4_path(G, e4m3):
+    # Nearest entry of the uniform table = rint clamped to +-7 (no exact
+    # half-integer quotients occur in these draws), so the codebook prep and
+    # decode must reproduce the independently pinned int4 prep and decode.
+    rng = np.random.default_rng(70)
+    w = workloads.make_weight(rng, 24, 512)
+    w[5] = 0
+    w[7, :64] = 0
+    wp_c, s_c = oracle.quantize_weight_convrot_codebook(w, CB_UNIFORM, group=G, e4m3=e4m3)
+    if e4m3:
+        wp_u, s_u = oracle.quantize_weight_convrot_e4m3(w, group=G)
+        s_uf = oracle.e4m3_decode(s_u)
+    else:
+        wp_u, s_u = oracle.quantize_weight_convrot(w, group=G)
+        s_uf = s_u
+    assert np.array_equal(s_c, s_u)
+    u = _unpack_independent(wp_c) & 15
+    assert np.array_equal(CB_UNIFORM[u], _unpack_independent(wp_u).astype(np.float32))
+    w8_c, sr_c = oracle.decode_w4a8_codebook(wp_c, s_c, CB_UNIFORM, G)
+    w8_u, sr_u = oracle.decode_w4a8(wp_u, s_uf, G)
+    assert np.array_equal(w8_c, w8_u) and np.array_equal(sr_c, sr_u)
+
+
+def test_codebook_prep_picks_nearest_entry_bruteforce():
+    # Unordered table with a repeated entry (index 11 repeats index 3, so it
+    # must never be chosen), a zero and an asymmetric range (cmax from a
+    # negative entry). Checked in float64 against every entry.
+    cb = np.array([0.9, -0.2, 0.05, 0.5, -1.3, 0.0, 0.3, -0.6, 1.1, -0.05, 0.7, 0.5, -0.9, 0.15, -0.35, 0.2],
+                  np.float32)
+    cmax = 1.3
+    rng = np.random.default_rng(71)
+    w = workloads.make_weight(rng, 6, 256)
+    G = 16
+    wp, s = oracle.quantize_weight_convrot_codebook(w, cb, group=G)
+    r = oracle.rotate_f32(w).astype(np.float64).reshape(6, -1, G)
+    amax = np.abs(r).max(axis=2)
+    np.testing.assert_allclose(s.astype(np.float64), amax / cmax, rtol=2 * 2 ** -24)
+    u = (_unpack_independent(wp) & 15).reshape(6, -1, G)
+    t = r / s.astype(np.float64)[..., None]
+    d = np.abs(t[..., None] - cb.astype(np.float64))          # [6, groups, G, 16]
+    chosen = np.take_along_axis(d, u[..., None], axis=3)[..., 0]
+    assert np.all(chosen <= d.min(axis=3) + 2 ** -20 * (1 + np.abs(t)))
+    assert not np.any(u == 11)
+    # every entry but the repeated one is used somewhere
+    assert set(np.unique(u)) == set(range(16)) - {11}
+
+
+def test_codebook_zero_group_takes_the_entry_nearest_zero():
+    cb = np.array([0.5, -0.25, 0.25, 1, -1, 0.75, -0.5, -0.75, 0.125, -0.125, 0.875, -0.875, 0.375, -0.375, 0.625,
+                   -0.625], np.float32)
+    w = np.zeros((2, 256), np.float32)
+    w[1, 128:] = np.linspace(-1, 1, 128, dtype=np.float32)
+    wp, s = oracle.quantize_weight_convrot_codebook(w, cb, group=128)
+    assert s[0].tolist() == [0, 0] and s[1, 0] == 0 and s[1, 1] > 0
+    u = _unpack_independent(wp) & 15
+    assert np.all(u[0] == 8) and np.all(u[1, :128] == 8)      # 0.125 and -0.125 tie: lower index 8
+    w8, srow = oracle.decode_w4a8_codebook(wp, s, cb, 128)
+    assert np.all(w8[0] == 0) and srow[0] == 0 and np.all(w8[1, :128] == 0)
+
+
+@pytest.mark.parametrize("G", [4, 8, 32, 128])
+def test_codebook_decode_approximates_dequantised_value(G):
+    cb = workloads.make_codebook()
+    rng = np.random.default_rng(72)
+    n, k = 32, 512
+    w = workloads.make_weight(rng, n, k)
+    w[:, 7] *= 25
+    wp, s = oracle.quantize_weight_convrot_codebook(w, cb, group=G)
+    w8, srow = oracle.decode_w4a8_codebook(wp, s, cb, G)
+    u = _unpack_independent(wp) & 15
+    cmax = float(np.abs(cb.astype(np.float64)).max())
+    np.testing.assert_allclose(srow.astype(np.float64), s.max(1).astype(np.float64) * cmax / 127,
+                               rtol=3 * 2 ** -24)
+    deq = cb.astype(np.float64)[u] * np.repeat(s.astype(np.float64), G, axis=1)
+    sr = srow.astype(np.float64)[:, None]
+    assert np.all(np.abs(w8.astype(np.float64) * sr - deq) <= sr * (0.5 + 1e-5))
+    assert np.all(np.abs(w8.astype(int)) <= 127)
+    # a decode that keeps 7 in place of cmax (the int4 formula) breaks the bound
+    w8_bad, srow_bad = oracle.decode_w4a8(wp, s, G)
+    srb = srow_bad.astype(np.float64)[:, None]
+    assert np.any(np.abs(w8_bad.astype(np.float64) * srb - deq) > srb * 0.5 + 1e-3 * np.abs(deq).max())
+
+
+def test_codebook_e4m3_scales_round_the_fp32_scales():
+    cb = workloads.make_codebook()
+    rng = np.random.default_rng(73)
+    w = workloads.make_weight(rng, 8, 512)
+    w[2] *= 1e-6
+    for G in (8, 64):
+        wp8, s8 = oracle.quantize_weight_convrot_codebook(w, cb, group=G, e4m3=True)
+        _, s32 = oracle.quantize_weight_convrot_codebook(w, cb, group=G)
+        assert np.array_equal(s8, oracle.e4m3_encode(s32))
+        # the codes are the nearest entries against the decoded byte
+        sd = oracle.e4m3_decode(s8).astype(np.float64)
+        r = oracle.rotate_f32(w).astype(np.float64).reshape(8, -1, G)
+        u = (_unpack_independent(wp8) & 15).reshape(8, -1, G)
+        ok = sd > 0
+        t = np.where(ok[..., None], r / np.where(ok, sd, 1)[..., None], 0.0)
+        d = np.abs(t[..., None] - cb.astype(np.float64))
+        chosen = np.take_along_axis(d, u[..., None], axis=3)[..., 0]
+        assert np.all(chosen <= d.min(axis=3) + 2 ** -20 * (1 + np.abs(t)))
+
+
+def test_codebook_linear_close_to_float():
+    lay = workloads.make_layer(16, 512, 64, seed=74)
+    cb = workloads.make_codebook()
+    wp, s = oracle.quantize_weight_convrot_codebook(lay.weights[0], cb, group=32)
+    y = workloads.bf16_bits_to_f32(oracle.linear_w4a8_codebook(lay.x_bf16, wp, s, cb, 32)).astype(np.float64)
+    ref = workloads.bf16_bits_to_f32(lay.x_bf16).astype(np.float64) @ lay.weights[0].astype(np.float64).T
+    rel = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+    assert rel < 0.15
 
 
 # --------------------------------------------------------------------------

@@ -17,6 +17,12 @@ transformer's hidden states and linear weights):
   ``[N, rank]`` rounded to bf16, both drawn from N(0, 0.02), so that the LoRA
   term is a visible fraction of the layer's output.
 
+* codebook (grouped W4A8 with a frozen 16-entry codebook): the pages give no
+  values, so the stand-in is the 16 quantiles of a standard normal at
+  (u + 1/2) / 16, divided by the largest, in ascending order of index: a
+  non-uniform, zero-free table that exercises everything uniform int4 codes
+  do not (no deterministic draw is involved).
+
 Draw order for one seed: outlier channel indices, then ``x``, then each weight
 in turn. The same host arrays feed the oracle and the GPU, so the two sides
 never need a shared RNG.
@@ -76,6 +82,14 @@ def make_lora(rng: np.random.Generator, rank: int, k: int, n: int):
     a = rng.normal(0.0, LORA_STD, (rank, k)).astype(np.float32)
     b = f32_to_bf16_bits(rng.normal(0.0, LORA_STD, (n, rank)).astype(np.float32))
     return a, b
+
+
+def make_codebook() -> np.ndarray:
+    """fp32 ``[16]``: normal quantiles at (u + 1/2) / 16 scaled to max |.| = 1."""
+    from statistics import NormalDist
+    nd = NormalDist()
+    q = np.array([nd.inv_cdf((u + 0.5) / 16.0) for u in range(16)], np.float64)
+    return (q / np.abs(q).max()).astype(np.float32)
 
 
 @dataclass
