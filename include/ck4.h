@@ -180,6 +180,48 @@ ck4_status ck4_gemm_w4a4_acc_i32(const int8_t *x_q, const int8_t *w_packed, int6
                                  int32_t *acc, int64_t ldacc, void *stream);
 
 /*
+ * W4A4 on the FP6 matrix cores (the same layer, [PR #63] Description, at
+ * twice the int8 matrix rate of gfx950, which has no int4 matrix
+ * instruction). Every int4 code q in [-7, 7] is exactly the FP6 E2M3 value
+ * q / 8 (a subnormal: sign bit 5, |q| in bits 0-2), products of two codes
+ * are q_a q_b / 64, and the fp32 accumulator holds 64 x the integer sum
+ * exactly for k <= 131072, so ck4_linear_w4a4_fp6 gives the same bits as
+ * ck4_linear_w4a4 on the same codes and scales. The codes take 6 bits
+ * instead of 4 (1.5x the bytes): this is the layout for large m; the int4
+ * layout stays the one for weight-streaming (small m) calls.
+ *
+ * FP6 operand layout ("q6", ck4_fp6_bytes(rows, k) bytes, 16-byte aligned):
+ * rows padded to a multiple of 16 (the padding rows are never written by the
+ * quantisers and never reach an output), k a multiple of 128. The 16-row x
+ * 128-k block (r / 16, k / 128) is 1536 bytes at ((r / 16) * (k / 128) +
+ * k / 128) * 1536; in it, row i = r % 16 and k group g = (k % 128) / 32 own
+ * the 24 bytes at 24 (16 g + i), holding the codes of k % 32 = t at bits
+ * 6 t, least significant bit first (the MFMA operand register image).
+ *
+ * ck4_rotate_quantize_act_fp6, ck4_quantize_weight_convrot_fp6: the codes and
+ *   scales of ck4_rotate_quantize_act(bits = 4) and
+ *   ck4_quantize_weight_convrot(group = 0) (same rotation, scale and
+ *   rounding), written as q6. x bf16 [m, ldx] / w fp32 [n, ldw], 16-byte
+ *   aligned rows; scales fp32 [rows].
+ * ck4_linear_w4a4_fp6: y as ck4_linear_w4a4, from q6 operands.
+ * ck4_gemm_w4a4_fp6_acc_i32: its integer accumulators (int32, as
+ *   ck4_gemm_w4a4_acc_i32).
+ * Unsupported: k % 128 != 0; k > 16384 for the quantisers, k > 131072 for the
+ * GEMM; other errors as the int4 calls. ck4_fp6_bytes returns 0 for k not a
+ * multiple of 128.
+ */
+size_t ck4_fp6_bytes(int64_t rows, int64_t k);
+ck4_status ck4_rotate_quantize_act_fp6(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                       uint8_t *x_q6, float *x_scales, void *stream);
+ck4_status ck4_quantize_weight_convrot_fp6(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                           uint8_t *w_q6, float *w_scales, void *stream);
+ck4_status ck4_linear_w4a4_fp6(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
+                               const float *w_scales, const float *bias, int64_t m, int64_t n, int64_t k,
+                               uint16_t *y, int64_t ldy, void *stream);
+ck4_status ck4_gemm_w4a4_fp6_acc_i32(const uint8_t *x_q6, const uint8_t *w_q6, int64_t m, int64_t n, int64_t k,
+                                     int32_t *acc, int64_t ldacc, void *stream);
+
+/*
  * Grouped int4 -> int8 weight decode of rows [n0, n0 + nc) ([PR #97] What
  * this adds: grouped int4 -> int8 weight decode; Chunk sizing: one chunk of
  * output columns at a time).

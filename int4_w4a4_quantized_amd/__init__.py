@@ -61,6 +61,11 @@ SIGNATURES = {
     "ck4_dequant_w4a8_codebook": ([_P, _P, _I, _PF, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
     "ck4_linear_w4a8_codebook": ([_P, _P, _P, _P, _I, _PF, _I64, _I64, _I64, _I, _P, _I64, _I64, _P,
                                   ctypes.c_size_t, _P], _I),
+    "ck4_fp6_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "ck4_rotate_quantize_act_fp6": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
+    "ck4_quantize_weight_convrot_fp6": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
+    "ck4_linear_w4a4_fp6": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_gemm_w4a4_fp6_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_lora_prepare_down": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_lora_prepare_up": ([_P, _I64, _I64, _I64, _P, _P], _I),
     "ck4_lora_down": ([_P, _I64, _I64, _I64, _I, _P, _I64, ctypes.c_float, _P, _P], _I),
@@ -329,6 +334,72 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
 
 def _rows16(n: int) -> int:
     return (n + 15) // 16 * 16
+
+
+# FP6 operand path (large m): int4 codes held as FP6 E2M3 q / 8 in the MFMA
+# operand layout, uint8 [rows16, k * 3 / 4]; bit-identical results to the
+# int4 path at twice the matrix rate.
+
+def fp6_bytes(rows: int, k: int) -> int:
+    return int(lib().ck4_fp6_bytes(rows, k))
+
+
+def rotate_quantize_act_fp6(x: torch.Tensor, rot_block: int = 128, out=None, scales=None):
+    """bf16 [m, k] -> (uint8 [rows16(m), 3k/4] FP6 codes, fp32 [m] scales)."""
+    _need(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    if out is None:
+        out = torch.empty((_rows16(m), k * 3 // 4), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m,), dtype=torch.float32, device=x.device)
+    if out.numel() < fp6_bytes(m, k):
+        raise ValueError("FP6 output buffer too small")
+    _check("ck4_rotate_quantize_act_fp6",
+           lib().ck4_rotate_quantize_act_fp6(_ptr(x), m, k, x.stride(0), rot_block, _ptr(out), _ptr(scales),
+                                             _stream(x.device)))
+    return out, scales
+
+
+def quantize_weight_convrot_fp6(w: torch.Tensor, rot_block: int = 128):
+    """fp32 [n, k] -> (uint8 [rows16(n), 3k/4] FP6 codes, fp32 [n] row scales)."""
+    _need(w, torch.float32, "w", 2)
+    n, k = w.shape
+    wq = torch.empty((_rows16(n), k * 3 // 4), dtype=torch.uint8, device=w.device)
+    ws = torch.empty((n,), dtype=torch.float32, device=w.device)
+    _check("ck4_quantize_weight_convrot_fp6",
+           lib().ck4_quantize_weight_convrot_fp6(_ptr(w), n, k, w.stride(0), rot_block, _ptr(wq), _ptr(ws),
+                                                 _stream(w.device)))
+    return wq, ws
+
+
+def linear_w4a4_fp6(x_q6, x_scales, w_q6, w_scales, bias=None, out=None, m: int | None = None,
+                    n: int | None = None):
+    """W4A4 GEMM + epilogue from FP6 operands -> bf16 [m, n] (m, n default to the scale lengths)."""
+    m = x_scales.numel() if m is None else m
+    n = w_scales.numel() if n is None else n
+    k = x_q6.shape[1] * 4 // 3
+    if out is None:
+        out = _out_bf16(m, n, x_q6.device)
+    _check("ck4_linear_w4a4_fp6",
+           lib().ck4_linear_w4a4_fp6(_ptr(x_q6), _ptr(x_scales), _ptr(w_q6), _ptr(w_scales), _ptr(bias), m, n, k,
+                                     _ptr(out), out.stride(0), _stream(x_q6.device)))
+    return out
+
+
+def gemm_w4a4_fp6_acc_i32(x_q6, w_q6, m: int, n: int):
+    """Integer accumulators of the FP6 GEMM -> int32 [m, n]."""
+    k = x_q6.shape[1] * 4 // 3
+    acc = torch.empty((m, (n + 3) // 4 * 4), dtype=torch.int32, device=x_q6.device)
+    _check("ck4_gemm_w4a4_fp6_acc_i32",
+           lib().ck4_gemm_w4a4_fp6_acc_i32(_ptr(x_q6), _ptr(w_q6), m, n, k, _ptr(acc), acc.stride(0),
+                                           _stream(x_q6.device)))
+    return acc[:, :n]
+
+
+def w4a4_linear_fp6(x: torch.Tensor, w_q6: torch.Tensor, w_scales: torch.Tensor, bias=None, rot_block: int = 128):
+    """The whole layer on the FP6 path: rotate + quantise x to FP6 codes, then the GEMM + epilogue."""
+    x_q6, sx = rotate_quantize_act_fp6(x, rot_block)
+    return linear_w4a4_fp6(x_q6, sx, w_q6, w_scales, bias)
 
 
 def lora_prepare_down(a: torch.Tensor, rot_block: int = 128):

@@ -16,7 +16,7 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libck4.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["rotate_quant.hip", "gemm.hip", "w4a8_decode.hip", "lora.hip", "ck4_api.cpp"]
+SOURCES = ["rotate_quant.hip", "gemm.hip", "gemm_fp6.hip", "w4a8_decode.hip", "lora.hip", "ck4_api.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

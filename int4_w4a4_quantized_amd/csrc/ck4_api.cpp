@@ -89,7 +89,7 @@ constexpr int64_t kMaxRows = 0x7FFFFFFF;
 
 ck4_status check_rot(const char *fn, int64_t k, int rot_block) {
     if (!pow2(rot_block) || rot_block < 16 || rot_block > 1024)
-        return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d (need a power of two in [4, 1024])", fn, rot_block);
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rot_block=%d (need a power of two in [16, 1024])", fn, rot_block);
     if (k % rot_block != 0)
         return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of rot_block=%d", fn, (long long)k,
                     rot_block);
@@ -284,6 +284,63 @@ ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8
                            void *stream) {
     return gemm_entry("ck4_linear_w8a8", false, x_q8, x_scales, w8, w_scales, bias, m, n, k, false, y, ldy,
                       stream);
+}
+
+size_t ck4_fp6_bytes(int64_t rows, int64_t k) {
+    if (rows <= 0 || k <= 0 || k % 128 != 0) return 0;
+    return (size_t)((rows + 15) / 16 * 16) * (size_t)(k / 128) * 96;
+}
+
+static ck4_status quantize_fp6(const char *fn, const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx,
+                               int rot_block, uint8_t *q6, float *scales, void *stream) {
+    const size_t esz = in_kind == 0 ? 2 : 4;
+    if (!x || !q6 || !scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (rows <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: rows and k must be positive", fn);
+    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
+    if (!aligned(x, 16) || ((size_t)ldx * esz) % 16 != 0)
+        return fail(CK4_ERR_INVALID, "%s: input/ldx not 16-byte aligned", fn);
+    if (!aligned(q6, 16) || !aligned(scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
+    if (rows > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: too many rows", fn);
+    if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_rotate_quant(x, in_kind, rows, k, ldx, rot_block, 4, 0, q6, 0, scales,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_rotate_quantize_act_fp6(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                       uint8_t *x_q6, float *x_scales, void *stream) {
+    return quantize_fp6("ck4_rotate_quantize_act_fp6", x, 0, m, k, ldx, rot_block, x_q6, x_scales, stream);
+}
+
+ck4_status ck4_quantize_weight_convrot_fp6(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                           uint8_t *w_q6, float *w_scales, void *stream) {
+    return quantize_fp6("ck4_quantize_weight_convrot_fp6", w, 1, n, k, ldw, rot_block, w_q6, w_scales, stream);
+}
+
+static ck4_status gemm_fp6_entry(const char *fn, const uint8_t *a, const float *sa, const uint8_t *b,
+                                 const float *sb, const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32,
+                                 void *y, int64_t ldy, void *stream) {
+    if (!a || !b || !y || (!out_i32 && (!sa || !sb))) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, out_i32 ? 16 : 8)) return s;
+    if (!aligned(a, 16) || !aligned(b, 16)) return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
+    if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
+    if (ck4_status s = check_device(fn)) return s;
+    return launched(fn, ck4::launch_gemm_fp6(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+ck4_status ck4_linear_w4a4_fp6(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
+                               const float *w_scales, const float *bias, int64_t m, int64_t n, int64_t k,
+                               uint16_t *y, int64_t ldy, void *stream) {
+    return gemm_fp6_entry("ck4_linear_w4a4_fp6", x_q6, x_scales, w_q6, w_scales, bias, m, n, k, false, y, ldy,
+                          stream);
+}
+
+ck4_status ck4_gemm_w4a4_fp6_acc_i32(const uint8_t *x_q6, const uint8_t *w_q6, int64_t m, int64_t n, int64_t k,
+                                     int32_t *acc, int64_t ldacc, void *stream) {
+    return gemm_fp6_entry("ck4_gemm_w4a4_fp6_acc_i32", x_q6, nullptr, w_q6, nullptr, nullptr, m, n, k, true, acc,
+                          ldacc, stream);
 }
 
 }  // extern "C"

@@ -36,7 +36,9 @@ struct WeightOpts {
 //   in_kind   0: bf16 input, 1: fp32 input
 //   out_kind  0: packed int4 (+ scales), 1: int8 codes (+ scales), 2: fp32 rotation
 //             (bf16 input only), 3: the rotation rounded to bf16, in MFMA fragment
-//             order (rows a multiple of 16, k a multiple of 32; ldo unused)
+//             order (rows a multiple of 16, k a multiple of 32; ldo unused), 4: int4
+//             codes as FP6 E2M3 in the f8f6f4 MFMA operand image (group 0, k a
+//             multiple of 128, rows padded to 16; ldo unused; see launch_gemm_fp6)
 //   group     0: one scale per row; > 0: one scale per `group` elements (int4 only)
 //   scales    fp32, or E4M3 bytes when wo.scale_e4m3
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
@@ -65,6 +67,16 @@ struct LoraUp {
 hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *sa, const float *sb,
                        const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy,
                        hipStream_t stream, LoraUp lora = LoraUp{});
+
+// The same GEMM and epilogue on FP6 operands: a and b hold the int4 codes as
+// FP6 E2M3 values q / 8 in the f8f6f4 MFMA operand image (rotate_quant
+// out_kind 4): rows padded to 16, k a multiple of 128, 16-row x 128-k blocks
+// of 1536 bytes at ((r / 16) * (k / 128) + k / 128) * 1536, lane image
+// 16 g + i (row i, k group g) of 24 bytes at 24 (16 g + i), code of k =
+// 32 g + t at bits 6 t. Bit-identical to launch_gemm(s4 = true) on the same
+// codes.
+hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
+                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream);
 
 // b (bf16 [n, rank], row stride ldb) to fragment order, zero rows padding n
 // to a multiple of 16.

@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include "ck4_kernels.h"
+#include "tile_map.h"
 
 namespace ck4 {
 namespace {
@@ -125,23 +126,8 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
     static_assert(BM % 8 == 0 && BN % 8 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "bad tile");
     __shared__ __attribute__((aligned(1024))) uint4 smem[2 * STAGE / 16];
 
-    // Tile order. Ids are dealt round-robin to the 8 XCDs (id & 7). With
-    // xcd_m > 0 the tile grid is cut into xcd_m x (8 / xcd_m) blocks, one per
-    // XCD, walked row-major inside, so an XCD's L2 holds only its block's A
-    // rows and B rows; otherwise each XCD walks a contiguous run of tiles.
-    int tile = blockIdx.x;
     int tm, tn;
-    if (xcd_m > 0) {
-        const int xcd_n = 8 / xcd_m;
-        const int x = tile & 7, li = tile >> 3;
-        const int bm = (tiles_total / tiles_n) / xcd_m, bn = tiles_n / xcd_n;
-        tm = (x / xcd_n) * bm + li / bn;
-        tn = (x % xcd_n) * bn + li % bn;
-    } else {
-        if ((tiles_total & 7) == 0) tile = (tile & 7) * (tiles_total >> 3) + (tile >> 3);
-        tm = tile / tiles_n;
-        tn = tile - tm * tiles_n;
-    }
+    tile_coords(blockIdx.x, tiles_n, tiles_total, xcd_m, tm, tn);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
 
@@ -384,24 +370,6 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
             }
         }
     }
-}
-
-// Shape of the per-XCD tile blocks: xcd_m rows of blocks by 8 / xcd_m
-// columns, chosen to minimise the A and B rows one XCD fetches (0: the grid
-// does not split evenly; fall back to contiguous runs).
-int pick_xcd_m(int tiles_m, int tiles_n, int bm, int bn) {
-    int best = 0;
-    long best_rows = 0;
-    for (int xm = 1; xm <= 8; xm *= 2) {
-        const int xn = 8 / xm;
-        if (tiles_m % xm != 0 || tiles_n % xn != 0) continue;
-        const long rows = (long)(tiles_m / xm) * bm + (long)(tiles_n / xn) * bn;
-        if (best == 0 || rows < best_rows) {
-            best = xm;
-            best_rows = rows;
-        }
-    }
-    return best;
 }
 
 template <bool S4, int BM, int BN, int WGM, int WGN, int WPE>

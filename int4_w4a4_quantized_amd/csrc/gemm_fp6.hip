@@ -1,0 +1,308 @@
+// W4A4 GEMM on the gfx950 FP6 matrix cores, with the rank-one epilogue.
+//
+// What it computes is the s4.s4 GEMM of "[PR #63] int4_tensorwise: W4A4
+// layout (+ConvRot) with fused CUDA kernels" (Description: carried integer
+// accumulators, |acc| <= 49 K, per-row and per-column scales applied once
+// after the K loop):
+//   acc[m, n] = sum_k qa[m, k] * qb[n, k]
+//   y[m, n]   = bf16(((float)acc * sa[m]) * sb[n] (+ bias[n]))
+// bit for bit as the int8-MFMA kernel computes it, at twice its matrix rate.
+//
+// Why it is exact. Every int4 code q in [-7, 7] is exactly the FP6 E2M3
+// value q / 8: exponent field 0 (a subnormal), mantissa |q|, sign bit 5. The
+// product of two codes is q_a q_b / 64, and each partial sum of
+// v_mfma_scale_f32_16x16x128_f8f6f4 (block scales 2^0) is an integer multiple
+// of 2^-6 of magnitude <= 49 K / 64, which fp32 holds exactly for K <=
+// 131072 (49 * 131072 < 2^24); so the fp32 accumulator is acc / 64 exactly,
+// whatever the order of the additions, and acc * 64 is the integer
+// accumulator as a float, as the int8 kernel converts it.
+//
+// Operand layout (FP6 fragment order, written by the quantiser's FP6 output):
+// rows padded to a multiple of 16, K a multiple of 128; the 16-row x 128-k
+// block (r / 16, k / 128) is 1536 bytes at ((r / 16) * (K / 128) + k / 128) *
+// 1536, holding the 64 lane images of the MFMA operand: lane l = 16 g + i
+// (row i, k group g) has 24 bytes at 24 l with the 32 codes of k = 128 kb +
+// 32 g + t at bits 6 t, least significant bit first. A block is therefore
+// one contiguous copy, and a fragment read (lane l reads 24 bytes at 24 l)
+// touches every LDS bank once per 16 lanes.
+//
+// Tiling: 288 x 192 output tiles (one per CU on the 4608 x 3072 layer), 8
+// waves of 144 x 48 (9 x 3 MFMA fragments; the first MFMA operand is the
+// weight fragment, so each lane's 4 accumulators are 4 consecutive output
+// columns of one row). One k step is 128 k: 30 blocks, 45 KB, copied
+// global -> LDS with buffer_load ... lds into a ring of 3 stages, two steps
+// ahead of the MFMAs. Rows past the padded operands read as zeros through the
+// buffer descriptors' range check (the block offset is in the copy's vector
+// offset).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ck4_kernels.h"
+#include "tile_map.h"
+
+namespace ck4 {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kBlk = 1536;          // bytes of one 16-row x 128-k operand block
+constexpr int kBlkChunks = kBlk / 16;  // 16-byte copy chunks per block
+
+// s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0.
+constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// One lane's 24-byte operand image (8-byte aligned) as the MFMA's register
+// operand; FP6 reads the first six registers.
+__device__ __forceinline__ v8i load_frag(const uint8_t *p) {
+    const uint2 a = *reinterpret_cast<const uint2 *>(p);
+    const uint2 b = *reinterpret_cast<const uint2 *>(p + 8);
+    const uint2 c = *reinterpret_cast<const uint2 *>(p + 16);
+    return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+}
+
+__device__ __forceinline__ v4f mfma_fp6(v8i w, v8i x, v4f acc) {
+    // cbsz = blgp = 2: both operands FP6 E2M3; scale bytes 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, 2, 2, 0, 127, 0, 127);
+}
+
+template <int BM, int BN, int WGM, int WGN, int WPE, int NST, bool OUT_I32>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
+                          amdgpu_waves_per_eu(WPE, WPE))) void
+gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const float *__restrict__ sa,
+                const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int kb,
+                void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m) {
+    constexpr int NW = WGM * WGN;
+    constexpr int WTM = BM / WGM;
+    constexpr int WTN = BN / WGN;
+    constexpr int FM = WTM / 16;
+    constexpr int FN = WTN / 16;
+    constexpr int BLK_A = BM / 16;
+    constexpr int BLK_B = BN / 16;
+    constexpr int STAGE = (BLK_A + BLK_B) * kBlk;
+    constexpr int NINS_A = BLK_A * kBlkChunks / 64;  // copy instructions (64 x 16 bytes) per step
+    constexpr int NINS = (BLK_A + BLK_B) * kBlkChunks / 64;
+    constexpr int PER_WAVE = (NINS + NW - 1) / NW;
+    constexpr int LD = BN + 8;  // bf16 epilogue tile row pitch
+    constexpr int LDS_BYTES = NST * STAGE > BM * LD * 2 ? NST * STAGE : BM * LD * 2;
+    static_assert(BM % 16 == 0 && BN % 16 == 0 && WTM % 16 == 0 && WTN % 16 == 0, "bad tile");
+    static_assert((BLK_A * kBlkChunks) % 64 == 0 && (BLK_B * kBlkChunks) % 64 == 0, "bad copy split");
+    static_assert(NST >= 2, "need two stages");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+
+    int tm, tn;
+    tile_coords(blockIdx.x, tiles_n, tiles_total, xcd_m, tm, tn);
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / WGN;
+    const int wn = wave - wm * WGN;
+
+    // the row blocks of this tile that exist in the (16-row padded) operands
+    const int64_t rowblk = (int64_t)kb * kBlk;
+    const int blk_a = min(BLK_A, (M + 15) / 16 - m0 / 16);
+    const int blk_b = min(BLK_B, (N + 15) / 16 - n0 / 16);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(A) + (int64_t)(m0 / 16) * rowblk, (short)0, (int)(blk_a * rowblk), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(B) + (int64_t)(n0 / 16) * rowblk, (short)0, (int)(blk_b * rowblk), 0x00020000);
+
+    // Copy plan of one step: 16-byte chunk c = 64 q + lane of the stage,
+    // block c / 96 (A blocks first), byte 16 (c % 96) of it. Every wave issues
+    // PER_WAVE instructions so that its vmcnt arithmetic is uniform; the
+    // surplus slots repeat an instruction of another wave (same bytes to the
+    // same place).
+    uint32_t voff[PER_WAVE];
+    int qi[PER_WAVE];
+#pragma unroll
+    for (int t = 0; t < PER_WAVE; ++t) {
+        int q = t * NW + wave;
+        if (q >= NINS) q -= NW;
+        qi[t] = q;
+        const bool is_a = q < NINS_A;
+        const int c = (is_a ? q : q - NINS_A) * 64 + lane;
+        voff[t] = (uint32_t)(c / kBlkChunks) * (uint32_t)rowblk + (uint32_t)((c % kBlkChunks) * 16);
+    }
+    auto issue_stage = [&](uint8_t *dst, int s) {
+#pragma unroll
+        for (int t = 0; t < PER_WAVE; ++t) {
+            const bool is_a = qi[t] < NINS_A;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(is_a ? ra : rb,
+                                                     (__attribute__((address_space(3))) void *)(dst + qi[t] * 1024),
+                                                     16, (int)voff[t], s * kBlk, 0, 0);
+        }
+    };
+
+    v4f acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int frow = lane & 15;
+    const int fgrp = lane >> 4;
+    float sa_r[FM], sb_r[FN][4];
+    if constexpr (!OUT_I32) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) sa_r[j] = sa[min(m0 + wm * WTM + j * 16 + frow, M - 1)];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sb_r[i][r] = sb[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
+    }
+
+    // One step: the FN weight fragments, then the FM activation fragments,
+    // each read from LDS once and fed to FN MFMAs.
+    const int a_off = wm * FM * kBlk + lane * 24;
+    const int b_off = (BLK_A + wn * FN) * kBlk + lane * 24;
+    auto compute_stage = [&](const uint8_t *src) {
+        v8i wf[FN];
+#pragma unroll
+        for (int i = 0; i < FN; ++i) wf[i] = load_frag(src + b_off + i * kBlk);
+        v8i xn = load_frag(src + a_off);
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const v8i xf = xn;
+            if (j + 1 < FM) xn = load_frag(src + a_off + (j + 1) * kBlk);
+#pragma unroll
+            for (int i = 0; i < FN; ++i) acc[i][j] = mfma_fp6(wf[i], xf, acc[i][j]);
+        }
+    };
+
+    // The copy into one slot and the reads from another go through
+    // __restrict__ parameters of an inlined function, so the compiler knows
+    // they never alias and does not make the fragment reads wait for the copy.
+    auto body = [&](uint8_t *__restrict__ dst, const uint8_t *__restrict__ src, int s) {
+        if (s + NST - 1 < kb) issue_stage(dst, s + NST - 1);
+        compute_stage(src);
+    };
+
+    // Ring of NST stages: the copy of step s + NST - 1 is issued once every
+    // wave has finished reading step s - 1 (the barrier), into that step's
+    // slot; before the barrier each wave waits for its own copies of step s,
+    // leaving the later steps' copies in flight.
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p)
+        if (p < kb) issue_stage(smem + p * STAGE, p);
+    for (int s = 0; s < kb; ++s) {
+        // This wave's copies of step s have landed (the later steps' copies
+        // may still be in flight) and its LDS reads of step s - 1 are done;
+        // then a bare s_barrier (__syncthreads would also drain the copies
+        // in flight) and a compiler-only fence, so that no LDS read of step s
+        // is scheduled above it.
+        const int ahead = min(NST - 2, kb - 1 - s);  // steps issued after s
+        if constexpr (NST == 2) {
+            __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+        } else if constexpr (NST == 3) {
+            if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PER_WAVE));
+            else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+        } else {
+            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * PER_WAVE));
+            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PER_WAVE));
+            else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+        }
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        body(smem + ((s + NST - 1) % NST) * STAGE, smem + (s % NST) * STAGE, s);
+    }
+
+    if constexpr (OUT_I32) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int m = m0 + wm * WTM + j * 16 + frow;
+            if (m >= M) continue;
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int nb = n0 + wn * WTN + i * 16 + 4 * fgrp;
+                if (nb >= N) continue;
+                int a4[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a4[r] = (int)(acc[i][j][r] * 64.0f);
+                int32_t *yr = reinterpret_cast<int32_t *>(Y) + (int64_t)m * ldy + nb;
+                if (nb + 3 < N) {
+                    *reinterpret_cast<int4 *>(yr) = make_int4(a4[0], a4[1], a4[2], a4[3]);
+                } else {
+                    for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = a4[r];
+                }
+            }
+        }
+    } else {
+        // Rank-one epilogue through LDS, so the tile leaves as whole rows:
+        // y = bf16((acc * sa[m]) * sb[n] (+ bias[n])) with acc = 64 x the fp32
+        // accumulator (exact), into a [BM][BN + 8] bf16 tile, then 16-byte
+        // row-contiguous stores.
+        uint16_t *tile_lds = reinterpret_cast<uint16_t *>(smem);
+        __syncthreads();  // every wave has finished reading the last stage
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int ml = wm * WTM + j * 16 + frow;
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+                const int nl = wn * WTN + i * 16 + 4 * fgrp;
+                uint16_t o[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a = acc[i][j][r] * 64.0f;
+                    float v = (a * sa_r[j]) * sb_r[i][r];
+                    if (bias) v = v + bias[min(n0 + nl + r, N - 1)];
+                    o[r] = f32_to_bf16(v);
+                }
+                *reinterpret_cast<uint2 *>(tile_lds + ml * LD + nl) =
+                    make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = BN / 8;  // 16-byte chunks per tile row
+        for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+            const int r = c / CPR;
+            const int cn = (c - r * CPR) * 8;
+            const int m = m0 + r;
+            const int n = n0 + cn;
+            if (m >= M || n >= N) continue;
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile_lds + r * LD + cn);
+            uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + n;
+            if (n + 7 < N && ((reinterpret_cast<uintptr_t>(yr) & 15) == 0)) {
+                *reinterpret_cast<uint4 *>(yr) = v;
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    if (n + t < N) yr[t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+            }
+        }
+    }
+}
+
+template <int BM, int BN, int WGM, int WGN, int WPE, int NST>
+hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
+                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+    const int kb = (int)(k / 128);
+    const int tiles_m = (int)((m + BM - 1) / BM);
+    const int tiles_n = (int)((n + BN - 1) / BN);
+    const int total = tiles_m * tiles_n;
+    const int xcd_m = pick_xcd_m(tiles_m, tiles_n, BM, BN);
+    dim3 grid((unsigned)total), block(64 * WGM * WGN);
+    if (out_i32)
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, true><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m);
+    else
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
+                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+    return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+}
+
+}  // namespace ck4

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
         }
         return;
     } else {
-        const float qmax = OUT == 0 ? 7.0f : 127.0f;
+        const float qmax = OUT == 0 || OUT == 4 ? 7.0f : 127.0f;
         constexpr int BIAS = OUT == 0 ? 8 : 0;
         float s_row = 0.0f, y_row = 0.0f;
         bool fast_row = false;
@@ -246,6 +246,36 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             fast_row = s_row >= 0x1p-120f && s_row <= 0x1p120f;
             y_row = fast_row ? 1.0f / s_row : 0.0f;
             if (tid == 0) scales[row] = s_row;
+        }
+        if constexpr (OUT == 4) {
+            // int4 codes as FP6 E2M3 values q/8 (sign bit 5, |q| in bits 0-2: a
+            // subnormal, exact), in the MFMA operand image: a 16-value chunk is
+            // 96 bits at byte 12 (ch & 1) of lane image 16 ((ch >> 1) & 3) + (row & 15)
+            // of block (row / 16, ch / 8), 1536 bytes per block, fields LSB-first.
+            uint8_t *o = reinterpret_cast<uint8_t *>(out) + (row >> 4) * (int64_t)(k / 128) * 1536 + (row & 15) * 24;
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) {
+                const int ch = tid + j * nthreads;
+                if (ch >= nchunks) continue;
+                uint32_t c[kElems];
+                if (fast_row) {
+#pragma unroll
+                    for (int i = 0; i < kElems; ++i) c[i] = code_fast<0>(fabsf(v[j][i]), s_row, y_row) & 7u;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kElems; ++i) c[i] = code_exact<0>(fabsf(v[j][i]), s_row, qmax);
+                }
+#pragma unroll
+                for (int i = 0; i < kElems; ++i) c[i] |= (__float_as_uint(v[j][i]) >> 26) & 0x20u;
+                const uint32_t d0 = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18) | (c[4] << 24) | (c[5] << 30);
+                const uint32_t d1 =
+                    (c[5] >> 2) | (c[6] << 4) | (c[7] << 10) | (c[8] << 16) | (c[9] << 22) | (c[10] << 28);
+                const uint32_t d2 =
+                    (c[10] >> 4) | (c[11] << 2) | (c[12] << 8) | (c[13] << 14) | (c[14] << 20) | (c[15] << 26);
+                uint8_t *dst = o + (int64_t)(ch >> 3) * 1536 + ((ch >> 1) & 3) * 16 * 24 + (ch & 1) * 12;
+                *reinterpret_cast<uint3 *>(dst) = make_uint3(d0, d1, d2);
+            }
+            return;
         }
 #pragma unroll
         for (int j = 0; j < NCH; ++j) {
@@ -411,6 +441,9 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
                             wo, stream);
     else if (out_kind == 3)
         launch_mode<TIn, 3>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
+                            wo, stream);
+    else if (out_kind == 4)
+        launch_mode<TIn, 4>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
                             wo, stream);
     else if constexpr (sizeof(TIn) == 4)
         return hipErrorInvalidValue;  // fp32 rows: codes or the bf16 rotation only

@@ -116,6 +116,33 @@ def test_w4a8_validation(L):
     assert l8(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 192, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
 
 
+def test_fp6_validation_and_layout_helper(L):
+    f = L.ck4_rotate_quantize_act_fp6
+    assert f(FAKE, 4, 320, 320, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 128
+    assert f(NULL, 4, 256, 256, 128, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, 4, 256, 256, 128, ODD, FAKE, NULL) == ck.CK4_ERR_INVALID       # q6 alignment
+    w = L.ck4_quantize_weight_convrot_fp6
+    assert w(FAKE, 4, 256, 200, 128, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID      # ldw < k
+    g = L.ck4_linear_w4a4_fp6
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 320, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 128
+    assert g(ODD, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
+    a = L.ck4_gemm_w4a4_fp6_acc_i32
+    assert a(FAKE, FAKE, 8, 8, 256, ODD, 8, NULL) == ck.CK4_ERR_INVALID
+    assert L.ck4_fp6_bytes(17, 256) == 32 * 192 and L.ck4_fp6_bytes(16, 100) == 0
+    import fp6_layout
+    # worked example: codes 1, -1, 7, -7 are FP6 codes 0x01, 0x21, 0x07, 0x27,
+    # packed LSB first into 24 bits: 0x9C7841
+    q = np.zeros((16, 128), np.int64)
+    q[0, :4] = [1, -1, 7, -7]
+    b = fp6_layout.encode(q)
+    assert b[:3].tolist() == [0x41, 0x78, 0x9C] and not b[3:].any()
+    # row 5, k 40 (k group 1, field 8) lands in image 16 + 5 at bit 48
+    q2 = np.zeros((16, 128), np.int64)
+    q2[5, 40] = -3
+    b2 = fp6_layout.encode(q2)
+    assert np.flatnonzero(b2).tolist() == [21 * 24 + 6] and b2[21 * 24 + 6] == 0x23
+
+
 def test_codebook_validation(L):
     cb = (ctypes.c_float * 16)(*[float(i - 8) / 8 for i in range(16)])
     zero = (ctypes.c_float * 16)()

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import fp6_layout
 import frag_layout
 import oracle
 import workloads
@@ -286,6 +287,96 @@ def test_e4m3_linear_fused_chunked_single_equal_and_match_oracle(ck, m, n, k):
     yc = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, s8d, 128, 256))
     assert np.array_equal(y0, y1) and np.array_equal(y0, yc)
     assert_bf16_close(y0, oracle.linear_w4a8_grouped_e4m3(xb, wp_ref, s8_ref))
+
+
+# --------------------------------------------------------------------------
+# The FP6 operand path (int4 codes as FP6 E2M3 q / 8 on the f8f6f4 matrix cores)
+
+FP6_CASES = [
+    (64, 256, 256), (1, 1, 128), (3, 17, 384), (17, 3, 512), (130, 200, 768), (16, 64, 3072),
+    (64, 130, 1024), (257, 129, 640), (33, 77, 256), (8, 1000, 512), (300, 8, 1280), (577, 385, 1152),
+]
+
+
+@pytest.mark.parametrize("m,k,rb", [(64, 256, 128), (17, 384, 128), (5, 3072, 128), (3, 12288, 128),
+                                    (9, 1024, 16), (9, 2048, 256), (2, 16384, 128)])
+def test_fp6_activation_codes_bitexact(ck, m, k, rb):
+    xb = act(m, k, 2000 + m + k)
+    xb[0] = 0                          # an all-zero row: scale 0, codes 0
+    q6, sx = ck.rotate_quantize_act_fp6(dev_bf16(xb), rb)
+    q_ref, s_ref = oracle.rotate_quantize_act(xb, rb, 4)
+    assert np.array_equal(host(sx).view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(fp6_layout.decode(host(q6), m, k), oracle.unpack_int4(q_ref))
+
+
+@pytest.mark.parametrize("n,k,rb", [(64, 256, 128), (300, 3072, 128), (5, 12288, 128), (33, 1024, 64)])
+def test_fp6_weight_codes_bitexact(ck, n, k, rb):
+    rng = np.random.default_rng(2100 + n)
+    w = workloads.make_weight(rng, n, k)
+    w[1] = 0
+    w[2, 5] = 3.0
+    q6, ws = ck.quantize_weight_convrot_fp6(torch.from_numpy(w).cuda(), rb)
+    wp_ref, ws_ref = oracle.quantize_weight_convrot(w, rb, 0)
+    assert np.array_equal(host(ws).view(np.uint32), ws_ref.view(np.uint32))
+    assert np.array_equal(fp6_layout.decode(host(q6), n, k), oracle.unpack_int4(wp_ref))
+
+
+def _fp6_operands(ck, m, n, k, seed):
+    """Oracle codes and scales, and the same codes uploaded in the FP6 layout."""
+    rng = np.random.default_rng(seed)
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    xq, sx = oracle.rotate_quantize_act(xb, 128, 4)
+    wp, ws = oracle.quantize_weight_convrot(w, 128, 0)
+    xq6 = torch.from_numpy(fp6_layout.encode(oracle.unpack_int4(xq)).reshape(-1, k * 3 // 4)).cuda()
+    wq6 = torch.from_numpy(fp6_layout.encode(oracle.unpack_int4(wp)).reshape(-1, k * 3 // 4)).cuda()
+    return xb, xq, sx, wp, ws, xq6, wq6
+
+
+@pytest.mark.parametrize("m,n,k", FP6_CASES)
+def test_fp6_gemm_acc_i32_bitexact(ck, m, n, k):
+    _, xq, _, wp, _, xq6, wq6 = _fp6_operands(ck, m, n, k, 2200 + m + n)
+    acc = host(ck.gemm_w4a4_fp6_acc_i32(xq6, wq6, m, n))
+    assert np.array_equal(acc, oracle.gemm_acc(xq, wp, k, bits=4))
+
+
+@pytest.mark.parametrize("m,n,k", FP6_CASES)
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_fp6_linear_matches_int4_path_and_oracle(ck, m, n, k, with_bias):
+    xb, xq, sx, wp, ws, xq6, wq6 = _fp6_operands(ck, m, n, k, 2300 + m + n)
+    bias = np.random.default_rng(2301).normal(0, 0.1, n).astype(np.float32) if with_bias else None
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    sxd, wsd = torch.from_numpy(sx).cuda(), torch.from_numpy(ws).cuda()
+    y6 = bf16_host_bits(ck.linear_w4a4_fp6(xq6, sxd, wq6, wsd, bd))
+    if k % 256 == 0:
+        # the int8-MFMA kernel on the same codes gives the same bits
+        y4 = bf16_host_bits(ck.linear_w4a4(torch.from_numpy(xq).cuda(), sxd, torch.from_numpy(wp).cuda(), wsd, bd))
+        assert np.array_equal(y6, y4)
+    acc = oracle.gemm_acc(xq, wp, k, bits=4)
+    ref = oracle.epilogue_bf16(acc, sx, ws, bias)
+    atol = None
+    if bias is not None:
+        terms = np.abs(acc * sx.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]) + np.abs(bias)
+        atol = 2.0 ** -21 * terms
+    assert_bf16_close(y6, ref, atol=atol)
+
+
+@pytest.mark.parametrize("name", ["square_3072", "up_3072_12288", "down_12288_3072"])
+def test_fp6_full_size_layer_equals_int4_path(ck, name):
+    # the whole layer at full size through both paths, from the same bf16
+    # input and fp32 weight: FP6 quantisers + FP6 GEMM against the int4
+    # quantisers + int8-MFMA GEMM, bit for bit; the int4 path is pinned to
+    # the oracle by test_full_size_layer
+    cfg = workloads.WORKLOADS[name]
+    lay = workloads.make_layer(cfg["m"], cfg["k"], cfg["n"], seed=7)
+    x = dev_bf16(lay.x_bf16)
+    w = torch.from_numpy(lay.weights[0]).cuda()
+    wq6, ws6 = ck.quantize_weight_convrot_fp6(w, 128)
+    wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+    assert torch.equal(ws6, ws)
+    y6 = bf16_host_bits(ck.w4a4_linear_fp6(x, wq6, ws6))
+    y4 = bf16_host_bits(ck.w4a4_linear(x, wp, ws))
+    assert np.array_equal(y6, y4)
 
 
 # --------------------------------------------------------------------------
