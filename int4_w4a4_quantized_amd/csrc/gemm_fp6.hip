@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ck4_kernels.h"
 #include "tile_map.h"
 
@@ -49,26 +51,32 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kBlk = 1536;          // bytes of one 16-row x 128-k operand block
 constexpr int kBlkChunks = kBlk / 16;  // 16-byte copy chunks per block
 
-// s_waitcnt immediate that waits for vmcnt <= n and lgkmcnt == 0.
+// s_waitcnt immediates: vmcnt <= n and lgkmcnt == 0, or vmcnt <= n alone.
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     __bf16 h = (__bf16)f;
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// One lane's 24-byte operand image (8-byte aligned) as the MFMA's register
-// operand; FP6 reads the first six registers.
-__device__ __forceinline__ v8i load_frag(const uint8_t *p) {
+typedef int v6i __attribute__((ext_vector_type(6)));
+
+// One lane's 24-byte operand image (8-byte aligned): six registers, the
+// part of the MFMA's eight-register operand that FP6 reads.
+__device__ __forceinline__ v6i load_frag(const uint8_t *p) {
     const uint2 a = *reinterpret_cast<const uint2 *>(p);
     const uint2 b = *reinterpret_cast<const uint2 *>(p + 8);
     const uint2 c = *reinterpret_cast<const uint2 *>(p + 16);
-    return v8i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y, 0, 0};
+    return v6i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y};
 }
 
-__device__ __forceinline__ v4f mfma_fp6(v8i w, v8i x, v4f acc) {
-    // cbsz = blgp = 2: both operands FP6 E2M3; scale bytes 127 = 2^0
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, acc, 2, 2, 0, 127, 0, 127);
+__device__ __forceinline__ v4f mfma_fp6(v6i w, v6i x, v4f acc) {
+    // cbsz = blgp = 2: both operands FP6 E2M3; scale bytes 127 = 2^0; the two
+    // operand registers past the sixth are not read
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(__builtin_shufflevector(w, w, 0, 1, 2, 3, 4, 5, -1, -1),
+                                                            __builtin_shufflevector(x, x, 0, 1, 2, 3, 4, 5, -1, -1),
+                                                            acc, 2, 2, 0, 127, 0, 127);
 }
 
 template <int BM, int BN, int WGM, int WGN, int WPE, int NST, bool OUT_I32>
@@ -148,70 +156,86 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
 
     const int frow = lane & 15;
     const int fgrp = lane >> 4;
-    float sa_r[FM], sb_r[FN][4];
-    if constexpr (!OUT_I32) {
-#pragma unroll
-        for (int j = 0; j < FM; ++j) sa_r[j] = sa[min(m0 + wm * WTM + j * 16 + frow, M - 1)];
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sb_r[i][r] = sb[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
-    }
 
-    // One step: the FN weight fragments, then the FM activation fragments,
-    // each read from LDS once and fed to FN MFMAs.
+    // LDS offsets of this lane's fragment images in a stage.
     const int a_off = wm * FM * kBlk + lane * 24;
     const int b_off = (BLK_A + wn * FN) * kBlk + lane * 24;
-    auto compute_stage = [&](const uint8_t *src) {
-        v8i wf[FN];
-#pragma unroll
-        for (int i = 0; i < FN; ++i) wf[i] = load_frag(src + b_off + i * kBlk);
-        v8i xn = load_frag(src + a_off);
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const v8i xf = xn;
-            if (j + 1 < FM) xn = load_frag(src + a_off + (j + 1) * kBlk);
-#pragma unroll
-            for (int i = 0; i < FN; ++i) acc[i][j] = mfma_fp6(wf[i], xf, acc[i][j]);
-        }
-    };
-
-    // The copy into one slot and the reads from another go through
-    // __restrict__ parameters of an inlined function, so the compiler knows
-    // they never alias and does not make the fragment reads wait for the copy.
-    auto body = [&](uint8_t *__restrict__ dst, const uint8_t *__restrict__ src, int s) {
-        if (s + NST - 1 < kb) issue_stage(dst, s + NST - 1);
-        compute_stage(src);
-    };
-
-    // Ring of NST stages: the copy of step s + NST - 1 is issued once every
-    // wave has finished reading step s - 1 (the barrier), into that step's
-    // slot; before the barrier each wave waits for its own copies of step s,
-    // leaving the later steps' copies in flight.
-#pragma unroll
-    for (int p = 0; p < NST - 1; ++p)
-        if (p < kb) issue_stage(smem + p * STAGE, p);
-    for (int s = 0; s < kb; ++s) {
-        // This wave's copies of step s have landed (the later steps' copies
-        // may still be in flight) and its LDS reads of step s - 1 are done;
-        // then a bare s_barrier (__syncthreads would also drain the copies
-        // in flight) and a compiler-only fence, so that no LDS read of step s
-        // is scheduled above it.
-        const int ahead = min(NST - 2, kb - 1 - s);  // steps issued after s
-        if constexpr (NST == 2) {
-            __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
-        } else if constexpr (NST == 3) {
-            if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PER_WAVE));
-            else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
-        } else {
-            if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * PER_WAVE));
-            else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PER_WAVE));
-            else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
-        }
+    auto stage_ptr = [&](int s) { return smem + (s % NST) * STAGE; };
+    auto sync_stage = [&](int outstanding_steps) {
+        // this wave's copies of the step are done (later steps' may be in
+        // flight), then a bare s_barrier: __syncthreads would also drain the
+        // copies in flight; the empty asm keeps LDS reads below it
+        if (outstanding_steps > 0) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PER_WAVE));
+        else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
-        body(smem + ((s + NST - 1) % NST) * STAGE, smem + (s % NST) * STAGE, s);
+    };
+
+    // Software pipeline over k steps. The FN weight fragments of a step are
+    // held in registers; the FM activation fragments stream through a ring of
+    // D + 1 registers, each read D fragments ahead of the MFMAs that use it,
+    // and the stream runs on into the next step without a pause: D fragments
+    // before the end of step s the wave waits for step s + 1's copy and meets
+    // the others at the barrier (after which step s - 1's slot is free for
+    // the copy of step s + 2), reads step s + 1's weight fragments into the
+    // other weight set and continues the activation stream with step s + 1.
+    // The next weight set moves into place at the end of the step (18
+    // register moves against 27 MFMAs). Slots go through __restrict__
+    // parameters of an inlined function, so the compiler knows the slot being
+    // copied into is neither of the slots being read.
+    constexpr int D = 2;
+    static_assert(FM % (D + 1) == 0 && FM > D, "the ring must realign at step boundaries");
+    v6i ring[D + 1];
+    auto step = [&](auto more_c, const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
+                    uint8_t *__restrict__ dst, int s, v6i(&wb)[FN], v6i(&wn)[FN]) {
+        constexpr bool more = decltype(more_c)::value;  // step s + 1 exists
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int jn = j + D;
+            if (jn < FM) {
+                ring[jn % (D + 1)] = load_frag(cur + a_off + jn * kBlk);
+            } else if constexpr (more) {
+                if (jn == FM) {
+                    // this wave's copy of step s + 1 has landed; the ring's
+                    // reads of step s may stay in flight across the barrier
+                    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                    // past the last step the copy repeats the last step into
+                    // the free slot (never read), which keeps the step
+                    // branch-free
+                    issue_stage(dst, min(s + NST - 1, kb - 1));
+#pragma unroll
+                    for (int i = 0; i < FN; ++i) wn[i] = load_frag(nxt + b_off + i * kBlk);
+                }
+                ring[jn % (D + 1)] = load_frag(nxt + a_off + (jn - FM) * kBlk);
+            }
+            const v6i x = ring[j % (D + 1)];
+#pragma unroll
+            for (int i = 0; i < FN; ++i) acc[i][j] = mfma_fp6(wb[i], x, acc[i][j]);
+            // keep the schedule as written: loads hoisted further would only
+            // raise register pressure
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+#pragma unroll
+    for (int p = 0; p < NST - 1; ++p)
+        if (p < kb) issue_stage(stage_ptr(p), p);
+    sync_stage(kb > 1 ? 1 : 0);
+    v6i w0[FN], w1[FN];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) w0[i] = load_frag(stage_ptr(0) + b_off + i * kBlk);
+#pragma unroll
+    for (int j = 0; j < D; ++j) ring[j] = load_frag(stage_ptr(0) + a_off + j * kBlk);
+    using more_t = std::integral_constant<bool, true>;
+    using last_t = std::integral_constant<bool, false>;
+    for (int s = 0; s + 1 < kb; ++s) {
+        step(more_t{}, stage_ptr(s), stage_ptr(s + 1), stage_ptr(s + NST - 1), s, w0, w1);
+#pragma unroll
+        for (int i = 0; i < FN; ++i) w0[i] = w1[i];
     }
+    step(last_t{}, stage_ptr(kb - 1), stage_ptr(kb), stage_ptr(kb + NST - 2), kb - 1, w0, w1);
 
     if constexpr (OUT_I32) {
 #pragma unroll
@@ -238,6 +262,14 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
         // y = bf16((acc * sa[m]) * sb[n] (+ bias[n])) with acc = 64 x the fp32
         // accumulator (exact), into a [BM][BN + 8] bf16 tile, then 16-byte
         // row-contiguous stores.
+        // the scales are read after the K loop, whose registers are all in use
+        float sa_r[FM], sb_r[FN][4];
+#pragma unroll
+        for (int j = 0; j < FM; ++j) sa_r[j] = sa[min(m0 + wm * WTM + j * 16 + frow, M - 1)];
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sb_r[i][r] = sb[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
         uint16_t *tile_lds = reinterpret_cast<uint16_t *>(smem);
         __syncthreads();  // every wave has finished reading the last stage
 #pragma unroll

@@ -166,7 +166,18 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
                                                                   WeightOpts wo) {
     __shared__ float red[kThreads / 64];
     const int lane = threadIdx.x & 63;
-    const int64_t row = WAVE_ROW ? (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6) : blockIdx.x;
+    int64_t wg = blockIdx.x;
+    if constexpr (OUT == 4) {
+        // FP6 blocks span 16 rows: 4 workgroups of 4 rows, or 16 workgroups
+        // of one row. Workgroup ids are dealt round-robin to the 8 XCDs
+        // (id & 7), each with its own L2; remap so that the workgroups of a
+        // block share an XCD and their partial 24-byte writes of each line
+        // meet in one L2.
+        const int64_t b = blockIdx.x, j = b >> 3;
+        if (WAVE_ROW && (gridDim.x & 31) == 0 && blockDim.x == 256) wg = ((j >> 2) * 8 + (b & 7)) * 4 + (j & 3);
+        if (!WAVE_ROW && (gridDim.x & 127) == 0) wg = ((j >> 4) * 8 + (b & 7)) * 16 + (j & 15);
+    }
+    const int64_t row = WAVE_ROW ? wg * (blockDim.x / 64) + (threadIdx.x >> 6) : wg;
     if (WAVE_ROW && row >= rows) return;  // whole wavefronts only; this mode has no barrier
     const int tid = WAVE_ROW ? lane : (int)threadIdx.x;
     const int nthreads = WAVE_ROW ? 64 : (int)blockDim.x;
