@@ -2,16 +2,20 @@
 """Benchmark of the W4A4 ConvRot linear on one MI355X.
 
 One step = one pass of the layer over a resident batch: the fused activation
-rotate + int4 quantise kernel, then the s4 x s4 int8-MFMA GEMM with its bf16
-rank-one epilogue, back to back on one stream. The weight is prepared once,
+rotate + int4 quantise kernel, then the s4 x s4 GEMM with its bf16 rank-one
+epilogue, back to back on one stream. The weight is prepared once,
 before timing (offline weight prep). Workload: 4608 tokens through a 3072 x
 3072 projection (M=4608, K=N=3072, Hadamard block 128), bf16 activations drawn
 N(0,1) with 1 % outlier channels x20, weights N(0, 0.02).
 
-Prints one JSON line. ``value`` is the layer's int8-op throughput in TOP/s
+The layer runs on two bit-identical paths: the int4 codes as exact FP6
+E2M3 operands of the FP6 matrix cores (the headline step) and the packed-int4
+path on the int8 matrix cores (reported beside it).
+
+Prints one JSON line. ``value`` is the layer's int4-op throughput in TOP/s
 (2 M N K per step / step time; the K steps are one HIP graph replay between
-two synchronisations), ``roofline`` reports the GEMM kernel against the int8
-dense MFMA peak using its per-launch time from HIP events around K
+two synchronisations), ``roofline`` reports the GEMM kernel against the dense
+FP6 MFMA peak using its per-launch time from HIP events around K
 back-to-back launches, and ``cpu_baseline`` times the CPU oracle on the
 workload's rows.
 """
@@ -36,24 +40,28 @@ import workloads  # noqa: E402
 METRIC = "W4A4 linear TOPS & ms/layer (quantize+GEMM), M=4608 K=N=3072; % int8 MFMA peak"
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4a4_square_3072_traffic.json")
+FP6_PEAK_TOPS = 10100.0     # MI355X dense FP6/FP4 MFMA, 10.1 PFLOP/s
+TRAFFIC_FILES = {
+    "gemm_fp6.hip": os.path.join(ROOT, "profiles", "gemm_w4a4_fp6_square_3072_traffic.json"),
+    "gemm.hip": os.path.join(ROOT, "profiles", "gemm_w4a4_square_3072_traffic.json"),
+}
 
 
-def _kernel_source_digest() -> str:
+def _kernel_source_digest(source: str) -> str:
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "int4_w4a4_quantized_amd", "csrc", "gemm.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "int4_w4a4_quantized_amd", "csrc", source), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def _traffic_for_current_kernel():
+def _traffic_for_current_kernel(source: str):
     """Measured HBM bytes per GEMM launch, if taken on the current kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[source]) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("gemm_source_sha256_16") != _kernel_source_digest():
+    if t.get("gemm_source_sha256_16") != _kernel_source_digest(source):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -248,7 +256,15 @@ def layer_sweep(ck, torch, args) -> int:
             ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
         _clock_warmup(torch, step)
         line(f"w4a4 layer {name}", lay.m, lay.n, lay.k, graph_ms(step, reps))
-        del x, wp, ws, xq, sx, y, lay
+        del wp, ws, xq
+        wq6, ws6 = ck.quantize_weight_convrot_fp6(torch.from_numpy(lay.weights[0]).to(dev), 128)
+        xq6 = torch.empty((lay.m, lay.k * 3 // 4), dtype=torch.uint8, device=dev)
+
+        def step6():
+            ck.rotate_quantize_act_fp6(x, 128, out=xq6, scales=sx)
+            ck.linear_w4a4_fp6(xq6, sx, wq6, ws6, None, out=y)
+        line(f"w4a4 layer {name}, FP6 operands", lay.m, lay.n, lay.k, graph_ms(step6, reps))
+        del x, wq6, ws6, xq6, sx, y, lay
 
     # Weight preparation (offline, HBM-bound): nearest and stochastic rounding
     # of the up projection's weight, N=12288 x K=3072.
@@ -287,7 +303,16 @@ def layer_sweep(ck, torch, args) -> int:
             ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
     line("w4a4 q/k/v, one shared activation quantisation", m, n, k, graph_ms(qkv_reuse, reps), 3)
     line("w4a4 q/k/v, activation quantised per projection", m, n, k, graph_ms(qkv_separate, reps), 3)
-    del wts, ys
+    del wts
+    wts6 = [ck.quantize_weight_convrot_fp6(torch.from_numpy(w).to(dev), 128) for w in lay.weights]
+    xq6 = torch.empty((m, k * 3 // 4), dtype=torch.uint8, device=dev)
+
+    def qkv_reuse6():
+        ck.rotate_quantize_act_fp6(x, 128, out=xq6, scales=sx)
+        for (wq6, ws6), y in zip(wts6, ys):
+            ck.linear_w4a4_fp6(xq6, sx, wq6, ws6, None, out=y)
+    line("w4a4 q/k/v, one shared activation quantisation, FP6 operands", m, n, k, graph_ms(qkv_reuse6, reps), 3)
+    del wts6, xq6, ys
 
     wd = torch.from_numpy(lay.weights[0]).to(dev)
     w8, ws8 = ck.quantize_weight_convrot_int8(wd)
@@ -435,84 +460,102 @@ def main() -> int:
     torch.cuda.set_device(dev)
     x = torch.from_numpy(lay.x_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
     w = torch.from_numpy(lay.weights[0]).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # Two implementations of the same layer, bit for bit: the int4 codes fed
+    # to the FP6 matrix cores (as exact E2M3 values q / 8, twice the int8
+    # rate) and the packed-int4 path on the int8 matrix cores. The step the
+    # headline times is the faster one; both are timed the same way.
+    wq6, ws6 = ck.quantize_weight_convrot_fp6(w, 128)
     wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+    xq6 = torch.empty((m, k * 3 // 4), dtype=torch.uint8, device=dev)
     xq = torch.empty((m, k // 2), dtype=torch.int8, device=dev)
     sx = torch.empty((m,), dtype=torch.float32, device=dev)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    paths = {
+        "fp6": (lambda: ck.rotate_quantize_act_fp6(x, 128, out=xq6, scales=sx),
+                lambda: ck.linear_w4a4_fp6(xq6, sx, wq6, ws6, None, out=y)),
+        "int4": (lambda: ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx),
+                 lambda: ck.linear_w4a4(xq, sx, wp, ws, None, out=y)),
+    }
 
-    # Eager reference output of one step.
-    ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
-    ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
-    torch.cuda.synchronize()
-    y_eager = y.clone()
+    # Eager reference output of one step on each path; they must agree.
+    ref = {}
+    for name, (quant, gemm) in paths.items():
+        quant()
+        gemm()
+        torch.cuda.synchronize()
+        ref[name] = y.clone()
+    if not torch.equal(ref["fp6"].view(torch.int16), ref["int4"].view(torch.int16)):
+        print("bench.py: the FP6 and int4 paths disagree", file=sys.stderr)
+        return 1
 
     # The host launch path (Python + ctypes + HIP) costs about as much as a
     # step, so the K timed steps are captured in one HIP graph and replayed
     # once: the kernels then run back to back as a serving loop would issue
     # them. Warm-up steps are a graph of their own.
-    def capture(n_steps, quant=True, gemm=True):
+    def capture(quant, gemm, n_steps, do_quant=True, do_gemm=True):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for _ in range(n_steps):
-                if quant:
-                    ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
-                if gemm:
-                    ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
+                if do_quant:
+                    quant()
+                if do_gemm:
+                    gemm()
         return g
 
-    g_warm = capture(max(args.warmup, 1))
-    g_steps = capture(args.steps)
-    g_gemm_only = capture(args.steps, quant=False)
-    g_quant_only = capture(args.steps, gemm=False)
-    torch.cuda.synchronize()
-    g_warm.replay()
-    torch.cuda.synchronize()
-    # clear the outputs so that the check below sees the timed replay's work
-    xq.zero_()
-    sx.zero_()
-    y.zero_()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    t0 = time.perf_counter()
-    g_steps.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if not torch.equal(y.view(torch.int16), y_eager.view(torch.int16)):
-        print("bench.py: graph replay output differs from the eager step", file=sys.stderr)
-        return 1
-
-    # Per-kernel durations: the same launches, one kernel at a time, back to
-    # back, bracketed by HIP events on the stream they run on.
-    def per_launch_ms(g):
+    def events_ms(g, launches):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
+        return e0.elapsed_time(e1) / launches
 
-    gemm_ms = per_launch_ms(g_gemm_only)
-    quant_ms = per_launch_ms(g_quant_only)
-
-    # Spread: min and median over 5 graphs of 100 layer steps (the pages time
-    # min of 5 x 100 iterations); reported beside the contract's single timing.
-    g_100 = capture(100)
-    spread = []
-    for _ in range(5):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g_100.replay()
-        e1.record(stream)
+    res = {}
+    for name, (quant, gemm) in paths.items():
+        g_warm = capture(quant, gemm, max(args.warmup, 1))
+        g_steps = capture(quant, gemm, args.steps)
+        g_gemm_only = capture(quant, gemm, args.steps, do_quant=False)
+        g_quant_only = capture(quant, gemm, args.steps, do_gemm=False)
+        g_100 = capture(quant, gemm, 100)
         torch.cuda.synchronize()
-        spread.append(e0.elapsed_time(e1) / 100)
-    ms_per_step = wall * 1e3 / args.steps
+        g_warm.replay()
+        torch.cuda.synchronize()
+        # clear the outputs so that the check below sees the timed replay's work
+        xq6.zero_()
+        xq.zero_()
+        sx.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g_steps.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if not torch.equal(y.view(torch.int16), ref[name].view(torch.int16)):
+            print(f"bench.py: {name} graph replay output differs from the eager step", file=sys.stderr)
+            return 1
+        # Per-kernel durations: the same launches, one kernel at a time, back
+        # to back, bracketed by HIP events on the stream they run on. Spread:
+        # min and median over 5 graphs of 100 layer steps (the pages time min
+        # of 5 x 100 iterations), beside the contract's single timing.
+        res[name] = {
+            "ms_per_step": wall * 1e3 / args.steps,
+            "gemm_ms": events_ms(g_gemm_only, args.steps),
+            "quant_ms": events_ms(g_quant_only, args.steps),
+            "spread": [events_ms(g_100, 100) for _ in range(5)],
+        }
+
     ops = 2.0 * m * n * k
-    tops = ops / (ms_per_step * 1e-3) / 1e12
-    gemm_tops = ops / (gemm_ms * 1e-3) / 1e12
-    quant_bytes = m * k * 2 + m * k // 2 + m * 4
-    gemm_bytes = m * k // 2 + n * k // 2 + m * 4 + n * 4 + m * n * 2
-    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+    r6, r4 = res["fp6"], res["int4"]
+    tops = ops / (r6["ms_per_step"] * 1e-3) / 1e12
+    tops4 = ops / (r4["ms_per_step"] * 1e-3) / 1e12
+    gemm_tops = ops / (r6["gemm_ms"] * 1e-3) / 1e12
+    gemm4_tops = ops / (r4["gemm_ms"] * 1e-3) / 1e12
+    quant6_bytes = m * k * 2 + m * k * 3 // 4 + m * 4
+    quant4_bytes = m * k * 2 + m * k // 2 + m * 4
+    gemm6_bytes = m * k * 3 // 4 + n * k * 3 // 4 + m * 4 + n * 4 + m * n * 2
+    gemm4_bytes = m * k // 2 + n * k // 2 + m * 4 + n * 4 + m * n * 2
 
     out = {
         "metric": METRIC,
@@ -521,35 +564,52 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(r6["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int4",
         "data": "synthetic",
         "config": {"workload": "square_3072 (W4A4 ConvRot linear M=4608 K=3072 N=3072, Hadamard block 128)",
-                   "m": m, "k": k, "n": n, "rot_block": 128, "parallelism": "single GPU"},
+                   "m": m, "k": k, "n": n, "rot_block": 128, "parallelism": "single GPU",
+                   "path": "int4 codes as exact FP6 E2M3 MFMA operands (bit-identical to the int8-MFMA path)"},
         "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_big_kernel<s4, 288x192 tile, 8 waves> (W4A4 GEMM + rank-one epilogue)",
+            "kernel": "gemm_fp6_kernel<288x192 tile, 8 waves> (W4A4 GEMM on FP6 MFMA + rank-one epilogue)",
             "achieved": round(gemm_tops, 2),
-            "peak": INT8_PEAK_TOPS,
+            "peak": FP6_PEAK_TOPS,
             "unit": "TOP/s",
-            "frac": round(gemm_tops / INT8_PEAK_TOPS, 4),
-            "traffic": _traffic_for_current_kernel(),
-            "algorithmic_bytes": gemm_bytes,
-            "avg_kernel_ms": round(gemm_ms, 5),
+            "frac": round(gemm_tops / FP6_PEAK_TOPS, 4),
+            "traffic": _traffic_for_current_kernel("gemm_fp6.hip"),
+            "algorithmic_bytes": gemm6_bytes,
+            "avg_kernel_ms": round(r6["gemm_ms"], 5),
+            "note": "peak = dense FP6 MFMA; the kernel is bound by its global->LDS copies (each CU re-reads "
+                    "its 288 + 192 operand rows: 283 MB per launch from L2)",
         },
         "kernels": {
-            "rotate_quant_ms": round(quant_ms, 5),
-            "rotate_quant_GBps": round(quant_gbs, 1),
-            "rotate_quant_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
-            "gemm_ms": round(gemm_ms, 5),
-            "gemm_TOPS": round(gemm_tops, 2),
+            "rotate_quant_fp6_ms": round(r6["quant_ms"], 5),
+            "rotate_quant_fp6_GBps": round(quant6_bytes / (r6["quant_ms"] * 1e-3) / 1e9, 1),
+            "gemm_fp6_ms": round(r6["gemm_ms"], 5),
+            "gemm_fp6_TOPS": round(gemm_tops, 2),
+            "gemm_fp6_pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
         },
-        "spread": {"batches": 5, "steps_per_batch": 100, "ms_per_step_min": round(min(spread), 5),
-                   "ms_per_step_median": round(statistics.median(spread), 5)},
+        "int4_path": {
+            "ms_per_step": round(r4["ms_per_step"], 5),
+            "TOPS": round(tops4, 2),
+            "pct_int8_peak": round(100.0 * tops4 / INT8_PEAK_TOPS, 2),
+            "rotate_quant_ms": round(r4["quant_ms"], 5),
+            "rotate_quant_hbm_frac": round(quant4_bytes / (r4["quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemm_ms": round(r4["gemm_ms"], 5),
+            "gemm_TOPS": round(gemm4_tops, 2),
+            "gemm_frac_int8_peak": round(gemm4_tops / INT8_PEAK_TOPS, 4),
+            "gemm_traffic": _traffic_for_current_kernel("gemm.hip"),
+            "gemm_algorithmic_bytes": gemm4_bytes,
+        },
+        "spread": {"batches": 5, "steps_per_batch": 100, "ms_per_step_min": round(min(r6["spread"]), 5),
+                   "ms_per_step_median": round(statistics.median(r6["spread"]), 5),
+                   "int4_ms_per_step_min": round(min(r4["spread"]), 5),
+                   "int4_ms_per_step_median": round(statistics.median(r4["spread"]), 5)},
         "peaks": _device_peaks(torch, sclk_mhz),
         "context": {"L4_ms_per_layer_same_shape": 0.54, "note": "another machine's number; context only"},
     }
