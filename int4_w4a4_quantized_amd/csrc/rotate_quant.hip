@@ -58,6 +58,8 @@ namespace ck4 {
 namespace {
 
 constexpr int kMaxChunks = 4;  // chunks per thread: k <= 16 * 256 * 4 = 16384
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef int v6i_t __attribute__((ext_vector_type(6)));
 constexpr int kThreads = 256;
 // The kernel is instantiated per chunks-per-thread count NCH (1..4), so a row
 // of K <= 4096 keeps 16 values per lane in VGPRs and the occupancy stays high.
@@ -263,28 +265,48 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             // subnormal, exact), in the MFMA operand image: a 16-value chunk is
             // 96 bits at byte 12 (ch & 1) of lane image 16 ((ch >> 1) & 3) + (row & 15)
             // of block (row / 16, ch / 8), 1536 bytes per block, fields LSB-first.
+            // q is formed as an integer-valued float (the rounding add of 1.5 * 2^23
+            // and its subtraction are exact for |q| <= 7), and the hardware
+            // converter packs two chunks at once: it divides by its scale (8) and
+            // interleaves its sources (field 2i from the first, 2i + 1 from the
+            // second), so the even elements of both chunks go in the first source.
             uint8_t *o = reinterpret_cast<uint8_t *>(out) + (row >> 4) * (int64_t)(k / 128) * 1536 + (row & 15) * 24;
+            float qf[NCH][kElems];
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
-                const int ch = tid + j * nthreads;
-                if (ch >= nchunks) continue;
-                uint32_t c[kElems];
                 if (fast_row) {
 #pragma unroll
-                    for (int i = 0; i < kElems; ++i) c[i] = code_fast<0>(fabsf(v[j][i]), s_row, y_row) & 7u;
+                    for (int i = 0; i < kElems; ++i) {
+                        const float q0 = v[j][i] * y_row;
+                        const float e = __builtin_fmaf(-q0, s_row, v[j][i]);
+                        const float q1 = __builtin_fmaf(e, y_row, q0);
+                        qf[j][i] = (q1 + 12582912.0f) - 12582912.0f;
+                    }
                 } else {
 #pragma unroll
-                    for (int i = 0; i < kElems; ++i) c[i] = code_exact<0>(fabsf(v[j][i]), s_row, qmax);
+                    for (int i = 0; i < kElems; ++i)
+                        qf[j][i] = s_row == 0.0f ? 0.0f : fminf(fmaxf(rintf(v[j][i] / s_row), -qmax), qmax);
                 }
+            }
 #pragma unroll
-                for (int i = 0; i < kElems; ++i) c[i] |= (__float_as_uint(v[j][i]) >> 26) & 0x20u;
-                const uint32_t d0 = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18) | (c[4] << 24) | (c[5] << 30);
-                const uint32_t d1 =
-                    (c[5] >> 2) | (c[6] << 4) | (c[7] << 10) | (c[8] << 16) | (c[9] << 22) | (c[10] << 28);
-                const uint32_t d2 =
-                    (c[10] >> 4) | (c[11] << 2) | (c[12] << 8) | (c[13] << 14) | (c[14] << 20) | (c[15] << 26);
-                uint8_t *dst = o + (int64_t)(ch >> 3) * 1536 + ((ch >> 1) & 3) * 16 * 24 + (ch & 1) * 12;
-                *reinterpret_cast<uint3 *>(dst) = make_uint3(d0, d1, d2);
+            for (int j = 0; j < NCH; j += 2) {
+                const int j1 = j + 1 < NCH ? j + 1 : j;  // an odd count pairs the last chunk with itself
+                v16f_t ev, od;
+#pragma unroll
+                for (int i = 0; i < kElems / 2; ++i) {
+                    ev[i] = qf[j][2 * i];
+                    od[i] = qf[j][2 * i + 1];
+                    ev[8 + i] = qf[j1][2 * i];
+                    od[8 + i] = qf[j1][2 * i + 1];
+                }
+                const v6i_t p6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
+                const int ch0 = tid + j * nthreads, ch1 = tid + j1 * nthreads;
+                if (ch0 < nchunks)
+                    *reinterpret_cast<uint3 *>(o + (int64_t)(ch0 >> 3) * 1536 + ((ch0 >> 1) & 3) * 16 * 24 +
+                                               (ch0 & 1) * 12) = make_uint3(p6[0], p6[1], p6[2]);
+                if (j1 != j && ch1 < nchunks)
+                    *reinterpret_cast<uint3 *>(o + (int64_t)(ch1 >> 3) * 1536 + ((ch1 >> 1) & 3) * 16 * 24 +
+                                               (ch1 & 1) * 12) = make_uint3(p6[3], p6[4], p6[5]);
             }
             return;
         }
