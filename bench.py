@@ -370,6 +370,8 @@ def lora_sweep(ck, torch, args) -> int:
                           "pct_int8_peak": round(100 * ops / (ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2)}), flush=True)
 
     wp, ws = ck.quantize_weight_convrot(wd, 128, 0)
+    wq6, ws6 = ck.quantize_weight_convrot_fp6(wd, 128)
+    xq6 = torch.empty(((m + 15) // 16 * 16, k * 3 // 4), dtype=torch.uint8, device=dev)
 
     def base_gemm():
         ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
@@ -403,6 +405,12 @@ def lora_sweep(ck, torch, args) -> int:
                           "base_gemm_ms": round(base_ms, 5), "epilogue_overhead_ms": round(g_ms - base_ms, 5)}),
               flush=True)
         line(f"w4a4 layer square_3072 + dynamic lora rank={rank}", graph_ms(lora_step, reps))
+
+        def lora_step6():
+            ck.rotate_quantize_act_fp6(x, 128, out=xq6, scales=sx)
+            ck.lora_down(x, a_rot, 0.5, 128, out=t)
+            ck.linear_w4a4_fp6_lora(xq6, sx, wq6, ws6, t, bd, None, out=y)
+        line(f"w4a4 layer square_3072 + dynamic lora rank={rank}, FP6 operands", graph_ms(lora_step6, reps))
         del a_rot, bd, t
     return 0
 

@@ -401,6 +401,17 @@ ck4_status ck4_linear_w4a4_lora(const int8_t *x_q, const float *x_scales, const 
                                 const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k, uint16_t *y,
                                 int64_t ldy, void *stream);
 
+/*
+ * The same LoRA epilogue on the FP6 operand path (the FP6 block above):
+ * ck4_linear_w4a4_lora from x_q6 and w_q6, bit for bit. Arguments, ranks,
+ * alignment and errors as ck4_linear_w4a4_lora and ck4_linear_w4a4_fp6. For
+ * the callers of the FP6 layout (large m).
+ */
+ck4_status ck4_linear_w4a4_fp6_lora(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
+                                    const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                    const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k,
+                                    uint16_t *y, int64_t ldy, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

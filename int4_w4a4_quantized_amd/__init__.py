@@ -66,6 +66,7 @@ SIGNATURES = {
     "ck4_quantize_weight_convrot_fp6": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
     "ck4_linear_w4a4_fp6": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_gemm_w4a4_fp6_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_linear_w4a4_fp6_lora": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_lora_prepare_down": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_lora_prepare_up": ([_P, _I64, _I64, _I64, _P, _P], _I),
     "ck4_lora_down": ([_P, _I64, _I64, _I64, _I, _P, _I64, ctypes.c_float, _P, _P], _I),
@@ -463,6 +464,29 @@ def linear_w4a4_lora(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.
            lib().ck4_linear_w4a4_lora(_ptr(x_q), _ptr(x_scales), _ptr(w_packed), _ptr(w_scales), _ptr(bias),
                                       _ptr(t_pack), _ptr(b_pack), rank, m, n, k, _ptr(out), out.stride(0),
                                       _stream(x_q.device)))
+    return out
+
+
+def linear_w4a4_fp6_lora(x_q6: torch.Tensor, x_scales: torch.Tensor, w_q6: torch.Tensor, w_scales: torch.Tensor,
+                         t_pack: torch.Tensor, b_pack: torch.Tensor, bias: torch.Tensor | None = None,
+                         out: torch.Tensor | None = None):
+    """linear_w4a4_lora on the FP6 operand path (same bits): y = base + t B^T, bf16 [m, n]."""
+    m, n = x_scales.numel(), w_scales.numel()
+    k = x_q6.shape[1] * 4 // 3
+    _need(t_pack, torch.bfloat16, "t_pack", 2)
+    _need(b_pack, torch.bfloat16, "b_pack", 2)
+    rank = t_pack.shape[1]
+    if tuple(t_pack.shape) != (_rows16(m), rank) or not t_pack.is_contiguous():
+        raise ValueError("t_pack must be a contiguous [16 * ceil(m / 16), rank] tensor")
+    if tuple(b_pack.shape) != (_rows16(n), rank) or not b_pack.is_contiguous():
+        raise ValueError("b_pack must be a contiguous [16 * ceil(n / 16), rank] tensor")
+    if out is None:
+        out = _out_bf16(m, n, x_q6.device)
+    _need(out, torch.bfloat16, "out", 2)
+    _check("ck4_linear_w4a4_fp6_lora",
+           lib().ck4_linear_w4a4_fp6_lora(_ptr(x_q6), _ptr(x_scales), _ptr(w_q6), _ptr(w_scales), _ptr(bias),
+                                          _ptr(t_pack), _ptr(b_pack), rank, m, n, k, _ptr(out), out.stride(0),
+                                          _stream(x_q6.device)))
     return out
 
 

@@ -320,14 +320,14 @@ ck4_status ck4_quantize_weight_convrot_fp6(const float *w, int64_t n, int64_t k,
 
 static ck4_status gemm_fp6_entry(const char *fn, const uint8_t *a, const float *sa, const uint8_t *b,
                                  const float *sb, const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32,
-                                 void *y, int64_t ldy, void *stream) {
+                                 void *y, int64_t ldy, void *stream, ck4::LoraUp lora = ck4::LoraUp{}) {
     if (!a || !b || !y || (!out_i32 && (!sa || !sb))) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, out_i32 ? 16 : 8)) return s;
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
     if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_gemm_fp6(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy,
-                                             static_cast<hipStream_t>(stream)));
+                                             static_cast<hipStream_t>(stream), lora));
 }
 
 ck4_status ck4_linear_w4a4_fp6(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
@@ -574,6 +574,21 @@ ck4_status ck4_linear_w4a4_lora(const int8_t *x_q, const float *x_scales, const 
         return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
     return gemm_entry(fn, true, x_q, x_scales, w_packed, w_scales, bias, m, n, k, false, y, ldy, stream,
                       ck4::LoraUp{t, b_up, (int)rank});
+}
+
+
+ck4_status ck4_linear_w4a4_fp6_lora(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
+                                    const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                    const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k,
+                                    uint16_t *y, int64_t ldy, void *stream) {
+    const char *fn = "ck4_linear_w4a4_fp6_lora";
+    if (!t_pack || !b_pack) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (!aligned(t_pack, 16) || !aligned(b_pack, 16))
+        return fail(CK4_ERR_INVALID, "%s: t_pack or b_pack misaligned", fn);
+    if (!lora_rank_ok(rank))
+        return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
+    return gemm_fp6_entry(fn, x_q6, x_scales, w_q6, w_scales, bias, m, n, k, false, y, ldy, stream,
+                          ck4::LoraUp{t_pack, b_pack, (int)rank});
 }
 
 }  // extern "C"

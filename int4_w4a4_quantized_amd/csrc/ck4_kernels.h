@@ -76,7 +76,8 @@ hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *s
 // 32 g + t at bits 6 t. Bit-identical to launch_gemm(s4 = true) on the same
 // codes.
 hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
-                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream);
+                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                           LoraUp lora = LoraUp{});
 
 // b (bf16 [n, rank], row stride ldb) to fragment order, zero rows padding n
 // to a multiple of 16.

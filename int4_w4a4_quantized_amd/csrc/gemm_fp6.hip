@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "ck4_kernels.h"
+#include "lora_up.h"
 #include "tile_map.h"
 
 namespace ck4 {
@@ -79,12 +80,12 @@ __device__ __forceinline__ v4f mfma_fp6(v6i w, v6i x, v4f acc) {
                                                             acc, 2, 2, 0, 127, 0, 127);
 }
 
-template <int BM, int BN, int WGM, int WGN, int WPE, int NST, bool OUT_I32>
+template <int BM, int BN, int WGM, int WGN, int WPE, int NST, bool OUT_I32, bool LORA>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WPE, WPE))) void
 gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const float *__restrict__ sa,
                 const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int kb,
-                void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m) {
+                void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m, LoraUp lora) {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM;
     constexpr int WTN = BN / WGN;
@@ -271,6 +272,21 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
 #pragma unroll
             for (int r = 0; r < 4; ++r) sb_r[i][r] = sb[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
         uint16_t *tile_lds = reinterpret_cast<uint16_t *>(smem);
+        if constexpr (LORA) {
+            // the fp32 values of the wave tile first, in place, then the LoRA
+            // up projection accumulates onto them on the bf16 matrix cores
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float v = ((acc[i][j][r] * 64.0f) * sa_r[j]) * sb_r[i][r];
+                        if (bias) v = v + bias[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
+                        acc[i][j][r] = v;
+                    }
+            lora_up<FN, FM>(acc, lora, n0 + wn * WTN, m0 + wm * WTM, N, M, lane);
+        }
         __syncthreads();  // every wave has finished reading the last stage
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
@@ -281,10 +297,14 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
                 uint16_t o[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float a = acc[i][j][r] * 64.0f;
-                    float v = (a * sa_r[j]) * sb_r[i][r];
-                    if (bias) v = v + bias[min(n0 + nl + r, N - 1)];
-                    o[r] = f32_to_bf16(v);
+                    if constexpr (LORA) {
+                        o[r] = f32_to_bf16(acc[i][j][r]);
+                    } else {
+                        const float a = acc[i][j][r] * 64.0f;
+                        float v = (a * sa_r[j]) * sb_r[i][r];
+                        if (bias) v = v + bias[min(n0 + nl + r, N - 1)];
+                        o[r] = f32_to_bf16(v);
+                    }
                 }
                 *reinterpret_cast<uint2 *>(tile_lds + ml * LD + nl) =
                     make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
@@ -314,7 +334,8 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
 
 template <int BM, int BN, int WGM, int WGN, int WPE, int NST>
 hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
-                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
+                      int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                      LoraUp lora) {
     const int kb = (int)(k / 128);
     const int tiles_m = (int)((m + BM - 1) / BM);
     const int tiles_n = (int)((n + BN - 1) / BN);
@@ -322,19 +343,24 @@ hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const
     const int xcd_m = pick_xcd_m(tiles_m, tiles_n, BM, BN);
     dim3 grid((unsigned)total), block(64 * WGM * WGN);
     if (out_i32)
-        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, true><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m);
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, true, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m, lora);
+    else if (lora.rank > 0)
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false, true><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m, lora);
     else
-        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m);
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false, false><<<grid, block, 0, stream>>>(
+            a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m, lora);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
-                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream) {
-    return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream);
+                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                           LoraUp lora) {
+    if (out_i32 || lora.t == nullptr) lora.rank = 0;
+    return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 }  // namespace ck4

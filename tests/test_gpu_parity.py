@@ -752,6 +752,28 @@ def test_full_size_square_layer_with_lora(ck):
 
 
 
+@pytest.mark.parametrize("m,n,k,rank", [(1, 77, 256, 32), (16, 300, 512, 64), (33, 130, 1024, 128),
+                                         (300, 200, 768, 256), (97, 1000, 384, 32)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_fp6_lora_epilogue_matches_int4_path_and_oracle(ck, m, n, k, rank, with_bias):
+    xb, xq, sx, wp, ws, xq6, wq6 = _fp6_operands(ck, m, n, k, 2400 + m + rank)
+    rng = np.random.default_rng(2410 + rank)
+    t = workloads.f32_to_bf16_bits(rng.normal(0.0, 2.0, (m, rank)).astype(np.float32))
+    _, b = workloads.make_lora(rng, rank, k, n)
+    bias = rng.standard_normal(n).astype(np.float32) if with_bias else None
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    td, bpd = dev_bf16(frag_layout.pack(t)), dev_bf16(frag_layout.pack(b))
+    sxd, wsd = torch.from_numpy(sx).cuda(), torch.from_numpy(ws).cuda()
+    y6 = bf16_host_bits(ck.linear_w4a4_fp6_lora(xq6, sxd, wq6, wsd, td, bpd, bd))
+    if k % 256 == 0:
+        y4 = bf16_host_bits(ck.linear_w4a4_lora(torch.from_numpy(xq).cuda(), sxd, torch.from_numpy(wp).cuda(), wsd,
+                                                td, bpd, bd))
+        assert np.array_equal(y6, y4)
+    acc = oracle.gemm_acc(xq, wp, k)
+    assert_bf16_close(y6, oracle.epilogue_lora(acc, sx, ws, t, b, bias),
+                      atol=_lora_atol(acc, sx, ws, bias, t, b, rank))
+
+
 # --------------------------------------------------------------------------
 # Graph capture: every path launches only kernels (no memset or allocation
 # nodes), so a captured graph replays to the eager result, bit for bit, on
