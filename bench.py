@@ -48,9 +48,25 @@ TRAFFIC_FILES = {
 
 
 def _kernel_source_digest(source: str) -> str:
+    """sha256 (first 16 hex digits) of a kernel source and of every local
+    header it includes, directly or not, in include order."""
+    csrc = os.path.join(ROOT, "int4_w4a4_quantized_amd", "csrc")
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "int4_w4a4_quantized_amd", "csrc", source), "rb") as f:
-        h.update(f.read())
+    seen = set()
+
+    def add(name: str) -> None:
+        if name in seen or not os.path.exists(os.path.join(csrc, name)):
+            return
+        seen.add(name)
+        with open(os.path.join(csrc, name), "rb") as f:
+            text = f.read()
+        h.update(text)
+        for line in text.decode("utf-8", "replace").splitlines():
+            line = line.strip()
+            if line.startswith("#include \""):
+                add(line.split('"')[1])
+
+    add(source)
     return h.hexdigest()[:16]
 
 

@@ -299,7 +299,10 @@ FP6_CASES = [
 
 
 @pytest.mark.parametrize("m,k,rb", [(64, 256, 128), (17, 384, 128), (5, 3072, 128), (3, 12288, 128),
-                                    (9, 1024, 16), (9, 2048, 256), (2, 16384, 128)])
+                                    (9, 1024, 16), (9, 2048, 256), (2, 16384, 128),
+                                    # row counts divisible by 4 (images gathered in LDS), up to k = 4096
+                                    (20, 384, 128), (8, 2048, 64), (36, 4096, 128), (132, 3072, 128),
+                                    (4, 128, 16)])
 def test_fp6_activation_codes_bitexact(ck, m, k, rb):
     xb = act(m, k, 2000 + m + k)
     xb[0] = 0                          # an all-zero row: scale 0, codes 0
