@@ -381,6 +381,7 @@ def linear_w4a4_fp6(x_q6, x_scales, w_q6, w_scales, bias=None, out=None, m: int 
     k = x_q6.shape[1] * 4 // 3
     if out is None:
         out = _out_bf16(m, n, x_q6.device)
+    _need(out, torch.bfloat16, "out", 2)
     _check("ck4_linear_w4a4_fp6",
            lib().ck4_linear_w4a4_fp6(_ptr(x_q6), _ptr(x_scales), _ptr(w_q6), _ptr(w_scales), _ptr(bias), m, n, k,
                                      _ptr(out), out.stride(0), _stream(x_q6.device)))
@@ -496,3 +497,12 @@ def w4a4_lora_linear(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Te
     x_q, sx = rotate_quantize_act(x, rot_block, 4)
     t = lora_down(x, a_pack, alpha, rot_block)
     return linear_w4a4_lora(x_q, sx, w_packed, w_scales, t, b_pack, bias)
+
+
+def w4a4_lora_linear_fp6(x: torch.Tensor, w_q6: torch.Tensor, w_scales: torch.Tensor, a_pack: torch.Tensor,
+                         b_pack: torch.Tensor, alpha: float = 1.0, bias=None, rot_block: int = 128):
+    """w4a4_lora_linear on the FP6 operand path (same bits): FP6 codes of x, LoRA down projection, FP6 GEMM with
+    the fused up projection."""
+    x_q6, sx = rotate_quantize_act_fp6(x, rot_block)
+    t = lora_down(x, a_pack, alpha, rot_block)
+    return linear_w4a4_fp6_lora(x_q6, sx, w_q6, w_scales, t, b_pack, bias)

@@ -328,6 +328,10 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
             uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + n;
             if (n + 7 < N && ((reinterpret_cast<uintptr_t>(yr) & 15) == 0)) {
                 *reinterpret_cast<uint4 *>(yr) = v;
+            } else if (n + 7 < N) {
+                // rows of y are 8-byte aligned (ldy % 4 == 0), 16-byte only if ldy % 8 == 0
+                reinterpret_cast<uint2 *>(yr)[0] = make_uint2(v.x, v.y);
+                reinterpret_cast<uint2 *>(yr)[1] = make_uint2(v.z, v.w);
             } else {
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll

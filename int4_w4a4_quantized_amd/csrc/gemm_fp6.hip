@@ -29,11 +29,12 @@
 // Tiling: 288 x 192 output tiles (one per CU on the 4608 x 3072 layer), 8
 // waves of 144 x 48 (9 x 3 MFMA fragments; the first MFMA operand is the
 // weight fragment, so each lane's 4 accumulators are 4 consecutive output
-// columns of one row). One k step is 128 k: 30 blocks, 45 KB, copied
-// global -> LDS with buffer_load ... lds into a ring of 3 stages, two steps
-// ahead of the MFMAs. Rows past the padded operands read as zeros through the
-// buffer descriptors' range check (the block offset is in the copy's vector
-// offset).
+// columns of one row). Problems with fewer than 192 such tiles use 96 x 128
+// tiles of 4 waves (48 x 64, 3 x 4 fragments), two workgroups per CU. One k
+// step is 128 k (on the large tile: 30 blocks, 45 KB), copied global -> LDS
+// with buffer_load ... lds into a ring of 3 stages, two steps ahead of the
+// MFMAs. Rows past the padded operands read as zeros through the buffer
+// descriptors' range check (the block offset is in the copy's vector offset).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -322,6 +323,10 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
             uint16_t *yr = reinterpret_cast<uint16_t *>(Y) + (int64_t)m * ldy + n;
             if (n + 7 < N && ((reinterpret_cast<uintptr_t>(yr) & 15) == 0)) {
                 *reinterpret_cast<uint4 *>(yr) = v;
+            } else if (n + 7 < N) {
+                // rows of y are 8-byte aligned (ldy % 4 == 0), 16-byte only if ldy % 8 == 0
+                reinterpret_cast<uint2 *>(yr)[0] = make_uint2(v.x, v.y);
+                reinterpret_cast<uint2 *>(yr)[1] = make_uint2(v.z, v.w);
             } else {
                 const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -360,7 +365,12 @@ hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, 
                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                            LoraUp lora) {
     if (out_i32 || lora.t == nullptr) lora.rank = 0;
-    return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    // one 288 x 192 tile per CU when that fills the chip; otherwise 96 x 128
+    // tiles of 4 waves (48 x 64 each), two workgroups per CU
+    const int64_t big_tiles = ((m + 287) / 288) * ((n + 191) / 192);
+    if (big_tiles >= 192)
+        return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_fp6<96, 128, 2, 2, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 }  // namespace ck4

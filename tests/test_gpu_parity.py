@@ -364,6 +364,28 @@ def test_fp6_linear_matches_int4_path_and_oracle(ck, m, n, k, with_bias):
     assert_bf16_close(y6, ref, atol=atol)
 
 
+@pytest.mark.parametrize("m,n,k", [(4600, 3000, 1024), (4100, 2900, 512), (2000, 1500, 1536), (1000, 700, 768)])
+def test_fp6_ragged_large_equals_int4_path(ck, m, n, k):
+    """Ragged edges on both tile sizes of the FP6 GEMM, against the int4 path (itself pinned to the oracle)."""
+    rng = np.random.default_rng(3100 + m)
+    xb = workloads.make_activations(rng, m, k)
+    w = torch.from_numpy(workloads.make_weight(rng, n, k)).cuda()
+    bias = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
+    x = dev_bf16(xb)
+    wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+    wq6, ws6 = ck.quantize_weight_convrot_fp6(w, 128)
+    xq, sx = ck.rotate_quantize_act(x, 128, 4)
+    xq6, sx6 = ck.rotate_quantize_act_fp6(x, 128)
+    ldy = (n + 7) // 8 * 8 + 4          # rows 8-byte but not 16-byte aligned
+    y4 = torch.full((m, ldy), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    y6 = y4.clone()
+    ck.linear_w4a4(xq, sx, wp, ws, bias, out=y4[:, :n])
+    ck.linear_w4a4_fp6(xq6, sx6, wq6, ws6, bias, out=y6[:, :n])
+    assert np.array_equal(bf16_host_bits(y4), bf16_host_bits(y6))
+    assert (bf16_host_bits(y6)[:, n:] == 0xFFFF).all()   # nothing written past n
+    assert torch.equal(ck.gemm_w4a4_acc_i32(xq, wp), ck.gemm_w4a4_fp6_acc_i32(xq6, wq6, m, n))
+
+
 @pytest.mark.parametrize("name", ["square_3072", "up_3072_12288", "down_12288_3072"])
 def test_fp6_full_size_layer_equals_int4_path(ck, name):
     # the whole layer at full size through both paths, from the same bf16
@@ -724,6 +746,23 @@ def test_w4a4_lora_layer_end_to_end(ck, m, n, k, rank, rb):
     dt = 2.0 ** -7 * 1.01 * np.abs(f64_of(t_ref)) + 1.01 * _t_atol(lay.x_bf16, a_rot, alpha, rb)
     atol = _lora_atol(acc, sx, ws, None, t_ref, b, rank) + dt @ np.abs(f64_of(b)).T
     assert_bf16_close(bf16_host_bits(y), y_ref, atol=atol)
+
+
+@pytest.mark.parametrize("m,n,k,rank,rb", [(200, 384, 2048, 32, 256), (97, 1000, 512, 256, 16),
+                                           (4608, 3072, 3072, 128, 128)])
+def test_w4a4_lora_layer_fp6_equals_int4_path(ck, m, n, k, rank, rb):
+    lay = workloads.make_layer(m, k, n, seed=970 + m)
+    a, b = workloads.make_lora(np.random.default_rng(971 + m), rank, k, n)
+    w = torch.from_numpy(lay.weights[0]).cuda()
+    wp, ws = ck.quantize_weight_convrot(w, rb, 0)
+    wq6, ws6 = ck.quantize_weight_convrot_fp6(w, rb)
+    a_pack = ck.lora_prepare_down(torch.from_numpy(a).cuda(), rb)
+    b_pack = ck.lora_prepare_up(dev_bf16(b))
+    bias = torch.from_numpy(np.random.default_rng(972).standard_normal(n).astype(np.float32)).cuda()
+    x = dev_bf16(lay.x_bf16)
+    y4 = bf16_host_bits(ck.w4a4_lora_linear(x, wp, ws, a_pack, b_pack, 0.5, bias, rb))
+    y6 = bf16_host_bits(ck.w4a4_lora_linear_fp6(x, wq6, ws6, a_pack, b_pack, 0.5, bias, rb))
+    assert np.array_equal(y4, y6)
 
 
 def test_full_size_square_layer_with_lora(ck):
