@@ -29,7 +29,7 @@
 // Tiling: 288 x 192 output tiles (one per CU on the 4608 x 3072 layer), 8
 // waves of 144 x 48 (9 x 3 MFMA fragments; the first MFMA operand is the
 // weight fragment, so each lane's 4 accumulators are 4 consecutive output
-// columns of one row). Problems with fewer than 192 such tiles use 96 x 128
+// columns of one row). Where it takes fewer rounds of workgroups, 96 x 128
 // tiles of 4 waves (48 x 64, 3 x 4 fragments), two workgroups per CU. One k
 // step is 128 k (on the large tile: 30 blocks, 45 KB), copied global -> LDS
 // with buffer_load ... lds into a ring of 3 stages, two steps ahead of the
@@ -365,10 +365,14 @@ hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, 
                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                            LoraUp lora) {
     if (out_i32 || lora.t == nullptr) lora.rank = 0;
-    // one 288 x 192 tile per CU when that fills the chip; otherwise 96 x 128
-    // tiles of 4 waves (48 x 64 each), two workgroups per CU
-    const int64_t big_tiles = ((m + 287) / 288) * ((n + 191) / 192);
-    if (big_tiles >= 192)
+    // 288 x 192 tiles (one workgroup per CU) or 96 x 128 tiles of 4 waves
+    // (48 x 64 each, two workgroups per CU), whichever needs less time by the
+    // rounds of workgroups over the 256 CUs: on the part a round of large
+    // tiles takes about 16/9 the time of a round of small ones at the same K
+    // (30 against 17 us at K = 3072)
+    const int64_t big_rounds = (((m + 287) / 288) * ((n + 191) / 192) + 255) / 256;
+    const int64_t small_rounds = (((m + 95) / 96) * ((n + 127) / 128) + 511) / 512;
+    if (9 * small_rounds >= 16 * big_rounds)
         return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     return launch_fp6<96, 128, 2, 2, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
