@@ -681,9 +681,15 @@ hipError_t launch_s(const int8_t *a, const int8_t *b, const float *sa, const flo
                     int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                     LoraUp lora) {
     if (m <= 64) return launch_skinny<S4>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
-    // large shapes: one 288 x 192 tile per CU when that fills the chip
+    // 288 x 192 tiles (one workgroup per CU) or 128 x 128 tiles (two per CU).
+    // Packed int4: whichever needs less time by the rounds of workgroups over
+    // the 256 CUs (on the part a round of large tiles takes about 8/5 the time
+    // of a round of small ones at the same K: 40 against 25 us at K = 3072).
+    // int8 operands: large tiles once there are 192 of them.
     const int64_t big_tiles = ((m + 287) / 288) * ((n + 191) / 192);
-    if (big_tiles >= 192)
+    const int64_t big_rounds = (big_tiles + 255) / 256;
+    const int64_t small_rounds = (((m + 127) / 128) * ((n + 127) / 128) + 511) / 512;
+    if (S4 ? 5 * small_rounds > 8 * big_rounds : big_tiles >= 192)
         return launch_big<S4, 288, 192, 2, 4, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     return launch_big<S4, 128, 128, 2, 2, 2>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
