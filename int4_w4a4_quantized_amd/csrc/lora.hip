@@ -41,10 +41,11 @@
 // hold every fragment of every block size from 32 up; 16-blocks use P masked
 // to one half of the slice.
 //
-// A workgroup owns RT 16-row tiles; its 8 wavefronts split K in chunks of
-// max(128, b) elements. Each wavefront prefetches the next chunk of x while
-// it multiplies the current one. The partial sums meet in a fixed-order tree
-// through LDS.
+// A workgroup owns RT 16-row tiles (two when there are more than 256 tiles
+// and rank and block are at most 128, else one); its 8 wavefronts split K in
+// chunks of max(128, b) elements. Each wavefront prefetches the next chunks
+// of x (and, at rank 32, of a_rot) while it multiplies the current one. The
+// partial sums meet in a fixed-order tree through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -145,7 +146,14 @@ __global__ __launch_bounds__(64 * kWaves) void lora_down_kernel(const uint16_t *
 #pragma unroll
         for (int fr = 0; fr < NF; ++fr) tacc[rt][fr] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    v8bf xf[RT][KS], xn[RT][KS];
+    // One chunk's operands: its x fragments and its down-projection
+    // fragments. Two chunks are in flight ahead of the MFMAs, each loaded as
+    // a whole (x and a_rot together): memory loads retire in order, so a
+    // fragment load issued after a later chunk's prefetch would make the
+    // MFMAs wait for that prefetch too. Ranks whose fragments do not fit
+    // twice in registers load them per output pair, one chunk ahead.
+    constexpr bool PIPE = NP * NF <= 8;
+    constexpr int NA = PIPE ? NP : 1;
     auto load_x = [&](v8bf (&dst)[RT][KS], int ci) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -153,22 +161,29 @@ __global__ __launch_bounds__(64 * kWaves) void lora_down_kernel(const uint16_t *
             for (int kk = 0; kk < KS; ++kk)
                 dst[rt][kk] = *reinterpret_cast<const v8bf *>(xrow[rt] + (int64_t)ci * CH + 32 * kk);
     };
-    if (c_begin < c_end) load_x(xn, c_begin);
-
-    for (int ci = c_begin; ci < c_end; ++ci) {
+    auto load_af = [&](v8bf (&dst)[NF], int ci, int p) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int fr = 0; fr < NF; ++fr) {
+            const uint32_t so = (uint32_t)(fr * kq + ci * (CH / 32) + p) * 1024u;
+            dst[fr] = as_v8bf(__builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff, so, 0)));
+        }
+    };
+    auto load_chunk = [&](v8bf (&xd)[RT][KS], v8bf (&ad)[NA][NF], int ci) {
+        if constexpr (PIPE) {
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) xf[rt][kk] = xn[rt][kk];
-        if (ci + 1 < c_end) load_x(xn, ci + 1);
-        const int cb = ci * CH;
+            for (int p = 0; p < NP; ++p) load_af(ad[p], ci, p);
+        }
+        load_x(xd, ci);
+    };
+    auto compute = [&](const v8bf (&xf)[RT][KS], const v8bf (&ad)[NA][NF], int ci) {
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
             v8bf af[NF];
+            if constexpr (PIPE) {
 #pragma unroll
-            for (int fr = 0; fr < NF; ++fr) {
-                const uint32_t so = (uint32_t)(fr * kq + cb / 32 + p) * 1024u;
-                af[fr] = as_v8bf(__builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff, so, 0)));
+                for (int fr = 0; fr < NF; ++fr) af[fr] = ad[p][fr];
+            } else {
+                load_af(af, ci, p);
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -188,6 +203,31 @@ __global__ __launch_bounds__(64 * kWaves) void lora_down_kernel(const uint16_t *
 #pragma unroll
                 for (int fr = 0; fr < NF; ++fr) tacc[rt][fr] = mfma(af[fr], xr, tacc[rt][fr]);
             }
+        }
+    };
+
+    if constexpr (PIPE) {
+        v8bf x0[RT][KS], x1[RT][KS], a0[NA][NF], a1[NA][NF];
+        if (c_begin < c_end) load_chunk(x0, a0, c_begin);
+        if (c_begin + 1 < c_end) load_chunk(x1, a1, c_begin + 1);
+        for (int ci = c_begin; ci < c_end; ci += 2) {
+            compute(x0, a0, ci);
+            if (ci + 2 < c_end) load_chunk(x0, a0, ci + 2);
+            if (ci + 1 < c_end) {
+                compute(x1, a1, ci + 1);
+                if (ci + 3 < c_end) load_chunk(x1, a1, ci + 3);
+            }
+        }
+    } else {
+        v8bf xf[RT][KS], xn[RT][KS], none[NA][NF];
+        if (c_begin < c_end) load_x(xn, c_begin);
+        for (int ci = c_begin; ci < c_end; ++ci) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int kk = 0; kk < KS; ++kk) xf[rt][kk] = xn[rt][kk];
+            if (ci + 1 < c_end) load_x(xn, ci + 1);
+            compute(xf, none, ci);
         }
     }
 
@@ -259,10 +299,19 @@ __global__ __launch_bounds__(256) void lora_pack_kernel(const uint16_t *__restri
 template <int G, int RANK>
 hipError_t launch_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, const uint16_t *a_rot, float alpha,
                        uint16_t *t, hipStream_t stream) {
-    constexpr int RT = (RANK <= 128 && G <= 128) ? 2 : 1;
+    // two 16-row tiles per workgroup (half the re-reads of a_rot) once one
+    // tile per workgroup would take more than one workgroup per CU
+    constexpr bool CAN_RT2 = RANK <= 128 && G <= 128;
     const float c = (float)(1.0 / __builtin_sqrt((double)G));
-    const dim3 grid((unsigned)((m + 16 * RT - 1) / (16 * RT))), block(64 * kWaves);
-    lora_down_kernel<G, RANK, RT><<<grid, block, 0, stream>>>(x, (int)m, (int)k, ldx, c, a_rot, alpha, t);
+    const dim3 block(64 * kWaves);
+    if (CAN_RT2 && (m + 15) / 16 > 256) {
+        const dim3 grid((unsigned)((m + 31) / 32));
+        lora_down_kernel<G, RANK, CAN_RT2 ? 2 : 1><<<grid, block, 0, stream>>>(x, (int)m, (int)k, ldx, c, a_rot,
+                                                                                alpha, t);
+    } else {
+        const dim3 grid((unsigned)((m + 15) / 16));
+        lora_down_kernel<G, RANK, 1><<<grid, block, 0, stream>>>(x, (int)m, (int)k, ldx, c, a_rot, alpha, t);
+    }
     return hipGetLastError();
 }
 
