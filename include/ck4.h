@@ -187,9 +187,10 @@ ck4_status ck4_gemm_w4a4_acc_i32(const int8_t *x_q, const int8_t *w_packed, int6
  * are q_a q_b / 64, and the fp32 accumulator holds 64 x the integer sum
  * exactly for k <= 131072, so ck4_linear_w4a4_fp6 gives the same bits as
  * ck4_linear_w4a4 on the same codes and scales. The codes take 6 bits
- * instead of 4 (1.5x the bytes): this is the layout for m above 64; the int4
- * layout stays the one for weight-streaming calls (m <= 64, where
- * ck4_linear_w4a4 has a kernel of its own).
+ * instead of 4 (1.5x the bytes): this is the layout for compute-bound calls
+ * (m of a few hundred and more); the int4 layout stays the one for
+ * weight-streaming calls (small m, where the extra weight bytes cost more
+ * than the doubled matrix rate saves, and m <= 64 has a kernel of its own).
  *
  * FP6 operand layout ("q6", ck4_fp6_bytes(rows, k) bytes, 16-byte aligned):
  * rows padded to a multiple of 16 (the padding rows are never written by the
@@ -406,7 +407,7 @@ ck4_status ck4_linear_w4a4_lora(const int8_t *x_q, const float *x_scales, const 
  * The same LoRA epilogue on the FP6 operand path (the FP6 block above):
  * ck4_linear_w4a4_lora from x_q6 and w_q6, bit for bit. Arguments, ranks,
  * alignment and errors as ck4_linear_w4a4_lora and ck4_linear_w4a4_fp6. For
- * the callers of the FP6 layout (m above 64).
+ * the callers of the FP6 layout (compute-bound calls).
  */
 ck4_status ck4_linear_w4a4_fp6_lora(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
                                     const float *w_scales, const float *bias, const uint16_t *t_pack,
