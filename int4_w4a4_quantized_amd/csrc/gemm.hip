@@ -616,6 +616,170 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
     }
 }
 
+// Skinny GEMM for 16 < M <= 64 (packed int4, bf16 epilogue) with the waves of
+// a workgroup splitting N instead of K: wave w owns the 16 weight rows
+// 16 (NW blockIdx + w) and all of K, and the workgroup's waves share one LDS
+// copy of the activation, so each workgroup reads the activation once for
+// 16 NW weight rows (the K-split kernel above reads it once per 16). Both
+// operands move through a ring of three chunks of CS k-steps (two in flight
+// while one is read), copied
+// global -> LDS with buffer_load ... lds (8 rows x 128 bytes per instruction,
+// 16-byte chunks XOR-swizzled by row as above), the copies of a chunk split
+// over the waves. Memory operations retire in order, so waiting for all but
+// the next chunks' copies leaves exactly the current chunk complete; every
+// operand then comes from LDS. No partial sums are exchanged.
+template <bool S4, int FM, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_shared_kernel(
+    const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
+    const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int steps,
+    uint16_t *__restrict__ Y, int64_t ldy) {
+    constexpr int SLAB = 128;                 // bytes of a row per k-step
+    constexpr int CS = 2;                     // k-steps per chunk
+    constexpr int AROWS = 16 * FM;            // activation rows (padded)
+    constexpr int ROWS = AROWS + 16 * NW;     // staged rows per k-step: activation, then weights
+    constexpr int STEP_B = ROWS * SLAB;       // LDS bytes of one k-step
+    constexpr int NINS = ROWS / 8 * CS;       // copy instructions per chunk
+    constexpr int PER = (NINS + NW - 1) / NW; // per wave (surplus slots repeat another wave's)
+    static_assert(NINS >= NW && 2 * PER <= 63, "copy plan");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * CS * STEP_B];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int nw0 = blockIdx.x * NW * 16;                 // the workgroup's first weight row
+    const int rows_w = min(16 * NW, N - nw0);             // weight rows that exist
+    const bool has_rows = 16 * wave < rows_w;             // this wave's rows exist
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(A), (short)0, M * row_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(B) + (int64_t)nw0 * row_bytes, (short)0, rows_w * row_bytes, 0x00020000);
+    const int frow = lane & 15;
+    const int fgrp = lane >> 4;
+    const int crow = lane >> 3;
+    const uint32_t c_off = (uint32_t)(((lane & 7) ^ crow) * 16);
+    const int nch = (steps + CS - 1) / CS;
+
+    v4i acc[FM];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[j] = v4i{0, 0, 0, 0};
+
+    // this wave's share of chunk c's copies into `slot` (steps past the last
+    // repeat the last step; they are never read)
+    auto issue = [&](int c, uint8_t *slot) {
+#pragma unroll
+        for (int t = 0; t < PER; ++t) {
+            int q = t * NW + wave;
+            if (q >= NINS) q -= NW;
+            const int st = q / (ROWS / 8), rg = q % (ROWS / 8);
+            const int s = min(c * CS + st, steps - 1);
+            const bool is_a = 8 * rg < AROWS;
+            const int r = (is_a ? 8 * rg : 8 * rg - AROWS) + crow;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                is_a ? ra : rb, (__attribute__((address_space(3))) void *)(slot + st * STEP_B + rg * 1024), 16,
+                (uint32_t)r * (uint32_t)row_bytes + (uint32_t)(s * SLAB) + c_off, 0, 0, 0);
+        }
+    };
+    // wait for chunk c (`later` next chunks' copies may stay in flight), then
+    // every wave's part of it has landed
+    auto wait_chunk = [&](int later) {
+        constexpr int P1 = PER, P2 = 2 * PER;
+        if (later == 2) __builtin_amdgcn_s_waitcnt((P2 & 15) | ((P2 >> 4) << 14) | 0x0f70);
+        else if (later == 1) __builtin_amdgcn_s_waitcnt((P1 & 15) | ((P1 >> 4) << 14) | 0x0f70);
+        else __builtin_amdgcn_s_waitcnt(0x0f70);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+    auto compute = [&](int c, const uint8_t *slot) {
+#pragma unroll
+        for (int st = 0; st < CS; ++st) {
+            if (c * CS + st >= steps) break;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int coff = ((4 * h + fgrp) ^ (frow & 7)) * 16;
+                const uint8_t *sp = slot + st * STEP_B;
+                const uint4 wp = *reinterpret_cast<const uint4 *>(sp + (AROWS + 16 * wave + frow) * SLAB + coff);
+                const v4i wl = widen_lo(wp), wh = widen_hi(wp);
+#pragma unroll
+                for (int j = 0; j < FM; ++j) {
+                    const uint4 xp = *reinterpret_cast<const uint4 *>(sp + (j * 16 + frow) * SLAB + coff);
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wl, widen_lo(xp), acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wh, widen_hi(xp), acc[j], 0, 0, 0);
+                }
+            }
+        }
+        // every wave is done reading the slot before it is filled again
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    // one chunk: copy chunk c + 2 into the slot chunk c - 1 used (every wave
+    // has left it at the barrier ending chunk c - 1), wait for chunk c,
+    // compute. The slots arrive as __restrict__ parameters of an inlined
+    // function, so the compiler knows the copies in flight do not write the
+    // slot being read and adds no wait of its own for them.
+    auto body = [&](int c, const uint8_t *__restrict__ cur, uint8_t *__restrict__ nxt2) {
+        if (c + 2 < nch) issue(c + 2, nxt2);
+        wait_chunk(c + 2 < nch ? 2 : (c + 1 < nch ? 1 : 0));
+        compute(c, cur);
+    };
+    uint8_t *slot0 = lds, *slot1 = lds + CS * STEP_B, *slot2 = lds + 2 * CS * STEP_B;
+    issue(0, slot0);
+    if (nch > 1) issue(1, slot1);
+    for (int c = 0; c < nch; c += 3) {
+        body(c, slot0, slot2);
+        if (c + 1 >= nch) break;
+        body(c + 1, slot1, slot0);
+        if (c + 2 >= nch) break;
+        body(c + 2, slot2, slot1);
+    }
+
+    if (!has_rows) return;
+    const int n0 = nw0 + 16 * wave;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+        const int m = j * 16 + frow;
+        if (m >= M) continue;
+        const float sam = sa[m];
+        const int nb = n0 + 4 * fgrp;
+        if (nb >= N) continue;
+        uint16_t o[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int n = nb + r < N ? nb + r : N - 1;
+            float v = ((float)(acc[j][r] >> 8) * sam) * sb[n];
+            if (bias) v = v + bias[n];
+            o[r] = f32_to_bf16(v);
+        }
+        uint16_t *yr = Y + (int64_t)m * ldy + nb;
+        if (nb + 3 < N) {
+            *reinterpret_cast<uint2 *>(yr) =
+                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+        } else {
+            for (int r = 0; r < 4 && nb + r < N; ++r) yr[r] = o[r];
+        }
+    }
+}
+
+template <int FM, int NW>
+hipError_t launch_skinny_shared_nw(const int8_t *a, const int8_t *b, const float *sa, const float *sb,
+                                   const float *bias, int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy,
+                                   hipStream_t stream) {
+    const int64_t tiles = (n + 15) / 16;
+    const dim3 grid((unsigned)((tiles + NW - 1) / NW)), block(64 * NW);
+    gemm_skinny_shared_kernel<true, FM, NW><<<grid, block, 0, stream>>>(a, b, sa, sb, bias, (int)m, (int)n,
+                                                                         (int)(k / 2), (int)(k / 256), y, ldy);
+    return hipGetLastError();
+}
+
+// waves per workgroup: about one workgroup per CU on the weight tiles
+template <int FM>
+hipError_t launch_skinny_shared(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
+                                int64_t m, int64_t n, int64_t k, uint16_t *y, int64_t ldy, hipStream_t stream) {
+    const int64_t per_cu = ((n + 15) / 16) / 256;
+    if (per_cu >= 4) return launch_skinny_shared_nw<FM, 4>(a, b, sa, sb, bias, m, n, k, y, ldy, stream);
+    if (per_cu == 3) return launch_skinny_shared_nw<FM, 3>(a, b, sa, sb, bias, m, n, k, y, ldy, stream);
+    return launch_skinny_shared_nw<FM, 2>(a, b, sa, sb, bias, m, n, k, y, ldy, stream);
+}
+
 // MAXS: k-steps in flight per wavefront. Direct loads: 4, or 2 with a 64-row
 // activation (the VGPR budget of 2 waves per SIMD). Staged: 1 to 4, about
 // 20 KB of copy slots per wavefront, so that a CU's 160 KB of LDS holds eight
@@ -672,6 +836,13 @@ hipError_t launch_skinny(const int8_t *a, const int8_t *b, const float *sa, cons
                          int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                          LoraUp lora) {
     if (m <= 16) return launch_skinny_ks<S4, 1, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    if constexpr (S4) {
+        // the shared-activation kernel needs two or more weight tiles per CU
+        if (m > 32 && !out_i32 && lora.rank == 0 && (n + 15) / 16 >= 512)
+            return launch_skinny_shared<4>(a, b, sa, sb, bias, m, n, k, static_cast<uint16_t *>(y), ldy, stream);
+        if (m > 16 && !out_i32 && lora.rank == 0 && (n + 15) / 16 >= 512)
+            return launch_skinny_shared<2>(a, b, sa, sb, bias, m, n, k, static_cast<uint16_t *>(y), ldy, stream);
+    }
     if (m <= 32) return launch_skinny_ks<S4, 2, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     return launch_skinny_ks<S4, 4, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }

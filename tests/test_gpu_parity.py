@@ -589,6 +589,28 @@ def test_full_size_layer(ck, name):
         assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], ws_ref))
 
 
+@pytest.mark.parametrize("m,n,k", [(17, 12288, 3072), (32, 12288, 3072), (33, 8200, 768), (48, 8200, 1280),
+                                   (64, 16384, 512), (40, 12288, 256), (24, 8200, 2304)])
+def test_skinny_shared_activation_kernel(ck, m, n, k):
+    """16 < m <= 64 with at least 512 weight tiles of 16 rows: the kernel whose waves split N over one LDS copy of
+    the activation (ragged N leaves a wave with no rows; k = 256 is a single step). It must give the bits of the
+    K-split kernel, reached through the LoRA epilogue with t = 0 (bias present, so no -0 can meet the + 0), and
+    stay within the oracle's bf16 bound."""
+    _, xq, sx, wp, ws = _quantised_pair(m, n, k, 3300 + m)
+    bias = np.random.default_rng(3301).standard_normal(n).astype(np.float32)
+    d = [torch.from_numpy(v).cuda() for v in (xq, sx, wp, ws)]
+    bd = torch.from_numpy(bias).cuda()
+    y = bf16_host_bits(ck.linear_w4a4(*d, bd))
+    t0 = torch.zeros((frag_layout.rows16(m), 32), dtype=torch.bfloat16, device="cuda")
+    b0 = torch.zeros((frag_layout.rows16(n), 32), dtype=torch.bfloat16, device="cuda")
+    y_ksplit = bf16_host_bits(ck.linear_w4a4_lora(*d, t0, b0, bd))
+    assert np.array_equal(y, y_ksplit)
+    acc = oracle.gemm_acc(xq, wp, k)
+    # fp32 epilogue: a few fp32 roundings of the two summands, then bf16 (as test_linear_w4a4)
+    terms = np.abs(acc * sx.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]) + np.abs(bias)
+    assert_bf16_close(y, oracle.epilogue_bf16(acc, sx, ws, bias), atol=2.0 ** -21 * terms)
+
+
 @pytest.mark.parametrize("m", [1, 8, 16, 64])
 @pytest.mark.parametrize("n,k", [(12288, 3072), (5120, 5120)])
 def test_skinny_layers(ck, m, n, k):
