@@ -82,7 +82,7 @@ def _traffic_for_current_kernel(source: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(m: int, k: int, n: int, rows: int, reps: int = 3) -> dict:
+def cpu_baseline(m: int, k: int, n: int, rows: int, reps: int = 11) -> dict:
     """The CPU oracle, as it stands, on the first `rows` rows of the workload
     (median of `reps` runs)."""
     import oracle
