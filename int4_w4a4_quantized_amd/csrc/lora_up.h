@@ -35,16 +35,26 @@ __device__ __forceinline__ void lora_up(lora_v4f (&y)[FN][FM], const LoraUp lo, 
     for (int i = 0; i < FN; ++i) bp[i] = lo.b + (int64_t)min(nbase / 16 + i, nb_last) * tq * 512 + lane * 8;
 #pragma unroll
     for (int j = 0; j < FM; ++j) tp[j] = lo.t + (int64_t)min(mbase / 16 + j, mb_last) * tq * 512 + lane * 8;
-    for (int kk = 0; kk < tq; ++kk) {
-        lora_v8bf bf[FN], tf[FM];
+    // slices in pairs, the second slice's loads issued before the first
+    // slice's MFMAs (loads retire in order, so those MFMAs do not wait for them)
+    auto load = [&](lora_v8bf (&bf)[FN], lora_v8bf (&tf)[FM], int kk) {
 #pragma unroll
         for (int i = 0; i < FN; ++i) bf[i] = *reinterpret_cast<const lora_v8bf *>(bp[i] + kk * 512);
 #pragma unroll
         for (int j = 0; j < FM; ++j) tf[j] = *reinterpret_cast<const lora_v8bf *>(tp[j] + kk * 512);
+    };
+    auto madd = [&](const lora_v8bf (&bf)[FN], const lora_v8bf (&tf)[FM]) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j) y[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf[i], tf[j], y[i][j], 0, 0, 0);
+    };
+    for (int kk = 0; kk < tq; kk += 2) {
+        lora_v8bf b0[FN], t0[FM], b1[FN], t1[FM];
+        load(b0, t0, kk);
+        if (kk + 1 < tq) load(b1, t1, kk + 1);
+        madd(b0, t0);
+        if (kk + 1 < tq) madd(b1, t1);
     }
 }
 
