@@ -611,6 +611,40 @@ def test_skinny_shared_activation_kernel(ck, m, n, k):
     assert_bf16_close(y, oracle.epilogue_bf16(acc, sx, ws, bias), atol=2.0 ** -21 * terms)
 
 
+def test_random_shapes_kernel_variants_agree(ck):
+    """Seeded random shapes through the kernel choices that must give the same bits: the N-split skinny kernel
+    against the K-split one (through its LoRA epilogue with t = 0), and the FP6 GEMM (either tile) against the
+    int4 GEMM, with a bias, on device-quantised operands."""
+    rng = np.random.default_rng(4242)
+    for _ in range(8):
+        m = int(rng.integers(17, 65))
+        n = int(rng.integers(2048, 5000)) * 4
+        k = 256 * int(rng.integers(1, 13))
+        x = dev_bf16(workloads.make_activations(rng, m, k))
+        w = torch.from_numpy(workloads.make_weight(rng, n, k)).cuda()
+        bias = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
+        wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+        xq, sx = ck.rotate_quantize_act(x, 128, 4)
+        t0 = torch.zeros((frag_layout.rows16(m), 32), dtype=torch.bfloat16, device="cuda")
+        b0 = torch.zeros((frag_layout.rows16(n), 32), dtype=torch.bfloat16, device="cuda")
+        y = bf16_host_bits(ck.linear_w4a4(xq, sx, wp, ws, bias))
+        assert np.array_equal(y, bf16_host_bits(ck.linear_w4a4_lora(xq, sx, wp, ws, t0, b0, bias))), (m, n, k)
+    for _ in range(8):
+        m = int(rng.integers(65, 3000))
+        n = int(rng.integers(16, 1000)) * 4
+        k = 256 * int(rng.integers(1, 9))
+        x = dev_bf16(workloads.make_activations(rng, m, k))
+        w = torch.from_numpy(workloads.make_weight(rng, n, k)).cuda()
+        bias = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
+        wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+        wq6, ws6 = ck.quantize_weight_convrot_fp6(w, 128)
+        xq, sx = ck.rotate_quantize_act(x, 128, 4)
+        xq6, sx6 = ck.rotate_quantize_act_fp6(x, 128)
+        y4 = bf16_host_bits(ck.linear_w4a4(xq, sx, wp, ws, bias))
+        y6 = bf16_host_bits(ck.linear_w4a4_fp6(xq6, sx6, wq6, ws6, bias))
+        assert np.array_equal(y4, y6), (m, n, k)
+
+
 @pytest.mark.parametrize("m", [1, 8, 16, 64])
 @pytest.mark.parametrize("n,k", [(12288, 3072), (5120, 5120)])
 def test_skinny_layers(ck, m, n, k):
