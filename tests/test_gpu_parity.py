@@ -611,6 +611,31 @@ def test_skinny_shared_activation_kernel(ck, m, n, k):
     assert_bf16_close(y, oracle.epilogue_bf16(acc, sx, ws, bias), atol=2.0 ** -21 * terms)
 
 
+@pytest.mark.parametrize("m,n,k,group,e4m3", [(17, 12288, 3072, 128, False), (32, 12288, 1024, 64, True),
+                                               (33, 12300, 3072, 128, False), (64, 12288, 3072, 256, True),
+                                               (48, 16000, 2048, 128, False), (64, 12296, 256, 128, False),
+                                               (40, 12288, 4096, 64, False)])
+def test_w4a8_fused_wide_n_equals_decode_path(ck, m, n, k, group, e4m3):
+    """16 < m <= 64 at large and ragged N (k = 256 is a single step): the fused W4A8 kernel must give the bits of
+    one decode pass + the int8 GEMM, and stay within the oracle's bf16 bound."""
+    rng = np.random.default_rng(3500 + m + group)
+    xb = workloads.make_activations(rng, m, k)
+    w = torch.from_numpy(workloads.make_weight(rng, n, k)).cuda()
+    if e4m3:
+        wp, gs = ck.quantize_weight_convrot_e4m3(w, 128, group)
+    else:
+        wp, gs = ck.quantize_weight_convrot(w, 128, group)
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    y0 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wp, gs, group, 0))
+    y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wp, gs, group, -1))
+    assert np.array_equal(y0, y1)
+    if e4m3:
+        ref = oracle.linear_w4a8_grouped_e4m3(xb, host(wp), host(gs).view(np.uint8), group)
+    else:
+        ref = oracle.linear_w4a8_grouped(xb, host(wp), host(gs), group)
+    assert_bf16_close(y0, ref)
+
+
 def test_random_shapes_kernel_variants_agree(ck):
     """Seeded random shapes through the kernel choices that must give the same bits: the N-split skinny kernel
     against the K-split one (through its LoRA epilogue with t = 0), and the FP6 GEMM (either tile) against the
