@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped (not failed) where no GPU is visible; on a GPU machine
+    # GPU tests are skipped (not failed) where no GPU is visible; on a machine with one
     # they run through the C ABI of the built library.
     try:
         import torch
