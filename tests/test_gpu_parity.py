@@ -924,6 +924,17 @@ def test_graph_replays_match_eager(ck):
     y8 = torch.empty((8, n), dtype=torch.bfloat16, device="cuda")
     y8c = torch.empty((8, 528), dtype=torch.bfloat16, device="cuda")[:, :n]  # the chunked path needs ldy % 16 == 0
     wsp = torch.empty((ck.w4a8_workspace_bytes(8, n, k, 256),), dtype=torch.uint8, device="cuda")
+    # the FP6 operand path, plain and with the LoRA epilogue
+    wq6, ws6 = ck.quantize_weight_convrot_fp6(wd, 128)
+    xq6 = torch.zeros((frag_layout.rows16(m), k * 3 // 4), dtype=torch.uint8, device="cuda")  # padding rows stay 0
+    sx6 = torch.empty((m,), dtype=torch.float32, device="cuda")
+    y6 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    y6l = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    # the N-split skinny kernel (16 < m <= 64, at least 512 weight tiles)
+    ns, ms = 8192, 40
+    wsk, wssk = ck.quantize_weight_convrot(
+        torch.from_numpy(workloads.make_weight(np.random.default_rng(972), ns, k)).cuda(), 128, 0)
+    ysk = torch.empty((ms, ns), dtype=torch.bfloat16, device="cuda")
 
     def step():
         ck.rotate_quantize_act(xd, 128, 4, out=xq, scales=sx)
@@ -933,8 +944,12 @@ def test_graph_replays_match_eager(ck):
         ck.rotate_quantize_act(xs, 128, 8, out=xq8, scales=sx8)
         ck.linear_w4a8_grouped(xq8, sx8, wg, gs, 128, 0, out=y8)
         ck.linear_w4a8_grouped(xq8, sx8, wg, gs, 128, 256, out=y8c, workspace=wsp)
+        ck.rotate_quantize_act_fp6(xd, 128, out=xq6, scales=sx6)
+        ck.linear_w4a4_fp6(xq6, sx6, wq6, ws6, None, out=y6)
+        ck.linear_w4a4_fp6_lora(xq6, sx6, wq6, ws6, t, b_pack, None, out=y6l)
+        ck.linear_w4a4(xq[:ms], sx[:ms], wsk, wssk, None, out=ysk)
 
-    outs = (xq, sx, t, y, yl, y8, y8c)
+    outs = (xq, sx, t, y, yl, y8, y8c, xq6, sx6, y6, y6l, ysk)
     step()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
