@@ -616,7 +616,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
     }
 }
 
-// Skinny GEMM for 16 < M <= 64 (packed int4, bf16 epilogue) with the waves of
+// Skinny GEMM for 4 < M <= 64 (packed int4, bf16 epilogue) with the waves of
 // a workgroup splitting N instead of K: wave w owns the 16 weight rows
 // 16 (NW blockIdx + w) and all of K, and the workgroup's waves share one LDS
 // copy of the activation, so each workgroup reads the activation once for
@@ -835,9 +835,14 @@ template <bool S4>
 hipError_t launch_skinny(const int8_t *a, const int8_t *b, const float *sa, const float *sb, const float *bias,
                          int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                          LoraUp lora) {
+    if constexpr (S4) {
+        // the shared-activation kernel needs two or more weight tiles per CU;
+        // at M <= 4 the activation is too small for sharing it to pay
+        if (m > 4 && m <= 16 && !out_i32 && lora.rank == 0 && (n + 15) / 16 >= 512)
+            return launch_skinny_shared<1>(a, b, sa, sb, bias, m, n, k, static_cast<uint16_t *>(y), ldy, stream);
+    }
     if (m <= 16) return launch_skinny_ks<S4, 1, 1>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     if constexpr (S4) {
-        // the shared-activation kernel needs two or more weight tiles per CU
         if (m > 32 && !out_i32 && lora.rank == 0 && (n + 15) / 16 >= 512)
             return launch_skinny_shared<4>(a, b, sa, sb, bias, m, n, k, static_cast<uint16_t *>(y), ldy, stream);
         if (m > 16 && !out_i32 && lora.rank == 0 && (n + 15) / 16 >= 512)

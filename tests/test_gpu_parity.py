@@ -590,9 +590,10 @@ def test_full_size_layer(ck, name):
 
 
 @pytest.mark.parametrize("m,n,k", [(17, 12288, 3072), (32, 12288, 3072), (33, 8200, 768), (48, 8200, 1280),
-                                   (64, 16384, 512), (40, 12288, 256), (24, 8200, 2304)])
+                                   (64, 16384, 512), (40, 12288, 256), (24, 8200, 2304), (5, 12288, 3072),
+                                   (8, 8200, 768), (16, 12288, 1280)])
 def test_skinny_shared_activation_kernel(ck, m, n, k):
-    """16 < m <= 64 with at least 512 weight tiles of 16 rows: the kernel whose waves split N over one LDS copy of
+    """4 < m <= 64 with at least 512 weight tiles of 16 rows: the kernel whose waves split N over one LDS copy of
     the activation (ragged N leaves a wave with no rows; k = 256 is a single step). It must give the bits of the
     K-split kernel, reached through the LoRA epilogue with t = 0 (bias present, so no -0 can meet the + 0), and
     stay within the oracle's bf16 bound."""
@@ -642,7 +643,7 @@ def test_random_shapes_kernel_variants_agree(ck):
     int4 GEMM, with a bias, on device-quantised operands."""
     rng = np.random.default_rng(4242)
     for _ in range(8):
-        m = int(rng.integers(17, 65))
+        m = int(rng.integers(5, 65))
         n = int(rng.integers(2048, 5000)) * 4
         k = 256 * int(rng.integers(1, 13))
         x = dev_bf16(workloads.make_activations(rng, m, k))
