@@ -622,12 +622,12 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
 // copy of the activation, so each workgroup reads the activation once for
 // 16 NW weight rows (the K-split kernel above reads it once per 16). Both
 // operands move through a ring of three chunks of CS k-steps (two in flight
-// while one is read), copied
-// global -> LDS with buffer_load ... lds (8 rows x 128 bytes per instruction,
-// 16-byte chunks XOR-swizzled by row as above), the copies of a chunk split
-// over the waves. Memory operations retire in order, so waiting for all but
-// the next chunks' copies leaves exactly the current chunk complete; every
-// operand then comes from LDS. No partial sums are exchanged.
+// while one is read), copied global -> LDS with buffer_load ... lds (8 rows
+// x 128 bytes per instruction, 16-byte chunks XOR-swizzled by row as above),
+// the copies of a chunk split over the waves. Memory operations retire in
+// order, so waiting for all but the next chunks' copies leaves exactly the
+// current chunk complete; every operand then comes from LDS. No partial sums
+// are exchanged.
 template <bool S4, int FM, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_shared_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
@@ -641,6 +641,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_shared_kernel(
     constexpr int NINS = ROWS / 8 * CS;       // copy instructions per chunk
     constexpr int PER = (NINS + NW - 1) / NW; // per wave (surplus slots repeat another wave's)
     static_assert(NINS >= NW && 2 * PER <= 63, "copy plan");
+    static_assert(S4, "packed int4 operands only (both are widened)");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[3 * CS * STEP_B];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
