@@ -222,6 +222,15 @@ ck4_status ck4_linear_w4a4_fp6(const uint8_t *x_q6, const float *x_scales, const
                                uint16_t *y, int64_t ldy, void *stream);
 ck4_status ck4_gemm_w4a4_fp6_acc_i32(const uint8_t *x_q6, const uint8_t *w_q6, int64_t m, int64_t n, int64_t k,
                                      int32_t *acc, int64_t ldacc, void *stream);
+/*
+ * The output tile (tile_m x tile_n, host ints) that ck4_linear_w4a4_fp6 and
+ * ck4_gemm_w4a4_fp6_acc_i32 use for an m x n x k product: 288 x 192 with
+ * eight waves, or 96 x 128 with four, whichever takes fewer estimated rounds
+ * of workgroups over the 256 compute units. Host-only (launches nothing,
+ * needs no device); the same shape errors as ck4_gemm_w4a4_fp6_acc_i32.
+ * For benchmarks and tests that must know which kernel a shape reaches.
+ */
+ck4_status ck4_gemm_fp6_tile(int64_t m, int64_t n, int64_t k, int *tile_m, int *tile_n);
 
 /*
  * Grouped int4 -> int8 weight decode of rows [n0, n0 + nc) ([PR #97] What

@@ -66,6 +66,7 @@ SIGNATURES = {
     "ck4_quantize_weight_convrot_fp6": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
     "ck4_linear_w4a4_fp6": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_gemm_w4a4_fp6_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_gemm_fp6_tile": ([_I64, _I64, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
     "ck4_linear_w4a4_fp6_lora": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_lora_prepare_down": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_lora_prepare_up": ([_P, _I64, _I64, _I64, _P, _P], _I),
@@ -108,15 +109,71 @@ def _stream(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t: torch.Tensor, dtype: torch.dtype, name: str, dims: int | None = None) -> None:
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
-    if t.dtype != dtype:
-        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+# Argument checks. Every wrapper checks types, dtypes, shapes, lengths and
+# layouts of all its tensors first and their device last, before it calls the
+# library: the kernels derive every buffer extent from m, n and k, so a short or
+# mismatched tensor must be refused here rather than read out of bounds.
+
+def _typed(t, dtype, name: str, dims: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
     if dims is not None and t.dim() != dims:
         raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
-    if t.stride(-1) != 1:
+    if t.dim() > 0 and t.stride(-1) != 1:
         raise ValueError(f"{name} must have unit stride in its last dim")
+
+
+def _dense(t, dtype, name: str, dims: int | None = None) -> None:
+    """A contiguous tensor (the kernels take its rows back to back)."""
+    _typed(t, dtype, name, dims)
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _vec(t, dtype, name: str, count: int) -> None:
+    """A contiguous vector holding at least `count` elements."""
+    _dense(t, dtype, name)
+    if t.numel() < count:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {count}")
+
+
+def _on_gpu(**tensors) -> None:
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other operands on {dev}")
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str, dims: int | None = None) -> None:
+    _typed(t, dtype, name, dims)
+    _on_gpu(**{name: t})
+
+
+def _out_checked(out, m: int, n: int, dtype=torch.bfloat16, name: str = "out") -> None:
+    _typed(out, dtype, name, 2)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"{name} must have shape {(m, n)}, got {tuple(out.shape)}")
+
+
+def _fp6_nbytes(rows: int, k: int) -> int:
+    return (rows + 15) // 16 * 16 * (k // 128) * 96
+
+
+def _fp6_k(q6, name: str) -> int:
+    """k of an FP6 operand [rows16, 3k/4] (k a multiple of 128)."""
+    _dense(q6, torch.uint8, name, 2)
+    if q6.shape[1] % 96 != 0:
+        raise ValueError(f"{name} has {q6.shape[1]} bytes per row: not 3k/4 for k a multiple of 128")
+    return q6.shape[1] * 4 // 3
 
 
 def _out_bf16(m: int, n: int, device) -> torch.Tensor:
@@ -203,8 +260,15 @@ def quantize_weight_convrot_int8(w: torch.Tensor, rot_block: int = 128):
 
 def rotate_quantize_act(x: torch.Tensor, rot_block: int = 128, bits: int = 4, out=None, scales=None):
     """Dynamic rotate + quantise: bf16 [m, k] -> (int8 [m, k/2] (bits 4) or [m, k] (bits 8), fp32 [m])."""
-    _need(x, torch.bfloat16, "x", 2)
+    _typed(x, torch.bfloat16, "x", 2)
     m, k = x.shape
+    if out is not None:
+        _dense(out, torch.int8, "out", 2)
+        if tuple(out.shape) != (m, k // 2 if bits == 4 else k):
+            raise ValueError(f"out must have shape {(m, k // 2 if bits == 4 else k)}, got {tuple(out.shape)}")
+    if scales is not None:
+        _vec(scales, torch.float32, "scales", m)
+    _on_gpu(x=x, out=out, scales=scales)
     if out is None:
         out = torch.empty((m, k // 2 if bits == 4 else k), dtype=torch.int8, device=x.device)
     if scales is None:
@@ -225,14 +289,33 @@ def rotate_act_f32(x: torch.Tensor, rot_block: int = 128):
     return r
 
 
+def _check_gemm(x, w, x_scales, w_scales, bias, out, dtype, what: str):
+    """Operands of a GEMM wrapper: x [m, c] and w [n, c] of `dtype`, contiguous,
+    with the same row width c; scales and bias long enough; out [m, n] bf16."""
+    _dense(x, dtype, "x_" + what, 2)
+    _dense(w, dtype, "w_" + what, 2)
+    if w.shape[1] != x.shape[1]:
+        raise ValueError(f"the weight rows hold {w.shape[1]} bytes, the activation rows {x.shape[1]}: k differs")
+    m, n = x.shape[0], w.shape[0]
+    if x_scales is not None:
+        _vec(x_scales, torch.float32, "x_scales", m)
+    if w_scales is not None:
+        _vec(w_scales, torch.float32, "w_scales", n)
+    if bias is not None:
+        _vec(bias, torch.float32, "bias", n)
+    if out is not None:
+        _out_checked(out, m, n)
+    _on_gpu(x=x, w=w, x_scales=x_scales, w_scales=w_scales, bias=bias, out=out)
+    return m, n
+
+
 def linear_w4a4(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
                 bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
     """y bf16 [m, n] from a quantised activation and a prepared weight."""
-    m, k = x_q.shape[0], x_q.shape[1] * 2
-    n = w_packed.shape[0]
+    m, n = _check_gemm(x_q, w_packed, x_scales, w_scales, bias, out, torch.int8, "q")
+    k = x_q.shape[1] * 2
     if out is None:
         out = _out_bf16(m, n, x_q.device)
-    _need(out, torch.bfloat16, "out", 2)
     _check("ck4_linear_w4a4",
            lib().ck4_linear_w4a4(_ptr(x_q), _ptr(x_scales), _ptr(w_packed), _ptr(w_scales), _ptr(bias), m, n, k,
                                  _ptr(out), out.stride(0), _stream(x_q.device)))
@@ -241,8 +324,8 @@ def linear_w4a4(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.Tenso
 
 def gemm_w4a4_acc_i32(x_q: torch.Tensor, w_packed: torch.Tensor):
     """Exact int32 accumulators [m, n] of the W4A4 GEMM (same kernel, int32 store)."""
-    m, k = x_q.shape[0], x_q.shape[1] * 2
-    n = w_packed.shape[0]
+    m, n = _check_gemm(x_q, w_packed, None, None, None, None, torch.int8, "q")
+    k = x_q.shape[1] * 2
     ldacc = (n + 3) // 4 * 4
     acc = torch.empty((m, ldacc), dtype=torch.int32, device=x_q.device)
     _check("ck4_gemm_w4a4_acc_i32",
@@ -263,9 +346,16 @@ def dequant_w4a8_grouped(w_packed: torch.Tensor, group_scales: torch.Tensor, gro
     group_scales: fp32, or uint8 holding E4M3 bytes. codebook: the 16 host
     entries the weight was prepared with, or None for plain int4 codes.
     """
+    _dense(w_packed, torch.int8, "w_packed", 2)
     n, k = w_packed.shape[0], w_packed.shape[1] * 2
     if nc is None:
         nc = n - n0
+    if group <= 0 or k % group != 0:
+        raise ValueError(f"group={group} must divide k={k}")
+    _vec(group_scales, (torch.float32, torch.uint8), "group_scales", n * (k // group))
+    if not (0 <= n0 and 0 < nc and n0 + nc <= n):
+        raise ValueError(f"rows [{n0}, {n0 + nc}) are not inside [0, {n})")
+    _on_gpu(w_packed=w_packed, group_scales=group_scales)
     w8 = torch.empty((nc, k), dtype=torch.int8, device=w_packed.device)
     sr = torch.empty((nc,), dtype=torch.float32, device=w_packed.device)
     e4m3 = group_scales.dtype == torch.uint8
@@ -282,8 +372,8 @@ def dequant_w4a8_grouped(w_packed: torch.Tensor, group_scales: torch.Tensor, gro
 
 def linear_w8a8(x_q8, x_scales, w8, w_scales, bias=None, out=None):
     """Rowwise int8 linear from int8 activations and int8 weights -> bf16 [m, n]."""
-    m, k = x_q8.shape
-    n = w8.shape[0]
+    m, n = _check_gemm(x_q8, w8, x_scales, w_scales, bias, out, torch.int8, "q8")
+    k = x_q8.shape[1]
     if out is None:
         out = _out_bf16(m, n, x_q8.device)
     _check("ck4_linear_w8a8",
@@ -311,8 +401,22 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
     group_scales: fp32, or uint8 holding E4M3 bytes. codebook: the 16 host
     entries the weight was prepared with, or None.
     """
+    _dense(x_q8, torch.int8, "x_q8", 2)
+    _dense(w_packed, torch.int8, "w_packed", 2)
     m, k = x_q8.shape
     n = w_packed.shape[0]
+    if w_packed.shape[1] * 2 != k:
+        raise ValueError(f"w_packed rows hold {w_packed.shape[1]} bytes, the int8 activation has k={k}")
+    if group <= 0 or k % group != 0:
+        raise ValueError(f"group={group} must divide k={k}")
+    _vec(x_scales, torch.float32, "x_scales", m)
+    _vec(group_scales, (torch.float32, torch.uint8), "group_scales", n * (k // group))
+    if out is not None:
+        _out_checked(out, m, n)
+    if workspace is not None:
+        _dense(workspace, torch.uint8, "workspace")
+    _on_gpu(x_q8=x_q8, x_scales=x_scales, w_packed=w_packed, group_scales=group_scales, out=out,
+            workspace=workspace)
     if out is None:
         out = _out_bf16(m, n, x_q8.device)
     need = w4a8_workspace_bytes(m, n, k, chunk_cols)
@@ -345,16 +449,26 @@ def fp6_bytes(rows: int, k: int) -> int:
     return int(lib().ck4_fp6_bytes(rows, k))
 
 
+def gemm_fp6_tile(m: int, n: int, k: int):
+    """(tile_m, tile_n): the output tile the FP6 GEMM launches for an m x n x k product."""
+    tm, tn = ctypes.c_int(0), ctypes.c_int(0)
+    _check("ck4_gemm_fp6_tile", lib().ck4_gemm_fp6_tile(m, n, k, ctypes.byref(tm), ctypes.byref(tn)))
+    return tm.value, tn.value
+
+
 def rotate_quantize_act_fp6(x: torch.Tensor, rot_block: int = 128, out=None, scales=None):
     """bf16 [m, k] -> (uint8 [rows16(m), 3k/4] FP6 codes, fp32 [m] scales)."""
-    _need(x, torch.bfloat16, "x", 2)
+    _typed(x, torch.bfloat16, "x", 2)
     m, k = x.shape
+    if out is not None:
+        _vec(out, torch.uint8, "out", _fp6_nbytes(m, k))
+    if scales is not None:
+        _vec(scales, torch.float32, "scales", m)
+    _on_gpu(x=x, out=out, scales=scales)
     if out is None:
         out = torch.empty((_rows16(m), k * 3 // 4), dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty((m,), dtype=torch.float32, device=x.device)
-    if out.numel() < fp6_bytes(m, k):
-        raise ValueError("FP6 output buffer too small")
     _check("ck4_rotate_quantize_act_fp6",
            lib().ck4_rotate_quantize_act_fp6(_ptr(x), m, k, x.stride(0), rot_block, _ptr(out), _ptr(scales),
                                              _stream(x.device)))
@@ -376,21 +490,45 @@ def quantize_weight_convrot_fp6(w: torch.Tensor, rot_block: int = 128):
 def linear_w4a4_fp6(x_q6, x_scales, w_q6, w_scales, bias=None, out=None, m: int | None = None,
                     n: int | None = None):
     """W4A4 GEMM + epilogue from FP6 operands -> bf16 [m, n] (m, n default to the scale lengths)."""
+    _typed(x_scales, torch.float32, "x_scales")
+    _typed(w_scales, torch.float32, "w_scales")
     m = x_scales.numel() if m is None else m
     n = w_scales.numel() if n is None else n
-    k = x_q6.shape[1] * 4 // 3
+    k = _check_fp6_gemm(x_q6, w_q6, m, n, x_scales, w_scales, bias, out)
     if out is None:
         out = _out_bf16(m, n, x_q6.device)
-    _need(out, torch.bfloat16, "out", 2)
     _check("ck4_linear_w4a4_fp6",
            lib().ck4_linear_w4a4_fp6(_ptr(x_q6), _ptr(x_scales), _ptr(w_q6), _ptr(w_scales), _ptr(bias), m, n, k,
                                      _ptr(out), out.stride(0), _stream(x_q6.device)))
     return out
 
 
+def _check_fp6_gemm(x_q6, w_q6, m: int, n: int, x_scales, w_scales, bias, out) -> int:
+    """Operands of an FP6 GEMM wrapper; returns k."""
+    k = _fp6_k(x_q6, "x_q6")
+    if _fp6_k(w_q6, "w_q6") != k:
+        raise ValueError(f"w_q6 rows hold {w_q6.shape[1]} bytes, x_q6 rows {x_q6.shape[1]}: k differs")
+    if m <= 0 or n <= 0:
+        raise ValueError("m and n must be positive")
+    if x_q6.numel() < _fp6_nbytes(m, k):
+        raise ValueError(f"x_q6 holds {x_q6.numel()} bytes, {m} rows need {_fp6_nbytes(m, k)}")
+    if w_q6.numel() < _fp6_nbytes(n, k):
+        raise ValueError(f"w_q6 holds {w_q6.numel()} bytes, {n} rows need {_fp6_nbytes(n, k)}")
+    if x_scales is not None:
+        _vec(x_scales, torch.float32, "x_scales", m)
+    if w_scales is not None:
+        _vec(w_scales, torch.float32, "w_scales", n)
+    if bias is not None:
+        _vec(bias, torch.float32, "bias", n)
+    if out is not None:
+        _out_checked(out, m, n)
+    _on_gpu(x_q6=x_q6, w_q6=w_q6, x_scales=x_scales, w_scales=w_scales, bias=bias, out=out)
+    return k
+
+
 def gemm_w4a4_fp6_acc_i32(x_q6, w_q6, m: int, n: int):
     """Integer accumulators of the FP6 GEMM -> int32 [m, n]."""
-    k = x_q6.shape[1] * 4 // 3
+    k = _check_fp6_gemm(x_q6, w_q6, m, n, None, None, None, None)
     acc = torch.empty((m, (n + 3) // 4 * 4), dtype=torch.int32, device=x_q6.device)
     _check("ck4_gemm_w4a4_fp6_acc_i32",
            lib().ck4_gemm_w4a4_fp6_acc_i32(_ptr(x_q6), _ptr(w_q6), m, n, k, _ptr(acc), acc.stride(0),
@@ -449,8 +587,8 @@ def linear_w4a4_lora(x_q: torch.Tensor, x_scales: torch.Tensor, w_packed: torch.
     """W4A4 linear with the LoRA up projection in its epilogue: y = base + t B^T, bf16 [m, n].
 
     t_pack from lora_down, b_pack from lora_prepare_up (both in fragment order)."""
-    m, k = x_q.shape[0], x_q.shape[1] * 2
-    n = w_packed.shape[0]
+    m, n = _check_gemm(x_q, w_packed, x_scales, w_scales, bias, out, torch.int8, "q")
+    k = x_q.shape[1] * 2
     _need(t_pack, torch.bfloat16, "t_pack", 2)
     _need(b_pack, torch.bfloat16, "b_pack", 2)
     rank = t_pack.shape[1]
@@ -472,8 +610,10 @@ def linear_w4a4_fp6_lora(x_q6: torch.Tensor, x_scales: torch.Tensor, w_q6: torch
                          t_pack: torch.Tensor, b_pack: torch.Tensor, bias: torch.Tensor | None = None,
                          out: torch.Tensor | None = None):
     """linear_w4a4_lora on the FP6 operand path (same bits): y = base + t B^T, bf16 [m, n]."""
+    _typed(x_scales, torch.float32, "x_scales")
+    _typed(w_scales, torch.float32, "w_scales")
     m, n = x_scales.numel(), w_scales.numel()
-    k = x_q6.shape[1] * 4 // 3
+    k = _check_fp6_gemm(x_q6, w_q6, m, n, x_scales, w_scales, bias, out)
     _need(t_pack, torch.bfloat16, "t_pack", 2)
     _need(b_pack, torch.bfloat16, "b_pack", 2)
     rank = t_pack.shape[1]

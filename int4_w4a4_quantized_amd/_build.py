@@ -1,4 +1,5 @@
-"""Builds libck4.so (the HIP kernels + C ABI) in-tree with hipcc for gfx950.
+"""Builds libck4.so (the HIP kernels + C ABI) in-tree with hipcc for gfx950,
+and libck4_bench.so (the benchmark's streaming-read probe, outside the ABI).
 
 Usage: ``python -m int4_w4a4_quantized_amd._build`` or ``build()`` from Python.
 Compiles every source each time it is called (objects in parallel), then links.
@@ -14,9 +15,11 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 LIB = os.path.join(PKG, "libck4.so")
+BENCH_LIB = os.path.join(PKG, "libck4_bench.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["rotate_quant.hip", "gemm.hip", "gemm_fp6.hip", "w4a8_decode.hip", "lora.hip", "ck4_api.cpp"]
+BENCH_SOURCES = ["bench_read.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -55,14 +58,15 @@ def build(verbose: bool = False, extra_flags: list | None = None) -> str:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
         return obj
 
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(BENCH_SOURCES))) as ex:
+        objs = list(ex.map(compile_one, SOURCES + BENCH_SOURCES))
+    for lib, lib_objs in ((LIB, objs[:len(SOURCES)]), (BENCH_LIB, objs[len(SOURCES):])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *lib_objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

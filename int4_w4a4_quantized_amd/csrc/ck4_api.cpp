@@ -343,6 +343,19 @@ ck4_status ck4_gemm_w4a4_fp6_acc_i32(const uint8_t *x_q6, const uint8_t *w_q6, i
                           ldacc, stream);
 }
 
+ck4_status ck4_gemm_fp6_tile(int64_t m, int64_t n, int64_t k, int *tile_m, int *tile_n) {
+    const char *fn = "ck4_gemm_fp6_tile";
+    if (!tile_m || !tile_n) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (m <= 0 || n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m, n, k must be positive", fn);
+    if (m > kMaxRows || n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m or n too large", fn);
+    if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
+    if (k > kMaxGemmK) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld > %lld", fn, (long long)k, (long long)kMaxGemmK);
+    const bool large = ck4::gemm_fp6_large_tile(m, n);
+    *tile_m = large ? 288 : 96;
+    *tile_n = large ? 192 : 128;
+    return ok();
+}
+
 }  // extern "C"
 
 namespace {

@@ -79,6 +79,10 @@ hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, 
                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                            LoraUp lora = LoraUp{});
 
+// The output tile launch_gemm_fp6 uses for an m x n product: true for
+// 288 x 192, false for 96 x 128.
+bool gemm_fp6_large_tile(int64_t m, int64_t n);
+
 // b (bf16 [n, rank], row stride ldb) to fragment order, zero rows padding n
 // to a multiple of 16.
 hipError_t launch_lora_pack(const uint16_t *b, int64_t n, int64_t rank, int64_t ldb, uint16_t *out,

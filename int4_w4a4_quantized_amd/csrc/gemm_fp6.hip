@@ -238,6 +238,9 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
         for (int i = 0; i < FN; ++i) w0[i] = w1[i];
     }
     step(last_t{}, stage_ptr(kb - 1), stage_ptr(kb), stage_ptr(kb + NST - 2), kb - 1, w0, w1);
+    // the last step's repeat copy (issued one step earlier into a slot no
+    // one reads) must land before the epilogue reuses the LDS for its tile
+    __builtin_amdgcn_s_waitcnt(vm_wait(0));
 
     if constexpr (OUT_I32) {
 #pragma unroll
@@ -263,11 +266,16 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
         // Rank-one epilogue through LDS, so the tile leaves as whole rows:
         // y = bf16((acc * sa[m]) * sb[n] (+ bias[n])) with acc = 64 x the fp32
         // accumulator (exact), into a [BM][BN + 8] bf16 tile, then 16-byte
-        // row-contiguous stores.
+        // row-contiguous stores. The factor 64 goes into the row scale:
+        // f * (64 sa) and (64 f) * sa are the same rounding of 64 f sa, because
+        // 64 sa is exact; a row scale whose 64-fold overflows is capped at the
+        // largest float, so that 0 stays 0 and any nonzero product still
+        // overflows as (64 f) * sa does.
         // the scales are read after the K loop, whose registers are all in use
         float sa_r[FM], sb_r[FN][4];
 #pragma unroll
-        for (int j = 0; j < FM; ++j) sa_r[j] = sa[min(m0 + wm * WTM + j * 16 + frow, M - 1)];
+        for (int j = 0; j < FM; ++j)
+            sa_r[j] = fminf(sa[min(m0 + wm * WTM + j * 16 + frow, M - 1)] * 64.0f, 3.40282347e38f);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -282,7 +290,7 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
                 for (int i = 0; i < FN; ++i)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float v = ((acc[i][j][r] * 64.0f) * sa_r[j]) * sb_r[i][r];
+                        float v = (acc[i][j][r] * sa_r[j]) * sb_r[i][r];
                         if (bias) v = v + bias[min(n0 + wn * WTN + i * 16 + 4 * fgrp + r, N - 1)];
                         acc[i][j][r] = v;
                     }
@@ -301,8 +309,7 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
                     if constexpr (LORA) {
                         o[r] = f32_to_bf16(acc[i][j][r]);
                     } else {
-                        const float a = acc[i][j][r] * 64.0f;
-                        float v = (a * sa_r[j]) * sb_r[i][r];
+                        float v = (acc[i][j][r] * sa_r[j]) * sb_r[i][r];
                         if (bias) v = v + bias[min(n0 + nl + r, N - 1)];
                         o[r] = f32_to_bf16(v);
                     }
@@ -361,10 +368,7 @@ hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const
 
 }  // namespace
 
-hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
-                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
-                           LoraUp lora) {
-    if (out_i32 || lora.t == nullptr) lora.rank = 0;
+bool gemm_fp6_large_tile(int64_t m, int64_t n) {
     // 288 x 192 tiles (one workgroup per CU) or 96 x 128 tiles of 4 waves
     // (48 x 64 each, two workgroups per CU), whichever needs less time by the
     // rounds of workgroups over the 256 CUs: on the part a round of large
@@ -372,7 +376,14 @@ hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, 
     // (30 against 17 us at K = 3072)
     const int64_t big_rounds = (((m + 287) / 288) * ((n + 191) / 192) + 255) / 256;
     const int64_t small_rounds = (((m + 95) / 96) * ((n + 127) / 128) + 511) / 512;
-    if (9 * small_rounds >= 16 * big_rounds)
+    return 9 * small_rounds >= 16 * big_rounds;
+}
+
+hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
+                           int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
+                           LoraUp lora) {
+    if (out_i32 || lora.t == nullptr) lora.rank = 0;
+    if (gemm_fp6_large_tile(m, n))
         return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
     return launch_fp6<96, 128, 2, 2, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import int4_w4a4_quantized_amd as ck
+import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ck4.h")
@@ -219,3 +220,18 @@ def test_fragment_order_helper_is_the_documented_permutation():
     t = frag_layout.pack(z).reshape(64, 8)
     assert list(t[16 * 2 + 5]) == [5 * 32 + c for c in (8, 9, 10, 11, 24, 25, 26, 27)]
 
+
+
+def test_fp6_tile_query(L):
+    """Host-only: the tile the FP6 GEMM launches per shape, and its shape errors."""
+    import test_gpu_parity  # the oracle-checked FP6 shapes must reach both tiles
+    tiles = {ck.gemm_fp6_tile(m, n, k) for m, n, k in test_gpu_parity.FP6_CASES}
+    assert tiles == {(288, 192), (96, 128)}
+    for name in ("square_3072", "up_3072_12288", "down_12288_3072"):
+        cfg = workloads.WORKLOADS[name]
+        assert ck.gemm_fp6_tile(cfg["m"], cfg["n"], cfg["k"]) == (288, 192)
+    tm, tn = ctypes.c_int(0), ctypes.c_int(0)
+    f = L.ck4_gemm_fp6_tile
+    assert f(8, 8, 192, ctypes.byref(tm), ctypes.byref(tn)) == ck.CK4_ERR_UNSUPPORTED
+    assert f(0, 8, 128, ctypes.byref(tm), ctypes.byref(tn)) == ck.CK4_ERR_INVALID
+    assert f(8, 8, 128, None, ctypes.byref(tn)) == ck.CK4_ERR_INVALID

@@ -295,6 +295,9 @@ def test_e4m3_linear_fused_chunked_single_equal_and_match_oracle(ck, m, n, k):
 FP6_CASES = [
     (64, 256, 256), (1, 1, 128), (3, 17, 384), (17, 3, 512), (130, 200, 768), (16, 64, 3072),
     (64, 130, 1024), (257, 129, 640), (33, 77, 256), (8, 1000, 512), (300, 8, 1280), (577, 385, 1152),
+    # shapes the launcher sends to the 288 x 192 tile (the benchmarked one):
+    # ragged in m and n, an odd number of 128-k steps, and whole tiles
+    (2000, 3500, 384), (2304, 3072, 256),
 ]
 
 
@@ -402,6 +405,64 @@ def test_fp6_full_size_layer_equals_int4_path(ck, name):
     y6 = bf16_host_bits(ck.w4a4_linear_fp6(x, wq6, ws6))
     y4 = bf16_host_bits(ck.w4a4_linear(x, wp, ws))
     assert np.array_equal(y6, y4)
+
+
+def _fp6_uniform_block(row_codes) -> np.ndarray:
+    """One 1536-byte FP6 operand block (16 rows x 128 k) whose row i holds the code row_codes[i] at every k."""
+    q = np.repeat(np.asarray(row_codes, np.int64)[:, None], 128, axis=1)
+    return fp6_layout.encode(q)
+
+
+@pytest.mark.parametrize("k", [128, 3072, 12288, 131072])
+@pytest.mark.parametrize("m,n,tile", [(16, 8, (96, 128)), (2304, 3072, (288, 192))])
+def test_fp6_accumulator_bound_is_reached_exactly(ck, m, n, tile, k):
+    """Codes +7 everywhere against rows of +7 and -7 give acc = +-49 K exactly on both tiles of the FP6 GEMM,
+    up to the largest k it accepts ([PR #63] Description: |acc| <= 49 K; the fp32 accumulator of the FP6 matrix
+    instruction holds 49 K / 64 exactly for K <= 131072)."""
+    assert ck.gemm_fp6_tile(m, n, k) == tile
+    blocks = k // 128
+    a = torch.from_numpy(_fp6_uniform_block([7] * 16)).cuda().repeat(m // 16 * blocks)
+    b = torch.from_numpy(_fp6_uniform_block([7, -7] * 8)).cuda().repeat((n + 15) // 16 * blocks)
+    acc = host(ck.gemm_w4a4_fp6_acc_i32(a.view(-1, k * 3 // 4), b.view(-1, k * 3 // 4), m, n))
+    expect = np.where(np.arange(n) % 2 == 0, 49 * k, -49 * k).astype(np.int32)
+    assert np.array_equal(acc, np.broadcast_to(expect, (m, n)))
+
+
+def _rows_per_tile_row(m, bm, per_tile, seed):
+    """Sample rows so that each bm-row band of output tiles holds `per_tile` of them, plus the first and last."""
+    rng = np.random.default_rng(seed)
+    rows = [0, m - 1]
+    for r0 in range(0, m, bm):
+        span = min(bm, m - r0)
+        rows.extend(r0 + rng.choice(span, min(per_tile, span), replace=False))
+    return np.unique(np.asarray(rows))
+
+
+@pytest.mark.parametrize("name", ["square_3072", "up_3072_12288", "down_12288_3072"])
+def test_fp6_full_size_layer_against_oracle(ck, name):
+    """The benchmarked path at full size, seed 0 (the benchmark's inputs), directly against the oracle: the FP6
+    quantisers' codes (all rows, decoded from the operand layout) and scales bit-exact, the int32 accumulators of
+    the 288 x 192-tile FP6 GEMM bit-exact on two sampled rows of every 288-row band of tiles (all columns), and
+    the bf16 outputs of those rows within 1e-2."""
+    cfg = workloads.WORKLOADS[name]
+    lay = workloads.make_layer(seed=0, **cfg)
+    m, k, n = lay.m, lay.k, lay.n
+    assert ck.gemm_fp6_tile(m, n, k) == (288, 192)
+    xq6, sx6 = ck.rotate_quantize_act_fp6(dev_bf16(lay.x_bf16), 128)
+    xq_ref, sx_ref = oracle.rotate_quantize_act(lay.x_bf16)
+    assert np.array_equal(host(sx6).view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(fp6_layout.decode(host(xq6), m, k), oracle.unpack_int4(xq_ref))
+    wq6, ws6 = ck.quantize_weight_convrot_fp6(torch.from_numpy(lay.weights[0]).cuda(), 128)
+    wp_ref, ws_ref = oracle.quantize_weight_convrot(lay.weights[0])
+    assert np.array_equal(host(ws6).view(np.uint32), ws_ref.view(np.uint32))
+    assert np.array_equal(fp6_layout.decode(host(wq6), n, k), oracle.unpack_int4(wp_ref))
+    rows = _rows_per_tile_row(m, 288, 2, 11)
+    acc = host(ck.gemm_w4a4_fp6_acc_i32(xq6, wq6, m, n))
+    acc_ref = oracle.gemm_acc(np.ascontiguousarray(xq_ref[rows]), wp_ref, k)
+    assert np.array_equal(acc[rows], acc_ref)
+    assert np.abs(acc).max() <= 49 * k
+    y = bf16_host_bits(ck.linear_w4a4_fp6(xq6, sx6, wq6, ws6))
+    assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], ws_ref))
 
 
 # --------------------------------------------------------------------------
