@@ -292,6 +292,26 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
 
 
 /*
+ * ck4_linear_w4a8_grouped for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same three paths
+ * and the same results bit for bit. The decode buffer of the chunked and
+ * single-pass paths is a fixed device array inside the library,
+ * CK4_NOALLOC_SCRATCH_BYTES (64 MiB) on each GPU it runs on, held until the
+ * process ends; the call allocates nothing. CK4_ERR_UNSUPPORTED when
+ * ck4_w4a8_workspace_bytes(m, n, k, chunk_cols) exceeds that size (choose a
+ * chunk width that fits). Every call on a GPU shares that GPU's array and
+ * leaves the last call's decoded weights in it (each call writes all of the
+ * buffer it reads, so nothing has to start at zero): calls that overlap in time
+ * on one GPU (several streams or host threads) race and must be serialised by
+ * the caller.
+ */
+#define CK4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ck4_status ck4_linear_w4a8_grouped_noalloc(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                           const float *group_scales, int64_t m, int64_t n, int64_t k, int group,
+                                           uint16_t *y, int64_t ldy, int64_t chunk_cols, void *stream);
+
+/*
  * Grouped W4A8 with FP8 E4M3 group scales ([PR #97] What this adds: group
  * scales in fp32 or e4m3, one decode for both). E4M3 is the OCP format: sign,
  * 4 exponent bits (bias 7), 3 mantissa bits, largest 448, no infinities.

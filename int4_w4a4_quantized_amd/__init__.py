@@ -53,6 +53,7 @@ SIGNATURES = {
     "ck4_linear_w8a8": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_w4a8_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
     "ck4_linear_w4a8_grouped": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t, _P], _I),
+    "ck4_linear_w4a8_grouped_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P], _I),
     "ck4_quantize_weight_convrot_e4m3": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "ck4_dequant_w4a8_grouped_e4m3": ([_P, _P, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
     "ck4_linear_w4a8_grouped_e4m3": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t,
@@ -434,6 +435,33 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
     _check(name, getattr(lib(), name)(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales), m, n, k,
                                       group, _ptr(out), out.stride(0), chunk_cols, _ptr(workspace),
                                       0 if workspace is None else workspace.numel(), _stream(x_q8.device)))
+    return out
+
+
+def linear_w4a8_grouped_noalloc(x_q8, x_scales, w_packed, group_scales, group: int = 128, chunk_cols: int = 0,
+                                out=None):
+    """linear_w4a8_grouped (fp32 group scales) without a workspace: the decode paths use the library's fixed
+    device buffer (ck4.h: CK4_NOALLOC_SCRATCH_BYTES per GPU), so the call allocates nothing beyond `out` when
+    one is given. Calls that overlap on one GPU race on that buffer."""
+    _dense(x_q8, torch.int8, "x_q8", 2)
+    _dense(w_packed, torch.int8, "w_packed", 2)
+    m, k = x_q8.shape
+    n = w_packed.shape[0]
+    if w_packed.shape[1] * 2 != k:
+        raise ValueError(f"w_packed rows hold {w_packed.shape[1]} bytes, the int8 activation has k={k}")
+    if group <= 0 or k % group != 0:
+        raise ValueError(f"group={group} must divide k={k}")
+    _vec(x_scales, torch.float32, "x_scales", m)
+    _vec(group_scales, torch.float32, "group_scales", n * (k // group))
+    if out is not None:
+        _out_checked(out, m, n)
+    _on_gpu(x_q8=x_q8, x_scales=x_scales, w_packed=w_packed, group_scales=group_scales, out=out)
+    if out is None:
+        out = _out_bf16(m, n, x_q8.device)
+    _check("ck4_linear_w4a8_grouped_noalloc",
+           lib().ck4_linear_w4a8_grouped_noalloc(_ptr(x_q8), _ptr(x_scales), _ptr(w_packed), _ptr(group_scales), m,
+                                                 n, k, group, _ptr(out), out.stride(0), chunk_cols,
+                                                 _stream(x_q8.device)))
     return out
 
 

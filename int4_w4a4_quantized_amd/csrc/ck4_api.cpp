@@ -16,6 +16,8 @@
 
 #define CK4_VERSION_STRING "ck4 0.1.0 gfx950"
 
+static_assert(CK4_NOALLOC_SCRATCH_BYTES == ck4::kNoallocScratchBytes, "ck4.h and the kernels disagree");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -488,6 +490,30 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
                                    void *stream) {
     return linear_w4a8("ck4_linear_w4a8_grouped", x_q8, x_scales, w_packed, group_scales, false, m, n, k, group, y,
                        ldy, chunk_cols, workspace, ws_bytes, stream);
+}
+
+ck4_status ck4_linear_w4a8_grouped_noalloc(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                                           const float *group_scales, int64_t m, int64_t n, int64_t k, int group,
+                                           uint16_t *y, int64_t ldy, int64_t chunk_cols, void *stream) {
+    const char *fn = "ck4_linear_w4a8_grouped_noalloc";
+    if (m <= 0 || n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m, n, k must be positive", fn);
+    if (chunk_cols < 0 && (size_t)(align_up(n * k, 256) + align_up(n * 4, 256)) > ck4::kNoallocScratchBytes)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: the single-pass decode of n=%lld x k=%lld needs more than the %zu-byte "
+                    "fixed buffer; pass a chunk width", fn, (long long)n, (long long)k, ck4::kNoallocScratchBytes);
+    int dev = 0;
+    if (ck4_status s = check_device(fn, &dev)) return s;
+    const size_t need = ck4_w4a8_workspace_bytes(m, n, k, chunk_cols);
+    if (need > ck4::kNoallocScratchBytes)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: the decode needs %zu bytes, more than the %zu-byte fixed buffer; pass a "
+                    "smaller chunk width", fn, need, ck4::kNoallocScratchBytes);
+    void *scratch = nullptr;
+    if (need > 0) {
+        const hipError_t e = ck4::noalloc_scratch(dev, &scratch);
+        if (e != hipSuccess || !scratch)
+            return fail(CK4_ERR_DEVICE, "%s: no address for the fixed buffer: %s", fn, hipGetErrorString(e));
+    }
+    return linear_w4a8(fn, x_q8, x_scales, w_packed, group_scales, false, m, n, k, group, y, ldy, chunk_cols, scratch,
+                       need > 0 ? ck4::kNoallocScratchBytes : 0, stream);
 }
 
 ck4_status ck4_linear_w4a8_grouped_e4m3(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,

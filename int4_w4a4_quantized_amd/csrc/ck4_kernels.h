@@ -111,4 +111,11 @@ hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const in
                              const void *group_scales, bool scale_e4m3, int64_t m, int64_t n, int64_t k, int group,
                              uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb = Codebook{});
 
+// The fixed device buffer behind ck4_linear_w4a8_grouped_noalloc (a
+// file-scope device array of kNoallocScratchBytes in w4a8_decode.hip): its
+// device address on device `dev`, which must be the current device. The
+// address is looked up once per device; the result (and error) is kept.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(int dev, void **ptr);
+
 }  // namespace ck4

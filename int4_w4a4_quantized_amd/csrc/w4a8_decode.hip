@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ck4_kernels.h"
 #include "fp8_e4m3.h"
 
@@ -555,6 +557,32 @@ hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const in
     if (scale_e4m3)
         return launch_fused_cb<true>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
     return launch_fused_cb<false>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
+}
+
+// The decode buffer of ck4_linear_w4a8_grouped_noalloc: a file-scope device
+// array, so that entry point allocates nothing. Each device that runs the
+// library holds its own copy until the process ends. Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): the device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void *g_scratch_ptr[kScratchDevices];
+hipError_t g_scratch_err[kScratchDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(int dev, void **ptr) {
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void *p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    *ptr = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
 }
 
 }  // namespace ck4

@@ -235,3 +235,12 @@ def test_fp6_tile_query(L):
     assert f(8, 8, 192, ctypes.byref(tm), ctypes.byref(tn)) == ck.CK4_ERR_UNSUPPORTED
     assert f(0, 8, 128, ctypes.byref(tm), ctypes.byref(tn)) == ck.CK4_ERR_INVALID
     assert f(8, 8, 128, None, ctypes.byref(tn)) == ck.CK4_ERR_INVALID
+
+
+def test_noalloc_validation(L):
+    """The no-allocation W4A8 entry point refuses, before any device call, a single-pass decode larger than its
+    fixed buffer, and a non-positive size."""
+    f = L.ck4_linear_w4a8_grouped_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 12288, 8192, 128, FAKE, 12288, -1, NULL) == ck.CK4_ERR_UNSUPPORTED
+    assert "fixed buffer" in last(L)
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 128, 256, 128, FAKE, 128, 0, NULL) == ck.CK4_ERR_INVALID
