@@ -88,6 +88,18 @@ ck4_status launched(const char *fn, hipError_t e) {
 constexpr int64_t kMaxActK = 16384;     // rotate/quantise kernels hold a row in VGPRs
 constexpr int64_t kMaxGemmK = 131072;   // 256 * 49 * K < 2^31 for the widened int4 products
 constexpr int64_t kMaxRows = 0x7FFFFFFF;
+constexpr int64_t kMaxStride = int64_t(1) << 40;  // elements; row * stride stays far inside int64
+
+// A row stride in elements that is at least `width`, a multiple of `mult`
+// (so rows stay aligned) and not absurdly large; checked without forming any
+// product of caller values.
+ck4_status check_stride(const char *fn, const char *name, int64_t ld, int64_t width, int64_t mult) {
+    if (ld < width) return fail(CK4_ERR_INVALID, "%s: %s=%lld < %lld", fn, name, (long long)ld, (long long)width);
+    if (ld % mult != 0)
+        return fail(CK4_ERR_INVALID, "%s: %s=%lld is not a multiple of %lld", fn, name, (long long)ld, (long long)mult);
+    if (ld > kMaxStride) return fail(CK4_ERR_UNSUPPORTED, "%s: %s=%lld too large", fn, name, (long long)ld);
+    return CK4_OK;
+}
 
 ck4_status check_rot(const char *fn, int64_t k, int rot_block) {
     if (!pow2(rot_block) || rot_block < 16 || rot_block > 1024)
@@ -103,8 +115,7 @@ ck4_status check_gemm_common(const char *fn, int64_t m, int64_t n, int64_t k, in
                              size_t y_align) {
     if (m <= 0 || n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m, n, k must be positive", fn);
     if (m > kMaxRows || n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m or n too large", fn);
-    if (ldy < n) return fail(CK4_ERR_INVALID, "%s: ldy=%lld < n=%lld", fn, (long long)ldy, (long long)n);
-    if (ldy % 4 != 0) return fail(CK4_ERR_INVALID, "%s: ldy=%lld is not a multiple of 4", fn, (long long)ldy);
+    if (ck4_status s = check_stride(fn, "ldy", ldy, n, 4)) return s;
     if (!aligned(y, y_align)) return fail(CK4_ERR_INVALID, "%s: output pointer not %zu-byte aligned", fn, y_align);
     if (k > kMaxGemmK) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld > %lld", fn, (long long)k, (long long)kMaxGemmK);
     return CK4_OK;
@@ -133,8 +144,8 @@ ck4_status ck4_quantize_weight_convrot(const float *w, int64_t n, int64_t k, int
     const char *fn = "ck4_quantize_weight_convrot";
     if (!w || !w_packed || !w_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
-    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
-    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldw", ldw, k, 4)) return s;
+    if (!aligned(w, 16)) return fail(CK4_ERR_INVALID, "%s: w not 16-byte aligned", fn);
     if (!aligned(w_packed, 8) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
@@ -152,9 +163,9 @@ ck4_status ck4_quantize_weight_convrot_sr(const float *w, int64_t n, int64_t k, 
     const char *fn = "ck4_quantize_weight_convrot_sr";
     if (!w || !u || !w_packed || !w_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
-    if (ldw < k || ldu < k) return fail(CK4_ERR_INVALID, "%s: ldw or ldu < k", fn);
-    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
-    if (!aligned(u, 16) || (ldu * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: u/ldu not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldw", ldw, k, 4)) return s;
+    if (ck4_status s = check_stride(fn, "ldu", ldu, k, 4)) return s;
+    if (!aligned(w, 16) || !aligned(u, 16)) return fail(CK4_ERR_INVALID, "%s: w or u not 16-byte aligned", fn);
     if (!aligned(w_packed, 8) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
@@ -171,8 +182,8 @@ ck4_status ck4_quantize_weight_convrot_e4m3(const float *w, int64_t n, int64_t k
     const char *fn = "ck4_quantize_weight_convrot_e4m3";
     if (!w || !w_packed || !group_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
-    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
-    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldw", ldw, k, 4)) return s;
+    if (!aligned(w, 16)) return fail(CK4_ERR_INVALID, "%s: w not 16-byte aligned", fn);
     if (!aligned(w_packed, 8)) return fail(CK4_ERR_INVALID, "%s: w_packed misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
@@ -192,8 +203,8 @@ ck4_status ck4_quantize_weight_convrot_codebook(const float *w, int64_t n, int64
     ck4::WeightOpts wo{nullptr, 0, scale_e4m3 != 0};
     if (ck4_status s = make_codebook(fn, codebook, &wo.cb)) return s;
     if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
-    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
-    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldw", ldw, k, 4)) return s;
+    if (!aligned(w, 16)) return fail(CK4_ERR_INVALID, "%s: w not 16-byte aligned", fn);
     if (!aligned(w_packed, 8) || (!scale_e4m3 && !aligned(group_scales, 4)))
         return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
@@ -211,8 +222,8 @@ ck4_status ck4_quantize_weight_convrot_int8(const float *w, int64_t n, int64_t k
     const char *fn = "ck4_quantize_weight_convrot_int8";
     if (!w || !w_q8 || !w_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: n and k must be positive", fn);
-    if (ldw < k) return fail(CK4_ERR_INVALID, "%s: ldw < k", fn);
-    if (!aligned(w, 16) || (ldw * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: w/ldw not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldw", ldw, k, 4)) return s;
+    if (!aligned(w, 16)) return fail(CK4_ERR_INVALID, "%s: w not 16-byte aligned", fn);
     if (!aligned(w_q8, 16) || !aligned(w_scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (n > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: n too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
@@ -226,9 +237,9 @@ ck4_status ck4_rotate_quantize_act(const uint16_t *x, int64_t m, int64_t k, int6
     const char *fn = "ck4_rotate_quantize_act";
     if (!x || !x_q || !x_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (m <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m and k must be positive", fn);
-    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
+    if (ck4_status s = check_stride(fn, "ldx", ldx, k, 8)) return s;
     if (bits != 4 && bits != 8) return fail(CK4_ERR_UNSUPPORTED, "%s: bits=%d (need 4 or 8)", fn, bits);
-    if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: x/ldx not 16-byte aligned", fn);
+    if (!aligned(x, 16)) return fail(CK4_ERR_INVALID, "%s: x not 16-byte aligned", fn);
     if (!aligned(x_q, bits == 4 ? 8 : 16) || !aligned(x_scales, 4))
         return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (m > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m too large", fn);
@@ -243,8 +254,8 @@ ck4_status ck4_rotate_act_f32(const uint16_t *x, int64_t m, int64_t k, int64_t l
     const char *fn = "ck4_rotate_act_f32";
     if (!x || !r) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (m <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m and k must be positive", fn);
-    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
-    if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: x/ldx not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldx", ldx, k, 8)) return s;
+    if (!aligned(x, 16)) return fail(CK4_ERR_INVALID, "%s: x not 16-byte aligned", fn);
     if (!aligned(r, 16)) return fail(CK4_ERR_INVALID, "%s: r not 16-byte aligned", fn);
     if (m > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m too large", fn);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
@@ -289,7 +300,7 @@ ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8
 }
 
 size_t ck4_fp6_bytes(int64_t rows, int64_t k) {
-    if (rows <= 0 || k <= 0 || k % 128 != 0) return 0;
+    if (rows <= 0 || rows > kMaxRows || k <= 0 || k > kMaxGemmK || k % 128 != 0) return 0;
     return (size_t)((rows + 15) / 16 * 16) * (size_t)(k / 128) * 96;
 }
 
@@ -298,9 +309,8 @@ static ck4_status quantize_fp6(const char *fn, const void *x, int in_kind, int64
     const size_t esz = in_kind == 0 ? 2 : 4;
     if (!x || !q6 || !scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (rows <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: rows and k must be positive", fn);
-    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
-    if (!aligned(x, 16) || ((size_t)ldx * esz) % 16 != 0)
-        return fail(CK4_ERR_INVALID, "%s: input/ldx not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldx", ldx, k, (int64_t)(16 / esz))) return s;
+    if (!aligned(x, 16)) return fail(CK4_ERR_INVALID, "%s: input not 16-byte aligned", fn);
     if (!aligned(q6, 16) || !aligned(scales, 4)) return fail(CK4_ERR_INVALID, "%s: outputs misaligned", fn);
     if (rows > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: too many rows", fn);
     if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
@@ -367,7 +377,8 @@ ck4_status dequant_w4a8(const char *fn, const int8_t *w_packed, const void *grou
                         const ck4::Codebook &cb = ck4::Codebook{}) {
     if (!w_packed || !group_scales || !w8 || !row_scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0 || k <= 0 || nc <= 0) return fail(CK4_ERR_INVALID, "%s: n, k, nc must be positive", fn);
-    if (n0 < 0 || n0 + nc > n) return fail(CK4_ERR_INVALID, "%s: rows [n0, n0+nc) outside [0, n)", fn);
+    if (n0 < 0 || n0 >= n || nc > n - n0) return fail(CK4_ERR_INVALID, "%s: rows [n0, n0+nc) outside [0, n)", fn);
+    if (n > kMaxRows || k > kMaxGemmK) return fail(CK4_ERR_UNSUPPORTED, "%s: n or k too large", fn);
     if (!pow2(group) || group < 4 || group > 1024 || k % group != 0)
         return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [4, 1024] dividing k)", fn, group);
     if (!aligned(w_packed, 16) || !aligned(w8, 16) || (k / 2) % 8 != 0)
@@ -422,6 +433,7 @@ static int64_t w4a8_chunk(int64_t m, int64_t n, int64_t k, int64_t chunk_cols, i
         if (c < 1024) c = 1024;
         if (c > 4096) c = 4096;
     }
+    if (c >= n) return n;
     c = (c + 15) / 16 * 16;
     return c < n ? c : n;
 }
@@ -429,7 +441,7 @@ static int64_t w4a8_chunk(int64_t m, int64_t n, int64_t k, int64_t chunk_cols, i
 static int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 size_t ck4_w4a8_workspace_bytes(int64_t m, int64_t n, int64_t k, int64_t chunk_cols) {
-    if (m <= 0 || n <= 0 || k <= 0) return 0;
+    if (m <= 0 || n <= 0 || k <= 0 || m > kMaxRows || n > kMaxRows || k > kMaxGemmK) return 0;
     int dev = 0;
     int64_t l2 = 4 << 20;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices && check_device("ws", &dev) == CK4_OK)
@@ -497,6 +509,8 @@ ck4_status ck4_linear_w4a8_grouped_noalloc(const int8_t *x_q8, const float *x_sc
                                            uint16_t *y, int64_t ldy, int64_t chunk_cols, void *stream) {
     const char *fn = "ck4_linear_w4a8_grouped_noalloc";
     if (m <= 0 || n <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m, n, k must be positive", fn);
+    if (m > kMaxRows || n > kMaxRows || k > kMaxGemmK)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: m, n or k too large", fn);
     if (chunk_cols < 0 && (size_t)(align_up(n * k, 256) + align_up(n * 4, 256)) > ck4::kNoallocScratchBytes)
         return fail(CK4_ERR_UNSUPPORTED, "%s: the single-pass decode of n=%lld x k=%lld needs more than the %zu-byte "
                     "fixed buffer; pass a chunk width", fn, (long long)n, (long long)k, ck4::kNoallocScratchBytes);
@@ -550,8 +564,8 @@ ck4_status ck4_lora_prepare_down(const float *a, int64_t rank, int64_t k, int64_
     const char *fn = "ck4_lora_prepare_down";
     if (!a || !a_pack) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (rank <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: rank and k must be positive", fn);
-    if (lda < k) return fail(CK4_ERR_INVALID, "%s: lda < k", fn);
-    if (!aligned(a, 16) || (lda * 4) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: a/lda not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "lda", lda, k, 4)) return s;
+    if (!aligned(a, 16)) return fail(CK4_ERR_INVALID, "%s: a not 16-byte aligned", fn);
     if (!aligned(a_pack, 16)) return fail(CK4_ERR_INVALID, "%s: a_pack not 16-byte aligned", fn);
     if (!lora_rank_ok(rank))
         return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
@@ -568,8 +582,8 @@ ck4_status ck4_lora_prepare_up(const uint16_t *b, int64_t n, int64_t rank, int64
     const char *fn = "ck4_lora_prepare_up";
     if (!b || !b_pack) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (n <= 0) return fail(CK4_ERR_INVALID, "%s: n must be positive", fn);
-    if (ldb < rank) return fail(CK4_ERR_INVALID, "%s: ldb < rank", fn);
-    if (!aligned(b, 8) || (ldb * 2) % 8 != 0) return fail(CK4_ERR_INVALID, "%s: b/ldb not 8-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldb", ldb, rank, 4)) return s;
+    if (!aligned(b, 8)) return fail(CK4_ERR_INVALID, "%s: b not 8-byte aligned", fn);
     if (!aligned(b_pack, 16)) return fail(CK4_ERR_INVALID, "%s: b_pack not 16-byte aligned", fn);
     if (!lora_rank_ok(rank))
         return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
@@ -585,8 +599,8 @@ ck4_status ck4_lora_down(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, i
     const char *fn = "ck4_lora_down";
     if (!x || !a_rot || !t) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (m <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: m and k must be positive", fn);
-    if (ldx < k) return fail(CK4_ERR_INVALID, "%s: ldx < k", fn);
-    if (!aligned(x, 16) || (ldx * 2) % 16 != 0) return fail(CK4_ERR_INVALID, "%s: x/ldx not 16-byte aligned", fn);
+    if (ck4_status s = check_stride(fn, "ldx", ldx, k, 8)) return s;
+    if (!aligned(x, 16)) return fail(CK4_ERR_INVALID, "%s: x not 16-byte aligned", fn);
     if (!aligned(a_rot, 16) || !aligned(t, 16)) return fail(CK4_ERR_INVALID, "%s: a_pack or t_pack misaligned", fn);
     if (m > kMaxRows) return fail(CK4_ERR_UNSUPPORTED, "%s: m too large", fn);
     if (!lora_rank_ok(rank))

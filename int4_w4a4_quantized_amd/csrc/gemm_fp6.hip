@@ -368,17 +368,6 @@ hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const
 
 }  // namespace
 
-bool gemm_fp6_large_tile(int64_t m, int64_t n) {
-    // 288 x 192 tiles (one workgroup per CU) or 96 x 128 tiles of 4 waves
-    // (48 x 64 each, two workgroups per CU), whichever needs less time by the
-    // rounds of workgroups over the 256 CUs: on the part a round of large
-    // tiles takes about 16/9 the time of a round of small ones at the same K
-    // (30 against 17 us at K = 3072)
-    const int64_t big_rounds = (((m + 287) / 288) * ((n + 191) / 192) + 255) / 256;
-    const int64_t small_rounds = (((m + 95) / 96) * ((n + 127) / 128) + 511) / 512;
-    return 9 * small_rounds >= 16 * big_rounds;
-}
-
 hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                            LoraUp lora) {
