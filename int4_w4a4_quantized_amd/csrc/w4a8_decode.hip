@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "ck4_kernels.h"
 #include "fp8_e4m3.h"
@@ -118,9 +119,9 @@ hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, 
 // fragment and the cache is the register file.)
 //
 // A workgroup owns 16*FNW weight rows; KS wavefronts split K and add their
-// int32 partial sums through LDS. The per-code decode costs about five VALU
-// instructions (byte convert, fma, clamp, rounding add, byte gather), since
-// the kernel is bound by VALU issue rather than by the weight stream.
+// int32 partial sums through LDS. Codes are decoded through a per-lane table
+// of the 16 int8 codes of one multiplier (groups of 64 and wider), or per code
+// (narrower groups).
 namespace ck4 {
 namespace {
 
@@ -260,6 +261,91 @@ __device__ __forceinline__ uint2 decode8_table2(uint32_t w, uint4 ta, uint4 tb) 
     return make_uint2(__builtin_amdgcn_perm(hi, lo, 0x05010400u), __builtin_amdgcn_perm(hi, lo, 0x07030602u));
 }
 
+// One k-step of one 16-row weight tile: the lane's 64 packed codes (8 words,
+// element 2j in the low nibble of byte j of its span) decoded to int8 codes
+// and multiplied against the FM activation fragments of the step's four
+// slices. gv holds the lane's group scales of the step (SG = 0: one per
+// 16-code slice; SG = 8 / 4: one per word / half word), srow its row scale.
+// Every path below forms the same fp32 values as the decode kernel.
+template <int FM, int NGV, int SG, bool CB>
+__device__ __forceinline__ void w4a8_tile_step(const uint32_t (&words)[8], const float (&gv)[NGV], float srow,
+                                               bool one_group, const v4i_t (&xv)[FM][4], v4i_t (&acc)[FM],
+                                               const Codebook &cb) {
+    if constexpr (SG != 0) {
+        // groups of 8 or 4: a multiplier per word or per half word
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            uint2 d[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int wi = 2 * h + e;
+                const int ga = SG == 8 ? wi : 2 * wi, gb = SG == 8 ? wi : 2 * wi + 1;
+                const float ma = srow == 0.0f ? 0.0f : gv[ga] / srow;
+                const float mb = SG == 8 ? ma : (srow == 0.0f ? 0.0f : gv[gb] / srow);
+                if constexpr (CB) {
+                    const uint4 ta = code_table_cb(ma, cb);
+                    d[e] = SG == 8 ? decode8_table(words[wi], ta) : decode8_table2(words[wi], ta, code_table_cb(mb, cb));
+                } else {
+                    d[e] = decode8_2(words[wi], ma, -8.0f * ma, mb, -8.0f * mb);
+                }
+            }
+            const v4i_t w8 = v4i_t{(int)d[0].x, (int)d[0].y, (int)d[1].x, (int)d[1].y};
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[j][h], acc[j], 0, 0, 0);
+        }
+        return;
+    } else {
+        if (one_group) {
+            // one multiplier for the lane's 64 codes: table decode
+            const float mu = srow == 0.0f ? 0.0f : gv[0] / srow;
+            uint4 tab;
+            if constexpr (CB) tab = code_table_cb(mu, cb);
+            else tab = code_table(mu);
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint2 a = decode8_table(words[2 * h], tab);
+                const uint2 b = decode8_table(words[2 * h + 1], tab);
+                const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[j][h], acc[j], 0, 0, 0);
+            }
+            return;
+        }
+        // groups of 16 and 32: a multiplier per 16 codes
+        if constexpr (CB) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint4 tab = code_table_cb(srow == 0.0f ? 0.0f : gv[h] / srow, cb);
+                const uint2 a = decode8_table(words[2 * h], tab);
+                const uint2 b = decode8_table(words[2 * h + 1], tab);
+                const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[j][h], acc[j], 0, 0, 0);
+            }
+            return;
+        } else {
+            // per-code decode
+            float mult[4], m8[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                mult[h] = srow == 0.0f ? 0.0f : gv[h] / srow;
+                m8[h] = -8.0f * mult[h];
+            }
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint2 a = decode8(words[2 * h], mult[h], m8[h]);
+                const uint2 b = decode8(words[2 * h + 1], mult[h], m8[h]);
+                const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[j][h], acc[j], 0, 0, 0);
+            }
+        }
+    }
+}
+
 // Operand layout: a k-step is 256 k. Lane l (row l & 15, part p = l >> 4)
 // owns the 64 contiguous k [256 s + 64 p, 256 s + 64 p + 64) of its weight row
 // and of its activation row; the MFMA of slice h (0..3) takes 16 of them,
@@ -267,17 +353,47 @@ __device__ __forceinline__ uint2 decode8_table2(uint32_t w, uint4 ta, uint4 tb) 
 // assignment, so each slice's 64 products are 64 distinct k and the four
 // slices cover the step. A lane's 64 k lie in one weight group when the group
 // is at least 64 wide, which makes the scale division once per step.
-// SG = 0 for groups of 16 and wider; SG = 8 or 4 for those narrow groups
-// (a multiplier per 8-code word, or per half word). CB: codes index the
-// codebook cb.
-template <int FM, int FNW, int KS, int MAXS, bool E4M3, int SG, bool CB>
-__global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__restrict__ X, const float *__restrict__ sx,
-                                                           const int8_t *__restrict__ W,
-                                                           const void *__restrict__ gs, int M, int N, int K,
-                                                           int group, uint16_t *__restrict__ Y, int64_t ldy,
-                                                           Codebook cb) {
-    constexpr int NGV = SG == 0 ? 4 : 64 / SG;  // group scales per lane and k-step
-    __shared__ v4i_t red[KS - 1][FNW][FM][64];
+//
+// Loading the operands straight into that layout puts four rows in each group
+// of four lanes (the MFMA row order), which costs the address unit about four
+// times a coalesced load. Instead each wavefront copies its k-steps global ->
+// LDS with buffer_load ... lds into a ring of NSLOT slots, NSLOT - 1 steps
+// ahead of the step it computes: the 16 FNW weight rows of a step (128 bytes
+// each, 8 rows per instruction) and AR activation rows (256 bytes each, 4 rows
+// per instruction; AR = 4 serves m <= 4, and fragment rows past AR read staged
+// rows, which only reach outputs that are never stored). Each 16-byte chunk
+// index is XORed with (row & 7), so the eight lanes of a fragment read that
+// the LDS serves together hit distinct banks. Fragments are then read from
+// LDS in the layout above. Group scales come straight from global memory, as
+// raw bits issued with each step's copies. G64: groups of 64 and wider (one
+// scale per lane and step).
+template <int AR, int FNW, int KS, int NSLOT, bool E4M3, int SG, bool CB, bool G64>
+__global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__restrict__ X,
+                                                            const float *__restrict__ sx,
+                                                            const int8_t *__restrict__ W,
+                                                            const void *__restrict__ gs, int M, int N, int K,
+                                                            int group, uint16_t *__restrict__ Y, int64_t ldy,
+                                                            Codebook cb) {
+    constexpr int FM = (AR + 15) / 16;
+    constexpr int NGV = SG == 0 ? 4 : 64 / SG;             // scales a tile step needs per lane
+    constexpr int NS = SG != 0 ? NGV : (G64 ? 1 : 4);      // scale loads per tile and step
+    constexpr int WB = 16 * FNW * 128;                     // weight bytes of a step
+    constexpr int XB = AR * 256;                           // activation bytes of a step
+    constexpr int SLOT = WB + XB;
+    constexpr int W_INS = WB / 1024, X_INS = (XB + 1023) / 1024;
+    // A step issues its INS copies, then its group-scale loads. Memory
+    // operations retire in order, so the copies of a step have landed once at
+    // most `later` x INS operations are outstanding, `later` being the number
+    // of steps issued after it (each issued at least INS operations after
+    // them; counting only the copies stays right however the compiler groups
+    // the scale loads).
+    constexpr int INS = W_INS + X_INS;
+    constexpr int RING = KS * NSLOT * SLOT;
+    constexpr int RED = (KS - 1) * FNW * FM * 64 * 16;
+    static_assert((NSLOT - 1) * INS <= 63, "vmcnt range");
+    static_assert(AR == 4 || AR % 16 == 0, "activation rows");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[RING > RED ? RING : RED];
+
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n0 = blockIdx.x * 16 * FNW;
@@ -291,160 +407,147 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(X), (short)0, M * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t *>(W) + (int64_t)n0 * wrow_bytes, (short)0, rows_b * wrow_bytes, 0x00020000);
+    uint8_t *ring = lds + wave * NSLOT * SLOT;
 
-    // Row scale of this lane's weight rows, (max group scale * 7) / 127: the
-    // four lanes of a row split its groups, then combine.
-    float srow[FNW];
-    int64_t gsr[FNW];  // index of the row's first group scale
+    // copy lanes: weights 8 rows x 8 chunks, activations 4 rows x 16 chunks
+    const int wrow = lane >> 3;
+    const uint32_t w_off = (uint32_t)wrow * (uint32_t)wrow_bytes + (uint32_t)(((lane & 7) ^ (wrow & 7)) * 16);
+    const int xrow = lane >> 4;
+
+    int64_t gsr[FNW];  // index of the first group scale of this lane's weight rows
+    float srow[FNW];   // row scales, set once the first copies are issued
 #pragma unroll
-    for (int i = 0; i < FNW; ++i) {
-        const int n = min(n0 + i * 16 + frow, N - 1);
-        gsr[i] = (int64_t)n * ng;
-        float smax = 0.0f;
-        for (int g = part; g < ng; g += 4) smax = fmaxf(smax, load_scale<E4M3>(gs, gsr[i] + g));
-        smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
-        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-        srow[i] = (smax * (CB ? cb.cmax : 7.0f)) / 127.0f;
-    }
+    for (int i = 0; i < FNW; ++i) gsr[i] = (int64_t)min(n0 + i * 16 + frow, N - 1) * ng;
 
     const int steps = K / 256;
     const int per_wave = (steps + KS - 1) / KS;
     const int s_begin = wave * per_wave;
-    const int s_end = min(steps, s_begin + per_wave);
+    const int nsteps = max(0, min(steps, s_begin + per_wave) - s_begin);
 
     v4i_t acc[FNW][FM];
 #pragma unroll
     for (int i = 0; i < FNW; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j) acc[i][j] = v4i_t{0, 0, 0, 0};
+    uint32_t gb[NSLOT][FNW][NS];  // raw group-scale bits, per slot
 
-    for (int s0 = s_begin; s0 < s_end; s0 += MAXS) {
-        // every load of this chunk first: weights, group scales, activations
-        v4i_t wv[MAXS][FNW][2];
-        float gv[MAXS][FNW][NGV];
-        v4i_t xv[MAXS][FM][4];
+    auto load_bits = [&](int64_t idx) __attribute__((always_inline)) -> uint32_t {
+        if constexpr (E4M3) return static_cast<const uint8_t *>(gs)[idx];
+        else return static_cast<const uint32_t *>(gs)[idx];
+    };
+    // copies of step s (of this wave) into slot `dst`, and its group scales
+    auto issue = [&](int s, uint8_t *__restrict__ dst, uint32_t (&g)[FNW][NS]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < MAXS; ++t) {
-            const int s = s0 + t;
-            if (s < s_end) {
-                const int kb = s * 256 + part * 64;  // first k of this lane's span
+        for (int q = 0; q < W_INS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)(dst + q * 1024), 16,
+                                                     (uint32_t)(q * 8) * (uint32_t)wrow_bytes + w_off +
+                                                         (uint32_t)(s * 128),
+                                                     0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < FNW; ++i) {
-                    const uint32_t off = (uint32_t)(i * 16 + frow) * (uint32_t)wrow_bytes + (uint32_t)(kb / 2);
-                    wv[t][i][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
-                    wv[t][i][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 16, 0);
-                    if constexpr (SG != 0) {
+        for (int q = 0; q < X_INS; ++q) {
+            const int r = q * 4 + xrow;  // activation row of this lane's chunk
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(dst + WB + q * 1024), 16,
+                (uint32_t)r * (uint32_t)K + (uint32_t)(((lane & 15) ^ (r & 7)) * 16) + (uint32_t)(s * 256), 0, 0, 0);
+        }
+        const int kb = s * 256 + part * 64;  // first k of this lane's span
 #pragma unroll
-                        for (int c = 0; c < NGV; ++c) gv[t][i][c] = load_scale<E4M3>(gs, gsr[i] + kb / SG + c);
-                    } else if (one_group) {
-                        const float g0 = load_scale<E4M3>(gs, gsr[i] + kb / group);
+        for (int i = 0; i < FNW; ++i) {
+            if constexpr (SG != 0) {
 #pragma unroll
-                        for (int h = 0; h < 4; ++h) gv[t][i][h] = g0;
-                    } else {
+                for (int c = 0; c < NS; ++c) g[i][c] = load_bits(gsr[i] + kb / SG + c);
+            } else if constexpr (G64) {
+                g[i][0] = load_bits(gsr[i] + kb / group);
+            } else {
 #pragma unroll
-                        for (int h = 0; h < 4; ++h) gv[t][i][h] = load_scale<E4M3>(gs, gsr[i] + (kb + 16 * h) / group);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < FM; ++j) {
-                    const uint32_t off = (uint32_t)(j * 16 + frow) * (uint32_t)K + (uint32_t)kb;
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) xv[t][j][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 16 * h, 0);
-                }
+                for (int h = 0; h < 4; ++h) g[i][h] = load_bits(gsr[i] + (kb + 16 * h) / group);
             }
         }
+    };
+    auto compute = [&](const uint8_t *__restrict__ cur, const uint32_t (&g)[FNW][NS]) __attribute__((always_inline)) {
+        v4i_t xv[FM][4];
 #pragma unroll
-        for (int t = 0; t < MAXS; ++t) {
-            if (s0 + t >= s_end) break;
+        for (int j = 0; j < FM; ++j) {
+            const int r = AR < 16 ? (frow & (AR - 1)) : j * 16 + frow;
 #pragma unroll
-            for (int i = 0; i < FNW; ++i) {
-                const uint32_t words[8] = {(uint32_t)wv[t][i][0][0], (uint32_t)wv[t][i][0][1],
-                                           (uint32_t)wv[t][i][0][2], (uint32_t)wv[t][i][0][3],
-                                           (uint32_t)wv[t][i][1][0], (uint32_t)wv[t][i][1][1],
-                                           (uint32_t)wv[t][i][1][2], (uint32_t)wv[t][i][1][3]};
-                if constexpr (SG != 0) {
-                    // groups of 8 or 4: a multiplier per word or per half word
+            for (int h = 0; h < 4; ++h)
+                xv[j][h] = *reinterpret_cast<const v4i_t *>(cur + WB + r * 256 + (((4 * part + h) ^ (r & 7)) * 16));
+        }
 #pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        uint2 d[2];
+        for (int i = 0; i < FNW; ++i) {
+            const int r = i * 16 + frow;
+            const uint4 a = *reinterpret_cast<const uint4 *>(cur + r * 128 + (((2 * part) ^ (r & 7)) * 16));
+            const uint4 b = *reinterpret_cast<const uint4 *>(cur + r * 128 + (((2 * part + 1) ^ (r & 7)) * 16));
+            const uint32_t words[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            float gv[NGV];
 #pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            const int wi = 2 * h + e;
-                            const int ga = SG == 8 ? wi : 2 * wi, gb = SG == 8 ? wi : 2 * wi + 1;
-                            const float ma = srow[i] == 0.0f ? 0.0f : gv[t][i][ga] / srow[i];
-                            const float mb = SG == 8 ? ma : (srow[i] == 0.0f ? 0.0f : gv[t][i][gb] / srow[i]);
-                            if constexpr (CB) {
-                                const uint4 ta = code_table_cb(ma, cb);
-                                d[e] = SG == 8 ? decode8_table(words[wi], ta)
-                                               : decode8_table2(words[wi], ta, code_table_cb(mb, cb));
-                            } else {
-                                d[e] = decode8_2(words[wi], ma, -8.0f * ma, mb, -8.0f * mb);
-                            }
-                        }
-                        const v4i_t w8 = v4i_t{(int)d[0].x, (int)d[0].y, (int)d[1].x, (int)d[1].y};
-#pragma unroll
-                        for (int j = 0; j < FM; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
-                    }
-                    continue;
-                }
-                if (one_group) {
-                    // one multiplier for the lane's 64 codes: table decode
-                    const float mu = srow[i] == 0.0f ? 0.0f : gv[t][i][0] / srow[i];
-                    uint4 tab;
-                    if constexpr (CB) tab = code_table_cb(mu, cb);
-                    else tab = code_table(mu);
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        const uint2 a = decode8_table(words[2 * h], tab);
-                        const uint2 b = decode8_table(words[2 * h + 1], tab);
-                        const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
-#pragma unroll
-                        for (int j = 0; j < FM; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
-                    }
-                    continue;
-                }
-                // groups of 16 and 32: a multiplier per 16 codes
-                if constexpr (CB) {
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        const uint4 tab = code_table_cb(srow[i] == 0.0f ? 0.0f : gv[t][i][h] / srow[i], cb);
-                        const uint2 a = decode8_table(words[2 * h], tab);
-                        const uint2 b = decode8_table(words[2 * h + 1], tab);
-                        const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
-#pragma unroll
-                        for (int j = 0; j < FM; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
-                    }
-                    continue;
-                }
-                // per-code decode
-                float mult[4], m8[4];
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    mult[h] = srow[i] == 0.0f ? 0.0f : gv[t][i][h] / srow[i];
-                    m8[h] = -8.0f * mult[h];
-                }
-#pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const uint2 a = decode8(words[2 * h], mult[h], m8[h]);
-                    const uint2 b = decode8(words[2 * h + 1], mult[h], m8[h]);
-                    const v4i_t w8 = v4i_t{(int)a.x, (int)a.y, (int)b.x, (int)b.y};
-#pragma unroll
-                    for (int j = 0; j < FM; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(w8, xv[t][j][h], acc[i][j], 0, 0, 0);
-                }
+            for (int c = 0; c < NGV; ++c) {
+                const uint32_t bits = g[i][SG == 0 && G64 ? 0 : c];
+                if constexpr (E4M3) gv[c] = e4m3_decode(bits);
+                else gv[c] = __uint_as_float(bits);
             }
+            w4a8_tile_step<FM, NGV, SG, CB>(words, gv, srow[i], one_group, xv, acc[i], cb);
+        }
+    };
+    // wait until the copies of the step `later` steps before the newest issued one have landed
+    auto wait_step = [&](int later) __attribute__((always_inline)) {
+        if (NSLOT > 2 && later >= 2) {
+            constexpr int C = (NSLOT > 2 ? 2 : 0) * INS;
+            __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | 0x0f70);
+        } else if (later >= 1) {
+            constexpr int C = INS;
+            __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | 0x0f70);
+        } else {
+            __builtin_amdgcn_s_waitcnt(0x0f70);
+        }
+        asm volatile("" ::: "memory");  // no LDS read moves above the wait
+    };
+    // step idx (0-based in this wave) computes from slot T; first the copy of
+    // step idx + NSLOT - 1 goes into the slot step idx - 1 was read from
+    // (those reads have completed: their results were used)
+    auto body = [&](int idx, auto t_c) __attribute__((always_inline)) {
+        constexpr int T = decltype(t_c)::value;
+        constexpr int TN = (T + NSLOT - 1) % NSLOT;
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+        const bool ahead = idx + NSLOT - 1 < nsteps;
+        if (ahead) issue(s_begin + idx + NSLOT - 1, ring + TN * SLOT, gb[TN]);
+        wait_step(min(NSLOT - 1, nsteps - 1 - idx));
+        compute(ring + T * SLOT, gb[T]);
+    };
+    if (nsteps > 0) issue(s_begin, ring, gb[0]);
+    if constexpr (NSLOT > 2) {
+        if (nsteps > 1) issue(s_begin + 1, ring + SLOT, gb[NSLOT > 2 ? 1 : 0]);
+    }
+    // Row scale of this lane's weight rows, (max group scale * cmax) / 127,
+    // taken after the first copies are on their way, so that its scattered
+    // loads overlap them instead of delaying the weight stream.
+#pragma unroll
+    for (int i = 0; i < FNW; ++i) {
+        float smax = 0.0f;
+        for (int g = part; g < ng; g += 4) smax = fmaxf(smax, load_scale<E4M3>(gs, gsr[i] + g));
+        smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
+        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
+        srow[i] = (smax * (CB ? cb.cmax : 7.0f)) / 127.0f;
+    }
+    for (int idx = 0; idx < nsteps; idx += NSLOT) {
+        body(idx, std::integral_constant<int, 0>{});
+        if (idx + 1 >= nsteps) break;
+        body(idx + 1, std::integral_constant<int, 1>{});
+        if constexpr (NSLOT > 2) {
+            if (idx + 2 >= nsteps) break;
+            body(idx + 2, std::integral_constant<int, (NSLOT > 2 ? 2 : 0)>{});
         }
     }
 
+    v4i_t *red = reinterpret_cast<v4i_t *>(lds);  // [KS - 1][FNW][FM][64], over the copy slots
     if (KS > 1) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __syncthreads();  // every wavefront is done with its slots
         if (wave > 0) {
 #pragma unroll
             for (int i = 0; i < FNW; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) red[wave - 1][i][j][lane] = acc[i][j];
+                for (int j = 0; j < FM; ++j) red[(((wave - 1) * FNW + i) * FM + j) * 64 + lane] = acc[i][j];
         }
         __syncthreads();
         if (wave > 0) return;
@@ -453,12 +556,11 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
 #pragma unroll
             for (int i = 0; i < FNW; ++i)
 #pragma unroll
-                for (int j = 0; j < FM; ++j) acc[i][j] += red[w][i][j][lane];
+                for (int j = 0; j < FM; ++j) acc[i][j] += red[((w * FNW + i) * FM + j) * 64 + lane];
     }
 
-    // Epilogue: lane holds acc[i][j][r] = y[m][n], m = 16j + (l & 15),
-    // n = n0 + 16i + 4(l >> 4) + r; the weight scale of row n is its s_row,
-    // which lives in lane (n - n0 - 16i) of the same 16-lane group.
+    // Epilogue (as the direct kernel): lane holds acc[i][j][r] = y[m][n],
+    // m = 16j + (l & 15), n = n0 + 16i + 4(l >> 4) + r.
 #pragma unroll
     for (int i = 0; i < FNW; ++i) {
         float sw4[4];
@@ -484,58 +586,49 @@ __global__ __launch_bounds__(64 * KS) void w4a8_fused_kernel(const int8_t *__res
     }
 }
 
-template <int FM, int FNW, int MAXS, bool E4M3, int SG, bool CB>
-hipError_t launch_fused_cfg(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
-                            int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
-    const int64_t groups = (n + 16 * FNW - 1) / (16 * FNW);
-    dim3 grid((unsigned)groups);
-    if constexpr (SG != 0 || CB) {
-        // narrow groups and codebooks: one K split (4 wavefronts) for every width
-        w4a8_fused_kernel<FM, FNW, 4, MAXS, E4M3, SG, CB><<<grid, dim3(256), 0, stream>>>(
+template <int AR, int FNW, int KS, int NSLOT, bool E4M3, int SG, bool CB>
+hipError_t launch_staged_cfg(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
+                             int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
+    const dim3 grid((unsigned)((n + 16 * FNW - 1) / (16 * FNW))), block(64 * KS);
+    if (SG == 0 && group >= 64)
+        w4a8_staged_kernel<AR, FNW, KS, NSLOT, E4M3, SG, CB, true><<<grid, block, 0, stream>>>(
             x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
-    } else if (groups >= 1024) {
-        w4a8_fused_kernel<FM, FNW, 2, MAXS, E4M3, 0, false><<<grid, dim3(128), 0, stream>>>(
+    else
+        w4a8_staged_kernel<AR, FNW, KS, NSLOT, E4M3, SG, CB, false><<<grid, block, 0, stream>>>(
             x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
-    } else if (groups >= 512) {
-        w4a8_fused_kernel<FM, FNW, 4, MAXS, E4M3, 0, false><<<grid, dim3(256), 0, stream>>>(
-            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
-    } else {
-        w4a8_fused_kernel<FM, FNW, 8, MAXS, E4M3, 0, false><<<grid, dim3(512), 0, stream>>>(
-            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
-    }
     return hipGetLastError();
 }
 
+#define CK4_STAGED(AR, FNW, KS, NSLOT) \
+    launch_staged_cfg<AR, FNW, KS, NSLOT, E4M3, SG, CB>(x, sx, w, gs, m, n, k, group, y, ldy, stream, cb)
+
 template <bool E4M3, int SG, bool CB>
-hipError_t launch_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed, const void *group_scales,
-                        int64_t m, int64_t n, int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream,
-                        const Codebook &cb) {
-    if (m <= 16)
-        return launch_fused_cfg<1, 1, 2, E4M3, SG, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
-                                                        stream, cb);
-    if (m <= 32)
-        return launch_fused_cfg<2, 1, 2, E4M3, SG, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
-                                                        stream, cb);
-    // 64-row activations: two weight tiles per workgroup (half the
-    // activation re-reads) when the weight has fewer than 512 tiles; with
-    // more, the extra workgroups win (N = 5120: 33.1 -> 25.4 us, N = 12288:
-    // 26.4 -> 32.3 us at M = 64)
-    if ((n + 15) / 16 < 512)
-        return launch_fused_cfg<4, 2, 1, E4M3, SG, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y,
-                                                        ldy, stream, cb);
-    return launch_fused_cfg<4, 1, 1, E4M3, SG, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
-                                                    stream, cb);
+hipError_t launch_staged(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
+                         int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
+    // With 512 or more weight tiles of 16 rows the workgroups are numerous
+    // enough to fill the CUs with two K splits each; with fewer, four (N =
+    // 12288 / 5120 at K = 3072 / 5120, 32 weight copies: the measured best of
+    // the staged configurations at every m).
+    const bool many = (n + 15) / 16 >= 512;
+    if (m <= 4) return CK4_STAGED(4, 1, 4, 3);
+    if (m <= 16) return many ? CK4_STAGED(16, 1, 2, 3) : CK4_STAGED(16, 1, 4, 3);
+    if (m <= 32) return many ? CK4_STAGED(32, 2, 2, 3) : CK4_STAGED(32, 1, 4, 2);
+    return many ? CK4_STAGED(64, 2, 2, 2) : CK4_STAGED(64, 2, 4, 2);
 }
+#undef CK4_STAGED
 
 template <bool E4M3, bool CB>
 hipError_t launch_fused_groups(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
                                const void *group_scales, int64_t m, int64_t n, int64_t k, int group, uint16_t *y,
                                int64_t ldy, hipStream_t stream, const Codebook &cb) {
     if (group == 4)
-        return launch_fused<E4M3, 4, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
+        return launch_staged<E4M3, 4, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
+                                                   stream, cb);
     if (group == 8)
-        return launch_fused<E4M3, 8, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
-    return launch_fused<E4M3, 0, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream, cb);
+        return launch_staged<E4M3, 8, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy,
+                                                   stream, cb);
+    return launch_staged<E4M3, 0, CB>(x_q8, x_scales, w_packed, group_scales, m, n, k, group, y, ldy, stream,
+                                               cb);
 }
 
 template <bool E4M3>
