@@ -164,7 +164,8 @@ ck4_status ck4_rotate_act_f32(const uint16_t *x, int64_t m, int64_t k, int64_t l
  * The epilogue is fp32 ((acc * x_scale) * w_scale + bias) rounded once to
  * bf16, nearest even.
  * Alignment: x_q and w_packed 16-byte aligned; y 8-byte aligned and ldy a
- * multiple of 4. Unsupported: k % 256 != 0, k > 131072.
+ * multiple of 4. Unsupported: k % 128 != 0, k < 256, k > 131072 (the rows are
+ * walked in 256-k steps; k = 128 (mod 256) ends in a half step).
  */
 ck4_status ck4_linear_w4a4(const int8_t *x_q, const float *x_scales, const int8_t *w_packed,
                            const float *w_scales, const float *bias, int64_t m, int64_t n, int64_t k,
@@ -272,7 +273,7 @@ ck4_status ck4_linear_w8a8(const int8_t *x_q8, const float *x_scales, const int8
  *                   column slice of y through ldy (a multiple of 16);
  *   chunk_cols < 0  one decode pass over all n, then one int8 GEMM;
  *   chunk_cols == 0 the default policy: for m <= 64 (env
- *                   CK4_W4A8_CHUNK_MAX_ROWS) and k % 256 == 0, one fused kernel
+ *                   CK4_W4A8_CHUNK_MAX_ROWS) and k >= 256, one fused kernel
  *                   that decodes in registers (no workspace); otherwise chunks
  *                   of the device L2 size / k rounded down to 128, clamped to
  *                   [1024, 4096] (env CK4_W4A8_CHUNK_COLS overrides the width)

@@ -270,10 +270,10 @@ static ck4_status gemm_entry(const char *fn, bool s4, const int8_t *a, const flo
     if (!a || !b || !y || (!out_i32 && (!sa || !sb))) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, out_i32 ? 16 : 8)) return s;
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
-    const int64_t step_k = s4 ? 256 : 128;
-    if (k % step_k != 0)
-        return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of %lld", fn, (long long)k,
-                    (long long)step_k);
+    if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
+    // packed int4 rows are walked in 128-byte windows, which a row of k = 128
+    // (64 bytes) cannot hold
+    if (s4 && k < 256) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld < 256 for packed int4", fn, (long long)k);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_gemm(s4, a, b, sa, sb, bias, m, n, k, out_i32, y, ldy,
                                          static_cast<hipStream_t>(stream), lora));
@@ -428,7 +428,7 @@ static int64_t w4a8_chunk(int64_t m, int64_t n, int64_t k, int64_t chunk_cols, i
     int64_t c = e_cols ? std::atoll(e_cols) : 0;
     if (c <= 0) {
         // skinny rows: decode in registers inside the GEMM (no round trip)
-        if (m <= 64 && k % 256 == 0) return 0;
+        if (m <= 64 && k >= 256) return 0;
         c = (l2_bytes / k) / 128 * 128;
         if (c < 1024) c = 1024;
         if (c > 4096) c = 4096;

@@ -113,7 +113,7 @@ hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, 
                               int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream,
                               const Codebook &cb = Codebook{});
 
-// Fused grouped W4A8 linear for m <= 64 and k % 256 == 0 (decode in registers
+// Fused grouped W4A8 linear for m <= 64 and k >= 256, k % 128 == 0 (decode in registers
 // + int8 MFMA + epilogue), bit-identical to decode followed by the int8 GEMM.
 hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
                              const void *group_scales, bool scale_e4m3, int64_t m, int64_t n, int64_t k, int group,

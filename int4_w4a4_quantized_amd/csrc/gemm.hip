@@ -79,7 +79,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM *
                           amdgpu_waves_per_eu(WPE, WPE))) void
 gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
                 const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes,
-                int ksteps, void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m,
+                int halves, void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m,
                 LoraUp lora) {
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM;
@@ -101,6 +101,13 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave / WGN;
     const int wn = wave - wm * WGN;
+
+    // K in 64-byte halves of a 128-byte step; an odd count ends in a half
+    // step, whose copy window is moved back by half a step (so it stays inside
+    // the row) and of which only the second half is multiplied
+    const int ksteps = (halves + 1) >> 1;
+    const bool half_tail = halves & 1;
+    auto kbyte = [&](int s) { return s * kRowBytes - (half_tail && s == ksteps - 1 ? kRowBytes / 2 : 0); };
 
     const int rows_a = min(BM, M - m0);
     const int rows_b = min(BN, N - n0);
@@ -127,7 +134,7 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
                 // the k offset within the row in soffset
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     is_a ? ra : rb, (__attribute__((address_space(3))) void *)(base + q * 1024), 16,
-                    lane_off + (uint32_t)(qr * 8) * (uint32_t)row_bytes, (uint32_t)(s * kRowBytes), 0, 0);
+                    lane_off + (uint32_t)(qr * 8) * (uint32_t)row_bytes, (uint32_t)kbyte(s), 0, 0);
             }
         }
     };
@@ -163,13 +170,14 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
     // widened and fragment j+2 is read from LDS. The scheduling groups put two
     // VALU instructions between consecutive MFMAs, so the widening of the next
     // fragment hides under the matrix-core time of the current one.
-    auto compute_stage = [&](const uint4 *src) {
+    auto compute_stage = [&](const uint4 *src, bool tail) {
         const char *base = reinterpret_cast<const char *>(src);
         auto xptr = [&](int j, int coff) {
             return reinterpret_cast<const uint4 *>(base + a_row0 + j * 16 * kRowBytes + coff);
         };
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
+            if (h == 0 && tail) continue;  // a half step: its k are the window's second half
             __builtin_amdgcn_sched_barrier(0);
             const int coff = h ? chunk_off1 : chunk_off0;
             uint4 wb[FN];
@@ -238,7 +246,7 @@ gemm_big_kernel(const int8_t *__restrict__ A, const int8_t *__restrict__ B, cons
     // not make the fragment reads wait for the DMA.
     auto body = [&](uint4 *__restrict__ dst, const uint4 *__restrict__ src, int s) {
         if (s + 1 < ksteps) issue_stage(dst, s + 1);
-        compute_stage(src);
+        compute_stage(src, half_tail && s == ksteps - 1);
     };
     issue_stage(smem, 0);
     for (int s = 0; s < ksteps; ++s) {
@@ -347,7 +355,7 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
                       int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                       LoraUp lora) {
     const int64_t row_bytes = S4 ? k / 2 : k;
-    const int ksteps = (int)(row_bytes / kRowBytes);
+    const int halves = (int)(row_bytes / (kRowBytes / 2));
     const int tiles_m = (int)((m + BM - 1) / BM);
     const int tiles_n = (int)((n + BN - 1) / BN);
     const int total = tiles_m * tiles_n;
@@ -355,13 +363,13 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
     dim3 grid((unsigned)total), block(64 * WGM * WGN);
     if (out_i32)
         gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, true, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m, lora);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, halves, y, ldy, tiles_n, total, xcd_m, lora);
     else if (lora.rank > 0)
         gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, false, true><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m, lora);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, halves, y, ldy, tiles_n, total, xcd_m, lora);
     else
         gemm_big_kernel<S4, BM, BN, WGM, WGN, WPE, false, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, ksteps, y, ldy, tiles_n, total, xcd_m, lora);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, halves, y, ldy, tiles_n, total, xcd_m, lora);
     return hipGetLastError();
 }
 
@@ -389,7 +397,7 @@ hipError_t launch_big(const int8_t *a, const int8_t *b, const float *sa, const f
 template <bool S4, int FM, int FNW, int KS, int MAXS, bool LDS_STAGE, bool OUT_I32, bool LORA>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
-    const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int steps,
+    const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int halves,
     void *__restrict__ Y, int64_t ldy, LoraUp lora) {
     constexpr int SLAB = 128;  // bytes of each row per k-step: 256 k for s4, 128 k for s8
     constexpr int ROWS = 16 * (FNW + FM);  // staged rows per step: weights, then activations
@@ -414,6 +422,11 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
     const int crow = lane >> 3;
     const uint32_t c_off = (uint32_t)(((lane & 7) ^ crow) * 16);
     uint8_t *ring = lds + wave * MAXS * SLOT;
+    // K in 64-byte halves of a step (as the large kernel): a half last step
+    // copies a window moved back by half a step and multiplies its second
+    // half; the direct loads read its first half where it lies
+    const int steps = (halves + 1) >> 1;
+    const bool half_tail = halves & 1;
 
     const int per_wave = (steps + KS - 1) / KS;
     const int s_begin = wave * per_wave;
@@ -439,7 +452,9 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
                         const int r = (is_w ? q : q - 2 * FNW) * 8 + crow;  // row within weights / activations
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(
                             is_w ? rb : ra, (__attribute__((address_space(3))) void *)(ring + t * SLOT + q * 1024), 16,
-                            (uint32_t)r * (uint32_t)row_bytes + (uint32_t)(s * SLAB) + c_off, 0, 0, 0);
+                            (uint32_t)r * (uint32_t)row_bytes +
+                                (uint32_t)(s * SLAB - (half_tail && s == steps - 1 ? SLAB / 2 : 0)) + c_off,
+                            0, 0, 0);
                     }
                 }
             }
@@ -449,8 +464,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
             for (int t = 0; t < MAXS; ++t) {
                 if (s0 + t >= s_end) break;
                 const uint8_t *slot = ring + t * SLOT;
+                const bool tail = half_tail && s0 + t == steps - 1;
     #pragma unroll
                 for (int h = 0; h < SLAB / 64; ++h) {
+                    if (h == 0 && tail) continue;
                     const int coff = ((4 * h + fgrp) ^ (frow & 7)) * 16;
                     uint4 wv[FNW], xv[FM];
     #pragma unroll
@@ -489,6 +506,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
                 if (s < s_end) {
     #pragma unroll
                     for (int h = 0; h < SLAB / 64; ++h) {
+                        if (h == 1 && half_tail && s == steps - 1) break;
     #pragma unroll
                         for (int i = 0; i < FNW; ++i)
                             wv[t][i][h] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -505,6 +523,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
                 if (s0 + t >= s_end) break;
     #pragma unroll
                 for (int h = 0; h < SLAB / 64; ++h) {
+                    if (h == 1 && half_tail && s0 + t == steps - 1) break;
                     if constexpr (S4) {
     #pragma unroll
                         for (int i = 0; i < FNW; ++i) {
@@ -631,7 +650,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(
 template <bool S4, int FM, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_shared_kernel(
     const int8_t *__restrict__ A, const int8_t *__restrict__ B, const float *__restrict__ sa,
-    const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int steps,
+    const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int row_bytes, int halves,
     uint16_t *__restrict__ Y, int64_t ldy) {
     constexpr int SLAB = 128;                 // bytes of a row per k-step
     constexpr int CS = 2;                     // k-steps per chunk
@@ -656,6 +675,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_shared_kernel(
     const int fgrp = lane >> 4;
     const int crow = lane >> 3;
     const uint32_t c_off = (uint32_t)(((lane & 7) ^ crow) * 16);
+    // K in 64-byte halves (as the large kernel): a half last step copies a
+    // window moved back by half a step and multiplies its second half
+    const int steps = (halves + 1) >> 1;
+    const bool half_tail = halves & 1;
     const int nch = (steps + CS - 1) / CS;
 
     v4i acc[FM];
@@ -675,7 +698,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_shared_kernel(
             const int r = (is_a ? 8 * rg : 8 * rg - AROWS) + crow;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 is_a ? ra : rb, (__attribute__((address_space(3))) void *)(slot + st * STEP_B + rg * 1024), 16,
-                (uint32_t)r * (uint32_t)row_bytes + (uint32_t)(s * SLAB) + c_off, 0, 0, 0);
+                (uint32_t)r * (uint32_t)row_bytes +
+                    (uint32_t)(s * SLAB - (half_tail && s == steps - 1 ? SLAB / 2 : 0)) + c_off,
+                0, 0, 0);
         }
     };
     // wait for chunk c (`later` next chunks' copies may stay in flight), then
@@ -692,8 +717,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_shared_kernel(
 #pragma unroll
         for (int st = 0; st < CS; ++st) {
             if (c * CS + st >= steps) break;
+            const bool tail = half_tail && c * CS + st == steps - 1;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
+                if (h == 0 && tail) continue;
                 const int coff = ((4 * h + fgrp) ^ (frow & 7)) * 16;
                 const uint8_t *sp = slot + st * STEP_B;
                 const uint4 wp = *reinterpret_cast<const uint4 *>(sp + (AROWS + 16 * wave + frow) * SLAB + coff);
@@ -767,7 +794,7 @@ hipError_t launch_skinny_shared_nw(const int8_t *a, const int8_t *b, const float
     const int64_t tiles = (n + 15) / 16;
     const dim3 grid((unsigned)((tiles + NW - 1) / NW)), block(64 * NW);
     gemm_skinny_shared_kernel<true, FM, NW><<<grid, block, 0, stream>>>(a, b, sa, sb, bias, (int)m, (int)n,
-                                                                         (int)(k / 2), (int)(k / 256), y, ldy);
+                                                                         (int)(k / 2), (int)(k / 128), y, ldy);
     return hipGetLastError();
 }
 
@@ -805,17 +832,17 @@ hipError_t launch_skinny_cfg(const int8_t *a, const int8_t *b, const float *sa, 
     constexpr bool STG = FM >= 4;
     constexpr int MAXS = skinny_maxs<FM, FNW, KS, STG>();
     const int64_t row_bytes = S4 ? k / 2 : k;
-    const int steps = (int)(row_bytes / 128);
+    const int halves = (int)(row_bytes / 64);
     dim3 grid((unsigned)((n + 16 * FNW - 1) / (16 * FNW))), block(64 * KS);
     if (out_i32)
         gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, STG, true, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, halves, y, ldy, lora);
     else if (lora.rank > 0)
         gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, STG, false, true><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, halves, y, ldy, lora);
     else
         gemm_skinny_kernel<S4, FM, FNW, KS, MAXS, STG, false, false><<<grid, block, 0, stream>>>(
-            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, steps, y, ldy, lora);
+            a, b, sa, sb, bias, (int)m, (int)n, (int)row_bytes, halves, y, ldy, lora);
     return hipGetLastError();
 }
 

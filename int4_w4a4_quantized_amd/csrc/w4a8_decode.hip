@@ -419,7 +419,14 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
 #pragma unroll
     for (int i = 0; i < FNW; ++i) gsr[i] = (int64_t)min(n0 + i * 16 + frow, N - 1) * ng;
 
-    const int steps = K / 256;
+    // K in 128-k halves of a step: an odd count ends in a half step, whose
+    // copy window is moved back by half a step (so it stays inside the rows)
+    // and whose first-half lanes (parts 0 and 1) multiply zeros
+    const int steps = (K / 128 + 1) >> 1;
+    const bool half_tail = (K / 128) & 1;
+    auto kfirst = [&](int s) __attribute__((always_inline)) {
+        return s * 256 - (half_tail && s == steps - 1 ? 128 : 0);
+    };
     const int per_wave = (steps + KS - 1) / KS;
     const int s_begin = wave * per_wave;
     const int nsteps = max(0, min(steps, s_begin + per_wave) - s_begin);
@@ -437,20 +444,21 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
     };
     // copies of step s (of this wave) into slot `dst`, and its group scales
     auto issue = [&](int s, uint8_t *__restrict__ dst, uint32_t (&g)[FNW][NS]) __attribute__((always_inline)) {
+        const int k0 = kfirst(s);  // first k of the step's window
 #pragma unroll
         for (int q = 0; q < W_INS; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)(dst + q * 1024), 16,
                                                      (uint32_t)(q * 8) * (uint32_t)wrow_bytes + w_off +
-                                                         (uint32_t)(s * 128),
+                                                         (uint32_t)(k0 / 2),
                                                      0, 0, 0);
 #pragma unroll
         for (int q = 0; q < X_INS; ++q) {
             const int r = q * 4 + xrow;  // activation row of this lane's chunk
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rx, (__attribute__((address_space(3))) void *)(dst + WB + q * 1024), 16,
-                (uint32_t)r * (uint32_t)K + (uint32_t)(((lane & 15) ^ (r & 7)) * 16) + (uint32_t)(s * 256), 0, 0, 0);
+                (uint32_t)r * (uint32_t)K + (uint32_t)(((lane & 15) ^ (r & 7)) * 16) + (uint32_t)k0, 0, 0, 0);
         }
-        const int kb = s * 256 + part * 64;  // first k of this lane's span
+        const int kb = k0 + part * 64;  // first k of this lane's span
 #pragma unroll
         for (int i = 0; i < FNW; ++i) {
             if constexpr (SG != 0) {
@@ -464,14 +472,18 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
             }
         }
     };
-    auto compute = [&](const uint8_t *__restrict__ cur, const uint32_t (&g)[FNW][NS]) __attribute__((always_inline)) {
+    auto compute = [&](const uint8_t *__restrict__ cur, const uint32_t (&g)[FNW][NS], bool tail)
+                       __attribute__((always_inline)) {
         v4i_t xv[FM][4];
+        const bool dead = tail && part < 2;  // this lane's k were counted in the previous step
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int r = AR < 16 ? (frow & (AR - 1)) : j * 16 + frow;
 #pragma unroll
-            for (int h = 0; h < 4; ++h)
+            for (int h = 0; h < 4; ++h) {
                 xv[j][h] = *reinterpret_cast<const v4i_t *>(cur + WB + r * 256 + (((4 * part + h) ^ (r & 7)) * 16));
+                if (dead) xv[j][h] = v4i_t{0, 0, 0, 0};
+            }
         }
 #pragma unroll
         for (int i = 0; i < FNW; ++i) {
@@ -512,7 +524,7 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
         const bool ahead = idx + NSLOT - 1 < nsteps;
         if (ahead) issue(s_begin + idx + NSLOT - 1, ring + TN * SLOT, gb[TN]);
         wait_step(min(NSLOT - 1, nsteps - 1 - idx));
-        compute(ring + T * SLOT, gb[T]);
+        compute(ring + T * SLOT, gb[T], half_tail && s_begin + idx == steps - 1);
     };
     if (nsteps > 0) issue(s_begin, ring, gb[0]);
     if constexpr (NSLOT > 2) {

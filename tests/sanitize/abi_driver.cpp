@@ -185,7 +185,9 @@ int main(int argc, char **argv) {
     REFUSED(ck4_linear_w4a4(I8, nullptr, I8, F, nullptr, 8, 8, 256, U16, 8, nullptr), CK4_ERR_INVALID);
     REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 256, U16, 6, nullptr), CK4_ERR_INVALID);
     REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 256, (uint16_t *)ODD, 8, nullptr), CK4_ERR_INVALID);
-    REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 384, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
+    REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 192, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
+    REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 128, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
+    VALID(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 384, U16, 8, nullptr), 1);
     REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 262144, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, BIG, 8, 256, U16, 8, nullptr));
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, BIG, 256, U16, BIG, nullptr));

@@ -64,7 +64,8 @@ def test_linear_validation(L):
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 4, NULL) == ck.CK4_ERR_INVALID  # ldy < n
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 10, NULL) == ck.CK4_ERR_INVALID  # ldy % 4
     assert f(ODD, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID  # alignment
-    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 384, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 256
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 192, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 128
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 128, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k < 256
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 262144, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k too big
     g = L.ck4_gemm_w4a4_acc_i32
     assert g(FAKE, FAKE, 8, 8, 256, ODD, 8, NULL) == ck.CK4_ERR_INVALID
@@ -195,7 +196,7 @@ def test_lora_validation(L):
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, NULL, FAKE, 32, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, ODD, 32, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 16, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
-    assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 32, 8, 8, 384, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 32, 8, 8, 192, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED
     assert f(FAKE, FAKE, FAKE, FAKE, NULL, FAKE, FAKE, 32, 8, 8, 256, FAKE, 4, NULL) == ck.CK4_ERR_INVALID
 
 

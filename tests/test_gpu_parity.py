@@ -24,6 +24,9 @@ ROT_CASES = [
 GEMM_CASES = [
     (64, 256, 256), (1, 1, 256), (3, 17, 256), (17, 3, 512), (130, 200, 768), (16, 64, 3072),
     (64, 130, 1024), (257, 129, 512), (33, 77, 256), (8, 1000, 512), (200, 8, 1280),
+    # k = 128 (mod 256): the last 256-k step is a half step (skinny direct and
+    # staged kernels, large kernel)
+    (3, 17, 384), (64, 130, 640), (130, 200, 1152), (257, 129, 384), (20, 1000, 1152),
 ]
 
 
@@ -211,7 +214,10 @@ def test_w4a8_decode_chunks_bitexact(ck):
 @pytest.mark.parametrize("m,n,k,chunk", [(8, 1152, 512, 384), (8, 1152, 512, 400), (1, 1152, 512, -1),
                                          (64, 1500, 1024, 0), (100, 300, 512, 0), (16, 5120, 5120, 0),
                                          (3, 1000, 768, 0), (40, 77, 1024, 0), (1, 12288, 3072, 0),
-                                         (64, 130, 384, 0)])
+                                         (64, 130, 384, 0),
+                                         # k = 128 (mod 256) through the fused kernel's half step
+                                         (1, 5000, 640, 0), (24, 333, 1152, 0), (64, 1000, 384, 0),
+                                         (33, 8200, 1152, 0), (12, 8200, 640, 0)])
 def test_w4a8_linear_chunked_equals_single_pass_and_oracle(ck, m, n, k, chunk):
     rng = np.random.default_rng(700 + m + n)
     xb = workloads.make_activations(rng, m, k)
@@ -222,6 +228,24 @@ def test_w4a8_linear_chunked_equals_single_pass_and_oracle(ck, m, n, k, chunk):
     y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, 128, -1))
     assert np.array_equal(y, y1)
     assert_bf16_close(y, oracle.linear_w4a8_grouped(xb, wp, gs))
+
+
+@pytest.mark.parametrize("group", [4, 8, 16, 64, 128])
+@pytest.mark.parametrize("m", [1, 24, 64])
+def test_w4a8_fused_half_step_matches_chunked(ck, m, group):
+    """k = 1152, four and a half 256-k steps: the fused kernel's moved-back last window on every decode path."""
+    rng = np.random.default_rng(950 + m + group)
+    n, k = 333, 1152
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    w[7] = 0
+    wp, gs = oracle.quantize_weight_convrot(w, group=group)
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    wpd, gsd = torch.from_numpy(wp).cuda(), torch.from_numpy(gs).cuda()
+    y0 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, group, 0))
+    yc = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wpd, gsd, group, 128))
+    assert np.array_equal(y0, yc)
+    assert_bf16_close(y0, oracle.linear_w4a8_grouped(xb, wp, gs, group))
 
 
 @pytest.mark.parametrize("group", [4, 8, 16, 64, 256])
@@ -354,7 +378,7 @@ def test_fp6_linear_matches_int4_path_and_oracle(ck, m, n, k, with_bias):
     bd = None if bias is None else torch.from_numpy(bias).cuda()
     sxd, wsd = torch.from_numpy(sx).cuda(), torch.from_numpy(ws).cuda()
     y6 = bf16_host_bits(ck.linear_w4a4_fp6(xq6, sxd, wq6, wsd, bd))
-    if k % 256 == 0:
+    if k >= 256:
         # the int8-MFMA kernel on the same codes gives the same bits
         y4 = bf16_host_bits(ck.linear_w4a4(torch.from_numpy(xq).cuda(), sxd, torch.from_numpy(wp).cuda(), wsd, bd))
         assert np.array_equal(y6, y4)
@@ -650,12 +674,13 @@ def test_full_size_layer(ck, name):
         assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], ws_ref))
 
 
-@pytest.mark.parametrize("m,n,k", [(17, 12288, 3072), (32, 12288, 3072), (33, 8200, 768), (48, 8200, 1280),
+@pytest.mark.parametrize("m,n,k", [(17, 12288, 640), (40, 8200, 384), (64, 8200, 1152), (8, 12288, 1152),
+                                   (17, 12288, 3072), (32, 12288, 3072), (33, 8200, 768), (48, 8200, 1280),
                                    (64, 16384, 512), (40, 12288, 256), (24, 8200, 2304), (5, 12288, 3072),
                                    (8, 8200, 768), (16, 12288, 1280)])
 def test_skinny_shared_activation_kernel(ck, m, n, k):
     """4 < m <= 64 with at least 512 weight tiles of 16 rows: the kernel whose waves split N over one LDS copy of
-    the activation (ragged N leaves a wave with no rows; k = 256 is a single step). It must give the bits of the
+    the activation (ragged N leaves a wave with no rows; k = 256 is a single step, k = 128 (mod 256) ends in a half step). It must give the bits of the
     K-split kernel, reached through the LoRA epilogue with t = 0 (bias present, so no -0 can meet the + 0), and
     stay within the oracle's bf16 bound."""
     _, xq, sx, wp, ws = _quantised_pair(m, n, k, 3300 + m)
@@ -706,7 +731,7 @@ def test_random_shapes_kernel_variants_agree(ck):
     for _ in range(8):
         m = int(rng.integers(5, 65))
         n = int(rng.integers(2048, 5000)) * 4
-        k = 256 * int(rng.integers(1, 13))
+        k = 128 * int(rng.integers(2, 25))
         x = dev_bf16(workloads.make_activations(rng, m, k))
         w = torch.from_numpy(workloads.make_weight(rng, n, k)).cuda()
         bias = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
@@ -719,7 +744,7 @@ def test_random_shapes_kernel_variants_agree(ck):
     for _ in range(8):
         m = int(rng.integers(65, 3000))
         n = int(rng.integers(16, 1000)) * 4
-        k = 256 * int(rng.integers(1, 9))
+        k = 128 * int(rng.integers(2, 17))
         x = dev_bf16(workloads.make_activations(rng, m, k))
         w = torch.from_numpy(workloads.make_weight(rng, n, k)).cuda()
         bias = torch.from_numpy(rng.standard_normal(n).astype(np.float32)).cuda()
@@ -841,7 +866,7 @@ def _lora_atol(acc, sx, ws, bias, t_bits, b_bits, rank):
 
 
 @pytest.mark.parametrize("m,n,k,rank", [(1, 77, 256, 32), (16, 300, 512, 64), (33, 130, 1024, 128),
-                                        (64, 1000, 768, 256), (65, 200, 512, 32), (130, 257, 768, 64),
+                                        (16, 300, 640, 64), (130, 257, 384, 32), (64, 1000, 768, 256), (65, 200, 512, 32), (130, 257, 768, 64),
                                         (300, 96, 1280, 128), (1000, 520, 512, 256)])
 @pytest.mark.parametrize("with_bias", [False, True])
 def test_linear_w4a4_lora_epilogue(ck, m, n, k, rank, with_bias):
@@ -950,7 +975,7 @@ def test_fp6_lora_epilogue_matches_int4_path_and_oracle(ck, m, n, k, rank, with_
     td, bpd = dev_bf16(frag_layout.pack(t)), dev_bf16(frag_layout.pack(b))
     sxd, wsd = torch.from_numpy(sx).cuda(), torch.from_numpy(ws).cuda()
     y6 = bf16_host_bits(ck.linear_w4a4_fp6_lora(xq6, sxd, wq6, wsd, td, bpd, bd))
-    if k % 256 == 0:
+    if k >= 256:
         y4 = bf16_host_bits(ck.linear_w4a4_lora(torch.from_numpy(xq).cuda(), sxd, torch.from_numpy(wp).cuda(), wsd,
                                                 td, bpd, bd))
         assert np.array_equal(y6, y4)
