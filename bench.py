@@ -234,7 +234,11 @@ def skinny_sweep(ck, torch, args) -> int:
     reps = max(args.steps // 20, 2)
     warm = max(args.warmup // 10, 1)
     nb = max(args.batches, 1)
+    only_m = {int(v) for v in args.skinny_m.split(",")} if args.skinny_m else None
+    only_nk = {tuple(int(d) for d in v.split("x")) for v in args.skinny_nk.split(",")} if args.skinny_nk else None
     for n, k in workloads.SKINNY_NK:
+        if only_nk is not None and (n, k) not in only_nk:
+            continue
         # what a plain kernel reaches reading the weight's bytes, 32 copies
         wbytes = n * k // 2 + 4 * n
         ceil_us = read_ceiling_us(torch, wbytes, copies, reps, nb)
@@ -252,6 +256,8 @@ def skinny_sweep(ck, torch, args) -> int:
             w8e.append(ck.quantize_weight_convrot_e4m3(w, 128, 128))
             del w
         for m in workloads.SKINNY_M:
+            if only_m is not None and m not in only_m:
+                continue
             x = torch.from_numpy(workloads.make_activations(rng, m, k).view(np.int16)).view(torch.bfloat16).to(dev)
             xq, sx = ck.rotate_quantize_act(x, 128, 4)
             xq8, sx8 = ck.rotate_quantize_act(x, 128, 8)
@@ -523,6 +529,8 @@ def main() -> int:
                     help="run only a plain 512 MiB device-to-device copy (scales the HBM byte counters)")
     ap.add_argument("--skinny", action="store_true",
                     help="run the skinny-M sweep (M in 1, 8, 16, 64; N,K = 12288,3072 and 5120,5120) instead")
+    ap.add_argument("--skinny-m", default="", help="with --skinny: only these M (comma-separated)")
+    ap.add_argument("--skinny-nk", default="", help="with --skinny: only these NxK shapes, e.g. 5120x5120")
     ap.add_argument("--batches", type=int, default=5,
                     help="timed batches per skinny case (min and median are reported)")
     ap.add_argument("--lora", action="store_true",

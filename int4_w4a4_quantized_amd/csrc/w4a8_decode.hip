@@ -20,6 +20,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "ck4_kernels.h"
 #include "fp8_e4m3.h"
@@ -346,6 +347,19 @@ __device__ __forceinline__ void w4a8_tile_step(const uint32_t (&words)[8], const
     }
 }
 
+// f(integral_constant<int, T>) for T = 0 .. sizeof...(T) - 1, unrolled.
+template <typename F, int... T>
+__device__ __forceinline__ void for_each_slot(F &&f, std::integer_sequence<int, T...>) {
+    (f(std::integral_constant<int, T>{}), ...);
+}
+
+// Wait until at most C vector memory operations of this wavefront are outstanding.
+template <int C>
+__device__ __forceinline__ void vm_wait_le() {
+    static_assert(C >= 0 && C <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | 0x0f70);
+}
+
 // Operand layout: a k-step is 256 k. Lane l (row l & 15, part p = l >> 4)
 // owns the 64 contiguous k [256 s + 64 p, 256 s + 64 p + 64) of its weight row
 // and of its activation row; the MFMA of slice h (0..3) takes 16 of them,
@@ -381,16 +395,18 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
     constexpr int XB = AR * 256;                           // activation bytes of a step
     constexpr int SLOT = WB + XB;
     constexpr int W_INS = WB / 1024, X_INS = (XB + 1023) / 1024;
-    // A step issues its INS copies, then its group-scale loads. Memory
-    // operations retire in order, so the copies of a step have landed once at
-    // most `later` x INS operations are outstanding, `later` being the number
-    // of steps issued after it (each issued at least INS operations after
-    // them; counting only the copies stays right however the compiler groups
-    // the scale loads).
+    // A step issues its group-scale loads, then its INS copies. Every
+    // iteration issues exactly one step (past the wavefront's last step, a
+    // copy out of the buffers' range: it moves no data), so when a step is
+    // computed, the NSLOT - 1 steps after it have been issued. Memory
+    // operations retire in order, so its copies have landed once at most
+    // (NSLOT - 1) x INS operations are outstanding (counting only the copies
+    // stays right however the compiler groups the scale loads; the counter
+    // holds 63, and a smaller bound only waits longer).
     constexpr int INS = W_INS + X_INS;
+    constexpr int VM_AHEAD = (NSLOT - 1) * INS < 63 ? (NSLOT - 1) * INS : 63;
     constexpr int RING = KS * NSLOT * SLOT;
     constexpr int RED = (KS - 1) * FNW * FM * 64 * 16;
-    static_assert((NSLOT - 1) * INS <= 63, "vmcnt range");
     static_assert(AR == 4 || AR % 16 == 0, "activation rows");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[RING > RED ? RING : RED];
 
@@ -442,23 +458,15 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
         if constexpr (E4M3) return static_cast<const uint8_t *>(gs)[idx];
         else return static_cast<const uint32_t *>(gs)[idx];
     };
-    // copies of step s (of this wave) into slot `dst`, and its group scales
-    auto issue = [&](int s, uint8_t *__restrict__ dst, uint32_t (&g)[FNW][NS]) __attribute__((always_inline)) {
-        const int k0 = kfirst(s);  // first k of the step's window
-#pragma unroll
-        for (int q = 0; q < W_INS; ++q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)(dst + q * 1024), 16,
-                                                     (uint32_t)(q * 8) * (uint32_t)wrow_bytes + w_off +
-                                                         (uint32_t)(k0 / 2),
-                                                     0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < X_INS; ++q) {
-            const int r = q * 4 + xrow;  // activation row of this lane's chunk
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (__attribute__((address_space(3))) void *)(dst + WB + q * 1024), 16,
-                (uint32_t)r * (uint32_t)K + (uint32_t)(((lane & 15) ^ (r & 7)) * 16) + (uint32_t)k0, 0, 0, 0);
-        }
-        const int kb = k0 + part * 64;  // first k of this lane's span
+    // group scales of step s (of the kernel) and its copies into slot
+    // `dst`; s past this wavefront's last step (`real` false): the scales of
+    // the kernel's last step, and copies past the end of the buffers' range
+    // (the buffer bounds check turns them into no-ops)
+    auto issue = [&](int s, bool real, uint8_t *__restrict__ dst, uint32_t (&g)[FNW][NS])
+                     __attribute__((always_inline)) {
+        const int k0 = kfirst(real ? s : steps - 1);  // first k of the step's window
+        const uint32_t oob = real ? 0u : 0x40000000u;  // > any buffer range here (at most 8 MB)
+        const int kb = k0 + part * 64;                 // first k of this lane's span
 #pragma unroll
         for (int i = 0; i < FNW; ++i) {
             if constexpr (SG != 0) {
@@ -470,6 +478,20 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
 #pragma unroll
                 for (int h = 0; h < 4; ++h) g[i][h] = load_bits(gsr[i] + (kb + 16 * h) / group);
             }
+        }
+#pragma unroll
+        for (int q = 0; q < W_INS; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (__attribute__((address_space(3))) void *)(dst + q * 1024), 16,
+                                                     (uint32_t)(q * 8) * (uint32_t)wrow_bytes + w_off +
+                                                         (uint32_t)(k0 / 2) + oob,
+                                                     0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < X_INS; ++q) {
+            const int r = q * 4 + xrow;  // activation row of this lane's chunk
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (__attribute__((address_space(3))) void *)(dst + WB + q * 1024), 16,
+                (uint32_t)r * (uint32_t)K + (uint32_t)(((lane & 15) ^ (r & 7)) * 16) + (uint32_t)k0 + oob, 0, 0,
+                0);
         }
     };
     auto compute = [&](const uint8_t *__restrict__ cur, const uint32_t (&g)[FNW][NS], bool tail)
@@ -501,56 +523,70 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
             w4a8_tile_step<FM, NGV, SG, CB>(words, gv, srow[i], one_group, xv, acc[i], cb);
         }
     };
-    // wait until the copies of the step `later` steps before the newest issued one have landed
-    auto wait_step = [&](int later) __attribute__((always_inline)) {
-        if (NSLOT > 2 && later >= 2) {
-            constexpr int C = (NSLOT > 2 ? 2 : 0) * INS;
-            __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | 0x0f70);
-        } else if (later >= 1) {
-            constexpr int C = INS;
-            __builtin_amdgcn_s_waitcnt((C & 15) | ((C >> 4) << 14) | 0x0f70);
-        } else {
-            __builtin_amdgcn_s_waitcnt(0x0f70);
-        }
-        asm volatile("" ::: "memory");  // no LDS read moves above the wait
-    };
-    // step idx (0-based in this wave) computes from slot T; first the copy of
-    // step idx + NSLOT - 1 goes into the slot step idx - 1 was read from
-    // (those reads have completed: their results were used)
+    // step idx (0-based in this wave) computes from slot T; first step
+    // idx + NSLOT - 1 goes into the slot step idx - 1 was read from (those
+    // reads have completed: their results were used)
     auto body = [&](int idx, auto t_c) __attribute__((always_inline)) {
         constexpr int T = decltype(t_c)::value;
         constexpr int TN = (T + NSLOT - 1) % NSLOT;
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-        const bool ahead = idx + NSLOT - 1 < nsteps;
-        if (ahead) issue(s_begin + idx + NSLOT - 1, ring + TN * SLOT, gb[TN]);
-        wait_step(min(NSLOT - 1, nsteps - 1 - idx));
+        issue(s_begin + idx + NSLOT - 1, idx + NSLOT - 1 < nsteps, ring + TN * SLOT, gb[TN]);
+        vm_wait_le<VM_AHEAD>();
+        asm volatile("" ::: "memory");  // no LDS read moves above the wait
         compute(ring + T * SLOT, gb[T], half_tail && s_begin + idx == steps - 1);
     };
-    if (nsteps > 0) issue(s_begin, ring, gb[0]);
-    if constexpr (NSLOT > 2) {
-        if (nsteps > 1) issue(s_begin + 1, ring + SLOT, gb[NSLOT > 2 ? 1 : 0]);
-    }
-    // Row scale of this lane's weight rows, (max group scale * cmax) / 127,
-    // taken after the first copies are on their way, so that its scattered
-    // loads overlap them instead of delaying the weight stream.
+    // Row scale of this lane's weight rows, (max group scale * cmax) / 127.
+    // The first RB loads per row are issued before the first copies, and all
+    // of them before any is used, so that they cost one memory latency that
+    // overlaps the copies'.
+    constexpr int RB = 16;
+    float rs[FNW][RB];
 #pragma unroll
-    for (int i = 0; i < FNW; ++i) {
-        float smax = 0.0f;
-        for (int g = part; g < ng; g += 4) smax = fmaxf(smax, load_scale<E4M3>(gs, gsr[i] + g));
-        smax = fmaxf(smax, __shfl_xor(smax, 16, 64));
-        smax = fmaxf(smax, __shfl_xor(smax, 32, 64));
-        srow[i] = (smax * (CB ? cb.cmax : 7.0f)) / 127.0f;
-    }
-    for (int idx = 0; idx < nsteps; idx += NSLOT) {
-        body(idx, std::integral_constant<int, 0>{});
-        if (idx + 1 >= nsteps) break;
-        body(idx + 1, std::integral_constant<int, 1>{});
-        if constexpr (NSLOT > 2) {
-            if (idx + 2 >= nsteps) break;
-            body(idx + 2, std::integral_constant<int, (NSLOT > 2 ? 2 : 0)>{});
+    for (int i = 0; i < FNW; ++i)
+#pragma unroll
+        for (int u = 0; u < RB; ++u) rs[i][u] = part + 4 * u < ng ? load_scale<E4M3>(gs, gsr[i] + part + 4 * u) : 0.0f;
+    // steps 0 .. NSLOT - 2 of this wave into slots 0 .. NSLOT - 2
+    for_each_slot(
+        [&](auto t_c) __attribute__((always_inline)) {
+            constexpr int T = decltype(t_c)::value;
+            if constexpr (T < NSLOT - 1) issue(s_begin + T, T < nsteps, ring + T * SLOT, gb[T]);
+        },
+        std::make_integer_sequence<int, NSLOT>{});
+    {
+        float smax[FNW];
+#pragma unroll
+        for (int i = 0; i < FNW; ++i) {
+            smax[i] = 0.0f;
+#pragma unroll
+            for (int u = 0; u < RB; ++u) smax[i] = fmaxf(smax[i], rs[i][u]);
+        }
+        for (int g0 = part + 4 * RB; g0 < ng; g0 += 32) {
+            float v[FNW][8];
+#pragma unroll
+            for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    v[i][u] = g0 + 4 * u < ng ? load_scale<E4M3>(gs, gsr[i] + g0 + 4 * u) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < FNW; ++i)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) smax[i] = fmaxf(smax[i], v[i][u]);
+        }
+#pragma unroll
+        for (int i = 0; i < FNW; ++i) {
+            float m = fmaxf(smax[i], __shfl_xor(smax[i], 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            srow[i] = (m * (CB ? cb.cmax : 7.0f)) / 127.0f;
         }
     }
+    for (int idx = 0; idx < nsteps; idx += NSLOT)
+        for_each_slot(
+            [&](auto t_c) __attribute__((always_inline)) {
+                if (idx + decltype(t_c)::value < nsteps) body(idx + decltype(t_c)::value, t_c);
+            },
+            std::make_integer_sequence<int, NSLOT>{});
 
+    vm_wait_le<0>();  // the copies issued past the last step have retired, too
     v4i_t *red = reinterpret_cast<v4i_t *>(lds);  // [KS - 1][FNW][FM][64], over the copy slots
     if (KS > 1) {
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -618,13 +654,14 @@ template <bool E4M3, int SG, bool CB>
 hipError_t launch_staged(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
                          int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
     // With 512 or more weight tiles of 16 rows the workgroups are numerous
-    // enough to fill the CUs with two K splits each; with fewer, four (N =
-    // 12288 / 5120 at K = 3072 / 5120, 32 weight copies: the measured best of
-    // the staged configurations at every m).
+    // enough to fill the CUs with two K splits each; with fewer, four, or two
+    // with a deeper ring at m <= 32 (N = 12288 / 5120 at K = 3072 / 5120, 32
+    // weight copies: the measured best of the staged configurations at every
+    // m; deeper rings than these lost, as did more K splits).
     const bool many = (n + 15) / 16 >= 512;
     if (m <= 4) return CK4_STAGED(4, 1, 4, 3);
     if (m <= 16) return many ? CK4_STAGED(16, 1, 2, 3) : CK4_STAGED(16, 1, 4, 3);
-    if (m <= 32) return many ? CK4_STAGED(32, 2, 2, 3) : CK4_STAGED(32, 1, 4, 2);
+    if (m <= 32) return many ? CK4_STAGED(32, 2, 2, 3) : CK4_STAGED(32, 1, 2, 4);
     return many ? CK4_STAGED(64, 2, 2, 2) : CK4_STAGED(64, 2, 4, 2);
 }
 #undef CK4_STAGED
