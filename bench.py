@@ -270,16 +270,24 @@ def skinny_sweep(ck, torch, args) -> int:
             byts = n * k // 2 + 4 * n + m * k // 2 + 4 * m + 2 * m * n
             print(_skinny_line(f"w4a4 skinny m={m} n={n} k={k}", _graph_time_us(torch, cold, reps, warm, nb),
                                _graph_time_us(torch, hot, reps, warm, nb), byts, ceil_gbps), flush=True)
-            # the whole layer: activation rotate + quantise, then the GEMM
+            # the whole layer: activation rotate + quantise, then the GEMM, as
+            # one library call (one kernel for m <= 4) and as two
             def w4a4_layer(c):
+                return lambda: ck.linear_w4a4_bf16(x, w4[c][0], w4[c][1], None, x_q=xq, x_scales=sx, out=y)
+
+            def w4a4_layer2(c):
                 def f():
                     ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
                     ck.linear_w4a4(xq, sx, w4[c][0], w4[c][1], None, out=y)
                 return f
             lbytes = 2 * m * k + n * k // 2 + 4 * n + 2 * m * n
-            print(_skinny_line(f"w4a4 skinny layer (quantise + GEMM) m={m} n={n} k={k}",
+            print(_skinny_line(f"w4a4 skinny layer (quantise + GEMM, one call) m={m} n={n} k={k}",
                                _graph_time_us(torch, [w4a4_layer(c) for c in range(copies)], reps, warm, nb),
                                _graph_time_us(torch, [w4a4_layer(0) for _ in range(copies)], reps, warm, nb),
+                               lbytes, ceil_gbps), flush=True)
+            print(_skinny_line(f"w4a4 skinny layer (quantise + GEMM, two calls) m={m} n={n} k={k}",
+                               _graph_time_us(torch, [w4a4_layer2(c) for c in range(copies)], reps, warm, nb),
+                               _graph_time_us(torch, [w4a4_layer2(0) for _ in range(copies)], reps, warm, nb),
                                lbytes, ceil_gbps), flush=True)
             ws_bytes = ck.w4a8_workspace_bytes(m, n, k, 0)
             ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)

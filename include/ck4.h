@@ -172,6 +172,33 @@ ck4_status ck4_linear_w4a4(const int8_t *x_q, const float *x_scales, const int8_
                            uint16_t *y, int64_t ldy, void *stream);
 
 /*
+ * The whole W4A4 layer from bf16 activations in one call: x rotated with
+ * 128-element Hadamard blocks, quantised to packed int4 with one scale per
+ * row, multiplied by the packed weight, epilogue as ck4_linear_w4a4
+ * ([PR #63] Description: the activation kernel rotates, takes the row
+ * scale, quantises and packs in one pass; the GEMM then applies the row and
+ * column scales once). The same arguments as ck4_rotate_quantize_act(bits =
+ * 4) followed by ck4_linear_w4a4, and the same results bit for bit: x_q
+ * [m, k/2] and x_scales [m] are written too (the caller's buffers; reuse
+ * them for other projections of the same activation), and y.
+ *
+ * For m <= 4 with rot_block 128 (and m * k / 2 <= 32 KB) one kernel does it
+ * all: each workgroup rotates and quantises the m rows into its own LDS
+ * while its first weight loads are in flight, which saves the quantiser's
+ * launch at decode sizes. Other shapes run the quantiser, then the GEMM, on
+ * `stream`.
+ *   x        bf16 [m, ldx], ldx a multiple of 8, 16-byte aligned.
+ *   w_packed, w_scales, bias, y, ldy  as ck4_linear_w4a4.
+ *   x_q      int8 [m, k/2], row stride k/2, 16-byte aligned (output).
+ *   x_scales fp32 [m] (output).
+ * Unsupported: k % 128 != 0, k < 256, k > 16384, rot_block not a power of
+ * two in [16, 1024] or not dividing k.
+ */
+ck4_status ck4_linear_w4a4_bf16(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                const int8_t *w_packed, const float *w_scales, const float *bias, int64_t n,
+                                int8_t *x_q, float *x_scales, uint16_t *y, int64_t ldy, void *stream);
+
+/*
  * The integer part of ck4_linear_w4a4 alone: acc[m, n] (int32, row stride
  * ldacc) = sum_k qx[m,k] qw[n,k], exact. Same kernel as ck4_linear_w4a4 with
  * an int32 store in place of the epilogue. Same alignment and shape rules;

@@ -48,6 +48,7 @@ SIGNATURES = {
     "ck4_rotate_quantize_act": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "ck4_rotate_act_f32": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_linear_w4a4": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_linear_w4a4_bf16": ([_P, _I64, _I64, _I64, _I, _P, _P, _P, _I64, _P, _P, _P, _I64, _P], _I),
     "ck4_gemm_w4a4_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_dequant_w4a8_grouped": ([_P, _P, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
     "ck4_linear_w8a8": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
@@ -334,10 +335,46 @@ def gemm_w4a4_acc_i32(x_q: torch.Tensor, w_packed: torch.Tensor):
     return acc[:, :n]
 
 
+def linear_w4a4_bf16(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, bias=None,
+                     rot_block: int = 128, x_q=None, x_scales=None, out=None):
+    """The whole layer in one library call: bf16 x [m, k] -> (y bf16 [m, n], x_q int8 [m, k/2], x_scales fp32 [m]).
+
+    Bitwise rotate_quantize_act(x, rot_block, 4) followed by linear_w4a4; for
+    m <= 4 (rot_block 128) one kernel does both."""
+    _typed(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    _dense(w_packed, torch.int8, "w_packed", 2)
+    if w_packed.shape[1] * 2 != k:
+        raise ValueError(f"the weight rows hold {w_packed.shape[1]} bytes, not k/2 = {k // 2}")
+    n = w_packed.shape[0]
+    _vec(w_scales, torch.float32, "w_scales", n)
+    if bias is not None:
+        _vec(bias, torch.float32, "bias", n)
+    if x_q is not None:
+        _dense(x_q, torch.int8, "x_q", 2)
+        if tuple(x_q.shape) != (m, k // 2):
+            raise ValueError(f"x_q must have shape {(m, k // 2)}, got {tuple(x_q.shape)}")
+    if x_scales is not None:
+        _vec(x_scales, torch.float32, "x_scales", m)
+    if out is not None:
+        _out_checked(out, m, n)
+    _on_gpu(x=x, w_packed=w_packed, w_scales=w_scales, bias=bias, x_q=x_q, x_scales=x_scales, out=out)
+    if x_q is None:
+        x_q = torch.empty((m, k // 2), dtype=torch.int8, device=x.device)
+    if x_scales is None:
+        x_scales = torch.empty((m,), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = _out_bf16(m, n, x.device)
+    _check("ck4_linear_w4a4_bf16",
+           lib().ck4_linear_w4a4_bf16(_ptr(x), m, k, x.stride(0), rot_block, _ptr(w_packed), _ptr(w_scales),
+                                      _ptr(bias), n, _ptr(x_q), _ptr(x_scales), _ptr(out), out.stride(0),
+                                      _stream(x.device)))
+    return out, x_q, x_scales
+
+
 def w4a4_linear(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor, bias=None, rot_block: int = 128):
-    """The whole layer: rotate + quantise x, then the W4A4 GEMM + epilogue."""
-    x_q, sx = rotate_quantize_act(x, rot_block, 4)
-    return linear_w4a4(x_q, sx, w_packed, w_scales, bias)
+    """The whole layer: rotate + quantise x, then the W4A4 GEMM + epilogue (one library call)."""
+    return linear_w4a4_bf16(x, w_packed, w_scales, bias, rot_block)[0]
 
 
 def dequant_w4a8_grouped(w_packed: torch.Tensor, group_scales: torch.Tensor, group: int = 128, n0: int = 0,

@@ -286,6 +286,30 @@ ck4_status ck4_linear_w4a4(const int8_t *x_q, const float *x_scales, const int8_
                       stream);
 }
 
+ck4_status ck4_linear_w4a4_bf16(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                const int8_t *w_packed, const float *w_scales, const float *bias, int64_t n,
+                                int8_t *x_q, float *x_scales, uint16_t *y, int64_t ldy, void *stream) {
+    const char *fn = "ck4_linear_w4a4_bf16";
+    if (!x || !w_packed || !w_scales || !x_q || !x_scales || !y) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, 8)) return s;
+    if (ck4_status s = check_stride(fn, "ldx", ldx, k, 8)) return s;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(x_q, 16) || !aligned(x_scales, 4))
+        return fail(CK4_ERR_INVALID, "%s: x, w_packed or x_q not 16-byte aligned, or x_scales misaligned", fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (k % 128 != 0 || k < 256)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld (need a multiple of 128, at least 256)", fn, (long long)k);
+    if (ck4_status s = check_device(fn)) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ck4::skinny_layer_fits(m, n, k, rot_block))
+        return launched(fn, ck4::launch_skinny_layer(x, ldx, w_packed, w_scales, bias, m, n, k, x_q, x_scales, y, ldy,
+                                                     st));
+    if (ck4_status s = launched(fn, ck4::launch_rotate_quant(x, 0, m, k, ldx, rot_block, 0, 0, x_q, k / 2, x_scales,
+                                                             st)))
+        return s;
+    return launched(fn, ck4::launch_gemm(true, x_q, w_packed, x_scales, w_scales, bias, m, n, k, false, y, ldy, st,
+                                         ck4::LoraUp{}));
+}
+
 ck4_status ck4_gemm_w4a4_acc_i32(const int8_t *x_q, const int8_t *w_packed, int64_t m, int64_t n, int64_t k,
                                  int32_t *acc, int64_t ldacc, void *stream) {
     return gemm_entry("ck4_gemm_w4a4_acc_i32", true, x_q, nullptr, w_packed, nullptr, nullptr, m, n, k, true, acc,

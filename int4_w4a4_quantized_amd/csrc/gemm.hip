@@ -39,40 +39,18 @@
 #include <stdint.h>
 
 #include "ck4_kernels.h"
+#include "int4_widen.h"
 #include "lora_up.h"
 #include "tile_map.h"
 
 namespace ck4 {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kRowBytes = 128;          // bytes of each row per K step
 
-__device__ __forceinline__ v4i as_v4i(uint4 u) {
-    v4i r;
-    r.x = (int)u.x;
-    r.y = (int)u.y;
-    r.z = (int)u.z;
-    r.w = (int)u.w;
-    return r;
-}
-
-__device__ __forceinline__ v4i widen_hi(uint4 p) {
-    return as_v4i(make_uint4(p.x & 0xF0F0F0F0u, p.y & 0xF0F0F0F0u, p.z & 0xF0F0F0F0u, p.w & 0xF0F0F0F0u));
-}
-
-__device__ __forceinline__ v4i widen_lo(uint4 p) {
-    return as_v4i(make_uint4((p.x << 4) & 0xF0F0F0F0u, (p.y << 4) & 0xF0F0F0F0u, (p.z << 4) & 0xF0F0F0F0u,
-                             (p.w << 4) & 0xF0F0F0F0u));
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    __bf16 h = (__bf16)f;
-    return __builtin_bit_cast(uint16_t, h);
-}
 
 template <bool S4, int BM, int BN, int WGM, int WGN, int WPE, bool OUT_I32, bool LORA>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),

@@ -59,6 +59,14 @@ hipError_t launch_w4a8_fused(const int8_t *, const float *, const int8_t *, cons
                              int64_t, int, uint16_t *, int64_t, hipStream_t, const Codebook &) {
     return ++g_launches, hipSuccess;
 }
+// the fused decode-time layer's shape rule, reduced to what these calls need:
+// m <= 4 with 128-blocks takes the one-launch kernel, anything else the
+// quantiser followed by the GEMM (two launches)
+bool skinny_layer_fits(int64_t m, int64_t, int64_t, int rot_block) { return m <= 4 && rot_block == 128; }
+hipError_t launch_skinny_layer(const uint16_t *, int64_t, const int8_t *, const float *, const float *, int64_t,
+                               int64_t, int64_t, int8_t *, float *, uint16_t *, int64_t, hipStream_t) {
+    return ++g_launches, hipSuccess;
+}
 alignas(256) static unsigned char g_fake_scratch[256];
 hipError_t noalloc_scratch(int, void **ptr) {
     *ptr = g_fake_scratch;
@@ -190,6 +198,26 @@ int main(int argc, char **argv) {
     VALID(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 384, U16, 8, nullptr), 1);
     REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 262144, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, BIG, 8, 256, U16, 8, nullptr));
+
+    // the whole layer from bf16: one launch for m <= 4 (128-blocks), else two
+    VALID(ck4_linear_w4a4_bf16(U16, 1, 3072, 3072, 128, I8, F, F, 12288, I8, F, U16, 12288, nullptr), 1);
+    VALID(ck4_linear_w4a4_bf16(U16, 4, 384, 392, 128, I8, F, nullptr, 5, I8, F, U16, 8, nullptr), 1);
+    VALID(ck4_linear_w4a4_bf16(U16, 64, 3072, 3072, 128, I8, F, nullptr, 300, I8, F, U16, 300, nullptr), 2);
+    VALID(ck4_linear_w4a4_bf16(U16, 2, 1024, 1024, 64, I8, F, nullptr, 300, I8, F, U16, 300, nullptr), 2);
+    REFUSED(ck4_linear_w4a4_bf16(nullptr, 1, 256, 256, 128, I8, F, F, 8, I8, F, U16, 8, nullptr), CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 256, 256, 128, I8, F, F, 8, nullptr, F, U16, 8, nullptr), CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 256, 256, 128, I8, F, F, 8, (int8_t *)ODD, F, U16, 8, nullptr),
+            CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 256, 200, 128, I8, F, F, 8, I8, F, U16, 8, nullptr), CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 256, 260, 128, I8, F, F, 8, I8, F, U16, 8, nullptr), CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 128, 128, 128, I8, F, F, 8, I8, F, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 320, 320, 64, I8, F, F, 8, I8, F, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 256, 256, 100, I8, F, F, 8, I8, F, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
+    REFUSED(ck4_linear_w4a4_bf16(U16, 1, 32768, 32768, 128, I8, F, F, 8, I8, F, U16, 8, nullptr),
+            CK4_ERR_UNSUPPORTED);
+    REJECTED(ck4_linear_w4a4_bf16(U16, BIG, 256, 256, 128, I8, F, F, 8, I8, F, U16, 8, nullptr));
+    REJECTED(ck4_linear_w4a4_bf16(U16, 1, 256, BIG, 128, I8, F, F, 8, I8, F, U16, 8, nullptr));
+    REJECTED(ck4_linear_w4a4_bf16(U16, 1, 256, 256, 128, I8, F, F, NEG, I8, F, U16, 8, nullptr));
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, BIG, 256, U16, BIG, nullptr));
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, BIG, U16, 8, nullptr));
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, NEG, NEG, NEG, U16, NEG, nullptr));

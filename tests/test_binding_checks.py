@@ -61,6 +61,18 @@ def test_linear_w4a4_checks():
     refused("CUDA", ck.gemm_w4a4_acc_i32, i8(M, K // 2), i8(N, K // 2))
 
 
+def test_linear_w4a4_bf16_checks():
+    ok = dict(x=bf16(M, K), w_packed=i8(N, K // 2), w_scales=f32(N))
+    refused("not k/2", ck.linear_w4a4_bf16, **{**ok, "w_packed": i8(N, K)})
+    refused("x must be torch.bfloat16", ck.linear_w4a4_bf16, **{**ok, "x": f32(M, K)})
+    refused("w_scales holds", ck.linear_w4a4_bf16, **{**ok, "w_scales": f32(N - 1)})
+    refused("bias holds", ck.linear_w4a4_bf16, **ok, bias=f32(N - 1))
+    refused("x_q must have shape", ck.linear_w4a4_bf16, **ok, x_q=i8(M, K))
+    refused("x_scales holds", ck.linear_w4a4_bf16, **ok, x_scales=f32(M - 1))
+    refused("out must have shape", ck.linear_w4a4_bf16, **ok, out=bf16(M + 1, N))
+    refused("CUDA", ck.linear_w4a4_bf16, **ok)
+
+
 def test_linear_w8a8_checks():
     refused("k differs", ck.linear_w8a8, i8(M, K), f32(M), i8(N, K // 2), f32(N))
     refused("w_scales holds", ck.linear_w8a8, i8(M, K), f32(M), i8(N, K), f32(3))

@@ -674,6 +674,84 @@ def test_full_size_layer(ck, name):
         assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], ws_ref))
 
 
+# --------------------------------------------------------------------------
+# The whole layer from bf16 in one call (one kernel for m <= 4)
+
+
+LAYER_CASES = [
+    # one kernel: m <= 4, every K-split width (N = 77 -> 8 waves, 8200 -> 4, 16400 -> 2), chunks per
+    # thread 1, 2 and 4, a half last step (k = 128 mod 256), ragged N
+    (1, 12288, 3072), (4, 12288, 3072), (1, 5120, 5120), (3, 5120, 5120), (2, 77, 256), (4, 17, 384),
+    (1, 8200, 16384), (2, 8200, 8192), (1, 16400, 1152), (4, 1000, 4096), (2, 999, 640),
+    # quantiser + GEMM: m > 4, or more rows than the fused kernel's registers hold at this K
+    (5, 300, 768), (17, 1000, 1024), (3, 8200, 8192), (2, 8200, 16384),
+]
+
+
+@pytest.mark.parametrize("m,n,k", LAYER_CASES)
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_linear_w4a4_bf16_equals_two_calls_and_oracle(ck, m, n, k, with_bias):
+    """The one-call layer gives the bits of rotate_quantize_act + linear_w4a4 (y, and the x_q and
+    x_scales it returns), including an all-zero row and rows whose scale leaves [2^-120, 2^120]
+    (the exact-divide path: a tiny row, and a row of one constant 128-block of 1e36: s = 1.6e36, and
+    |acc| <= 49 keeps the fp32 epilogue finite),
+    and y stays within the oracle's bf16 bound (not checked on the tiny row, whose outputs fall
+    among fp32 subnormals, where the epilogue's two roundings are not within 1e-2)."""
+    rng = np.random.default_rng(5100 + m + n + k)
+    xb = workloads.make_activations(rng, m, k)
+    if m >= 2:
+        xb[1] = 0
+    if m >= 3:
+        xb[2] = workloads.f32_to_bf16_bits(rng.standard_normal(k).astype(np.float32) * np.float32(1e-37))
+    if m >= 4:
+        xb[3] = 0
+        xb[3, :128] = workloads.f32_to_bf16_bits(np.full(128, 1e36, dtype=np.float32))
+    w = workloads.make_weight(rng, n, k)
+    wp, ws = oracle.quantize_weight_convrot(w)
+    bias = rng.standard_normal(n).astype(np.float32) if with_bias else None
+    xd = dev_bf16(xb)
+    wpd, wsd = torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda()
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    y, xq, sx = ck.linear_w4a4_bf16(xd, wpd, wsd, bd)
+    xq2, sx2 = ck.rotate_quantize_act(xd, 128, 4)
+    y2 = ck.linear_w4a4(xq2, sx2, wpd, wsd, bd)
+    assert np.array_equal(host(xq), host(xq2))
+    assert np.array_equal(host(sx).view(np.uint32), host(sx2).view(np.uint32))
+    assert np.array_equal(bf16_host_bits(y), bf16_host_bits(y2))
+    q_ref, s_ref = oracle.rotate_quantize_act(xb)
+    assert np.array_equal(host(xq), q_ref)
+    assert np.array_equal(host(sx).view(np.uint32), s_ref.view(np.uint32))
+    if m * n * k <= 4 * 8200 * 4096:
+        acc = oracle.gemm_acc(q_ref, wp, k)
+        ref = oracle.epilogue_bf16(acc, s_ref, ws, bias)
+        atol = None
+        if bias is not None:
+            terms = np.abs(acc * s_ref.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]) + np.abs(bias)
+            atol = 2.0 ** -21 * terms
+        rows = [i for i in range(m) if i != 2]
+        assert_bf16_close(bf16_host_bits(y)[rows], ref[rows], atol=None if atol is None else atol[rows])
+
+
+def test_linear_w4a4_bf16_reused_buffers(ck):
+    """Caller buffers are used and overwritten: two calls in a row into the same x_q, x_scales and y, the
+    second with fewer rows of a different activation, each equal to the two-call path."""
+    rng = np.random.default_rng(5200)
+    n, k = 3000, 1024
+    wp, ws = oracle.quantize_weight_convrot(workloads.make_weight(rng, n, k))
+    wpd, wsd = torch.from_numpy(wp).cuda(), torch.from_numpy(ws).cuda()
+    xq = torch.full((4, k // 2), 0x5A, dtype=torch.int8, device="cuda")
+    sx = torch.full((4,), 7.0, dtype=torch.float32, device="cuda")
+    y = torch.full((4, n), 1.0, dtype=torch.bfloat16, device="cuda")
+    for m in (4, 2):
+        xd = dev_bf16(workloads.make_activations(rng, m, k))
+        ck.linear_w4a4_bf16(xd, wpd, wsd, None, x_q=xq[:m], x_scales=sx[:m], out=y[:m])
+        xq2, sx2 = ck.rotate_quantize_act(xd, 128, 4)
+        y2 = ck.linear_w4a4(xq2, sx2, wpd, wsd)
+        assert np.array_equal(host(xq[:m]), host(xq2))
+        assert np.array_equal(host(sx[:m]).view(np.uint32), host(sx2).view(np.uint32))
+        assert np.array_equal(bf16_host_bits(y[:m]), bf16_host_bits(y2))
+
+
 @pytest.mark.parametrize("m,n,k", [(17, 12288, 640), (40, 8200, 384), (64, 8200, 1152), (8, 12288, 1152),
                                    (17, 12288, 3072), (32, 12288, 3072), (33, 8200, 768), (48, 8200, 1280),
                                    (64, 16384, 512), (40, 12288, 256), (24, 8200, 2304), (5, 12288, 3072),
@@ -1022,6 +1100,10 @@ def test_graph_replays_match_eager(ck):
     wsk, wssk = ck.quantize_weight_convrot(
         torch.from_numpy(workloads.make_weight(np.random.default_rng(972), ns, k)).cuda(), 128, 0)
     ysk = torch.empty((ms, ns), dtype=torch.bfloat16, device="cuda")
+    # the one-call layer's fused kernel (m <= 4)
+    xq1 = torch.empty((3, k // 2), dtype=torch.int8, device="cuda")
+    sx1 = torch.empty((3,), dtype=torch.float32, device="cuda")
+    y1 = torch.empty((3, n), dtype=torch.bfloat16, device="cuda")
 
     def step():
         ck.rotate_quantize_act(xd, 128, 4, out=xq, scales=sx)
@@ -1035,8 +1117,9 @@ def test_graph_replays_match_eager(ck):
         ck.linear_w4a4_fp6(xq6, sx6, wq6, ws6, None, out=y6)
         ck.linear_w4a4_fp6_lora(xq6, sx6, wq6, ws6, t, b_pack, None, out=y6l)
         ck.linear_w4a4(xq[:ms], sx[:ms], wsk, wssk, None, out=ysk)
+        ck.linear_w4a4_bf16(xd[:3], wp, ws, None, x_q=xq1, x_scales=sx1, out=y1)
 
-    outs = (xq, sx, t, y, yl, y8, y8c, xq6, sx6, y6, y6l, ysk)
+    outs = (xq, sx, t, y, yl, y8, y8c, xq6, sx6, y6, y6l, ysk, xq1, sx1, y1)
     step()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
