@@ -347,6 +347,9 @@ __device__ __forceinline__ void w4a8_tile_step(const uint32_t (&words)[8], const
     }
 }
 
+// The dynamic LDS of w4a8_staged_kernel (its group-scale table).
+extern __shared__ uint32_t w4a8_stab[];
+
 // f(integral_constant<int, T>) for T = 0 .. sizeof...(T) - 1, unrolled.
 template <typename F, int... T>
 __device__ __forceinline__ void for_each_slot(F &&f, std::integer_sequence<int, T...>) {
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
                                                             const int8_t *__restrict__ W,
                                                             const void *__restrict__ gs, int M, int N, int K,
                                                             int group, uint16_t *__restrict__ Y, int64_t ldy,
-                                                            Codebook cb) {
+                                                            Codebook cb, int tab) {
     constexpr int FM = (AR + 15) / 16;
     constexpr int NGV = SG == 0 ? 4 : 64 / SG;             // scales a tile step needs per lane
     constexpr int NS = SG != 0 ? NGV : (G64 ? 1 : 4);      // scale loads per tile and step
@@ -409,6 +412,9 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
     constexpr int RED = (KS - 1) * FNW * FM * 64 * 16;
     static_assert(AR == 4 || AR % 16 == 0, "activation rows");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[RING > RED ? RING : RED];
+    // tab != 0: w4a8_stab holds the raw group-scale bits of the workgroup's
+    // 16 FNW rows, [row][ng], then the per-wavefront row maxima, [KS][16 FNW]
+    uint32_t *const stab = w4a8_stab;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -467,16 +473,18 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
         const int k0 = kfirst(real ? s : steps - 1);  // first k of the step's window
         const uint32_t oob = real ? 0u : 0x40000000u;  // > any buffer range here (at most 8 MB)
         const int kb = k0 + part * 64;                 // first k of this lane's span
+        if (!tab) {
 #pragma unroll
-        for (int i = 0; i < FNW; ++i) {
-            if constexpr (SG != 0) {
+            for (int i = 0; i < FNW; ++i) {
+                if constexpr (SG != 0) {
 #pragma unroll
-                for (int c = 0; c < NS; ++c) g[i][c] = load_bits(gsr[i] + kb / SG + c);
-            } else if constexpr (G64) {
-                g[i][0] = load_bits(gsr[i] + kb / group);
-            } else {
+                    for (int c = 0; c < NS; ++c) g[i][c] = load_bits(gsr[i] + kb / SG + c);
+                } else if constexpr (G64) {
+                    g[i][0] = load_bits(gsr[i] + kb / group);
+                } else {
 #pragma unroll
-                for (int h = 0; h < 4; ++h) g[i][h] = load_bits(gsr[i] + (kb + 16 * h) / group);
+                    for (int h = 0; h < 4; ++h) g[i][h] = load_bits(gsr[i] + (kb + 16 * h) / group);
+                }
             }
         }
 #pragma unroll
@@ -533,18 +541,40 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
         issue(s_begin + idx + NSLOT - 1, idx + NSLOT - 1 < nsteps, ring + TN * SLOT, gb[TN]);
         vm_wait_le<VM_AHEAD>();
         asm volatile("" ::: "memory");  // no LDS read moves above the wait
+        if (tab) {
+            // this step's group scales from the table, at the indices issue() loads them from
+            const int kb = kfirst(s_begin + idx) + part * 64;
+#pragma unroll
+            for (int i = 0; i < FNW; ++i) {
+                const int trow = (i * 16 + frow) * ng;
+#pragma unroll
+                for (int c = 0; c < NS; ++c) {
+                    const int gi = SG != 0 ? kb / SG + c : G64 ? kb / group : (kb + 16 * c) / group;
+                    gb[T][i][c] = w4a8_stab[trow + gi];
+                }
+            }
+        }
         compute(ring + T * SLOT, gb[T], half_tail && s_begin + idx == steps - 1);
     };
     // Row scale of this lane's weight rows, (max group scale * cmax) / 127.
-    // The first RB loads per row are issued before the first copies, and all
-    // of them before any is used, so that they cost one memory latency that
-    // overlaps the copies'.
+    // The first loads per row are issued before the first copies, and all of
+    // them before any is used, so that they cost one memory latency that
+    // overlaps the copies'. Table mode: the wavefronts split the groups (wave
+    // w, part p: groups 4 w + p + 4 KS u), keep their raw bits in the table
+    // for the steps, and meet in one barrier for the row maxima. Otherwise
+    // each wavefront loads all of its rows' groups (part p: groups p + 4 u)
+    // and the steps load their scales again.
     constexpr int RB = 16;
-    float rs[FNW][RB];
+    const int g_first = tab ? wave * 4 + part : part;
+    const int g_step = tab ? 4 * KS : 4;
+    uint32_t rs[FNW][RB];
 #pragma unroll
     for (int i = 0; i < FNW; ++i)
 #pragma unroll
-        for (int u = 0; u < RB; ++u) rs[i][u] = part + 4 * u < ng ? load_scale<E4M3>(gs, gsr[i] + part + 4 * u) : 0.0f;
+        for (int u = 0; u < RB; ++u) {
+            const int g = g_first + g_step * u;
+            rs[i][u] = g < ng ? load_bits(gsr[i] + g) : 0u;
+        }
     // steps 0 .. NSLOT - 2 of this wave into slots 0 .. NSLOT - 2
     for_each_slot(
         [&](auto t_c) __attribute__((always_inline)) {
@@ -552,13 +582,57 @@ __global__ __launch_bounds__(64 * KS) void w4a8_staged_kernel(const int8_t *__re
             if constexpr (T < NSLOT - 1) issue(s_begin + T, T < nsteps, ring + T * SLOT, gb[T]);
         },
         std::make_integer_sequence<int, NSLOT>{});
-    {
+    auto scale_of = [](uint32_t bits) __attribute__((always_inline)) -> float {
+        if constexpr (E4M3) return e4m3_decode(bits);
+        else return __uint_as_float(bits);
+    };
+    if (tab) {
+        float smax[FNW];
+#pragma unroll
+        for (int i = 0; i < FNW; ++i) {
+            smax[i] = 0.0f;
+            const int trow = (i * 16 + frow) * ng;
+#pragma unroll
+            for (int u = 0; u < RB; ++u) {
+                const int g = g_first + g_step * u;
+                if (g < ng) {
+                    stab[trow + g] = rs[i][u];
+                    smax[i] = fmaxf(smax[i], scale_of(rs[i][u]));
+                }
+            }
+            for (int g = g_first + g_step * RB; g < ng; g += g_step) {
+                const uint32_t b = load_bits(gsr[i] + g);
+                stab[trow + g] = b;
+                smax[i] = fmaxf(smax[i], scale_of(b));
+            }
+        }
+        const int rmax = 16 * FNW * ng;  // [KS][16 FNW] row maxima after the table (fp32 bits)
+#pragma unroll
+        for (int i = 0; i < FNW; ++i) {
+            float m = fmaxf(smax[i], __shfl_xor(smax[i], 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (part == 0) stab[rmax + wave * 16 * FNW + i * 16 + frow] = __float_as_uint(m);
+        }
+        __syncthreads();  // the table and every wavefront's maxima are in LDS
+#pragma unroll
+        for (int i = 0; i < FNW; ++i) {
+            float m = __uint_as_float(stab[rmax + i * 16 + frow]);
+#pragma unroll
+            for (int w = 1; w < KS; ++w) m = fmaxf(m, __uint_as_float(stab[rmax + w * 16 * FNW + i * 16 + frow]));
+            srow[i] = (m * (CB ? cb.cmax : 7.0f)) / 127.0f;
+        }
+    } else {
+        float rsf[FNW][RB];
+#pragma unroll
+        for (int i = 0; i < FNW; ++i)
+#pragma unroll
+            for (int u = 0; u < RB; ++u) rsf[i][u] = scale_of(rs[i][u]);
         float smax[FNW];
 #pragma unroll
         for (int i = 0; i < FNW; ++i) {
             smax[i] = 0.0f;
 #pragma unroll
-            for (int u = 0; u < RB; ++u) smax[i] = fmaxf(smax[i], rs[i][u]);
+            for (int u = 0; u < RB; ++u) smax[i] = fmaxf(smax[i], rsf[i][u]);
         }
         for (int g0 = part + 4 * RB; g0 < ng; g0 += 32) {
             float v[FNW][8];
@@ -638,12 +712,23 @@ template <int AR, int FNW, int KS, int NSLOT, bool E4M3, int SG, bool CB>
 hipError_t launch_staged_cfg(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
                              int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
     const dim3 grid((unsigned)((n + 16 * FNW - 1) / (16 * FNW))), block(64 * KS);
+    // The group-scale table (raw bits of the workgroup's rows, plus the
+    // wavefronts' row maxima) when it is small and the LDS has room for it.
+    constexpr int FM = (AR + 15) / 16;
+    constexpr size_t SLOT = 16 * FNW * 128 + AR * 256;
+    constexpr size_t RING = (size_t)KS * NSLOT * SLOT, RED = (size_t)(KS - 1) * FNW * FM * 64 * 16;
+    constexpr size_t STATIC = RING > RED ? RING : RED;
+    const size_t table = (size_t)16 * FNW * (size_t)(k / group) * 4;
+    const size_t dyn = table + (size_t)KS * 16 * FNW * 4;
+    // only where it keeps as many workgroups per CU as the ring alone allows
+    constexpr size_t kLds = 160 * 1024;
+    const int tab = table <= 16384 && kLds / (STATIC + dyn) == kLds / STATIC ? 1 : 0;
     if (SG == 0 && group >= 64)
-        w4a8_staged_kernel<AR, FNW, KS, NSLOT, E4M3, SG, CB, true><<<grid, block, 0, stream>>>(
-            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
+        w4a8_staged_kernel<AR, FNW, KS, NSLOT, E4M3, SG, CB, true><<<grid, block, tab ? dyn : 0, stream>>>(
+            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb, tab);
     else
-        w4a8_staged_kernel<AR, FNW, KS, NSLOT, E4M3, SG, CB, false><<<grid, block, 0, stream>>>(
-            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb);
+        w4a8_staged_kernel<AR, FNW, KS, NSLOT, E4M3, SG, CB, false><<<grid, block, tab ? dyn : 0, stream>>>(
+            x, sx, w, gs, (int)m, (int)n, (int)k, group, y, ldy, cb, tab);
     return hipGetLastError();
 }
 
