@@ -322,6 +322,10 @@ def layer_sweep(ck, torch, args) -> int:
     W8A8 layer and the grouped W4A8 layer (int8 activations, M = 4608)."""
     dev = torch.device("cuda:0")
     reps = max(args.steps // 4, 10)
+    only = set(args.layers_only.split(",")) if args.layers_only else None
+
+    def want(tag):
+        return only is None or tag in only
 
     def graph_ms(fn, n_steps):
         torch.cuda.synchronize()
@@ -348,6 +352,8 @@ def layer_sweep(ck, torch, args) -> int:
         return torch.from_numpy(lay.x_bf16.view(np.int16)).view(torch.bfloat16).to(dev)
 
     for name in ("up_3072_12288", "down_12288_3072"):
+        if not want(name.split("_")[0]):
+            continue
         cfg = workloads.WORKLOADS[name]
         lay = workloads.make_layer(seed=0, **cfg)
         x = act(lay)
@@ -378,7 +384,7 @@ def layer_sweep(ck, torch, args) -> int:
     wd = torch.from_numpy(workloads.make_weight(rng, cfg["n"], cfg["k"])).to(dev)
     ud = torch.from_numpy(rng.random((cfg["n"], cfg["k"]), dtype=np.float32)).to(dev)
     nk, nn = cfg["n"] * cfg["k"], cfg["n"]
-    for case, fn, byts in (
+    for case, fn, byts in () if not want("prep") else (
             ("weight prep, nearest rounding", lambda: ck.quantize_weight_convrot(wd, 128, 0), nk * 4 + nk // 2 + 4 * nn),
             ("weight prep, stochastic rounding", lambda: ck.quantize_weight_convrot_sr(wd, ud, 128, 0),
              nk * 8 + nk // 2 + 4 * nn)):
@@ -406,8 +412,9 @@ def layer_sweep(ck, torch, args) -> int:
         for (wp, ws), y in zip(wts, ys):
             ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx)
             ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
-    line("w4a4 q/k/v, one shared activation quantisation", m, n, k, graph_ms(qkv_reuse, reps), 3)
-    line("w4a4 q/k/v, activation quantised per projection", m, n, k, graph_ms(qkv_separate, reps), 3)
+    if want("qkv"):
+        line("w4a4 q/k/v, one shared activation quantisation", m, n, k, graph_ms(qkv_reuse, reps), 3)
+        line("w4a4 q/k/v, activation quantised per projection", m, n, k, graph_ms(qkv_separate, reps), 3)
     del wts
     wts6 = [ck.quantize_weight_convrot_fp6(torch.from_numpy(w).to(dev), 128) for w in lay.weights]
     xq6 = torch.empty((m, k * 3 // 4), dtype=torch.uint8, device=dev)
@@ -416,7 +423,9 @@ def layer_sweep(ck, torch, args) -> int:
         ck.rotate_quantize_act_fp6(x, 128, out=xq6, scales=sx)
         for (wq6, ws6), y in zip(wts6, ys):
             ck.linear_w4a4_fp6(xq6, sx, wq6, ws6, None, out=y)
-    line("w4a4 q/k/v, one shared activation quantisation, FP6 operands", m, n, k, graph_ms(qkv_reuse6, reps), 3)
+    if want("qkv"):
+        line("w4a4 q/k/v, one shared activation quantisation, FP6 operands", m, n, k, graph_ms(qkv_reuse6, reps),
+             3)
     del wts6, xq6, ys
 
     wd = torch.from_numpy(lay.weights[0]).to(dev)
@@ -427,7 +436,8 @@ def layer_sweep(ck, torch, args) -> int:
     def w8a8_step():
         ck.rotate_quantize_act(x, 128, 8, out=xq8, scales=sx)
         ck.linear_w8a8(xq8, sx, w8, ws8, None, out=y)
-    line("w8a8 layer square_3072", m, n, k, graph_ms(w8a8_step, reps))
+    if want("w8a8"):
+        line("w8a8 layer square_3072", m, n, k, graph_ms(w8a8_step, reps))
 
     wg, gs = ck.quantize_weight_convrot(wd, 128, 128)
     wsp = torch.empty((ck.w4a8_workspace_bytes(m, n, k, 0),), dtype=torch.uint8, device=dev)
@@ -435,9 +445,10 @@ def layer_sweep(ck, torch, args) -> int:
     def w4a8_step():
         ck.rotate_quantize_act(x, 128, 8, out=xq8, scales=sx)
         ck.linear_w4a8_grouped(xq8, sx, wg, gs, 128, 0, out=y, workspace=wsp)
-    line("w4a8-grouped layer square_3072 (decode + int8 GEMM)", m, n, k, graph_ms(w4a8_step, reps))
+    if want("w4a8"):
+        line("w4a8-grouped layer square_3072 (decode + int8 GEMM)", m, n, k, graph_ms(w4a8_step, reps))
     del w8, ws8, xq8, wg, gs, wsp, wd, lay, x, xq, sx, y
-    return lora_sweep(ck, torch, args)
+    return lora_sweep(ck, torch, args) if want("lora") else 0
 
 
 def lora_sweep(ck, torch, args) -> int:
@@ -539,6 +550,8 @@ def main() -> int:
                     help="run the skinny-M sweep (M in 1, 8, 16, 64; N,K = 12288,3072 and 5120,5120) instead")
     ap.add_argument("--skinny-m", default="", help="with --skinny: only these M (comma-separated)")
     ap.add_argument("--skinny-nk", default="", help="with --skinny: only these NxK shapes, e.g. 5120x5120")
+    ap.add_argument("--layers-only", default="",
+                    help="with --layers: only these groups (comma-separated: up, down, prep, qkv, w8a8, w4a8, lora)")
     ap.add_argument("--batches", type=int, default=5,
                     help="timed batches per skinny case (min and median are reported)")
     ap.add_argument("--lora", action="store_true",

@@ -739,15 +739,15 @@ template <bool E4M3, int SG, bool CB>
 hipError_t launch_staged(const int8_t *x, const float *sx, const int8_t *w, const void *gs, int64_t m, int64_t n,
                          int64_t k, int group, uint16_t *y, int64_t ldy, hipStream_t stream, const Codebook &cb) {
     // With 512 or more weight tiles of 16 rows the workgroups are numerous
-    // enough to fill the CUs with two K splits each; with fewer, four, or two
-    // with a deeper ring at m <= 32 (N = 12288 / 5120 at K = 3072 / 5120, 32
-    // weight copies: the measured best of the staged configurations at every
-    // m; deeper rings than these lost, as did more K splits).
+    // enough to fill the CUs with two K splits each; with fewer, four at
+    // m <= 16, two with one weight tile above (N = 12288 / 5120 at K = 3072 /
+    // 5120, 32 weight copies: the measured best of the staged configurations
+    // at every m; deeper rings than these lost, as did more K splits).
     const bool many = (n + 15) / 16 >= 512;
     if (m <= 4) return CK4_STAGED(4, 1, 4, 3);
     if (m <= 16) return many ? CK4_STAGED(16, 1, 2, 3) : CK4_STAGED(16, 1, 4, 3);
-    if (m <= 32) return many ? CK4_STAGED(32, 2, 2, 3) : CK4_STAGED(32, 1, 2, 4);
-    return many ? CK4_STAGED(64, 2, 2, 2) : CK4_STAGED(64, 2, 4, 2);
+    if (m <= 32) return many ? CK4_STAGED(32, 2, 2, 3) : CK4_STAGED(32, 1, 2, 3);
+    return many ? CK4_STAGED(64, 2, 2, 2) : CK4_STAGED(64, 1, 2, 2);
 }
 #undef CK4_STAGED
 
