@@ -271,7 +271,7 @@ def skinny_sweep(ck, torch, args) -> int:
             print(_skinny_line(f"w4a4 skinny m={m} n={n} k={k}", _graph_time_us(torch, cold, reps, warm, nb),
                                _graph_time_us(torch, hot, reps, warm, nb), byts, ceil_gbps), flush=True)
             # the whole layer: activation rotate + quantise, then the GEMM, as
-            # one library call (one kernel for m <= 4) and as two
+            # one library call (one kernel for m <= 2) and as two
             def w4a4_layer(c):
                 return lambda: ck.linear_w4a4_bf16(x, w4[c][0], w4[c][1], None, x_q=xq, x_scales=sx, out=y)
 

@@ -182,11 +182,10 @@ ck4_status ck4_linear_w4a4(const int8_t *x_q, const float *x_scales, const int8_
  * [m, k/2] and x_scales [m] are written too (the caller's buffers; reuse
  * them for other projections of the same activation), and y.
  *
- * For m <= 4 with rot_block 128 (and m * k / 2 <= 32 KB) one kernel does it
- * all: each workgroup rotates and quantises the m rows into its own LDS
- * while its first weight loads are in flight, which saves the quantiser's
- * launch at decode sizes. Other shapes run the quantiser, then the GEMM, on
- * `stream`.
+ * For m <= 2 with rot_block 128 one kernel does it all: each workgroup
+ * rotates and quantises the m rows into its own LDS while its weight loads
+ * are in flight, which saves the quantiser's launch at decode sizes. Other
+ * shapes run the quantiser, then the GEMM, on `stream`.
  *   x        bf16 [m, ldx], ldx a multiple of 8, 16-byte aligned.
  *   w_packed, w_scales, bias, y, ldy  as ck4_linear_w4a4.
  *   x_q      int8 [m, k/2], row stride k/2, 16-byte aligned (output).

@@ -340,7 +340,7 @@ def linear_w4a4_bf16(x: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Te
     """The whole layer in one library call: bf16 x [m, k] -> (y bf16 [m, n], x_q int8 [m, k/2], x_scales fp32 [m]).
 
     Bitwise rotate_quantize_act(x, rot_block, 4) followed by linear_w4a4; for
-    m <= 4 (rot_block 128) one kernel does both."""
+    m <= 2 (rot_block 128) one kernel does both."""
     _typed(x, torch.bfloat16, "x", 2)
     m, k = x.shape
     _dense(w_packed, torch.int8, "w_packed", 2)

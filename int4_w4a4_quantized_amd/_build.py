@@ -18,8 +18,8 @@ LIB = os.path.join(PKG, "libck4.so")
 BENCH_LIB = os.path.join(PKG, "libck4_bench.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["rotate_quant.hip", "gemm.hip", "skinny_layer.hip", "gemm_fp6.hip", "w4a8_decode.hip", "lora.hip",
-           "ck4_api.cpp"]
+SOURCES = ["rotate_quant.hip", "gemm.hip", "gemv_w4a4.hip", "skinny_layer.hip", "gemm_fp6.hip", "w4a8_decode.hip",
+           "lora.hip", "ck4_api.cpp"]
 BENCH_SOURCES = ["bench_read.hip"]
 
 HIPCC_FLAGS = [

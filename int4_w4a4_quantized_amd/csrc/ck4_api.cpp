@@ -13,6 +13,7 @@
 
 #include "../../include/ck4.h"
 #include "ck4_kernels.h"
+#include "gemv.h"
 
 #define CK4_VERSION_STRING "ck4 0.1.0 gfx950"
 
@@ -275,6 +276,10 @@ static ck4_status gemm_entry(const char *fn, bool s4, const int8_t *a, const flo
     // (64 bytes) cannot hold
     if (s4 && k < 256) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld < 256 for packed int4", fn, (long long)k);
     if (ck4_status s = check_device(fn)) return s;
+    // one or two activation rows: the matrix-vector kernel (same bits)
+    if (s4 && !out_i32 && (lora.t == nullptr || lora.rank == 0) && ck4::gemv_w4a4_fits(m, k))
+        return launched(fn, ck4::launch_gemv_w4a4(a, sa, b, sb, bias, m, n, k, static_cast<uint16_t *>(y), ldy,
+                                                  static_cast<hipStream_t>(stream)));
     return launched(fn, ck4::launch_gemm(s4, a, b, sa, sb, bias, m, n, k, out_i32, y, ldy,
                                          static_cast<hipStream_t>(stream), lora));
 }

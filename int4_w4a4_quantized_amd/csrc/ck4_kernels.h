@@ -113,17 +113,6 @@ hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, 
                               int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream,
                               const Codebook &cb = Codebook{});
 
-// The whole W4A4 layer from bf16 activations in one launch (rotate with
-// 128-blocks, quantise to packed int4, GEMM + epilogue) for m <= 4 rows:
-// skinny_layer_fits says whether a shape takes it (rot_block 128, k % 128 ==
-// 0, k >= 256, the rows' codes fit the workgroup's LDS). Writes x_q [m, k/2]
-// and x_scales [m] as the quantiser does, and y, bitwise as the quantiser
-// followed by launch_gemm.
-bool skinny_layer_fits(int64_t m, int64_t n, int64_t k, int rot_block);
-hipError_t launch_skinny_layer(const uint16_t *x, int64_t ldx, const int8_t *w_packed, const float *w_scales,
-                               const float *bias, int64_t m, int64_t n, int64_t k, int8_t *x_q, float *x_scales,
-                               uint16_t *y, int64_t ldy, hipStream_t stream);
-
 // Fused grouped W4A8 linear for m <= 64 and k >= 256, k % 128 == 0 (decode in registers
 // + int8 MFMA + epilogue), bit-identical to decode followed by the int8 GEMM.
 hipError_t launch_w4a8_fused(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,

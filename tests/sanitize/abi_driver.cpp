@@ -20,6 +20,7 @@
 
 #include "ck4.h"
 #include "ck4_kernels.h"
+#include "gemv.h"
 
 static int g_mode = 0;  // 0: no device, 1: gfx950, 2: another GPU
 static int g_launches = 0;
@@ -62,9 +63,14 @@ hipError_t launch_w4a8_fused(const int8_t *, const float *, const int8_t *, cons
 // the fused decode-time layer's shape rule, reduced to what these calls need:
 // m <= 4 with 128-blocks takes the one-launch kernel, anything else the
 // quantiser followed by the GEMM (two launches)
-bool skinny_layer_fits(int64_t m, int64_t, int64_t, int rot_block) { return m <= 4 && rot_block == 128; }
+bool skinny_layer_fits(int64_t m, int64_t, int64_t k, int rot_block) { return m >= 1 && m <= 2 && rot_block == 128 && k <= 8192; }
 hipError_t launch_skinny_layer(const uint16_t *, int64_t, const int8_t *, const float *, const float *, int64_t,
                                int64_t, int64_t, int8_t *, float *, uint16_t *, int64_t, hipStream_t) {
+    return ++g_launches, hipSuccess;
+}
+bool gemv_w4a4_fits(int64_t m, int64_t k) { return m >= 1 && m <= 2 && k >= 256 && k % 128 == 0 && k <= 16384; }
+hipError_t launch_gemv_w4a4(const int8_t *, const float *, const int8_t *, const float *, const float *, int64_t,
+                            int64_t, int64_t, uint16_t *, int64_t, hipStream_t) {
     return ++g_launches, hipSuccess;
 }
 alignas(256) static unsigned char g_fake_scratch[256];
@@ -196,12 +202,15 @@ int main(int argc, char **argv) {
     REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 192, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
     REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 128, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
     VALID(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 384, U16, 8, nullptr), 1);
+    VALID(ck4_linear_w4a4(I8, F, I8, F, F, 3, 5000, 640, U16, 5000, nullptr), 1);   // the matrix-vector kernel
+    VALID(ck4_linear_w4a4(I8, F, I8, F, F, 1, 5000, 16384, U16, 5000, nullptr), 1);  // k past it: the GEMM
     REFUSED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, 262144, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, BIG, 8, 256, U16, 8, nullptr));
 
-    // the whole layer from bf16: one launch for m <= 4 (128-blocks), else two
+    // the whole layer from bf16: one launch for m <= 2 (128-blocks), else two
     VALID(ck4_linear_w4a4_bf16(U16, 1, 3072, 3072, 128, I8, F, F, 12288, I8, F, U16, 12288, nullptr), 1);
-    VALID(ck4_linear_w4a4_bf16(U16, 4, 384, 392, 128, I8, F, nullptr, 5, I8, F, U16, 8, nullptr), 1);
+    VALID(ck4_linear_w4a4_bf16(U16, 2, 384, 392, 128, I8, F, nullptr, 5, I8, F, U16, 8, nullptr), 1);
+    VALID(ck4_linear_w4a4_bf16(U16, 4, 384, 392, 128, I8, F, nullptr, 5, I8, F, U16, 8, nullptr), 2);
     VALID(ck4_linear_w4a4_bf16(U16, 64, 3072, 3072, 128, I8, F, nullptr, 300, I8, F, U16, 300, nullptr), 2);
     VALID(ck4_linear_w4a4_bf16(U16, 2, 1024, 1024, 64, I8, F, nullptr, 300, I8, F, U16, 300, nullptr), 2);
     REFUSED(ck4_linear_w4a4_bf16(nullptr, 1, 256, 256, 128, I8, F, F, 8, I8, F, U16, 8, nullptr), CK4_ERR_INVALID);

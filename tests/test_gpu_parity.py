@@ -674,38 +674,83 @@ def test_full_size_layer(ck, name):
         assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], ws_ref))
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 12288, 3072), (2, 5120, 5120), (1, 77, 256), (2, 1000, 8192), (1, 17, 384),
+                                   (2, 8200, 1152), (2, 16400, 640), (2, 5, 4096), (1, 3, 2048), (1, 8200, 16384),
+                                   (2, 300, 16256), (1, 2000, 12288)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_gemv_equals_mfma_skinny_kernel(ck, m, n, k, with_bias):
+    """m <= 2: linear_w4a4 runs the matrix-vector kernel (one or two weight rows per wavefront: n > 8192 or
+    not; 1-4 and 8 chunks per lane and row; ragged n and k); the K-split MFMA kernel, reached through the LoRA
+    epilogue with t = 0 (bias present or not, as the plain call), must give the same bits, and both stay
+    within the oracle's bf16 bound."""
+    _, xq, sx, wp, ws = _quantised_pair(m, n, k, 5300 + m + n + k)
+    bias = np.random.default_rng(5301).standard_normal(n).astype(np.float32) if with_bias else None
+    d = [torch.from_numpy(v).cuda() for v in (xq, sx, wp, ws)]
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    y = bf16_host_bits(ck.linear_w4a4(*d, bd))
+    t0 = torch.zeros((frag_layout.rows16(m), 32), dtype=torch.bfloat16, device="cuda")
+    b0 = torch.zeros((frag_layout.rows16(n), 32), dtype=torch.bfloat16, device="cuda")
+    y_mfma = bf16_host_bits(ck.linear_w4a4_lora(*d, t0, b0, bd))
+    if bias is not None:
+        assert np.array_equal(y, y_mfma)
+    else:
+        # without a bias the LoRA epilogue adds + 0 to every value, which turns -0 into +0
+        assert np.array_equal(workloads.bf16_bits_to_f32(y), workloads.bf16_bits_to_f32(y_mfma))
+    acc = oracle.gemm_acc(xq, wp, k)
+    atol = None
+    if bias is not None:
+        atol = 2.0 ** -21 * (np.abs(acc * sx.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]) +
+                             np.abs(bias))
+    assert_bf16_close(y, oracle.epilogue_bf16(acc, sx, ws, bias), atol=atol)
+
+
 # --------------------------------------------------------------------------
-# The whole layer from bf16 in one call (one kernel for m <= 4)
+# The whole layer from bf16 in one call (one kernel for m <= 2)
 
 
 LAYER_CASES = [
-    # one kernel: m <= 4, every K-split width (N = 77 -> 8 waves, 8200 -> 4, 16400 -> 2), chunks per
-    # thread 1, 2 and 4, a half last step (k = 128 mod 256), ragged N
-    (1, 12288, 3072), (4, 12288, 3072), (1, 5120, 5120), (3, 5120, 5120), (2, 77, 256), (4, 17, 384),
-    (1, 8200, 16384), (2, 8200, 8192), (1, 16400, 1152), (4, 1000, 4096), (2, 999, 640),
-    # quantiser + GEMM: m > 4, or more rows than the fused kernel's registers hold at this K
-    (5, 300, 768), (17, 1000, 1024), (3, 8200, 8192), (2, 8200, 16384),
+    # one kernel (m <= 2, k <= 8192): 4, 2 and 1 weight rows per wavefront (n >= 10177, >= 5089,
+    # less), 1-4 chunks per lane and row, ragged n and k (a row ending in a partial 1 KB chunk); the
+    # last row all zero, tiny (scale below 2^-120) or one 128-block of 1e36 (scale above 2^120)
+    (1, 12288, 3072, None), (2, 12288, 3072, "zero"), (1, 5120, 5120, None), (2, 5120, 5120, "huge"),
+    (2, 77, 256, "tiny"), (1, 17, 384, None), (2, 8200, 8192, "tiny"), (1, 16400, 1152, None),
+    (2, 10300, 6144, "huge"), (2, 999, 640, "zero"), (2, 12345, 2176, "tiny"), (1, 3, 1280, None),
+    # quantiser + GEMM: m > 2 or k > 8192
+    (3, 5120, 5120, None), (4, 12288, 3072, None), (4, 17, 384, None), (4, 1000, 4096, None),
+    (3, 8200, 8192, None), (5, 300, 768, None), (17, 1000, 1024, None), (1, 8200, 16384, None),
+    (2, 5100, 16256, "huge"),
 ]
 
 
-@pytest.mark.parametrize("m,n,k", LAYER_CASES)
+@pytest.mark.parametrize("m,n,k,special", LAYER_CASES)
 @pytest.mark.parametrize("with_bias", [False, True])
-def test_linear_w4a4_bf16_equals_two_calls_and_oracle(ck, m, n, k, with_bias):
+def test_linear_w4a4_bf16_equals_two_calls_and_oracle(ck, m, n, k, special, with_bias):
     """The one-call layer gives the bits of rotate_quantize_act + linear_w4a4 (y, and the x_q and
-    x_scales it returns), including an all-zero row and rows whose scale leaves [2^-120, 2^120]
+    x_scales it returns), including all-zero rows and rows whose scale leaves [2^-120, 2^120]
     (the exact-divide path: a tiny row, and a row of one constant 128-block of 1e36: s = 1.6e36, and
     |acc| <= 49 keeps the fp32 epilogue finite),
-    and y stays within the oracle's bf16 bound (not checked on the tiny row, whose outputs fall
+    and y stays within the oracle's bf16 bound (not checked on tiny rows, whose outputs fall
     among fp32 subnormals, where the epilogue's two roundings are not within 1e-2)."""
     rng = np.random.default_rng(5100 + m + n + k)
     xb = workloads.make_activations(rng, m, k)
-    if m >= 2:
-        xb[1] = 0
-    if m >= 3:
-        xb[2] = workloads.f32_to_bf16_bits(rng.standard_normal(k).astype(np.float32) * np.float32(1e-37))
-    if m >= 4:
-        xb[3] = 0
-        xb[3, :128] = workloads.f32_to_bf16_bits(np.full(128, 1e36, dtype=np.float32))
+    tiny_rows = []
+
+    def make(row, kind):
+        if kind == "zero":
+            xb[row] = 0
+        elif kind == "tiny":
+            xb[row] = workloads.f32_to_bf16_bits(rng.standard_normal(k).astype(np.float32) * np.float32(1e-37))
+            tiny_rows.append(row)
+        elif kind == "huge":
+            xb[row] = 0
+            xb[row, :128] = workloads.f32_to_bf16_bits(np.full(128, 1e36, dtype=np.float32))
+
+    if special is not None:
+        make(m - 1, special)
+    elif m >= 4:
+        make(1, "zero")
+        make(2, "tiny")
+        make(3, "huge")
     w = workloads.make_weight(rng, n, k)
     wp, ws = oracle.quantize_weight_convrot(w)
     bias = rng.standard_normal(n).astype(np.float32) if with_bias else None
@@ -728,7 +773,7 @@ def test_linear_w4a4_bf16_equals_two_calls_and_oracle(ck, m, n, k, with_bias):
         if bias is not None:
             terms = np.abs(acc * s_ref.astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]) + np.abs(bias)
             atol = 2.0 ** -21 * terms
-        rows = [i for i in range(m) if i != 2]
+        rows = [i for i in range(m) if i not in tiny_rows]
         assert_bf16_close(bf16_host_bits(y)[rows], ref[rows], atol=None if atol is None else atol[rows])
 
 

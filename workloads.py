@@ -121,5 +121,5 @@ WORKLOADS = {
     "qkv_3x3072": dict(m=4608, k=3072, n=3072, n_weights=3),
     "down_12288_3072": dict(m=4608, k=12288, n=3072),
 }
-SKINNY_M = (1, 8, 16, 64)
+SKINNY_M = (1, 2, 4, 8, 16, 64)
 SKINNY_NK = ((12288, 3072), (5120, 5120))
