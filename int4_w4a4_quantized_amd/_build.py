@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libck4.so")
 BENCH_LIB = os.path.join(PKG, "libck4_bench.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["rotate_quant.hip", "gemm.hip", "gemv_w4a4.hip", "skinny_layer.hip", "gemm_fp6.hip", "w4a8_decode.hip",
+SOURCES = ["rotate_quant.hip", "gemm.hip", "gemv_w4a4.hip", "skinny_layer.hip", "gemm_fp6.hip", "w4a8_decode.hip", "w4a8_gemv.hip",
            "lora.hip", "ck4_api.cpp"]
 BENCH_SOURCES = ["bench_read.hip"]
 

@@ -504,6 +504,9 @@ ck4_status linear_w4a8(const char *fn, const int8_t *x_q8, const float *x_scales
     if (ck4_status s = check_device(fn, &dev)) return s;
     const int64_t c = w4a8_chunk(m, n, k, chunk_cols, g_l2_bytes[dev]);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (c == 0 && ck4::w4a8_gemv_fits(m, n, k, group, cb.on))
+        return launched(fn, ck4::launch_w4a8_gemv(x_q8, x_scales, w_packed, group_scales, e4m3, m, n, k, group, y,
+                                                  ldy, st));
     if (c == 0) return launched(fn, ck4::launch_w4a8_fused(x_q8, x_scales, w_packed, group_scales, e4m3, m, n, k,
                                                            group, y, ldy, st, cb));
     const size_t need = (size_t)(align_up(c * k, 256) + align_up(c * 4, 256));

@@ -1,5 +1,6 @@
-// The matrix-vector W4A4 kernels for one or two activation rows: the GEMM
-// (gemv_w4a4.hip) and the whole layer in one launch (skinny_layer.hip).
+// The matrix-vector kernels for a few activation rows: the W4A4 GEMM
+// (gemv_w4a4.hip), the whole W4A4 layer in one launch (skinny_layer.hip) and
+// the fused grouped W4A8 linear (w4a8_gemv.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -27,5 +28,15 @@ bool skinny_layer_fits(int64_t m, int64_t n, int64_t k, int rot_block);
 hipError_t launch_skinny_layer(const uint16_t *x, int64_t ldx, const int8_t *w_packed, const float *w_scales,
                                const float *bias, int64_t m, int64_t n, int64_t k, int8_t *x_q, float *x_scales,
                                uint16_t *y, int64_t ldy, hipStream_t stream);
+
+// Fused grouped W4A8 linear (int4 codes with fp32 or E4M3 group scales,
+// decoded in registers, int8 activations) for the shapes w4a8_gemv_fits
+// takes (m <= 2, n <= 8192, 256 <= k <= 8192, k % 128 == 0, groups of 32 or
+// more codes, no codebook): y bf16 [m, ldy], bitwise the decode kernel
+// followed by the int8 GEMM.
+bool w4a8_gemv_fits(int64_t m, int64_t n, int64_t k, int group, bool codebook);
+hipError_t launch_w4a8_gemv(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
+                            const void *group_scales, bool scale_e4m3, int64_t m, int64_t n, int64_t k, int group,
+                            uint16_t *y, int64_t ldy, hipStream_t stream);
 
 }  // namespace ck4

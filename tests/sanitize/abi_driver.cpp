@@ -61,7 +61,7 @@ hipError_t launch_w4a8_fused(const int8_t *, const float *, const int8_t *, cons
     return ++g_launches, hipSuccess;
 }
 // the fused decode-time layer's shape rule, reduced to what these calls need:
-// m <= 4 with 128-blocks takes the one-launch kernel, anything else the
+// m <= 2 with 128-blocks takes the one-launch kernel, anything else the
 // quantiser followed by the GEMM (two launches)
 bool skinny_layer_fits(int64_t m, int64_t, int64_t k, int rot_block) { return m >= 1 && m <= 2 && rot_block == 128 && k <= 8192; }
 hipError_t launch_skinny_layer(const uint16_t *, int64_t, const int8_t *, const float *, const float *, int64_t,
@@ -71,6 +71,11 @@ hipError_t launch_skinny_layer(const uint16_t *, int64_t, const int8_t *, const 
 bool gemv_w4a4_fits(int64_t m, int64_t k) { return m >= 1 && m <= 2 && k >= 256 && k % 128 == 0 && k <= 16384; }
 hipError_t launch_gemv_w4a4(const int8_t *, const float *, const int8_t *, const float *, const float *, int64_t,
                             int64_t, int64_t, uint16_t *, int64_t, hipStream_t) {
+    return ++g_launches, hipSuccess;
+}
+bool w4a8_gemv_fits(int64_t m, int64_t n, int64_t, int, bool codebook) { return !codebook && m <= 2 && n <= 8192; }
+hipError_t launch_w4a8_gemv(const int8_t *, const float *, const int8_t *, const void *, bool, int64_t, int64_t,
+                            int64_t, int, uint16_t *, int64_t, hipStream_t) {
     return ++g_launches, hipSuccess;
 }
 alignas(256) static unsigned char g_fake_scratch[256];
@@ -278,6 +283,7 @@ int main(int argc, char **argv) {
         ++g_fails;
     }
     VALID(ck4_linear_w4a8_grouped(I8, F, I8, F, 8, 1000, 1024, 128, U16, 1008, 0, nullptr, 0, nullptr), 1);
+    VALID(ck4_linear_w4a8_grouped(I8, F, I8, F, 1, 1000, 1024, 128, U16, 1008, 0, nullptr, 0, nullptr), 1);
     VALID(ck4_linear_w4a8_grouped(I8, F, I8, F, 8, 1000, 1024, 128, U16, 1008, 256, P, ws, nullptr), 8);
     VALID(ck4_linear_w4a8_grouped(I8, F, I8, F, 100, 1000, 1024, 128, U16, 1008, 0, P, BIG, nullptr), 2);
     REFUSED(ck4_linear_w4a8_grouped(I8, F, I8, F, 8, 1000, 1024, 128, U16, 1008, 256, P, 100, nullptr),

@@ -846,6 +846,41 @@ def test_w4a8_fused_wide_n_equals_decode_path(ck, m, n, k, group, e4m3):
     assert_bf16_close(y0, ref)
 
 
+@pytest.mark.parametrize("m,n,k,group,e4m3", [(1, 8192, 3072, 128, False), (2, 5120, 5120, 64, True),
+                                               (1, 77, 256, 32, False), (1, 8000, 8192, 256, False),
+                                               (1, 17, 384, 128, True), (2, 4000, 1152, 32, False),
+                                               (1, 1000, 4096, 1024, True), (1, 3, 640, 128, False),
+                                               (2, 4100, 2176, 128, True), (2, 8192, 5120, 512, False),
+                                               # just outside the kernel's shapes: the MFMA fused kernel
+                                               (2, 8193, 1024, 128, False), (3, 100, 1024, 128, True),
+                                               (1, 100, 1024, 16, False), (2, 300, 6144, 128, False)])
+def test_w4a8_gemv_equals_decode_path(ck, m, n, k, group, e4m3):
+    """m <= 2, n <= 8192, groups of 32 codes or more: the matrix-vector W4A8 kernel (1-4 chunks per lane and row,
+    ragged n and k, fp32 and E4M3 scales, an all-zero weight row and one whose groups share a scale) must give the
+    bits of one decode pass + the int8 GEMM, and stay within the oracle's bf16 bound."""
+    rng = np.random.default_rng(3700 + m + n + group)
+    xb = workloads.make_activations(rng, m, k)
+    w = workloads.make_weight(rng, n, k)
+    w[0] = 0
+    w[min(1, n - 1)] = 0.5
+    wd = torch.from_numpy(w).cuda()
+    if e4m3:
+        wp, gs = ck.quantize_weight_convrot_e4m3(wd, 128, group)
+    else:
+        wp, gs = ck.quantize_weight_convrot(wd, 128, group)
+    xq8, sx = ck.rotate_quantize_act(dev_bf16(xb), 128, 8)
+    assert ck.w4a8_workspace_bytes(m, n, k, 0) == 0
+    y0 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wp, gs, group, 0))
+    y1 = bf16_host_bits(ck.linear_w4a8_grouped(xq8, sx, wp, gs, group, -1))
+    assert np.array_equal(y0, y1)
+    assert not y0[:, 0].any()
+    if e4m3:
+        ref = oracle.linear_w4a8_grouped_e4m3(xb, host(wp), host(gs).view(np.uint8), group)
+    else:
+        ref = oracle.linear_w4a8_grouped(xb, host(wp), host(gs), group)
+    assert_bf16_close(y0, ref)
+
+
 def test_random_shapes_kernel_variants_agree(ck):
     """Seeded random shapes through the kernel choices that must give the same bits: the N-split skinny kernel
     against the K-split one (through its LoRA epilogue with t = 0), and the FP6 GEMM (either tile) against the
