@@ -307,8 +307,15 @@ def skinny_sweep(ck, torch, args) -> int:
                         ck.rotate_quantize_act(x, 128, 8, out=xq8, scales=sx8)
                         ck.linear_w4a8_grouped(xq8, sx8, wl[c][0], wl[c][1], 128, 0, out=y, workspace=ws)
                     return f
+                def w4a8_layer1(c, wl=wl):
+                    return lambda: ck.linear_w4a8_grouped_bf16(x, wl[c][0], wl[c][1], 128, x_q8=xq8, x_scales=sx8,
+                                                               out=y, workspace=ws)
                 lbyt = 2 * m * k + n * k // 2 + gsb + 2 * m * n
-                print(_skinny_line(f"{label} skinny layer (quantise + GEMM) m={m} n={n} k={k}",
+                print(_skinny_line(f"{label} skinny layer (quantise + GEMM, one call) m={m} n={n} k={k}",
+                                   _graph_time_us(torch, [w4a8_layer1(c) for c in range(copies)], reps, warm, nb),
+                                   _graph_time_us(torch, [w4a8_layer1(0) for _ in range(copies)], reps, warm, nb),
+                                   lbyt, ceil_gbps), flush=True)
+                print(_skinny_line(f"{label} skinny layer (quantise + GEMM, two calls) m={m} n={n} k={k}",
                                    _graph_time_us(torch, [w4a8_layer(c) for c in range(copies)], reps, warm, nb),
                                    _graph_time_us(torch, [w4a8_layer(0) for _ in range(copies)], reps, warm, nb),
                                    lbyt, ceil_gbps), flush=True)

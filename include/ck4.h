@@ -319,6 +319,36 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
 
 
 /*
+ * The whole grouped W4A8 layer from bf16 activations in one call ([PR #97]
+ * What this adds: int8 activations from the same rotation with an absmax/127
+ * row scale, against the decoded int4 weight): the same arguments as
+ * ck4_rotate_quantize_act(bits = 8) followed by ck4_linear_w4a8_grouped (or
+ * its E4M3 form) with chunk_cols = 0, and the same results bit for bit:
+ * x_q8 [m, k] and x_scales [m] are written too (the caller's buffers), and y.
+ * For m = 1 with rot_block 128, k <= 8192 and groups of 32 or more codes
+ * (with E4M3 scales also n <= 8192) one kernel does it all: each workgroup
+ * rotates and quantises the row into its own LDS while its weight loads are
+ * in flight, which saves the quantiser's launch at decode sizes. Other
+ * shapes run the quantiser, then the W4A8 linear, on `stream`.
+ *   x               bf16 [m, ldx], ldx a multiple of 8, 16-byte aligned.
+ *   w_packed        int8 [n, k/2] from ck4_quantize_weight_convrot(group = g)
+ *                   or its E4M3 form.
+ *   group_scales    fp32 [n, k/g], or (scale_e4m3 != 0) E4M3 bytes [n, k/g].
+ *   x_q8            int8 [m, k], row stride k, 16-byte aligned (output).
+ *   x_scales        fp32 [m] (output).
+ *   y, ldy          as ck4_linear_w4a8_grouped.
+ *   workspace       as ck4_linear_w4a8_grouped with chunk_cols = 0: at least
+ *                   ck4_w4a8_workspace_bytes(m, n, k, 0) bytes, NULL when
+ *                   that is 0.
+ * Unsupported: k % 128 != 0, k < 256, k > 16384, rot_block not a power of
+ * two in [16, 1024] or not dividing k, g not a power of two in [4, 1024].
+ */
+ck4_status ck4_linear_w4a8_grouped_bf16(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                        const int8_t *w_packed, const void *group_scales, int scale_e4m3, int64_t n,
+                                        int group, int8_t *x_q8, float *x_scales, uint16_t *y, int64_t ldy,
+                                        void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * ck4_linear_w4a8_grouped for callers that cannot allocate device memory
  * (code under HIP graph capture, serving loops, harnesses that forbid
  * hipMalloc): the same arguments without the workspace, the same three paths

@@ -55,6 +55,8 @@ SIGNATURES = {
     "ck4_w4a8_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
     "ck4_linear_w4a8_grouped": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t, _P], _I),
     "ck4_linear_w4a8_grouped_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P], _I),
+    "ck4_linear_w4a8_grouped_bf16": ([_P, _I64, _I64, _I64, _I, _P, _P, _I, _I64, _I, _P, _P, _P, _I64, _P,
+                                      ctypes.c_size_t, _P], _I),
     "ck4_quantize_weight_convrot_e4m3": ([_P, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "ck4_dequant_w4a8_grouped_e4m3": ([_P, _P, _I64, _I64, _I, _I64, _I64, _P, _P, _P], _I),
     "ck4_linear_w4a8_grouped_e4m3": ([_P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _I64, _I64, _P, ctypes.c_size_t,
@@ -473,6 +475,53 @@ def linear_w4a8_grouped(x_q8, x_scales, w_packed, group_scales, group: int = 128
                                       group, _ptr(out), out.stride(0), chunk_cols, _ptr(workspace),
                                       0 if workspace is None else workspace.numel(), _stream(x_q8.device)))
     return out
+
+
+def linear_w4a8_grouped_bf16(x: torch.Tensor, w_packed: torch.Tensor, group_scales: torch.Tensor, group: int = 128,
+                             rot_block: int = 128, x_q8=None, x_scales=None, out=None, workspace=None):
+    """The whole grouped W4A8 layer in one library call: bf16 x [m, k] -> (y bf16 [m, n], x_q8 int8 [m, k],
+    x_scales fp32 [m]).
+
+    Bitwise rotate_quantize_act(x, rot_block, 8) followed by linear_w4a8_grouped(..., chunk_cols=0);
+    for m = 1 (rot_block 128, k <= 8192, groups of 32 or more) one kernel does both. group_scales:
+    fp32, or uint8 holding E4M3 bytes."""
+    _typed(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    _dense(w_packed, torch.int8, "w_packed", 2)
+    if w_packed.shape[1] * 2 != k:
+        raise ValueError(f"the weight rows hold {w_packed.shape[1]} bytes, not k/2 = {k // 2}")
+    n = w_packed.shape[0]
+    if group <= 0 or k % group != 0:
+        raise ValueError(f"group={group} must divide k={k}")
+    _vec(group_scales, (torch.float32, torch.uint8), "group_scales", n * (k // group))
+    if x_q8 is not None:
+        _dense(x_q8, torch.int8, "x_q8", 2)
+        if tuple(x_q8.shape) != (m, k):
+            raise ValueError(f"x_q8 must have shape {(m, k)}, got {tuple(x_q8.shape)}")
+    if x_scales is not None:
+        _vec(x_scales, torch.float32, "x_scales", m)
+    if out is not None:
+        _out_checked(out, m, n)
+    if workspace is not None:
+        _dense(workspace, torch.uint8, "workspace")
+    _on_gpu(x=x, w_packed=w_packed, group_scales=group_scales, x_q8=x_q8, x_scales=x_scales, out=out,
+            workspace=workspace)
+    if x_q8 is None:
+        x_q8 = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if x_scales is None:
+        x_scales = torch.empty((m,), dtype=torch.float32, device=x.device)
+    if out is None:
+        out = _out_bf16(m, n, x.device)
+    need = w4a8_workspace_bytes(m, n, k, 0)
+    if workspace is None and need > 0:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=x.device)
+    e4m3 = group_scales.dtype == torch.uint8
+    _check("ck4_linear_w4a8_grouped_bf16",
+           lib().ck4_linear_w4a8_grouped_bf16(_ptr(x), m, k, x.stride(0), rot_block, _ptr(w_packed),
+                                              _ptr(group_scales), int(e4m3), n, group, _ptr(x_q8), _ptr(x_scales),
+                                              _ptr(out), out.stride(0), _ptr(workspace),
+                                              0 if workspace is None else workspace.numel(), _stream(x.device)))
+    return out, x_q8, x_scales
 
 
 def linear_w4a8_grouped_noalloc(x_q8, x_scales, w_packed, group_scales, group: int = 128, chunk_cols: int = 0,

@@ -536,6 +536,35 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
                        ldy, chunk_cols, workspace, ws_bytes, stream);
 }
 
+ck4_status ck4_linear_w4a8_grouped_bf16(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                        const int8_t *w_packed, const void *group_scales, int scale_e4m3, int64_t n,
+                                        int group, int8_t *x_q8, float *x_scales, uint16_t *y, int64_t ldy,
+                                        void *workspace, size_t ws_bytes, void *stream) {
+    const char *fn = "ck4_linear_w4a8_grouped_bf16";
+    if (!x || !w_packed || !group_scales || !x_q8 || !x_scales || !y)
+        return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
+    if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, 8)) return s;
+    if (ck4_status s = check_stride(fn, "ldx", ldx, k, 8)) return s;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(x_q8, 16) || !aligned(x_scales, 4) ||
+        (workspace && !aligned(workspace, 16)))
+        return fail(CK4_ERR_INVALID, "%s: x, w_packed, x_q8 or workspace not 16-byte aligned, or x_scales misaligned",
+                    fn);
+    if (ck4_status s = check_rot(fn, k, rot_block)) return s;
+    if (k % 128 != 0 || k < 256)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld (need a multiple of 128, at least 256)", fn, (long long)k);
+    if (!pow2(group) || group < 4 || group > 1024 || k % group != 0)
+        return fail(CK4_ERR_UNSUPPORTED, "%s: group=%d (need a power of two in [4, 1024] dividing k)", fn, group);
+    if (ck4_status s = check_device(fn)) return s;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ck4::w4a8_layer_fits(m, n, k, rot_block, group, false, scale_e4m3 != 0))
+        return launched(fn, ck4::launch_w4a8_layer(x, ldx, w_packed, group_scales, scale_e4m3 != 0, m, n, k, group,
+                                                   x_q8, x_scales, y, ldy, st));
+    if (ck4_status s = launched(fn, ck4::launch_rotate_quant(x, 0, m, k, ldx, rot_block, 1, 0, x_q8, k, x_scales, st)))
+        return s;
+    return linear_w4a8(fn, x_q8, x_scales, w_packed, group_scales, scale_e4m3 != 0, m, n, k, group, y, ldy, 0,
+                       workspace, ws_bytes, stream);
+}
+
 ck4_status ck4_linear_w4a8_grouped_noalloc(const int8_t *x_q8, const float *x_scales, const int8_t *w_packed,
                                            const float *group_scales, int64_t m, int64_t n, int64_t k, int group,
                                            uint16_t *y, int64_t ldy, int64_t chunk_cols, void *stream) {

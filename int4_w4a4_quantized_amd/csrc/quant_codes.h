@@ -51,5 +51,12 @@ __device__ __forceinline__ uint32_t pack8_biased(const uint32_t *c) {
     return (lo | hi) ^ 0x88888888u;
 }
 
+// 4 int8 codes (low bytes) -> one word, byte j = code j.
+__device__ __forceinline__ uint32_t pack4_bytes(const uint32_t *c) {
+    const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x04000C0Cu);
+    return lo | hi;
+}
+
 }  // namespace
 }  // namespace ck4

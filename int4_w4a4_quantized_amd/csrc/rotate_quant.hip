@@ -111,13 +111,6 @@ __device__ __forceinline__ float group_scale(float gmax, float qdiv, bool e4m3, 
     return s;
 }
 
-// 4 int8 codes (low bytes) -> one word, byte j = code j.
-__device__ __forceinline__ uint32_t pack4_bytes(const uint32_t *c) {
-    const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0C0C0400u);
-    const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x04000C0Cu);
-    return lo | hi;
-}
-
 // out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation, 3 bf16 rotation in MFMA fragment order.
 // WAVE_ROW: each wavefront owns one row (K <= 64 * 16 * NCH), so the row
 // absmax is a wavefront reduction with no LDS and no barrier, and a 256-thread

@@ -78,6 +78,13 @@ hipError_t launch_w4a8_gemv(const int8_t *, const float *, const int8_t *, const
                             int64_t, int, uint16_t *, int64_t, hipStream_t) {
     return ++g_launches, hipSuccess;
 }
+bool w4a8_layer_fits(int64_t m, int64_t, int64_t k, int rot_block, int group, bool codebook, bool) {
+    return !codebook && m == 1 && rot_block == 128 && group >= 32 && k <= 8192;
+}
+hipError_t launch_w4a8_layer(const uint16_t *, int64_t, const int8_t *, const void *, bool, int64_t, int64_t,
+                             int64_t, int, int8_t *, float *, uint16_t *, int64_t, hipStream_t) {
+    return ++g_launches, hipSuccess;
+}
 alignas(256) static unsigned char g_fake_scratch[256];
 hipError_t noalloc_scratch(int, void **ptr) {
     *ptr = g_fake_scratch;
@@ -232,6 +239,34 @@ int main(int argc, char **argv) {
     REJECTED(ck4_linear_w4a4_bf16(U16, BIG, 256, 256, 128, I8, F, F, 8, I8, F, U16, 8, nullptr));
     REJECTED(ck4_linear_w4a4_bf16(U16, 1, 256, BIG, 128, I8, F, F, 8, I8, F, U16, 8, nullptr));
     REJECTED(ck4_linear_w4a4_bf16(U16, 1, 256, 256, 128, I8, F, F, NEG, I8, F, U16, 8, nullptr));
+    // the grouped W4A8 layer from bf16: one launch for m = 1 (128-blocks, groups >= 32), else the
+    // quantiser and the W4A8 linear (fused for m <= 64: two launches)
+    VALID(ck4_linear_w4a8_grouped_bf16(U16, 1, 3072, 3072, 128, I8, F, 0, 5120, 128, I8, F, U16, 5120, nullptr, 0,
+                                       nullptr), 1);
+    VALID(ck4_linear_w4a8_grouped_bf16(U16, 1, 384, 392, 128, I8, F, 1, 5, 128, I8, F, U16, 8, nullptr, 0, nullptr),
+          1);
+    VALID(ck4_linear_w4a8_grouped_bf16(U16, 2, 384, 392, 128, I8, F, 1, 5, 128, I8, F, U16, 8, nullptr, 0, nullptr),
+          2);
+    VALID(ck4_linear_w4a8_grouped_bf16(U16, 4, 384, 392, 128, I8, F, 0, 5, 128, I8, F, U16, 8, nullptr, 0, nullptr),
+          2);
+    VALID(ck4_linear_w4a8_grouped_bf16(U16, 1, 384, 384, 128, I8, F, 0, 5, 16, I8, F, U16, 8, nullptr, 0, nullptr),
+          2);
+    REFUSED(ck4_linear_w4a8_grouped_bf16(nullptr, 1, 256, 256, 128, I8, F, 0, 8, 128, I8, F, U16, 8, nullptr, 0,
+                                         nullptr), CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a8_grouped_bf16(U16, 1, 256, 256, 128, I8, F, 0, 8, 128, (int8_t *)ODD, F, U16, 8, nullptr,
+                                         0, nullptr), CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a8_grouped_bf16(U16, 1, 256, 200, 128, I8, F, 0, 8, 128, I8, F, U16, 8, nullptr, 0,
+                                         nullptr), CK4_ERR_INVALID);
+    REFUSED(ck4_linear_w4a8_grouped_bf16(U16, 1, 256, 256, 128, I8, F, 0, 8, 96, I8, F, U16, 8, nullptr, 0,
+                                         nullptr), CK4_ERR_UNSUPPORTED);
+    REFUSED(ck4_linear_w4a8_grouped_bf16(U16, 1, 128, 128, 128, I8, F, 0, 8, 128, I8, F, U16, 8, nullptr, 0,
+                                         nullptr), CK4_ERR_UNSUPPORTED);
+    REFUSED(ck4_linear_w4a8_grouped_bf16(U16, 1, 32768, 32768, 128, I8, F, 0, 8, 128, I8, F, U16, 8, nullptr, 0,
+                                         nullptr), CK4_ERR_UNSUPPORTED);
+    REJECTED(ck4_linear_w4a8_grouped_bf16(U16, BIG, 256, 256, 128, I8, F, 0, 8, 128, I8, F, U16, 8, nullptr, 0,
+                                          nullptr));
+    REJECTED(ck4_linear_w4a8_grouped_bf16(U16, 1, 256, 256, 128, I8, F, 0, NEG, 128, I8, F, U16, 8, nullptr, 0,
+                                          nullptr));
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, BIG, 256, U16, BIG, nullptr));
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, 8, 8, BIG, U16, 8, nullptr));
     REJECTED(ck4_linear_w4a4(I8, F, I8, F, nullptr, NEG, NEG, NEG, U16, NEG, nullptr));

@@ -73,6 +73,22 @@ def test_linear_w4a4_bf16_checks():
     refused("CUDA", ck.linear_w4a4_bf16, **ok)
 
 
+def test_linear_w4a8_bf16_checks():
+    g = 128
+    ok = dict(x=bf16(M, K), w_packed=i8(N, K // 2), group_scales=f32(N, K // g))
+    refused("not k/2", ck.linear_w4a8_grouped_bf16, **{**ok, "w_packed": i8(N, K)})
+    refused("x must be torch.bfloat16", ck.linear_w4a8_grouped_bf16, **{**ok, "x": f32(M, K)})
+    refused("group_scales holds", ck.linear_w4a8_grouped_bf16, **{**ok, "group_scales": f32(N, K // g - 1)})
+    refused("group_scales must be", ck.linear_w4a8_grouped_bf16, **{**ok, "group_scales": bf16(N, K // g)})
+    refused("must divide", ck.linear_w4a8_grouped_bf16, **ok, group=96)
+    refused("x_q8 must have shape", ck.linear_w4a8_grouped_bf16, **ok, x_q8=i8(M, K // 2))
+    refused("x_scales holds", ck.linear_w4a8_grouped_bf16, **ok, x_scales=f32(M - 1))
+    refused("out must have shape", ck.linear_w4a8_grouped_bf16, **ok, out=bf16(M + 1, N))
+    refused("workspace must be", ck.linear_w4a8_grouped_bf16, **ok, workspace=f32(64))
+    refused("CUDA", ck.linear_w4a8_grouped_bf16, **ok)
+    refused("CUDA", ck.linear_w4a8_grouped_bf16, **{**ok, "group_scales": u8(N, K // g)})
+
+
 def test_linear_w8a8_checks():
     refused("k differs", ck.linear_w8a8, i8(M, K), f32(M), i8(N, K // 2), f32(N))
     refused("w_scales holds", ck.linear_w8a8, i8(M, K), f32(M), i8(N, K), f32(3))

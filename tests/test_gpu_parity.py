@@ -777,6 +777,93 @@ def test_linear_w4a4_bf16_equals_two_calls_and_oracle(ck, m, n, k, special, with
         assert_bf16_close(bf16_host_bits(y)[rows], ref[rows], atol=None if atol is None else atol[rows])
 
 
+W4A8_LAYER_CASES = [
+    # one kernel (m = 1, k <= 8192, groups >= 32; E4M3 scales up to n = 8192): 1-4 chunks per lane and
+    # row, ragged n and k, fp32 and E4M3 group scales; the row all zero, tiny or one 128-block of 1e36
+    (1, 5120, 5120, 128, False, None), (1, 5120, 5120, 64, True, "zero"), (1, 12288, 3072, 128, False, None),
+    (1, 77, 256, 32, False, "tiny"), (1, 17, 384, 128, True, None), (1, 8200, 8192, 256, False, "huge"),
+    (1, 999, 1152, 128, True, "huge"), (1, 3, 2176, 128, False, None), (1, 4100, 6144, 1024, False, "tiny"),
+    # quantiser + W4A8 linear: m > 1, groups below 32, k > 8192, E4M3 scales with n > 8192
+    (2, 5120, 5120, 64, True, "zero"), (2, 999, 1152, 128, False, "huge"), (3, 1000, 1024, 128, False, None),
+    (1, 500, 1024, 16, False, None), (1, 300, 12288, 128, True, None), (1, 12288, 3072, 128, True, None),
+    (17, 640, 768, 64, False, None),
+]
+
+
+@pytest.mark.parametrize("m,n,k,group,e4m3,special", W4A8_LAYER_CASES)
+def test_linear_w4a8_bf16_equals_two_calls_and_oracle(ck, m, n, k, group, e4m3, special):
+    """The one-call grouped W4A8 layer gives the bits of rotate_quantize_act(bits=8) + linear_w4a8_grouped
+    (y, and the x_q8 and x_scales it returns), with all-zero rows, rows whose scale leaves [2^-120, 2^120]
+    (the exact-divide path) and an all-zero weight row, and y stays within the oracle's bf16 bound (tiny
+    rows excluded, as in the W4A4 layer test)."""
+    rng = np.random.default_rng(5500 + m + n + k + group)
+    xb = workloads.make_activations(rng, m, k)
+    tiny_rows = []
+    r = m - 1
+    if special == "zero":
+        xb[r] = 0
+    elif special == "tiny":
+        xb[r] = workloads.f32_to_bf16_bits(rng.standard_normal(k).astype(np.float32) * np.float32(1e-37))
+        tiny_rows.append(r)
+    elif special == "huge":
+        xb[r] = 0
+        xb[r, :128] = workloads.f32_to_bf16_bits(np.full(128, 1e36, dtype=np.float32))
+    w = workloads.make_weight(rng, n, k)
+    w[0] = 0
+    wd = torch.from_numpy(w).cuda()
+    wp, gs = (ck.quantize_weight_convrot_e4m3 if e4m3 else ck.quantize_weight_convrot)(wd, 128, group)
+    xd = dev_bf16(xb)
+    y, xq8, sx = ck.linear_w4a8_grouped_bf16(xd, wp, gs, group)
+    xq2, sx2 = ck.rotate_quantize_act(xd, 128, 8)
+    y2 = ck.linear_w4a8_grouped(xq2, sx2, wp, gs, group, 0)
+    assert np.array_equal(host(xq8), host(xq2))
+    assert np.array_equal(host(sx).view(np.uint32), host(sx2).view(np.uint32))
+    assert np.array_equal(bf16_host_bits(y), bf16_host_bits(y2))
+    assert not bf16_host_bits(y)[:, 0].any()
+    q_ref, s_ref = oracle.rotate_quantize_act(xb, bits=8)
+    assert np.array_equal(host(xq8), q_ref)
+    assert np.array_equal(host(sx).view(np.uint32), s_ref.view(np.uint32))
+    if m * n * k <= 4 * 8200 * 4096 and special != "huge":
+        if e4m3:
+            ref = oracle.linear_w4a8_grouped_e4m3(xb, host(wp), host(gs).view(np.uint8), group)
+        else:
+            ref = oracle.linear_w4a8_grouped(xb, host(wp), host(gs), group)
+        rows = [i for i in range(m) if i not in tiny_rows]
+        assert_bf16_close(bf16_host_bits(y)[rows], ref[rows])
+
+
+def test_linear_w4a8_bf16_reused_buffers_and_graph(ck):
+    """Caller buffers are used and overwritten (two calls in a row, the second with fewer rows of another
+    activation), and the one-call W4A8 layer replays inside a captured graph with the same bits each time."""
+    rng = np.random.default_rng(5600)
+    n, k, group = 3000, 1024, 128
+    wp, gs = ck.quantize_weight_convrot(torch.from_numpy(workloads.make_weight(rng, n, k)).cuda(), 128, group)
+    xq = torch.full((4, k), 0x5A, dtype=torch.int8, device="cuda")
+    sx = torch.full((4,), 7.0, dtype=torch.float32, device="cuda")
+    y = torch.full((4, n), 1.0, dtype=torch.bfloat16, device="cuda")
+    for m in (2, 1):
+        xd = dev_bf16(workloads.make_activations(rng, m, k))
+        ck.linear_w4a8_grouped_bf16(xd, wp, gs, group, x_q8=xq[:m], x_scales=sx[:m], out=y[:m])
+        assert ck.w4a8_workspace_bytes(m, n, k, 0) == 0
+        xq2, sx2 = ck.rotate_quantize_act(xd, 128, 8)
+        y2 = ck.linear_w4a8_grouped(xq2, sx2, wp, gs, group, 0)
+        assert np.array_equal(host(xq[:m]), host(xq2))
+        assert np.array_equal(host(sx[:m]).view(np.uint32), host(sx2).view(np.uint32))
+        assert np.array_equal(bf16_host_bits(y[:m]), bf16_host_bits(y2))
+    xd = dev_bf16(workloads.make_activations(rng, 1, k))
+    ref = bf16_host_bits(ck.linear_w4a8_grouped_bf16(xd, wp, gs, group)[0])
+    yg = torch.empty((1, n), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ck.linear_w4a8_grouped_bf16(xd, wp, gs, group, x_q8=xq[:1], x_scales=sx[:1], out=yg)
+    for _ in range(3):
+        yg.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_host_bits(yg), ref)
+
+
 def test_linear_w4a4_bf16_reused_buffers(ck):
     """Caller buffers are used and overwritten: two calls in a row into the same x_q, x_scales and y, the
     second with fewer rows of a different activation, each equal to the two-call path."""
