@@ -28,10 +28,17 @@ constexpr int kGemvWaves = 4;           // wavefronts per workgroup
 constexpr uint32_t kGemvOob = 0x40000000u;  // an offset past any operand here: the load returns zeros
 
 // Buffer descriptor over weight rows [n0, n0 + rows) of a [N, row_bytes] matrix.
+// n0 and rows are the same in every lane of the wavefront; the fields go
+// through readfirstlane so that the compiler keeps the descriptor in scalar
+// registers (a descriptor it cannot prove uniform costs a loop around every
+// load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t gemv_rows_rsrc(const int8_t *base, int n0, int rows,
                                                                  int row_bytes) {
-    const int8_t *p = rows > 0 ? base + (int64_t)n0 * row_bytes : base;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(p), (short)0, rows > 0 ? rows * row_bytes : 0,
+    const uint64_t p = reinterpret_cast<uint64_t>(rows > 0 ? base + (int64_t)n0 * row_bytes : base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const int nrec = __builtin_amdgcn_readfirstlane(rows > 0 ? rows * row_bytes : 0);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), (short)0, nrec,
                                              0x00020000);
 }
 
