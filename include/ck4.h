@@ -325,8 +325,8 @@ ck4_status ck4_linear_w4a8_grouped(const int8_t *x_q8, const float *x_scales, co
  * ck4_rotate_quantize_act(bits = 8) followed by ck4_linear_w4a8_grouped (or
  * its E4M3 form) with chunk_cols = 0, and the same results bit for bit:
  * x_q8 [m, k] and x_scales [m] are written too (the caller's buffers), and y.
- * For m = 1 with rot_block 128, k <= 8192 and groups of 32 or more codes
- * (with E4M3 scales also n <= 8192) one kernel does it all: each workgroup
+ * For m = 1 with n <= 8192, rot_block 128, k <= 8192 and groups of 32 or
+ * more codes one kernel does it all: each workgroup
  * rotates and quantises the row into its own LDS while its weight loads are
  * in flight, which saves the quantiser's launch at decode sizes. Other
  * shapes run the quantiser, then the W4A8 linear, on `stream`.

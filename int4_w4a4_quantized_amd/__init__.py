@@ -483,7 +483,7 @@ def linear_w4a8_grouped_bf16(x: torch.Tensor, w_packed: torch.Tensor, group_scal
     x_scales fp32 [m]).
 
     Bitwise rotate_quantize_act(x, rot_block, 8) followed by linear_w4a8_grouped(..., chunk_cols=0);
-    for m = 1 (rot_block 128, k <= 8192, groups of 32 or more) one kernel does both. group_scales:
+    for m = 1 (n <= 8192, rot_block 128, k <= 8192, groups of 32 or more) one kernel does both. group_scales:
     fp32, or uint8 holding E4M3 bytes."""
     _typed(x, torch.bfloat16, "x", 2)
     m, k = x.shape

@@ -42,8 +42,8 @@ hipError_t launch_w4a8_gemv(const int8_t *x_q8, const float *x_scales, const int
 // The whole grouped W4A8 layer from bf16 activations in one launch (rotate
 // with 128-blocks, quantise to int8 with s = absmax / 127, then the
 // matrix-vector W4A8 product) for the shapes w4a8_layer_fits takes (m = 1,
-// rot_block 128, 256 <= k <= 8192, k % 128 == 0, groups of 32 or more
-// codes, no codebook; with E4M3 scales n <= 8192). Writes x_q8 [m, k] and
+// n <= 8192, rot_block 128, 256 <= k <= 8192, k % 128 == 0, groups of 32 or
+// more codes, no codebook). Writes x_q8 [m, k] and
 // x_scales [m] as the quantiser does, and y, bitwise as the quantiser
 // followed by the W4A8 linear.
 bool w4a8_layer_fits(int64_t m, int64_t n, int64_t k, int rot_block, int group, bool codebook, bool scale_e4m3);

@@ -360,16 +360,18 @@ hipError_t launch_w4a8_gemv(const int8_t *x_q8, const float *x_scales, const int
 }
 
 // One-call layer against the quantiser + the W4A8 linear (32 weight copies in
-// turn, groups of 128): with one activation row it is faster on every shape
-// measured (N = K = 5120: 9.5 against 11.2 us; N = 12288, K = 3072: 12.1
-// against 13.8; N = 4096, K = 1024: 4.5 against 6.5), except E4M3 scales at
-// N = 12288, where the product's E4M3 decode loses what the launch saves;
-// with two rows the quantisation repeated per workgroup costs more than the
-// quantiser's launch (N = K = 5120: 13.7 against 12.0). Workgroups of eight
-// wavefronts measured faster than of sixteen on four of the five shapes.
+// turn, groups of 128): with one activation row it is faster up to N = 8192
+// (N = K = 5120: 10.2 against 11.2 us; N = 8192, K = 3072: 9.3 against
+// 11.0; N = 4096, K = 2048: 4.7 against 7.1); at N = 12288, K = 3072 the
+// product's table decode loses more than the launch saves (13.4 against
+// 12.7). With two rows the quantisation repeated per workgroup costs what
+// the quantiser's launch saves (N = K = 5120: 12.1 against 12.0).
+// Workgroups of eight wavefronts measured faster than of sixteen on four of
+// five shapes.
 bool w4a8_layer_fits(int64_t m, int64_t n, int64_t k, int rot_block, int group, bool codebook, bool scale_e4m3) {
-    if (codebook || m != 1 || rot_block != 128 || group < 32 || k < 256 || k % 128 != 0 || k > 8192) return false;
-    return !scale_e4m3 || n <= 8192;
+    (void)scale_e4m3;
+    return !codebook && m == 1 && n <= 8192 && rot_block == 128 && group >= 32 && k >= 256 && k % 128 == 0 &&
+           k <= 8192;
 }
 
 hipError_t launch_w4a8_layer(const uint16_t *x, int64_t ldx, const int8_t *w_packed, const void *group_scales,

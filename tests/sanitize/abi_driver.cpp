@@ -78,8 +78,8 @@ hipError_t launch_w4a8_gemv(const int8_t *, const float *, const int8_t *, const
                             int64_t, int, uint16_t *, int64_t, hipStream_t) {
     return ++g_launches, hipSuccess;
 }
-bool w4a8_layer_fits(int64_t m, int64_t, int64_t k, int rot_block, int group, bool codebook, bool) {
-    return !codebook && m == 1 && rot_block == 128 && group >= 32 && k <= 8192;
+bool w4a8_layer_fits(int64_t m, int64_t n, int64_t k, int rot_block, int group, bool codebook, bool) {
+    return !codebook && m == 1 && n <= 8192 && rot_block == 128 && group >= 32 && k <= 8192;
 }
 hipError_t launch_w4a8_layer(const uint16_t *, int64_t, const int8_t *, const void *, bool, int64_t, int64_t,
                              int64_t, int, int8_t *, float *, uint16_t *, int64_t, hipStream_t) {
@@ -243,6 +243,8 @@ int main(int argc, char **argv) {
     // quantiser and the W4A8 linear (fused for m <= 64: two launches)
     VALID(ck4_linear_w4a8_grouped_bf16(U16, 1, 3072, 3072, 128, I8, F, 0, 5120, 128, I8, F, U16, 5120, nullptr, 0,
                                        nullptr), 1);
+    VALID(ck4_linear_w4a8_grouped_bf16(U16, 1, 3072, 3072, 128, I8, F, 0, 12288, 128, I8, F, U16, 12288, nullptr, 0,
+                                       nullptr), 2);
     VALID(ck4_linear_w4a8_grouped_bf16(U16, 1, 384, 392, 128, I8, F, 1, 5, 128, I8, F, U16, 8, nullptr, 0, nullptr),
           1);
     VALID(ck4_linear_w4a8_grouped_bf16(U16, 2, 384, 392, 128, I8, F, 1, 5, 128, I8, F, U16, 8, nullptr, 0, nullptr),

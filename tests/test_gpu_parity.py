@@ -778,12 +778,12 @@ def test_linear_w4a4_bf16_equals_two_calls_and_oracle(ck, m, n, k, special, with
 
 
 W4A8_LAYER_CASES = [
-    # one kernel (m = 1, k <= 8192, groups >= 32; E4M3 scales up to n = 8192): 1-4 chunks per lane and
-    # row, ragged n and k, fp32 and E4M3 group scales; the row all zero, tiny or one 128-block of 1e36
-    (1, 5120, 5120, 128, False, None), (1, 5120, 5120, 64, True, "zero"), (1, 12288, 3072, 128, False, None),
+    # one kernel (m = 1, n <= 8192, k <= 8192, groups >= 32): 1-4 chunks per lane and row, ragged n and
+    # k, fp32 and E4M3 group scales; the row all zero, tiny or one 128-block of 1e36
+    (1, 5120, 5120, 128, False, None), (1, 5120, 5120, 64, True, "zero"), (1, 8192, 3072, 128, False, None),
     (1, 77, 256, 32, False, "tiny"), (1, 17, 384, 128, True, None), (1, 8200, 8192, 256, False, "huge"),
     (1, 999, 1152, 128, True, "huge"), (1, 3, 2176, 128, False, None), (1, 4100, 6144, 1024, False, "tiny"),
-    # quantiser + W4A8 linear: m > 1, groups below 32, k > 8192, E4M3 scales with n > 8192
+    # quantiser + W4A8 linear: m > 1, groups below 32, k > 8192, n > 8192
     (2, 5120, 5120, 64, True, "zero"), (2, 999, 1152, 128, False, "huge"), (3, 1000, 1024, 128, False, None),
     (1, 500, 1024, 16, False, None), (1, 300, 12288, 128, True, None), (1, 12288, 3072, 128, True, None),
     (17, 640, 768, 64, False, None),
