@@ -17,8 +17,9 @@
 // owned by thread c mod T of the row's T threads. A row of up to 4096
 // elements belongs to one wavefront (T = 64, four rows per workgroup), so its
 // absmax needs no barrier and every row of a 4608-row batch is resident at
-// once; a longer row, or any row of 2048 elements or more in a batch of at
-// most 1024 rows, belongs to a whole workgroup (T = blockDim). A Hadamard
+// once; a longer row, or a row of 2048 elements or more in a batch of at
+// most 2048 rows, of 4096 elements, or quantised to FP6 codes, belongs to a
+// whole workgroup (T = blockDim). A Hadamard
 // block of b elements is b/16 consecutive chunks, which sit in b/16
 // consecutive lanes of one wavefront (T is a multiple of 64 and b <= 1024).
 // Butterfly strides 1..8 are inside a lane; stride 16*m pairs lane L with
@@ -417,13 +418,17 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
                         void *out, int64_t ldo, float *scales, WeightOpts wo, hipStream_t stream) {
     const int nchunks = (int)(k / kElems);
     // A row fits one wavefront when it is at most 64 lanes x kMaxChunks
-    // chunks. With few rows the GPU is mostly idle and each row's latency
-    // chain (loads, butterflies, absmax, codes) is the time, so rows of 128
-    // chunks or more are spread over a workgroup of up to four wavefronts
-    // instead (same arithmetic, same bits; measured at 1-1024 rows: K = 3072
-    // 4.1-4.9 -> 2.6-3.7 us, K = 4096 5.7-6.9 -> 2.7-4.1 us; K = 1024 and
-    // rows beyond 1024 gain nothing).
-    const bool wave_row = nchunks <= 64 * kMaxChunks && !(rows <= 1024 && nchunks >= 128);
+    // chunks. Rows of 128 chunks or more are spread over a workgroup of up to
+    // four wavefronts instead (same arithmetic, same bits) where that
+    // measured faster: with few rows, where the GPU is mostly idle and each
+    // row's latency chain (loads, butterflies, absmax, codes) is the time
+    // (K = 3072, 1-2048 rows: 4.1-5.2 -> 2.6-4.7 us); at 256 chunks (K =
+    // 4096: 4608 rows 11.6 -> 11.3 us); and for the FP6 codes at any count
+    // (K = 3072, 4608 rows: 9.8 -> 9.5 us). Packed int4 codes of 4608 rows at
+    // K = 3072 stay a wavefront per row (8.4 against 8.5 us); K = 1024 gains
+    // nothing.
+    const bool wg_row = nchunks >= 128 && (rows <= 2048 || nchunks >= 256 || out_kind == 4);
+    const bool wave_row = nchunks <= 64 * kMaxChunks && !wg_row;
     const int per_thread = wave_row ? (nchunks + 63) / 64 : (nchunks + kThreads - 1) / kThreads;  // 1..kMaxChunks
     const float c = (float)(1.0 / __builtin_sqrt((double)rot_block));
     const int lanes_per_block = rot_block / kElems;
