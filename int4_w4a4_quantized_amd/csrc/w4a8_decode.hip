@@ -15,6 +15,8 @@
 //
 // One workgroup per output row: the row scale is a workgroup max-reduction
 // over that row's group scales, then each lane decodes 16-element chunks.
+// Groups of 32 codes or more with rows of up to 8192 codes take a wavefront
+// per row instead (w4a8_decode_rows_kernel below).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -97,11 +99,95 @@ void launch_decode_typed(const int8_t *w_packed, const void *group_scales, int64
             w_packed, group_scales, (int)k, group, n0, w8, row_scales, cb);
 }
 
+// The same decode with a wavefront per row, for groups of 32 codes or more
+// and rows of up to 8192 codes: lane l takes the 32-code chunks l, l + 64,
+// ... (CPL of them), one 16-byte load of codes and one group-scale load
+// each, all issued before the first is used; since every group has a chunk,
+// the wavefront maximum of the lane's scales is the row's, with no barrier.
+// A chunk's 16 possible int8 codes are tabulated once for its multiplier
+// with the same fp32 steps (w4a8_codes.h) and looked up per code, and its 32
+// codes leave as two 16-byte stores. Four rows per workgroup.
+template <int CPL, bool E4M3>
+__global__ __launch_bounds__(256) void w4a8_decode_rows_kernel(const int8_t *__restrict__ wp,
+                                                               const void *__restrict__ gs, int k, int group,
+                                                               int64_t n0, int nc, int8_t *__restrict__ w8,
+                                                               float *__restrict__ row_scales) {
+    constexpr int SB = E4M3 ? 1 : 4;  // bytes per group scale
+    constexpr uint32_t kOob = 0x40000000u;  // beyond any row here: the load returns zeros
+    const int lane = threadIdx.x & 63;
+    const int i = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (i >= nc) return;  // whole wavefronts; no barrier in this kernel
+    const int64_t row = n0 + i;
+    const int row_bytes = k / 2;
+    const int nch = k / 32;
+    const int ng = k / group;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(static_cast<const int8_t *>(gs) + row * ng * SB), (short)0, ng * SB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(wp + row * row_bytes), (short)0, row_bytes, 0x00020000);
+    float sg[CPL];
+    uint4 w[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;  // chunk c of 32 codes lies in group 32 c / group
+        const uint32_t off = c < nch ? (uint32_t)(((32 * c) / group) * SB) : kOob;
+        if constexpr (E4M3) sg[j] = e4m3_decode(__builtin_amdgcn_raw_buffer_load_b8(rs, off, 0, 0));
+        else sg[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        typedef int v4i_d __attribute__((ext_vector_type(4)));
+        const v4i_d t = __builtin_amdgcn_raw_buffer_load_b128(rb, c < nch ? (uint32_t)c * 16u : kOob, 0, 0);
+        w[j] = make_uint4((uint32_t)t.x, (uint32_t)t.y, (uint32_t)t.z, (uint32_t)t.w);
+    }
+    float smax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) smax = fmaxf(smax, sg[j]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
+    const float srow = (smax * 7.0f) / 127.0f;
+    if (lane == 0) row_scales[i] = srow;
+    int8_t *dst = w8 + (int64_t)i * k;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = lane + 64 * j;
+        if (c >= nch) continue;
+        const uint4 tab = code_table(srow == 0.0f ? 0.0f : sg[j] / srow);
+        const uint2 d0 = decode8_table(w[j].x, tab), d1 = decode8_table(w[j].y, tab);
+        const uint2 d2 = decode8_table(w[j].z, tab), d3 = decode8_table(w[j].w, tab);
+        *reinterpret_cast<uint4 *>(dst + c * 32) = make_uint4(d0.x, d0.y, d1.x, d1.y);
+        *reinterpret_cast<uint4 *>(dst + c * 32 + 16) = make_uint4(d2.x, d2.y, d3.x, d3.y);
+    }
+}
+
+template <int CPL>
+void launch_decode_rows(const int8_t *w_packed, const void *group_scales, bool scale_e4m3, int64_t k, int group,
+                        int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream) {
+    const dim3 grid((unsigned)((nc + 3) / 4)), block(256);
+    if (scale_e4m3)
+        w4a8_decode_rows_kernel<CPL, true><<<grid, block, 0, stream>>>(w_packed, group_scales, (int)k, group, n0,
+                                                                       (int)nc, w8, row_scales);
+    else
+        w4a8_decode_rows_kernel<CPL, false><<<grid, block, 0, stream>>>(w_packed, group_scales, (int)k, group, n0,
+                                                                        (int)nc, w8, row_scales);
+}
+
 }  // namespace
 
 hipError_t launch_w4a8_decode(const int8_t *w_packed, const void *group_scales, bool scale_e4m3, int64_t k, int group,
                               int64_t n0, int64_t nc, int8_t *w8, float *row_scales, hipStream_t stream,
                               const Codebook &cb) {
+    if (!cb.on && group >= 32 && k % 128 == 0 && k <= 8192) {
+        // the wavefront-per-row form (chunks of 32 codes in one group)
+        switch ((k / 32 + 63) / 64) {
+        case 1: launch_decode_rows<1>(w_packed, group_scales, scale_e4m3, k, group, n0, nc, w8, row_scales, stream); break;
+        case 2: launch_decode_rows<2>(w_packed, group_scales, scale_e4m3, k, group, n0, nc, w8, row_scales, stream); break;
+        case 3: launch_decode_rows<3>(w_packed, group_scales, scale_e4m3, k, group, n0, nc, w8, row_scales, stream); break;
+        default: launch_decode_rows<4>(w_packed, group_scales, scale_e4m3, k, group, n0, nc, w8, row_scales, stream); break;
+        }
+        return hipGetLastError();
+    }
     if (scale_e4m3)
         launch_decode_typed<true>(w_packed, group_scales, k, group, n0, nc, w8, row_scales, stream, cb);
     else
