@@ -8,9 +8,12 @@ before timing (offline weight prep). Workload: 4608 tokens through a 3072 x
 3072 projection (M=4608, K=N=3072, Hadamard block 128), bf16 activations drawn
 N(0,1) with 1 % outlier channels x20, weights N(0, 0.02).
 
-The layer runs on two bit-identical paths: the int4 codes as exact FP6
-E2M3 operands of the FP6 matrix cores (the headline step) and the packed-int4
-path on the int8 matrix cores (reported beside it).
+The layer runs on three bit-identical paths: the int4 codes as exact FP6
+E2M3 operands of the FP6 matrix cores, stored compact (4 bits a code,
+expanded in registers) or as the full 6-bit operand image, and the
+packed-int4 path on the int8 matrix cores. The headline is the faster of
+the two FP6 paths (named in ``config.path``); the others are reported beside
+it.
 
 Prints one JSON line. ``value`` is the layer's int4-op throughput in TOP/s
 (2 M N K per step / step time; the K steps are one HIP graph replay between
@@ -41,9 +44,11 @@ METRIC = "W4A4 linear TOPS & ms/layer (quantize+GEMM), M=4608 K=N=3072; % int8 M
 INT8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POP/s
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, 8 TB/s
 FP6_PEAK_TOPS = 10100.0     # MI355X dense FP6/FP4 MFMA, 10.1 PFLOP/s
+# per path: the HBM traffic digest of its GEMM and the kernel source it was taken on
 TRAFFIC_FILES = {
-    "gemm_fp6.hip": os.path.join(ROOT, "profiles", "gemm_w4a4_fp6_square_3072_traffic.json"),
-    "gemm.hip": os.path.join(ROOT, "profiles", "gemm_w4a4_square_3072_traffic.json"),
+    "fp6c": (os.path.join(ROOT, "profiles", "gemm_w4a4_fp6c_square_3072_traffic.json"), "gemm_fp6.hip"),
+    "fp6": (os.path.join(ROOT, "profiles", "gemm_w4a4_fp6_square_3072_traffic.json"), "gemm_fp6.hip"),
+    "int4": (os.path.join(ROOT, "profiles", "gemm_w4a4_square_3072_traffic.json"), "gemm.hip"),
 }
 
 
@@ -70,10 +75,11 @@ def _kernel_source_digest(source: str) -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic_for_current_kernel(source: str):
-    """Measured HBM bytes per GEMM launch, if taken on the current kernel source."""
+def _traffic_for_current_kernel(path: str):
+    """Measured HBM bytes per GEMM launch of a path, if taken on the current kernel source."""
+    fname, source = TRAFFIC_FILES[path]
     try:
-        with open(TRAFFIC_FILES[source]) as f:
+        with open(fname) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -382,7 +388,15 @@ def layer_sweep(ck, torch, args) -> int:
             ck.rotate_quantize_act_fp6(x, 128, out=xq6, scales=sx)
             ck.linear_w4a4_fp6(xq6, sx, wq6, ws6, None, out=y)
         line(f"w4a4 layer {name}, FP6 operands", lay.m, lay.n, lay.k, graph_ms(step6, reps))
-        del x, wq6, ws6, xq6, sx, y, lay
+        del wq6, ws6, xq6
+        wqc, wsc = ck.quantize_weight_convrot_fp6c(torch.from_numpy(lay.weights[0]).to(dev), 128)
+        xqc = torch.empty((lay.m, lay.k // 2), dtype=torch.uint8, device=dev)
+
+        def stepc():
+            ck.rotate_quantize_act_fp6c(x, 128, out=xqc, scales=sx)
+            ck.linear_w4a4_fp6c(xqc, sx, wqc, wsc, None, out=y)
+        line(f"w4a4 layer {name}, compact FP6 operands", lay.m, lay.n, lay.k, graph_ms(stepc, reps))
+        del x, wqc, wsc, xqc, sx, y, lay
 
     # Weight preparation (offline, HBM-bound): nearest and stochastic rounding
     # of the up projection's weight, N=12288 x K=3072.
@@ -433,7 +447,18 @@ def layer_sweep(ck, torch, args) -> int:
     if want("qkv"):
         line("w4a4 q/k/v, one shared activation quantisation, FP6 operands", m, n, k, graph_ms(qkv_reuse6, reps),
              3)
-    del wts6, xq6, ys
+    del wts6, xq6
+    wtsc = [ck.quantize_weight_convrot_fp6c(torch.from_numpy(w).to(dev), 128) for w in lay.weights]
+    xqc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+
+    def qkv_reusec():
+        ck.rotate_quantize_act_fp6c(x, 128, out=xqc, scales=sx)
+        for (wqc, wsc), y in zip(wtsc, ys):
+            ck.linear_w4a4_fp6c(xqc, sx, wqc, wsc, None, out=y)
+    if want("qkv"):
+        line("w4a4 q/k/v, one shared activation quantisation, compact FP6 operands", m, n, k,
+             graph_ms(qkv_reusec, reps), 3)
+    del wtsc, xqc, ys
 
     wd = torch.from_numpy(lay.weights[0]).to(dev)
     w8, ws8 = ck.quantize_weight_convrot_int8(wd)
@@ -601,18 +626,23 @@ def main() -> int:
     w = torch.from_numpy(lay.weights[0]).to(dev)
     stream = torch.cuda.current_stream(dev)
 
-    # Two implementations of the same layer, bit for bit: the int4 codes fed
-    # to the FP6 matrix cores (as exact E2M3 values q / 8, twice the int8
-    # rate) and the packed-int4 path on the int8 matrix cores. The headline
-    # (`value`, `roofline`) is the FP6 path, the faster of the two on this
-    # shape; the int4 path is timed the same way and reported beside it.
+    # Three implementations of the same layer, bit for bit: the int4 codes
+    # fed to the FP6 matrix cores (as exact E2M3 values q / 8, twice the int8
+    # rate) from compact operands (4 bits a code, expanded in registers) or
+    # from the full 6-bit operand image, and the packed-int4 path on the int8
+    # matrix cores. The headline (`value`, `roofline`) is the faster FP6
+    # path; the others are timed the same way and reported beside it.
+    wqc, wsc = ck.quantize_weight_convrot_fp6c(w, 128)
     wq6, ws6 = ck.quantize_weight_convrot_fp6(w, 128)
     wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+    xqc = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
     xq6 = torch.empty((m, k * 3 // 4), dtype=torch.uint8, device=dev)
     xq = torch.empty((m, k // 2), dtype=torch.int8, device=dev)
     sx = torch.empty((m,), dtype=torch.float32, device=dev)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     paths = {
+        "fp6c": (lambda: ck.rotate_quantize_act_fp6c(x, 128, out=xqc, scales=sx),
+                 lambda: ck.linear_w4a4_fp6c(xqc, sx, wqc, wsc, None, out=y)),
         "fp6": (lambda: ck.rotate_quantize_act_fp6(x, 128, out=xq6, scales=sx),
                 lambda: ck.linear_w4a4_fp6(xq6, sx, wq6, ws6, None, out=y)),
         "int4": (lambda: ck.rotate_quantize_act(x, 128, 4, out=xq, scales=sx),
@@ -626,9 +656,10 @@ def main() -> int:
         gemm()
         torch.cuda.synchronize()
         ref[name] = y.clone()
-    if not torch.equal(ref["fp6"].view(torch.int16), ref["int4"].view(torch.int16)):
-        print("bench.py: the FP6 and int4 paths disagree", file=sys.stderr)
-        return 1
+    for name in ("fp6c", "fp6"):
+        if not torch.equal(ref[name].view(torch.int16), ref["int4"].view(torch.int16)):
+            print(f"bench.py: the {name} and int4 paths disagree", file=sys.stderr)
+            return 1
 
     # The host launch path (Python + ctypes + HIP) costs about as much as a
     # step, so the K timed steps are captured in one HIP graph and replayed
@@ -670,6 +701,7 @@ def main() -> int:
         g_warm.replay()
         torch.cuda.synchronize()
         # clear the outputs so that the check below sees the timed replay's work
+        xqc.zero_()
         xq6.zero_()
         xq.zero_()
         sx.zero_()
@@ -702,16 +734,48 @@ def main() -> int:
         }
 
     ops = 2.0 * m * n * k
-    r6, r4 = res["fp6"], res["int4"]
-    tops = ops / (r6["ms_per_step"] * 1e-3) / 1e12
-    tops4 = ops / (r4["ms_per_step"] * 1e-3) / 1e12
-    gemm_tops = ops / (r6["gemm_ms"] * 1e-3) / 1e12
-    gemm4_tops = ops / (r4["gemm_ms"] * 1e-3) / 1e12
-    quant6_bytes = m * k * 2 + m * k * 3 // 4 + m * 4
-    quant4_bytes = m * k * 2 + m * k // 2 + m * 4
-    gemm6_bytes = m * k * 3 // 4 + n * k * 3 // 4 + m * 4 + n * 4 + m * n * 2
-    gemm4_bytes = m * k // 2 + n * k // 2 + m * 4 + n * 4 + m * n * 2
+    head = min(("fp6c", "fp6"), key=lambda p: res[p]["ms_per_step"])
+    quant_bytes = {"fp6c": m * k * 2 + m * k // 2 + m * 4, "fp6": m * k * 2 + m * k * 3 // 4 + m * 4,
+                   "int4": m * k * 2 + m * k // 2 + m * 4}
+    gemm_bytes = {"fp6c": m * k // 2 + n * k // 2 + m * 4 + n * 4 + m * n * 2,
+                  "fp6": m * k * 3 // 4 + n * k * 3 // 4 + m * 4 + n * 4 + m * n * 2,
+                  "int4": m * k // 2 + n * k // 2 + m * 4 + n * 4 + m * n * 2}
+    kernel_names = {
+        "fp6c": "gemm_fp6_kernel<288x192 tile, 8 waves, compact operands> (W4A4 GEMM on FP6 MFMA + rank-one "
+                "epilogue)",
+        "fp6": "gemm_fp6_kernel<288x192 tile, 8 waves> (W4A4 GEMM on FP6 MFMA + rank-one epilogue)",
+        "int4": "gemm_big_kernel<288x192 tile, 8 waves> (W4A4 GEMM on int8 MFMA + rank-one epilogue)",
+    }
+    path_desc = {
+        "fp6c": "int4 codes as exact FP6 E2M3 MFMA operands, stored compact (4 bits a code, expanded in "
+                "registers); bit-identical to the int8-MFMA path",
+        "fp6": "int4 codes as exact FP6 E2M3 MFMA operands (6-bit operand image); bit-identical to the "
+               "int8-MFMA path",
+    }
 
+    def tops_of(ms):
+        return ops / (ms * 1e-3) / 1e12
+
+    def path_summary(p):
+        r = res[p]
+        return {
+            "ms_per_step": round(r["ms_per_step"], 5),
+            "TOPS": round(tops_of(r["ms_per_step"]), 2),
+            "pct_int8_peak": round(100.0 * tops_of(r["ms_per_step"]) / INT8_PEAK_TOPS, 2),
+            "rotate_quant_ms": round(r["quant_ms"], 5),
+            "rotate_quant_GBps": round(quant_bytes[p] / (r["quant_ms"] * 1e-3) / 1e9, 1),
+            "gemm_ms": round(r["gemm_ms"], 5),
+            "gemm_TOPS": round(tops_of(r["gemm_ms"]), 2),
+            "gemm_pct_int8_peak": round(100.0 * tops_of(r["gemm_ms"]) / INT8_PEAK_TOPS, 2),
+            "gemm_traffic": _traffic_for_current_kernel(p),
+            "gemm_algorithmic_bytes": gemm_bytes[p],
+            "spread_ms_per_step_min": round(min(r["spread"]), 5),
+            "spread_ms_per_step_median": round(statistics.median(r["spread"]), 5),
+        }
+
+    rh = res[head]
+    tops = tops_of(rh["ms_per_step"])
+    gemm_tops = tops_of(rh["gemm_ms"])
     out = {
         "metric": METRIC,
         "value": round(tops, 2),
@@ -719,8 +783,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r6["ms_per_step"], 5),
-        "wall_ms_per_step": round(r6["wall_ms_per_step"], 5),
+        "ms_per_step": round(rh["ms_per_step"], 5),
+        "wall_ms_per_step": round(rh["wall_ms_per_step"], 5),
         "clock_warmup_s": args.clock_warmup,
         "higher_is_better": True,
         "scaling": "weak",
@@ -729,44 +793,32 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "square_3072 (W4A4 ConvRot linear M=4608 K=3072 N=3072, Hadamard block 128)",
                    "m": m, "k": k, "n": n, "rot_block": 128, "parallelism": "single GPU",
-                   "path": "int4 codes as exact FP6 E2M3 MFMA operands (bit-identical to the int8-MFMA path)"},
+                   "path": path_desc[head]},
         "pct_int8_peak": round(100.0 * tops / INT8_PEAK_TOPS, 2),
         "roofline": {
             "bound": "mfma",
-            "kernel": "gemm_fp6_kernel<288x192 tile, 8 waves> (W4A4 GEMM on FP6 MFMA + rank-one epilogue)",
+            "kernel": kernel_names[head],
             "achieved": round(gemm_tops, 2),
             "peak": FP6_PEAK_TOPS,
             "unit": "TOP/s",
             "frac": round(gemm_tops / FP6_PEAK_TOPS, 4),
-            "traffic": _traffic_for_current_kernel("gemm_fp6.hip"),
-            "algorithmic_bytes": gemm6_bytes,
-            "avg_kernel_ms": round(r6["gemm_ms"], 5),
-            "note": "peak = dense FP6 MFMA; the kernel is bound by its global->LDS copies (each CU re-reads "
-                    "its 288 + 192 operand rows: 283 MB per launch from L2)",
+            "traffic": _traffic_for_current_kernel(head),
+            "algorithmic_bytes": gemm_bytes[head],
+            "avg_kernel_ms": round(rh["gemm_ms"], 5),
+            "note": "peak = dense FP6 MFMA; the kernel is bound by its global->LDS copies (each CU copies "
+                    "its 288 + 192 operand rows from L2: %.0f MB per launch)"
+                    % (256 * 480 * k * (0.5 if head == "fp6c" else 0.75) / 1e6),
         },
         "kernels": {
-            "rotate_quant_fp6_ms": round(r6["quant_ms"], 5),
-            "rotate_quant_fp6_GBps": round(quant6_bytes / (r6["quant_ms"] * 1e-3) / 1e9, 1),
-            "gemm_fp6_ms": round(r6["gemm_ms"], 5),
-            "gemm_fp6_TOPS": round(gemm_tops, 2),
-            "gemm_fp6_pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
+            "rotate_quant_ms": round(rh["quant_ms"], 5),
+            "rotate_quant_GBps": round(quant_bytes[head] / (rh["quant_ms"] * 1e-3) / 1e9, 1),
+            "gemm_ms": round(rh["gemm_ms"], 5),
+            "gemm_TOPS": round(gemm_tops, 2),
+            "gemm_pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
         },
-        "int4_path": {
-            "ms_per_step": round(r4["ms_per_step"], 5),
-            "TOPS": round(tops4, 2),
-            "pct_int8_peak": round(100.0 * tops4 / INT8_PEAK_TOPS, 2),
-            "rotate_quant_ms": round(r4["quant_ms"], 5),
-            "rotate_quant_hbm_frac": round(quant4_bytes / (r4["quant_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "gemm_ms": round(r4["gemm_ms"], 5),
-            "gemm_TOPS": round(gemm4_tops, 2),
-            "gemm_frac_int8_peak": round(gemm4_tops / INT8_PEAK_TOPS, 4),
-            "gemm_traffic": _traffic_for_current_kernel("gemm.hip"),
-            "gemm_algorithmic_bytes": gemm4_bytes,
-        },
-        "spread": {"batches": 5, "steps_per_batch": 100, "ms_per_step_min": round(min(r6["spread"]), 5),
-                   "ms_per_step_median": round(statistics.median(r6["spread"]), 5),
-                   "int4_ms_per_step_min": round(min(r4["spread"]), 5),
-                   "int4_ms_per_step_median": round(statistics.median(r4["spread"]), 5)},
+        "paths": {p: path_summary(p) for p in ("fp6c", "fp6", "int4")},
+        "spread": {"batches": 5, "steps_per_batch": 100, "ms_per_step_min": round(min(rh["spread"]), 5),
+                   "ms_per_step_median": round(statistics.median(rh["spread"]), 5)},
         "peaks": _device_peaks(torch, sclk_mhz),
         "context": {"L4_ms_per_layer_same_shape": 0.54, "note": "another machine's number; context only"},
     }

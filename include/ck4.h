@@ -250,6 +250,37 @@ ck4_status ck4_linear_w4a4_fp6(const uint8_t *x_q6, const float *x_scales, const
 ck4_status ck4_gemm_w4a4_fp6_acc_i32(const uint8_t *x_q6, const uint8_t *w_q6, int64_t m, int64_t n, int64_t k,
                                      int32_t *acc, int64_t ldacc, void *stream);
 /*
+ * Compact FP6 operand layout ("q6c", ck4_fp6c_bytes(rows, k) = rows16 * k / 2
+ * bytes, 16-byte aligned): the q6 image with the two exponent bits of every
+ * code, always zero for |q| <= 7, squeezed out, so the matrix cores are fed
+ * from two thirds of the bytes. Blocks (r / 16, k / 128) of 1024 bytes at
+ * ((r / 16) * (k / 128) + k / 128) * 1024; row i and k group g own the 16
+ * bytes at 16 (16 g + i). Let W be the 96-bit q6 image of the codes of
+ * t = 0-15 (then of t = 16-31) with dwords V0 = W[0:32), V1 = W[32:64),
+ * V2 = W[64:96). Its two dwords (little-endian, bytes 0-7, then 8-15) are
+ *   D0 = V0 | (V1 & 0x18618618),  D1 = V2 | (V1 & 0x61861861);
+ * the masks are the zero exponent bits of V0 and of V2, and V1's data bits
+ * sit exactly at their union, so V0 = D0 & ~0x18618618,
+ * V2 = D1 & ~0x61861861, V1 = (D0 & 0x18618618) | (D1 & 0x61861861).
+ *
+ * ck4_rotate_quantize_act_fp6c, ck4_quantize_weight_convrot_fp6c,
+ * ck4_linear_w4a4_fp6c, ck4_gemm_w4a4_fp6c_acc_i32: the four q6 calls above on
+ * q6c operands, with the same arguments, bits, alignment and errors
+ * ("[PR #63] int4_tensorwise: W4A4 layout (+ConvRot) with fused CUDA
+ * kernels", Description: the same per-row quantisation and s4.s4 GEMM).
+ * ck4_fp6c_bytes returns 0 for k not a multiple of 128.
+ */
+size_t ck4_fp6c_bytes(int64_t rows, int64_t k);
+ck4_status ck4_rotate_quantize_act_fp6c(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                        uint8_t *x_q6c, float *x_scales, void *stream);
+ck4_status ck4_quantize_weight_convrot_fp6c(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                            uint8_t *w_q6c, float *w_scales, void *stream);
+ck4_status ck4_linear_w4a4_fp6c(const uint8_t *x_q6c, const float *x_scales, const uint8_t *w_q6c,
+                                const float *w_scales, const float *bias, int64_t m, int64_t n, int64_t k,
+                                uint16_t *y, int64_t ldy, void *stream);
+ck4_status ck4_gemm_w4a4_fp6c_acc_i32(const uint8_t *x_q6c, const uint8_t *w_q6c, int64_t m, int64_t n, int64_t k,
+                                      int32_t *acc, int64_t ldacc, void *stream);
+/*
  * The output tile (tile_m x tile_n, host ints) that ck4_linear_w4a4_fp6 and
  * ck4_gemm_w4a4_fp6_acc_i32 use for an m x n x k product: 288 x 192 with
  * eight waves, or 96 x 128 with four, whichever takes fewer estimated rounds

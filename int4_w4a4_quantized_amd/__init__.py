@@ -71,6 +71,11 @@ SIGNATURES = {
     "ck4_linear_w4a4_fp6": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_gemm_w4a4_fp6_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_gemm_fp6_tile": ([_I64, _I64, _I64, ctypes.POINTER(_I), ctypes.POINTER(_I)], _I),
+    "ck4_fp6c_bytes": ([_I64, _I64], ctypes.c_size_t),
+    "ck4_rotate_quantize_act_fp6c": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
+    "ck4_quantize_weight_convrot_fp6c": ([_P, _I64, _I64, _I64, _I, _P, _P, _P], _I),
+    "ck4_linear_w4a4_fp6c": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_gemm_w4a4_fp6c_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_linear_w4a4_fp6_lora": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_lora_prepare_down": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_lora_prepare_up": ([_P, _I64, _I64, _I64, _P, _P], _I),
@@ -168,16 +173,18 @@ def _out_checked(out, m: int, n: int, dtype=torch.bfloat16, name: str = "out") -
         raise ValueError(f"{name} must have shape {(m, n)}, got {tuple(out.shape)}")
 
 
-def _fp6_nbytes(rows: int, k: int) -> int:
-    return (rows + 15) // 16 * 16 * (k // 128) * 96
+def _fp6_nbytes(rows: int, k: int, compact: bool = False) -> int:
+    return (rows + 15) // 16 * 16 * (k // 128) * (64 if compact else 96)
 
 
-def _fp6_k(q6, name: str) -> int:
-    """k of an FP6 operand [rows16, 3k/4] (k a multiple of 128)."""
+def _fp6_k(q6, name: str, compact: bool = False) -> int:
+    """k of an FP6 operand [rows16, 3k/4], or of a compact one [rows16, k/2] (k a multiple of 128)."""
     _dense(q6, torch.uint8, name, 2)
-    if q6.shape[1] % 96 != 0:
-        raise ValueError(f"{name} has {q6.shape[1]} bytes per row: not 3k/4 for k a multiple of 128")
-    return q6.shape[1] * 4 // 3
+    per = 64 if compact else 96
+    if q6.shape[1] % per != 0:
+        form = "k/2" if compact else "3k/4"
+        raise ValueError(f"{name} has {q6.shape[1]} bytes per row: not {form} for k a multiple of 128")
+    return q6.shape[1] * 128 // per
 
 
 def _out_bf16(m: int, n: int, device) -> torch.Tensor:
@@ -617,17 +624,17 @@ def linear_w4a4_fp6(x_q6, x_scales, w_q6, w_scales, bias=None, out=None, m: int 
     return out
 
 
-def _check_fp6_gemm(x_q6, w_q6, m: int, n: int, x_scales, w_scales, bias, out) -> int:
-    """Operands of an FP6 GEMM wrapper; returns k."""
-    k = _fp6_k(x_q6, "x_q6")
-    if _fp6_k(w_q6, "w_q6") != k:
+def _check_fp6_gemm(x_q6, w_q6, m: int, n: int, x_scales, w_scales, bias, out, compact: bool = False) -> int:
+    """Operands of an FP6 (or compact FP6) GEMM wrapper; returns k."""
+    k = _fp6_k(x_q6, "x_q6", compact)
+    if _fp6_k(w_q6, "w_q6", compact) != k:
         raise ValueError(f"w_q6 rows hold {w_q6.shape[1]} bytes, x_q6 rows {x_q6.shape[1]}: k differs")
     if m <= 0 or n <= 0:
         raise ValueError("m and n must be positive")
-    if x_q6.numel() < _fp6_nbytes(m, k):
-        raise ValueError(f"x_q6 holds {x_q6.numel()} bytes, {m} rows need {_fp6_nbytes(m, k)}")
-    if w_q6.numel() < _fp6_nbytes(n, k):
-        raise ValueError(f"w_q6 holds {w_q6.numel()} bytes, {n} rows need {_fp6_nbytes(n, k)}")
+    if x_q6.numel() < _fp6_nbytes(m, k, compact):
+        raise ValueError(f"x_q6 holds {x_q6.numel()} bytes, {m} rows need {_fp6_nbytes(m, k, compact)}")
+    if w_q6.numel() < _fp6_nbytes(n, k, compact):
+        raise ValueError(f"w_q6 holds {w_q6.numel()} bytes, {n} rows need {_fp6_nbytes(n, k, compact)}")
     if x_scales is not None:
         _vec(x_scales, torch.float32, "x_scales", m)
     if w_scales is not None:
@@ -654,6 +661,77 @@ def w4a4_linear_fp6(x: torch.Tensor, w_q6: torch.Tensor, w_scales: torch.Tensor,
     """The whole layer on the FP6 path: rotate + quantise x to FP6 codes, then the GEMM + epilogue."""
     x_q6, sx = rotate_quantize_act_fp6(x, rot_block)
     return linear_w4a4_fp6(x_q6, sx, w_q6, w_scales, bias)
+
+
+# Compact FP6 operands: the same images without the two zero exponent bits
+# of each code, uint8 [rows16, k / 2] (ck4_fp6c_bytes); expanded in registers
+# before the MFMAs, with the FP6 path's results bit for bit.
+
+def fp6c_bytes(rows: int, k: int) -> int:
+    return int(lib().ck4_fp6c_bytes(rows, k))
+
+
+def rotate_quantize_act_fp6c(x: torch.Tensor, rot_block: int = 128, out=None, scales=None):
+    """bf16 [m, k] -> (uint8 [rows16(m), k/2] compact FP6 codes, fp32 [m] scales)."""
+    _typed(x, torch.bfloat16, "x", 2)
+    m, k = x.shape
+    if out is not None:
+        _vec(out, torch.uint8, "out", _fp6_nbytes(m, k, True))
+    if scales is not None:
+        _vec(scales, torch.float32, "scales", m)
+    _on_gpu(x=x, out=out, scales=scales)
+    if out is None:
+        out = torch.empty((_rows16(m), k // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((m,), dtype=torch.float32, device=x.device)
+    _check("ck4_rotate_quantize_act_fp6c",
+           lib().ck4_rotate_quantize_act_fp6c(_ptr(x), m, k, x.stride(0), rot_block, _ptr(out), _ptr(scales),
+                                              _stream(x.device)))
+    return out, scales
+
+
+def quantize_weight_convrot_fp6c(w: torch.Tensor, rot_block: int = 128):
+    """fp32 [n, k] -> (uint8 [rows16(n), k/2] compact FP6 codes, fp32 [n] row scales)."""
+    _need(w, torch.float32, "w", 2)
+    n, k = w.shape
+    wq = torch.empty((_rows16(n), k // 2), dtype=torch.uint8, device=w.device)
+    ws = torch.empty((n,), dtype=torch.float32, device=w.device)
+    _check("ck4_quantize_weight_convrot_fp6c",
+           lib().ck4_quantize_weight_convrot_fp6c(_ptr(w), n, k, w.stride(0), rot_block, _ptr(wq), _ptr(ws),
+                                                  _stream(w.device)))
+    return wq, ws
+
+
+def linear_w4a4_fp6c(x_q6c, x_scales, w_q6c, w_scales, bias=None, out=None, m: int | None = None,
+                     n: int | None = None):
+    """W4A4 GEMM + epilogue from compact FP6 operands -> bf16 [m, n]."""
+    _typed(x_scales, torch.float32, "x_scales")
+    _typed(w_scales, torch.float32, "w_scales")
+    m = x_scales.numel() if m is None else m
+    n = w_scales.numel() if n is None else n
+    k = _check_fp6_gemm(x_q6c, w_q6c, m, n, x_scales, w_scales, bias, out, compact=True)
+    if out is None:
+        out = _out_bf16(m, n, x_q6c.device)
+    _check("ck4_linear_w4a4_fp6c",
+           lib().ck4_linear_w4a4_fp6c(_ptr(x_q6c), _ptr(x_scales), _ptr(w_q6c), _ptr(w_scales), _ptr(bias), m, n, k,
+                                      _ptr(out), out.stride(0), _stream(x_q6c.device)))
+    return out
+
+
+def gemm_w4a4_fp6c_acc_i32(x_q6c, w_q6c, m: int, n: int):
+    """Integer accumulators of the compact FP6 GEMM -> int32 [m, n]."""
+    k = _check_fp6_gemm(x_q6c, w_q6c, m, n, None, None, None, None, compact=True)
+    acc = torch.empty((m, (n + 3) // 4 * 4), dtype=torch.int32, device=x_q6c.device)
+    _check("ck4_gemm_w4a4_fp6c_acc_i32",
+           lib().ck4_gemm_w4a4_fp6c_acc_i32(_ptr(x_q6c), _ptr(w_q6c), m, n, k, _ptr(acc), acc.stride(0),
+                                            _stream(x_q6c.device)))
+    return acc[:, :n]
+
+
+def w4a4_linear_fp6c(x: torch.Tensor, w_q6c: torch.Tensor, w_scales: torch.Tensor, bias=None, rot_block: int = 128):
+    """The whole layer on compact FP6 operands: rotate + quantise, then the GEMM + epilogue."""
+    x_q6c, sx = rotate_quantize_act_fp6c(x, rot_block)
+    return linear_w4a4_fp6c(x_q6c, sx, w_q6c, w_scales, bias)
 
 
 def lora_prepare_down(a: torch.Tensor, rot_block: int = 128):

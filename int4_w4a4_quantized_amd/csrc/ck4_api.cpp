@@ -333,8 +333,13 @@ size_t ck4_fp6_bytes(int64_t rows, int64_t k) {
     return (size_t)((rows + 15) / 16 * 16) * (size_t)(k / 128) * 96;
 }
 
+size_t ck4_fp6c_bytes(int64_t rows, int64_t k) {
+    if (rows <= 0 || rows > kMaxRows || k <= 0 || k > kMaxGemmK || k % 128 != 0) return 0;
+    return (size_t)((rows + 15) / 16 * 16) * (size_t)(k / 128) * 64;
+}
+
 static ck4_status quantize_fp6(const char *fn, const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx,
-                               int rot_block, uint8_t *q6, float *scales, void *stream) {
+                               int rot_block, uint8_t *q6, float *scales, void *stream, int out_kind = 4) {
     const size_t esz = in_kind == 0 ? 2 : 4;
     if (!x || !q6 || !scales) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (rows <= 0 || k <= 0) return fail(CK4_ERR_INVALID, "%s: rows and k must be positive", fn);
@@ -345,7 +350,7 @@ static ck4_status quantize_fp6(const char *fn, const void *x, int in_kind, int64
     if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
     if (ck4_status s = check_rot(fn, k, rot_block)) return s;
     if (ck4_status s = check_device(fn)) return s;
-    return launched(fn, ck4::launch_rotate_quant(x, in_kind, rows, k, ldx, rot_block, 4, 0, q6, 0, scales,
+    return launched(fn, ck4::launch_rotate_quant(x, in_kind, rows, k, ldx, rot_block, out_kind, 0, q6, 0, scales,
                                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -359,16 +364,27 @@ ck4_status ck4_quantize_weight_convrot_fp6(const float *w, int64_t n, int64_t k,
     return quantize_fp6("ck4_quantize_weight_convrot_fp6", w, 1, n, k, ldw, rot_block, w_q6, w_scales, stream);
 }
 
+ck4_status ck4_rotate_quantize_act_fp6c(const uint16_t *x, int64_t m, int64_t k, int64_t ldx, int rot_block,
+                                        uint8_t *x_q6c, float *x_scales, void *stream) {
+    return quantize_fp6("ck4_rotate_quantize_act_fp6c", x, 0, m, k, ldx, rot_block, x_q6c, x_scales, stream, 5);
+}
+
+ck4_status ck4_quantize_weight_convrot_fp6c(const float *w, int64_t n, int64_t k, int64_t ldw, int rot_block,
+                                            uint8_t *w_q6c, float *w_scales, void *stream) {
+    return quantize_fp6("ck4_quantize_weight_convrot_fp6c", w, 1, n, k, ldw, rot_block, w_q6c, w_scales, stream, 5);
+}
+
 static ck4_status gemm_fp6_entry(const char *fn, const uint8_t *a, const float *sa, const uint8_t *b,
                                  const float *sb, const float *bias, int64_t m, int64_t n, int64_t k, bool out_i32,
-                                 void *y, int64_t ldy, void *stream, ck4::LoraUp lora = ck4::LoraUp{}) {
+                                 void *y, int64_t ldy, void *stream, ck4::LoraUp lora = ck4::LoraUp{},
+                                 bool compact = false) {
     if (!a || !b || !y || (!out_i32 && (!sa || !sb))) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (ck4_status s = check_gemm_common(fn, m, n, k, ldy, y, out_i32 ? 16 : 8)) return s;
     if (!aligned(a, 16) || !aligned(b, 16)) return fail(CK4_ERR_INVALID, "%s: operands not 16-byte aligned", fn);
     if (k % 128 != 0) return fail(CK4_ERR_UNSUPPORTED, "%s: k=%lld is not a multiple of 128", fn, (long long)k);
     if (ck4_status s = check_device(fn)) return s;
     return launched(fn, ck4::launch_gemm_fp6(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy,
-                                             static_cast<hipStream_t>(stream), lora));
+                                             static_cast<hipStream_t>(stream), lora, compact));
 }
 
 ck4_status ck4_linear_w4a4_fp6(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
@@ -382,6 +398,19 @@ ck4_status ck4_gemm_w4a4_fp6_acc_i32(const uint8_t *x_q6, const uint8_t *w_q6, i
                                      int32_t *acc, int64_t ldacc, void *stream) {
     return gemm_fp6_entry("ck4_gemm_w4a4_fp6_acc_i32", x_q6, nullptr, w_q6, nullptr, nullptr, m, n, k, true, acc,
                           ldacc, stream);
+}
+
+ck4_status ck4_linear_w4a4_fp6c(const uint8_t *x_q6c, const float *x_scales, const uint8_t *w_q6c,
+                                const float *w_scales, const float *bias, int64_t m, int64_t n, int64_t k,
+                                uint16_t *y, int64_t ldy, void *stream) {
+    return gemm_fp6_entry("ck4_linear_w4a4_fp6c", x_q6c, x_scales, w_q6c, w_scales, bias, m, n, k, false, y, ldy,
+                          stream, ck4::LoraUp{}, true);
+}
+
+ck4_status ck4_gemm_w4a4_fp6c_acc_i32(const uint8_t *x_q6c, const uint8_t *w_q6c, int64_t m, int64_t n, int64_t k,
+                                      int32_t *acc, int64_t ldacc, void *stream) {
+    return gemm_fp6_entry("ck4_gemm_w4a4_fp6c_acc_i32", x_q6c, nullptr, w_q6c, nullptr, nullptr, m, n, k, true, acc,
+                          ldacc, stream, ck4::LoraUp{}, true);
 }
 
 ck4_status ck4_gemm_fp6_tile(int64_t m, int64_t n, int64_t k, int *tile_m, int *tile_n) {

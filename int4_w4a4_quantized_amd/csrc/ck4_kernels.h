@@ -38,7 +38,9 @@ struct WeightOpts {
 //             (bf16 input only), 3: the rotation rounded to bf16, in MFMA fragment
 //             order (rows a multiple of 16, k a multiple of 32; ldo unused), 4: int4
 //             codes as FP6 E2M3 in the f8f6f4 MFMA operand image (group 0, k a
-//             multiple of 128, rows padded to 16; ldo unused; see launch_gemm_fp6)
+//             multiple of 128, rows padded to 16; ldo unused; see launch_gemm_fp6),
+//             5: the same codes in the compact form of that image (see
+//             launch_gemm_fp6, compact)
 //   group     0: one scale per row; > 0: one scale per `group` elements (int4 only)
 //   scales    fp32, or E4M3 bytes when wo.scale_e4m3
 hipError_t launch_rotate_quant(const void *x, int in_kind, int64_t rows, int64_t k, int64_t ldx, int rot_block,
@@ -75,9 +77,17 @@ hipError_t launch_gemm(bool s4, const int8_t *a, const int8_t *b, const float *s
 // 16 g + i (row i, k group g) of 24 bytes at 24 (16 g + i), code of k =
 // 32 g + t at bits 6 t. Bit-identical to launch_gemm(s4 = true) on the same
 // codes.
+//
+// compact: a and b hold the same images in the compact form (rotate_quant
+// out_kind 5): 16-row x 128-k blocks of 1024 bytes at ((r / 16) * (k / 128) +
+// k / 128) * 1024, lane image 16 g + i of 16 bytes at 16 (16 g + i), and in
+// it the 96-bit FP6 image W of codes t = 0-15 (then of t = 16-31) as two
+// dwords D0 = V0 | (V1 & 0x18618618), D1 = V2 | (V1 & 0x61861861), with
+// V0, V1, V2 the dwords of W (the masks mark the zero exponent bits of V0
+// and V2, where V1's data bits go).
 hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
-                           LoraUp lora = LoraUp{});
+                           LoraUp lora = LoraUp{}, bool compact = false);
 
 // The output tile launch_gemm_fp6 uses for an m x n product (m, n in
 // [1, 2^31)): true for 288 x 192 tiles (one workgroup per CU), false for

@@ -26,14 +26,20 @@
 // one contiguous copy, and a fragment read (lane l reads 24 bytes at 24 l)
 // touches every LDS bank once per 16 lanes.
 //
+// Compact operands (C4). The two exponent bits of every code are zero, so
+// a lane image can travel in 16 bytes instead of 24 (1024-byte blocks, lane
+// l at 16 l) and be expanded in registers with 8 bitwise instructions after
+// its 16-byte LDS read (expand_c4). The copies then move two thirds of the
+// bytes: 189 MB instead of 283 MB from L2 per launch on the square layer.
+//
 // Tiling: 288 x 192 output tiles (one per CU on the 4608 x 3072 layer), 8
 // waves of 144 x 48 (9 x 3 MFMA fragments; the first MFMA operand is the
 // weight fragment, so each lane's 4 accumulators are 4 consecutive output
 // columns of one row). Where it takes fewer rounds of workgroups, 96 x 128
 // tiles of 4 waves (48 x 64, 3 x 4 fragments), two workgroups per CU. One k
-// step is 128 k (on the large tile: 30 blocks, 45 KB), copied global -> LDS
-// with buffer_load ... lds into a ring of 3 stages, two steps ahead of the
-// MFMAs. Rows past the padded operands read as zeros through the buffer
+// step is 128 k (on the large tile: 30 blocks, 45 KB, or 30 KB compact),
+// copied global -> LDS with buffer_load ... lds into a ring of 3 stages (4
+// for compact operands), NST - 1 steps ahead of the MFMAs. Rows past the padded operands read as zeros through the buffer
 // descriptors' range check (the block offset is in the copy's vector offset).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -50,8 +56,10 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kBlk = 1536;          // bytes of one 16-row x 128-k operand block
-constexpr int kBlkChunks = kBlk / 16;  // 16-byte copy chunks per block
+// bytes of one 16-row x 128-k operand block: 1536 for the FP6 image, 1024
+// for the compact form (C4)
+template <bool C4>
+constexpr int blk_bytes() { return C4 ? 1024 : 1536; }
 
 // s_waitcnt immediates: vmcnt <= n and lgkmcnt == 0, or vmcnt <= n alone.
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
@@ -73,6 +81,42 @@ __device__ __forceinline__ v6i load_frag(const uint8_t *p) {
     return v6i{(int)a.x, (int)a.y, (int)b.x, (int)b.y, (int)c.x, (int)c.y};
 }
 
+// The compact form of an FP6 operand image. Every code is a subnormal
+// (exponent bits 3-4 of its 6-bit field are zero), so the 96-bit image W of
+// 16 codes, split in dwords V0 = W[0:32), V1 = W[32:64), V2 = W[64:96), has
+// its 32 zero bits at fixed places: V0's at kZ0 (bits 3-4 of the fields of
+// codes 0-4), V2's at kZ2, and V1's 21 data bits exactly at kZ0 | kZ2. So
+// D0 = V0 | (V1 & kZ0) and D1 = V2 | (V1 & kZ2) hold the 16 codes in 8 bytes,
+// and V0 = D0 & ~kZ0, V2 = D1 & ~kZ2, V1 = (D0 & kZ0) | (D1 & kZ2): four
+// bitwise instructions restore 12 bytes of MFMA operand.
+constexpr uint32_t kZ0 = 0x18618618u;
+constexpr uint32_t kZ2 = 0x61861861u;
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// One lane's 16-byte compact image (16-byte aligned).
+__device__ __forceinline__ v4i load_frag_c4(const uint8_t *p) { return *reinterpret_cast<const v4i *>(p); }
+
+__device__ __forceinline__ v6i expand_c4(v4i d) {
+    const uint32_t d0 = (uint32_t)d[0], d1 = (uint32_t)d[1], d2 = (uint32_t)d[2], d3 = (uint32_t)d[3];
+    return v6i{(int)(d0 & ~kZ0), (int)((d0 & kZ0) | (d1 & kZ2)), (int)(d1 & ~kZ2),
+               (int)(d2 & ~kZ0), (int)((d2 & kZ0) | (d3 & kZ2)), (int)(d3 & ~kZ2)};
+}
+
+template <bool C4>
+struct FragT;
+template <>
+struct FragT<false> {
+    typedef v6i type;
+    static __device__ __forceinline__ v6i load(const uint8_t *p) { return load_frag(p); }
+    static __device__ __forceinline__ v6i op(v6i f) { return f; }
+};
+template <>
+struct FragT<true> {
+    typedef v4i type;
+    static __device__ __forceinline__ v4i load(const uint8_t *p) { return load_frag_c4(p); }
+    static __device__ __forceinline__ v6i op(v4i f) { return expand_c4(f); }
+};
+
 __device__ __forceinline__ v4f mfma_fp6(v6i w, v6i x, v4f acc) {
     // cbsz = blgp = 2: both operands FP6 E2M3; scale bytes 127 = 2^0; the two
     // operand registers past the sixth are not read
@@ -81,12 +125,17 @@ __device__ __forceinline__ v4f mfma_fp6(v6i w, v6i x, v4f acc) {
                                                             acc, 2, 2, 0, 127, 0, 127);
 }
 
-template <int BM, int BN, int WGM, int WGN, int WPE, int NST, bool OUT_I32, bool LORA>
+template <int BM, int BN, int WGM, int WGN, int WPE, int NST, bool OUT_I32, bool LORA, bool C4>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * WGM * WGN, 64 * WGM * WGN),
                           amdgpu_waves_per_eu(WPE, WPE))) void
 gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, const float *__restrict__ sa,
                 const float *__restrict__ sb, const float *__restrict__ bias, int M, int N, int kb,
                 void *__restrict__ Y, int64_t ldy, int tiles_n, int tiles_total, int xcd_m, LoraUp lora) {
+    constexpr int kBlk = blk_bytes<C4>();
+    constexpr int kBlkChunks = kBlk / 16;  // 16-byte copy chunks per block
+    constexpr int kLaneBytes = kBlk / 64;  // one lane's operand image
+    using Frag = FragT<C4>;
+    using frag_t = typename Frag::type;
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM;
     constexpr int WTN = BN / WGN;
@@ -160,18 +209,16 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
     const int fgrp = lane >> 4;
 
     // LDS offsets of this lane's fragment images in a stage.
-    const int a_off = wm * FM * kBlk + lane * 24;
-    const int b_off = (BLK_A + wn * FN) * kBlk + lane * 24;
+    const int a_off = wm * FM * kBlk + lane * kLaneBytes;
+    const int b_off = (BLK_A + wn * FN) * kBlk + lane * kLaneBytes;
     auto stage_ptr = [&](int s) { return smem + (s % NST) * STAGE; };
-    auto sync_stage = [&](int outstanding_steps) {
-        // this wave's copies of the step are done (later steps' may be in
-        // flight), then a bare s_barrier: __syncthreads would also drain the
-        // copies in flight; the empty asm keeps LDS reads below it
-        if (outstanding_steps > 0) __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(PER_WAVE));
-        else __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    };
+    // Every wave issues the same number of copy instructions per step, and
+    // the prologue always fills NST - 1 slots (past the last step it repeats
+    // the last step into a slot no step reads), so "step s has landed" is one
+    // constant vmcnt: the NST - 3 later steps issued after it may stay in
+    // flight.
+    static_assert(NST >= 3, "the pipeline keeps two steps ahead of the MFMAs");
+    constexpr int kAheadWait = (NST - 3) * PER_WAVE;
 
     // Software pipeline over k steps. The FN weight fragments of a step are
     // held in registers; the FM activation fragments stream through a ring of
@@ -182,25 +229,29 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
     // the copy of step s + 2), reads step s + 1's weight fragments into the
     // other weight set and continues the activation stream with step s + 1.
     // The next weight set moves into place at the end of the step (18
-    // register moves against 27 MFMAs). Slots go through __restrict__
+    // register moves, or the expansion of the compact images, against 27
+    // MFMAs). Slots go through __restrict__
     // parameters of an inlined function, so the compiler knows the slot being
     // copied into is neither of the slots being read.
     constexpr int D = 2;
     static_assert(FM % (D + 1) == 0 && FM > D, "the ring must realign at step boundaries");
-    v6i ring[D + 1];
+    // compact operands (C4) stay compact in the ring and the next weight set
+    // and are expanded where they are used: 8 bitwise instructions per
+    // 16-byte image, against 3 MFMAs per activation fragment
+    frag_t ring[D + 1];
     auto step = [&](auto more_c, const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
-                    uint8_t *__restrict__ dst, int s, v6i(&wb)[FN], v6i(&wn)[FN]) {
+                    uint8_t *__restrict__ dst, int s, v6i(&wb)[FN], frag_t(&wn)[FN]) {
         constexpr bool more = decltype(more_c)::value;  // step s + 1 exists
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int jn = j + D;
             if (jn < FM) {
-                ring[jn % (D + 1)] = load_frag(cur + a_off + jn * kBlk);
+                ring[jn % (D + 1)] = Frag::load(cur + a_off + jn * kBlk);
             } else if constexpr (more) {
                 if (jn == FM) {
                     // this wave's copy of step s + 1 has landed; the ring's
                     // reads of step s may stay in flight across the barrier
-                    __builtin_amdgcn_s_waitcnt(vm_wait(0));
+                    __builtin_amdgcn_s_waitcnt(vm_wait(kAheadWait));
                     __builtin_amdgcn_s_barrier();
                     asm volatile("" ::: "memory");
                     // past the last step the copy repeats the last step into
@@ -208,11 +259,11 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
                     // branch-free
                     issue_stage(dst, min(s + NST - 1, kb - 1));
 #pragma unroll
-                    for (int i = 0; i < FN; ++i) wn[i] = load_frag(nxt + b_off + i * kBlk);
+                    for (int i = 0; i < FN; ++i) wn[i] = Frag::load(nxt + b_off + i * kBlk);
                 }
-                ring[jn % (D + 1)] = load_frag(nxt + a_off + (jn - FM) * kBlk);
+                ring[jn % (D + 1)] = Frag::load(nxt + a_off + (jn - FM) * kBlk);
             }
-            const v6i x = ring[j % (D + 1)];
+            const v6i x = Frag::op(ring[j % (D + 1)]);
 #pragma unroll
             for (int i = 0; i < FN; ++i) acc[i][j] = mfma_fp6(wb[i], x, acc[i][j]);
             // keep the schedule as written: loads hoisted further would only
@@ -222,24 +273,29 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
     };
 
 #pragma unroll
-    for (int p = 0; p < NST - 1; ++p)
-        if (p < kb) issue_stage(stage_ptr(p), p);
-    sync_stage(kb > 1 ? 1 : 0);
-    v6i w0[FN], w1[FN];
+    for (int p = 0; p < NST - 1; ++p) issue_stage(stage_ptr(p), min(p, kb - 1));
+    // step 0 has landed in every wave's part (a bare s_barrier: __syncthreads
+    // would also drain the later steps' copies; the empty asm keeps the LDS
+    // reads below it)
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kAheadWait + PER_WAVE));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    v6i w0[FN];
+    frag_t w1[FN];
 #pragma unroll
-    for (int i = 0; i < FN; ++i) w0[i] = load_frag(stage_ptr(0) + b_off + i * kBlk);
+    for (int i = 0; i < FN; ++i) w0[i] = Frag::op(Frag::load(stage_ptr(0) + b_off + i * kBlk));
 #pragma unroll
-    for (int j = 0; j < D; ++j) ring[j] = load_frag(stage_ptr(0) + a_off + j * kBlk);
+    for (int j = 0; j < D; ++j) ring[j] = Frag::load(stage_ptr(0) + a_off + j * kBlk);
     using more_t = std::integral_constant<bool, true>;
     using last_t = std::integral_constant<bool, false>;
     for (int s = 0; s + 1 < kb; ++s) {
         step(more_t{}, stage_ptr(s), stage_ptr(s + 1), stage_ptr(s + NST - 1), s, w0, w1);
 #pragma unroll
-        for (int i = 0; i < FN; ++i) w0[i] = w1[i];
+        for (int i = 0; i < FN; ++i) w0[i] = Frag::op(w1[i]);
     }
     step(last_t{}, stage_ptr(kb - 1), stage_ptr(kb), stage_ptr(kb + NST - 2), kb - 1, w0, w1);
-    // the last step's repeat copy (issued one step earlier into a slot no
-    // one reads) must land before the epilogue reuses the LDS for its tile
+    // the repeat copies past the last step (into slots no one reads) must
+    // land before the epilogue reuses the LDS for its tile
     __builtin_amdgcn_s_waitcnt(vm_wait(0));
 
     if constexpr (OUT_I32) {
@@ -344,7 +400,7 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int WPE, int NST>
+template <int BM, int BN, int WGM, int WGN, int WPE, int NST, bool C4>
 hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
                       int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
                       LoraUp lora) {
@@ -355,13 +411,13 @@ hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const
     const int xcd_m = pick_xcd_m(tiles_m, tiles_n, BM, BN);
     dim3 grid((unsigned)total), block(64 * WGM * WGN);
     if (out_i32)
-        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, true, false><<<grid, block, 0, stream>>>(
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, true, false, C4><<<grid, block, 0, stream>>>(
             a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m, lora);
     else if (lora.rank > 0)
-        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false, true><<<grid, block, 0, stream>>>(
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false, true, C4><<<grid, block, 0, stream>>>(
             a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m, lora);
     else
-        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false, false><<<grid, block, 0, stream>>>(
+        gemm_fp6_kernel<BM, BN, WGM, WGN, WPE, NST, false, false, C4><<<grid, block, 0, stream>>>(
             a, b, sa, sb, bias, (int)m, (int)n, kb, y, ldy, tiles_n, total, xcd_m, lora);
     return hipGetLastError();
 }
@@ -370,11 +426,18 @@ hipError_t launch_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const
 
 hipError_t launch_gemm_fp6(const uint8_t *a, const uint8_t *b, const float *sa, const float *sb, const float *bias,
                            int64_t m, int64_t n, int64_t k, bool out_i32, void *y, int64_t ldy, hipStream_t stream,
-                           LoraUp lora) {
+                           LoraUp lora, bool compact) {
     if (out_i32 || lora.t == nullptr) lora.rank = 0;
-    if (gemm_fp6_large_tile(m, n))
-        return launch_fp6<288, 192, 2, 4, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
-    return launch_fp6<96, 128, 2, 2, 2, 3>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    const bool large = gemm_fp6_large_tile(m, n);
+    // stages: 3 x 45 KB of FP6 blocks on the large tile; the compact blocks
+    // (30 KB a step there) leave room for a fourth (3, 4 and 5 stages of
+    // them measured alike on the square layer: 29.5-29.9 us)
+    if (compact) {
+        if (large) return launch_fp6<288, 192, 2, 4, 2, 4, true>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+        return launch_fp6<96, 128, 2, 2, 2, 4, true>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    }
+    if (large) return launch_fp6<288, 192, 2, 4, 2, 3, false>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
+    return launch_fp6<96, 128, 2, 2, 2, 3, false>(a, b, sa, sb, bias, m, n, k, out_i32, y, ldy, stream, lora);
 }
 
 }  // namespace ck4

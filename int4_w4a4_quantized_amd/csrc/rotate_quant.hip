@@ -113,7 +113,8 @@ __device__ __forceinline__ float group_scale(float gmax, float qdiv, bool e4m3, 
     return s;
 }
 
-// out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation, 3 bf16 rotation in MFMA fragment order.
+// out_kind: 0 packed int4, 1 int8 codes, 2 fp32 rotation, 3 bf16 rotation in MFMA fragment order,
+// 4 FP6 operand image, 5 its compact form.
 // WAVE_ROW: each wavefront owns one row (K <= 64 * 16 * NCH), so the row
 // absmax is a wavefront reduction with no LDS and no barrier, and a 256-thread
 // workgroup handles 4 rows; otherwise the workgroup owns one row.
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
     __shared__ float red[kThreads / 64];
     const int lane = threadIdx.x & 63;
     int64_t wg = blockIdx.x;
-    if constexpr (OUT == 4) {
+    if constexpr (OUT == 4 || OUT == 5) {
         // FP6 blocks span 16 rows: 4 workgroups of 4 rows, or 16 workgroups
         // of one row. Workgroup ids are dealt round-robin to the 8 XCDs
         // (id & 7), each with its own L2; remap so that the workgroups of a
@@ -198,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
         }
         return;
     } else {
-        const float qmax = OUT == 0 || OUT == 4 ? 7.0f : 127.0f;
+        const float qmax = OUT == 0 || OUT == 4 || OUT == 5 ? 7.0f : 127.0f;
         constexpr int BIAS = OUT == 0 ? 8 : 0;
         float s_row = 0.0f, y_row = 0.0f;
         bool fast_row = false;
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             y_row = fast_row ? 1.0f / s_row : 0.0f;
             if (tid == 0) scales[row] = s_row;
         }
-        if constexpr (OUT == 4) {
+        if constexpr (OUT == 4 || OUT == 5) {
             // int4 codes as FP6 E2M3 values q/8 (sign bit 5, |q| in bits 0-2: a
             // subnormal, exact), in the MFMA operand image: a 16-value chunk is
             // 96 bits at byte 12 (ch & 1) of lane image 16 ((ch >> 1) & 3) + (row & 15)
@@ -226,7 +227,14 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
             // converter packs two chunks at once: it divides by its scale (8) and
             // interleaves its sources (field 2i from the first, 2i + 1 from the
             // second), so the even elements of both chunks go in the first source.
-            uint8_t *o = reinterpret_cast<uint8_t *>(out) + (row >> 4) * (int64_t)(k / 128) * 1536 + (row & 15) * 24;
+            // The compact form (OUT == 5) keeps 8 of each chunk's 12 bytes: its
+            // dwords V0, V1, V2 become V0 | (V1 & Z0), V2 | (V1 & Z2) (Z0, Z2 the
+            // zero exponent bits of V0 and V2), in 1024-byte blocks of 16-byte
+            // lane images.
+            constexpr int BLK = OUT == 5 ? 1024 : 1536;
+            constexpr int IMG = BLK / 64;
+            constexpr int CHB = IMG / 2;  // bytes of a 16-value chunk
+            uint8_t *o = reinterpret_cast<uint8_t *>(out) + (row >> 4) * (int64_t)(k / 128) * BLK + (row & 15) * IMG;
             float qf[NCH][kElems];
 #pragma unroll
             for (int j = 0; j < NCH; ++j) {
@@ -257,12 +265,19 @@ __global__ __launch_bounds__(kThreads) void rotate_quant_kernel(const TIn *__res
                 }
                 const v6i_t p6 = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, 8.0f);
                 const int ch0 = tid + j * nthreads, ch1 = tid + j1 * nthreads;
-                if (ch0 < nchunks)
-                    *reinterpret_cast<uint3 *>(o + (int64_t)(ch0 >> 3) * 1536 + ((ch0 >> 1) & 3) * 16 * 24 +
-                                               (ch0 & 1) * 12) = make_uint3(p6[0], p6[1], p6[2]);
-                if (j1 != j && ch1 < nchunks)
-                    *reinterpret_cast<uint3 *>(o + (int64_t)(ch1 >> 3) * 1536 + ((ch1 >> 1) & 3) * 16 * 24 +
-                                               (ch1 & 1) * 12) = make_uint3(p6[3], p6[4], p6[5]);
+                uint8_t *d0 = o + (int64_t)(ch0 >> 3) * BLK + ((ch0 >> 1) & 3) * 16 * IMG + (ch0 & 1) * CHB;
+                uint8_t *d1 = o + (int64_t)(ch1 >> 3) * BLK + ((ch1 >> 1) & 3) * 16 * IMG + (ch1 & 1) * CHB;
+                if constexpr (OUT == 5) {
+                    constexpr uint32_t Z0 = 0x18618618u, Z2 = 0x61861861u;
+                    const uint32_t a1 = (uint32_t)p6[1], b1 = (uint32_t)p6[4];
+                    if (ch0 < nchunks)
+                        *reinterpret_cast<uint2 *>(d0) = make_uint2((uint32_t)p6[0] | (a1 & Z0), (uint32_t)p6[2] | (a1 & Z2));
+                    if (j1 != j && ch1 < nchunks)
+                        *reinterpret_cast<uint2 *>(d1) = make_uint2((uint32_t)p6[3] | (b1 & Z0), (uint32_t)p6[5] | (b1 & Z2));
+                } else {
+                    if (ch0 < nchunks) *reinterpret_cast<uint3 *>(d0) = make_uint3(p6[0], p6[1], p6[2]);
+                    if (j1 != j && ch1 < nchunks) *reinterpret_cast<uint3 *>(d1) = make_uint3(p6[3], p6[4], p6[5]);
+                }
             }
             return;
         }
@@ -427,7 +442,7 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
     // (K = 3072, 4608 rows: 9.8 -> 9.5 us). Packed int4 codes of 4608 rows at
     // K = 3072 stay a wavefront per row (8.4 against 8.5 us); K = 1024 gains
     // nothing.
-    const bool wg_row = nchunks >= 128 && (rows <= 2048 || nchunks >= 256 || out_kind == 4);
+    const bool wg_row = nchunks >= 128 && (rows <= 2048 || nchunks >= 256 || out_kind == 4 || out_kind == 5);
     const bool wave_row = nchunks <= 64 * kMaxChunks && !wg_row;
     const int per_thread = wave_row ? (nchunks + 63) / 64 : (nchunks + kThreads - 1) / kThreads;  // 1..kMaxChunks
     const float c = (float)(1.0 / __builtin_sqrt((double)rot_block));
@@ -443,6 +458,9 @@ hipError_t launch_typed(const TIn *x, int64_t rows, int64_t k, int64_t ldx, int 
                             wo, stream);
     else if (out_kind == 4)
         launch_mode<TIn, 4>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
+                            wo, stream);
+    else if (out_kind == 5)
+        launch_mode<TIn, 5>(x, per_thread, wave_row, rows, ldx, (int)k, lanes_per_block, c, group, out, ldo, scales,
                             wo, stream);
     else if constexpr (sizeof(TIn) == 4)
         return hipErrorInvalidValue;  // fp32 rows: codes or the bf16 rotation only

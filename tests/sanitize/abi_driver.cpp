@@ -46,7 +46,7 @@ hipError_t launch_rotate_quant(const void *, int, int64_t, int64_t, int64_t, int
 hipError_t launch_gemm(bool, const int8_t *, const int8_t *, const float *, const float *, const float *, int64_t,
                        int64_t, int64_t, bool, void *, int64_t, hipStream_t, LoraUp) { return ++g_launches, hipSuccess; }
 hipError_t launch_gemm_fp6(const uint8_t *, const uint8_t *, const float *, const float *, const float *, int64_t,
-                           int64_t, int64_t, bool, void *, int64_t, hipStream_t, LoraUp) {
+                           int64_t, int64_t, bool, void *, int64_t, hipStream_t, LoraUp, bool) {
     return ++g_launches, hipSuccess;
 }
 hipError_t launch_lora_pack(const uint16_t *, int64_t, int64_t, int64_t, uint16_t *, hipStream_t) {
@@ -291,6 +291,19 @@ int main(int argc, char **argv) {
     REFUSED(ck4_linear_w4a4_fp6(U8, F, U8, F, nullptr, 8, 8, 192, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
     REJECTED(ck4_linear_w4a4_fp6(U8, F, U8, F, nullptr, BIG, BIG, BIG, U16, BIG, nullptr));
     VALID(ck4_gemm_w4a4_fp6_acc_i32(U8, U8, 8, 8, 128, I32, 8, nullptr), 1);
+    if (ck4_fp6c_bytes(17, 256) != 32 * 2 * 64 || ck4_fp6c_bytes(16, 200) != 0 || ck4_fp6c_bytes(0, 128) != 0 ||
+        ck4_fp6c_bytes(BIG, 128) != 0 || ck4_fp6c_bytes(16, BIG) != 0 || ck4_fp6c_bytes(NEG, NEG) != 0) {
+        std::fprintf(stderr, "ck4_fp6c_bytes edge values wrong\n");
+        ++g_fails;
+    }
+    VALID(ck4_rotate_quantize_act_fp6c(U16, 8, 256, 256, 128, U8, F, nullptr), 1);
+    REFUSED(ck4_rotate_quantize_act_fp6c(U16, 8, 192, 192, 64, U8, F, nullptr), CK4_ERR_UNSUPPORTED);
+    REJECTED(ck4_rotate_quantize_act_fp6c(U16, BIG, 256, BIG, 128, U8, F, nullptr));
+    VALID(ck4_quantize_weight_convrot_fp6c(F, 8, 256, 256, 128, U8, F, nullptr), 1);
+    VALID(ck4_linear_w4a4_fp6c(U8, F, U8, F, nullptr, 8, 8, 128, U16, 8, nullptr), 1);
+    REFUSED(ck4_linear_w4a4_fp6c(U8, F, U8, F, nullptr, 8, 8, 192, U16, 8, nullptr), CK4_ERR_UNSUPPORTED);
+    REJECTED(ck4_linear_w4a4_fp6c(U8, F, U8, F, nullptr, BIG, BIG, BIG, U16, BIG, nullptr));
+    VALID(ck4_gemm_w4a4_fp6c_acc_i32(U8, U8, 8, 8, 128, I32, 8, nullptr), 1);
     int tm = 0, tn = 0;
     if (ck4_gemm_fp6_tile(4608, 3072, 3072, &tm, &tn) != CK4_OK || tm != 288 || tn != 192 ||
         ck4_gemm_fp6_tile(16, 8, 128, &tm, &tn) != CK4_OK || tm != 96 || tn != 128) {

@@ -145,6 +145,53 @@ def test_fp6_validation_and_layout_helper(L):
     assert np.flatnonzero(b2).tolist() == [21 * 24 + 6] and b2[21 * 24 + 6] == 0x23
 
 
+def test_fp6c_validation_and_layout_helper(L):
+    f = L.ck4_rotate_quantize_act_fp6c
+    assert f(FAKE, 4, 320, 320, 64, FAKE, FAKE, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 128
+    assert f(NULL, 4, 256, 256, 128, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID
+    assert f(FAKE, 4, 256, 256, 128, ODD, FAKE, NULL) == ck.CK4_ERR_INVALID       # q6c alignment
+    w = L.ck4_quantize_weight_convrot_fp6c
+    assert w(FAKE, 4, 256, 200, 128, FAKE, FAKE, NULL) == ck.CK4_ERR_INVALID      # ldw < k
+    g = L.ck4_linear_w4a4_fp6c
+    assert g(FAKE, FAKE, FAKE, FAKE, NULL, 8, 8, 320, FAKE, 8, NULL) == ck.CK4_ERR_UNSUPPORTED  # k % 128
+    assert g(ODD, FAKE, FAKE, FAKE, NULL, 8, 8, 256, FAKE, 8, NULL) == ck.CK4_ERR_INVALID
+    a = L.ck4_gemm_w4a4_fp6c_acc_i32
+    assert a(FAKE, FAKE, 8, 8, 256, ODD, 8, NULL) == ck.CK4_ERR_INVALID
+    assert L.ck4_fp6c_bytes(17, 256) == 32 * 128 and L.ck4_fp6c_bytes(16, 100) == 0
+    import fp6c_layout
+    # worked examples from the definition: codes 1, -1, 7, -7 (FP6 0x9C7841 in
+    # V0) keep V0 as it is; code -5 at t = 6 (0x25 at bits 36-41 of W: V1 =
+    # 0x250) splits V1 into V1 & Z0 = 0x210 in D0 and V1 & Z2 = 0x040 in D1
+    q = np.zeros((16, 128), np.int64)
+    q[0, :4] = [1, -1, 7, -7]
+    b = fp6c_layout.encode(q)
+    assert b.size == 1024 and b[:3].tolist() == [0x41, 0x78, 0x9C] and not b[3:].any()
+    q2 = np.zeros((16, 128), np.int64)
+    q2[0, 6] = -5
+    b2 = fp6c_layout.encode(q2)
+    assert b2[:8].tolist() == [0x10, 0x02, 0, 0, 0x40, 0, 0, 0] and not b2[8:].any()
+    # the codes of t = 16-31 take the image's second 8 bytes; row 5, k 40 (image
+    # 16 + 5, t = 8: 0x23 at bits 16-21 of V1) splits into D0 bits 16, 21 and D1 bit 17
+    q3 = np.zeros((16, 128), np.int64)
+    q3[0, 16] = 3
+    q3[5, 40] = -3
+    b3 = fp6c_layout.encode(q3)
+    assert np.flatnonzero(b3).tolist() == [8, 21 * 16 + 2, 21 * 16 + 6]
+    assert b3[[8, 21 * 16 + 2, 21 * 16 + 6]].tolist() == [0x03, 0x21, 0x02]
+    # the masks are disjoint and the map is a bijection on every code at every place
+    assert int(fp6c_layout.Z0) & int(fp6c_layout.Z2) == 0
+    rng = np.random.default_rng(5)
+    for rows, k in [(16, 128), (33, 384), (5, 1024)]:
+        qr = rng.integers(-7, 8, size=(rows, k))
+        qr[0, :32] = np.arange(-15, 17) % 15 - 7
+        assert np.array_equal(fp6c_layout.decode(fp6c_layout.encode(qr), rows, k), qr)
+    for t in range(32):
+        for v in range(-7, 8):
+            qq = np.zeros((16, 128), np.int64)
+            qq[3, t] = v
+            assert np.array_equal(fp6c_layout.decode(fp6c_layout.encode(qq), 16, 128), qq)
+
+
 def test_codebook_validation(L):
     cb = (ctypes.c_float * 16)(*[float(i - 8) / 8 for i in range(16)])
     zero = (ctypes.c_float * 16)()
