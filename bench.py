@@ -522,6 +522,8 @@ def lora_sweep(ck, torch, args) -> int:
     wp, ws = ck.quantize_weight_convrot(wd, 128, 0)
     wq6, ws6 = ck.quantize_weight_convrot_fp6(wd, 128)
     xq6 = torch.empty(((m + 15) // 16 * 16, k * 3 // 4), dtype=torch.uint8, device=dev)
+    wqc, wsc = ck.quantize_weight_convrot_fp6c(wd, 128)
+    xqc = torch.empty(((m + 15) // 16 * 16, k // 2), dtype=torch.uint8, device=dev)
 
     def base_gemm():
         ck.linear_w4a4(xq, sx, wp, ws, None, out=y)
@@ -561,6 +563,13 @@ def lora_sweep(ck, torch, args) -> int:
             ck.lora_down(x, a_rot, 0.5, 128, out=t)
             ck.linear_w4a4_fp6_lora(xq6, sx, wq6, ws6, t, bd, None, out=y)
         line(f"w4a4 layer square_3072 + dynamic lora rank={rank}, FP6 operands", graph_ms(lora_step6, reps))
+
+        def lora_stepc():
+            ck.rotate_quantize_act_fp6c(x, 128, out=xqc, scales=sx)
+            ck.lora_down(x, a_rot, 0.5, 128, out=t)
+            ck.linear_w4a4_fp6c_lora(xqc, sx, wqc, wsc, t, bd, None, out=y)
+        line(f"w4a4 layer square_3072 + dynamic lora rank={rank}, compact FP6 operands",
+             graph_ms(lora_stepc, reps))
         del a_rot, bd, t
     return 0
 

@@ -530,6 +530,15 @@ ck4_status ck4_linear_w4a4_fp6_lora(const uint8_t *x_q6, const float *x_scales, 
                                     const float *w_scales, const float *bias, const uint16_t *t_pack,
                                     const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k,
                                     uint16_t *y, int64_t ldy, void *stream);
+/*
+ * The same LoRA epilogue on compact FP6 operands (the q6c layout above):
+ * ck4_linear_w4a4_lora from x_q6c and w_q6c, bit for bit ([HIPT] LoRA modes:
+ * Dynamic). Arguments, ranks, alignment and errors as ck4_linear_w4a4_fp6_lora.
+ */
+ck4_status ck4_linear_w4a4_fp6c_lora(const uint8_t *x_q6c, const float *x_scales, const uint8_t *w_q6c,
+                                     const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                     const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k,
+                                     uint16_t *y, int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }

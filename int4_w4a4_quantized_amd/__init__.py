@@ -77,6 +77,7 @@ SIGNATURES = {
     "ck4_linear_w4a4_fp6c": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_gemm_w4a4_fp6c_acc_i32": ([_P, _P, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_linear_w4a4_fp6_lora": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _I),
+    "ck4_linear_w4a4_fp6c_lora": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _I),
     "ck4_lora_prepare_down": ([_P, _I64, _I64, _I64, _I, _P, _P], _I),
     "ck4_lora_prepare_up": ([_P, _I64, _I64, _I64, _P, _P], _I),
     "ck4_lora_down": ([_P, _I64, _I64, _I64, _I, _P, _I64, ctypes.c_float, _P, _P], _I),
@@ -802,10 +803,21 @@ def linear_w4a4_fp6_lora(x_q6: torch.Tensor, x_scales: torch.Tensor, w_q6: torch
                          t_pack: torch.Tensor, b_pack: torch.Tensor, bias: torch.Tensor | None = None,
                          out: torch.Tensor | None = None):
     """linear_w4a4_lora on the FP6 operand path (same bits): y = base + t B^T, bf16 [m, n]."""
+    return _fp6_lora(x_q6, x_scales, w_q6, w_scales, t_pack, b_pack, bias, out, False)
+
+
+def linear_w4a4_fp6c_lora(x_q6c: torch.Tensor, x_scales: torch.Tensor, w_q6c: torch.Tensor,
+                          w_scales: torch.Tensor, t_pack: torch.Tensor, b_pack: torch.Tensor,
+                          bias: torch.Tensor | None = None, out: torch.Tensor | None = None):
+    """linear_w4a4_lora on compact FP6 operands (same bits): y = base + t B^T, bf16 [m, n]."""
+    return _fp6_lora(x_q6c, x_scales, w_q6c, w_scales, t_pack, b_pack, bias, out, True)
+
+
+def _fp6_lora(x_q6, x_scales, w_q6, w_scales, t_pack, b_pack, bias, out, compact: bool):
     _typed(x_scales, torch.float32, "x_scales")
     _typed(w_scales, torch.float32, "w_scales")
     m, n = x_scales.numel(), w_scales.numel()
-    k = _check_fp6_gemm(x_q6, w_q6, m, n, x_scales, w_scales, bias, out)
+    k = _check_fp6_gemm(x_q6, w_q6, m, n, x_scales, w_scales, bias, out, compact=compact)
     _need(t_pack, torch.bfloat16, "t_pack", 2)
     _need(b_pack, torch.bfloat16, "b_pack", 2)
     rank = t_pack.shape[1]
@@ -816,10 +828,10 @@ def linear_w4a4_fp6_lora(x_q6: torch.Tensor, x_scales: torch.Tensor, w_q6: torch
     if out is None:
         out = _out_bf16(m, n, x_q6.device)
     _need(out, torch.bfloat16, "out", 2)
-    _check("ck4_linear_w4a4_fp6_lora",
-           lib().ck4_linear_w4a4_fp6_lora(_ptr(x_q6), _ptr(x_scales), _ptr(w_q6), _ptr(w_scales), _ptr(bias),
-                                          _ptr(t_pack), _ptr(b_pack), rank, m, n, k, _ptr(out), out.stride(0),
-                                          _stream(x_q6.device)))
+    name = "ck4_linear_w4a4_fp6c_lora" if compact else "ck4_linear_w4a4_fp6_lora"
+    _check(name, getattr(lib(), name)(_ptr(x_q6), _ptr(x_scales), _ptr(w_q6), _ptr(w_scales), _ptr(bias),
+                                      _ptr(t_pack), _ptr(b_pack), rank, m, n, k, _ptr(out), out.stride(0),
+                                      _stream(x_q6.device)))
     return out
 
 
@@ -838,3 +850,12 @@ def w4a4_lora_linear_fp6(x: torch.Tensor, w_q6: torch.Tensor, w_scales: torch.Te
     x_q6, sx = rotate_quantize_act_fp6(x, rot_block)
     t = lora_down(x, a_pack, alpha, rot_block)
     return linear_w4a4_fp6_lora(x_q6, sx, w_q6, w_scales, t, b_pack, bias)
+
+
+def w4a4_lora_linear_fp6c(x: torch.Tensor, w_q6c: torch.Tensor, w_scales: torch.Tensor, a_pack: torch.Tensor,
+                          b_pack: torch.Tensor, alpha: float = 1.0, bias=None, rot_block: int = 128):
+    """w4a4_lora_linear on compact FP6 operands (same bits): compact codes of x, LoRA down projection, GEMM with
+    the fused up projection."""
+    x_q6c, sx = rotate_quantize_act_fp6c(x, rot_block)
+    t = lora_down(x, a_pack, alpha, rot_block)
+    return linear_w4a4_fp6c_lora(x_q6c, sx, w_q6c, w_scales, t, b_pack, bias)

@@ -720,18 +720,33 @@ ck4_status ck4_linear_w4a4_lora(const int8_t *x_q, const float *x_scales, const 
 }
 
 
-ck4_status ck4_linear_w4a4_fp6_lora(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
-                                    const float *w_scales, const float *bias, const uint16_t *t_pack,
-                                    const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k,
-                                    uint16_t *y, int64_t ldy, void *stream) {
-    const char *fn = "ck4_linear_w4a4_fp6_lora";
+static ck4_status fp6_lora_entry(const char *fn, const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
+                                 const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                 const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k, uint16_t *y,
+                                 int64_t ldy, void *stream, bool compact) {
     if (!t_pack || !b_pack) return fail(CK4_ERR_INVALID, "%s: null pointer", fn);
     if (!aligned(t_pack, 16) || !aligned(b_pack, 16))
         return fail(CK4_ERR_INVALID, "%s: t_pack or b_pack misaligned", fn);
     if (!lora_rank_ok(rank))
         return fail(CK4_ERR_UNSUPPORTED, "%s: rank=%lld (need 32, 64, 128 or 256)", fn, (long long)rank);
     return gemm_fp6_entry(fn, x_q6, x_scales, w_q6, w_scales, bias, m, n, k, false, y, ldy, stream,
-                          ck4::LoraUp{t_pack, b_pack, (int)rank});
+                          ck4::LoraUp{t_pack, b_pack, (int)rank}, compact);
+}
+
+ck4_status ck4_linear_w4a4_fp6_lora(const uint8_t *x_q6, const float *x_scales, const uint8_t *w_q6,
+                                    const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                    const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k,
+                                    uint16_t *y, int64_t ldy, void *stream) {
+    return fp6_lora_entry("ck4_linear_w4a4_fp6_lora", x_q6, x_scales, w_q6, w_scales, bias, t_pack, b_pack, rank,
+                          m, n, k, y, ldy, stream, false);
+}
+
+ck4_status ck4_linear_w4a4_fp6c_lora(const uint8_t *x_q6c, const float *x_scales, const uint8_t *w_q6c,
+                                     const float *w_scales, const float *bias, const uint16_t *t_pack,
+                                     const uint16_t *b_pack, int64_t rank, int64_t m, int64_t n, int64_t k,
+                                     uint16_t *y, int64_t ldy, void *stream) {
+    return fp6_lora_entry("ck4_linear_w4a4_fp6c_lora", x_q6c, x_scales, w_q6c, w_scales, bias, t_pack, b_pack,
+                          rank, m, n, k, y, ldy, stream, true);
 }
 
 }  // extern "C"

@@ -367,6 +367,7 @@ int main(int argc, char **argv) {
     REFUSED(ck4_linear_w4a4_lora(I8, F, I8, F, nullptr, U16, U16, 100, 100, 200, 1024, U16, 200, nullptr),
             CK4_ERR_UNSUPPORTED);
     VALID(ck4_linear_w4a4_fp6_lora(U8, F, U8, F, nullptr, U16, U16, 32, 100, 200, 1024, U16, 200, nullptr), 1);
+    VALID(ck4_linear_w4a4_fp6c_lora(U8, F, U8, F, nullptr, U16, U16, 32, 100, 200, 1024, U16, 200, nullptr), 1);
 
     std::printf("%s: %d calls checked, %d failures\n", mode.c_str(), g_checked, g_fails);
     return g_fails == 0 ? 0 : 1;

@@ -163,3 +163,46 @@ def test_fp6c_full_size_layer_against_oracle(ck, name):
     assert np.abs(acc).max() <= 49 * k
     y = bf16_host_bits(ck.w4a4_linear_fp6c(dev_bf16(lay.x_bf16), wqc, wsc))
     assert_bf16_close(y[rows], oracle.epilogue_bf16(acc_ref, sx_ref[rows], ws_ref))
+
+
+# --------------------------------------------------------------------------
+# Dynamic LoRA on compact operands: the up projection fused into the epilogue
+
+
+@pytest.mark.parametrize("m,n,k,rank", [(1, 77, 256, 32), (33, 130, 1024, 128), (300, 200, 768, 256),
+                                         (2304, 3072, 384, 64)])
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_fp6c_lora_epilogue_matches_int4_path_and_oracle(ck, m, n, k, rank, with_bias):
+    from test_gpu_parity import _lora_atol
+    import frag_layout
+    xb, xq, sx, wp, ws, xc, wc = _operands(m, n, k, 5500 + m + rank)
+    rng = np.random.default_rng(5510 + rank)
+    t = workloads.f32_to_bf16_bits(rng.normal(0.0, 2.0, (m, rank)).astype(np.float32))
+    _, b = workloads.make_lora(rng, rank, k, n)
+    bias = rng.standard_normal(n).astype(np.float32) if with_bias else None
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    td, bpd = dev_bf16(frag_layout.pack(t)), dev_bf16(frag_layout.pack(b))
+    sxd, wsd = torch.from_numpy(sx).cuda(), torch.from_numpy(ws).cuda()
+    yc = bf16_host_bits(ck.linear_w4a4_fp6c_lora(xc, sxd, wc, wsd, td, bpd, bd))
+    y4 = bf16_host_bits(ck.linear_w4a4_lora(torch.from_numpy(xq).cuda(), sxd, torch.from_numpy(wp).cuda(), wsd,
+                                            td, bpd, bd))
+    assert np.array_equal(yc, y4)
+    acc = oracle.gemm_acc(xq, wp, k)
+    assert_bf16_close(yc, oracle.epilogue_lora(acc, sx, ws, t, b, bias),
+                      atol=_lora_atol(acc, sx, ws, bias, t, b, rank))
+
+
+def test_fp6c_lora_layer_full_size_equals_int4_path(ck):
+    lay = workloads.make_layer(4608, 3072, 3072, seed=975)
+    rank = 128
+    a, b = workloads.make_lora(np.random.default_rng(976), rank, 3072, 3072)
+    w = torch.from_numpy(lay.weights[0]).cuda()
+    wp, ws = ck.quantize_weight_convrot(w, 128, 0)
+    wqc, wsc = ck.quantize_weight_convrot_fp6c(w, 128)
+    a_pack = ck.lora_prepare_down(torch.from_numpy(a).cuda(), 128)
+    b_pack = ck.lora_prepare_up(dev_bf16(b))
+    bias = torch.from_numpy(np.random.default_rng(977).standard_normal(3072).astype(np.float32)).cuda()
+    x = dev_bf16(lay.x_bf16)
+    y4 = bf16_host_bits(ck.w4a4_lora_linear(x, wp, ws, a_pack, b_pack, 0.5, bias, 128))
+    yc = bf16_host_bits(ck.w4a4_lora_linear_fp6c(x, wqc, wsc, a_pack, b_pack, 0.5, bias, 128))
+    assert np.array_equal(y4, yc)
