@@ -127,6 +127,27 @@ def test_fp6_checks():
     refused("CUDA", ck.gemm_w4a4_fp6_acc_i32, ok["x_q6"], ok["w_q6"], M, N)
 
 
+def test_fp6c_checks():
+    k = 384
+    b = lambda rows: (rows + 15) // 16 * 16  # noqa: E731
+    ok = dict(x_q6c=u8(b(M), k // 2), x_scales=f32(M), w_q6c=u8(b(N), k // 2), w_scales=f32(N))
+    refused("k differs", ck.linear_w4a4_fp6c, **{**ok, "w_q6c": u8(b(N), 64)})
+    refused("not k/2", ck.linear_w4a4_fp6c, **{**ok, "x_q6c": u8(b(M), 100)})
+    refused("not k/2", ck.linear_w4a4_fp6c, **{**ok, "x_q6c": u8(b(M), k * 3 // 4)})  # an FP6-image operand
+    refused("uint8", ck.linear_w4a4_fp6c, **{**ok, "x_q6c": i8(b(M), k // 2)})
+    refused("x_q6 holds", ck.linear_w4a4_fp6c, **ok, m=40)
+    refused("w_q6 holds", ck.linear_w4a4_fp6c, **ok, n=40)
+    refused("x_scales holds", ck.linear_w4a4_fp6c, **ok, m=9)
+    refused("bias holds", ck.linear_w4a4_fp6c, **ok, bias=f32(1))
+    refused("CUDA", ck.linear_w4a4_fp6c, **ok)
+    refused("x_q6 holds", ck.gemm_w4a4_fp6c_acc_i32, ok["x_q6c"], ok["w_q6c"], 17, N)
+    refused("CUDA", ck.gemm_w4a4_fp6c_acc_i32, ok["x_q6c"], ok["w_q6c"], M, N)
+    refused("out holds", ck.rotate_quantize_act_fp6c, bf16(M, K), 128, out=u8(4, 64))
+    refused("CUDA", ck.rotate_quantize_act_fp6c, bf16(M, K), 128)
+    t, bp = bf16(b(M), 32), bf16(b(N), 32)
+    refused("CUDA", ck.linear_w4a4_fp6c_lora, ok["x_q6c"], ok["x_scales"], ok["w_q6c"], ok["w_scales"], t, bp)
+
+
 def test_quantiser_output_checks():
     refused("out must have shape", ck.rotate_quantize_act, bf16(M, K), 128, 4, out=i8(M, K))
     refused("scales holds", ck.rotate_quantize_act, bf16(M, K), 128, 8, out=i8(M, K), scales=f32(2))
