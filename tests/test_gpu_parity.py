@@ -1262,6 +1262,12 @@ def test_graph_replays_match_eager(ck):
     sx6 = torch.empty((m,), dtype=torch.float32, device="cuda")
     y6 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
     y6l = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    # and on compact FP6 operands
+    wqc, wsc = ck.quantize_weight_convrot_fp6c(wd, 128)
+    xqc = torch.zeros((frag_layout.rows16(m), k // 2), dtype=torch.uint8, device="cuda")  # padding rows stay 0
+    sxc = torch.empty((m,), dtype=torch.float32, device="cuda")
+    yc = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    ycl = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
     # the N-split skinny kernel (16 < m <= 64, at least 512 weight tiles)
     ns, ms = 8192, 40
     wsk, wssk = ck.quantize_weight_convrot(
@@ -1283,13 +1289,19 @@ def test_graph_replays_match_eager(ck):
         ck.rotate_quantize_act_fp6(xd, 128, out=xq6, scales=sx6)
         ck.linear_w4a4_fp6(xq6, sx6, wq6, ws6, None, out=y6)
         ck.linear_w4a4_fp6_lora(xq6, sx6, wq6, ws6, t, b_pack, None, out=y6l)
+        ck.rotate_quantize_act_fp6c(xd, 128, out=xqc, scales=sxc)
+        ck.linear_w4a4_fp6c(xqc, sxc, wqc, wsc, None, out=yc)
+        ck.linear_w4a4_fp6c_lora(xqc, sxc, wqc, wsc, t, b_pack, None, out=ycl)
         ck.linear_w4a4(xq[:ms], sx[:ms], wsk, wssk, None, out=ysk)
         ck.linear_w4a4_bf16(xd[:3], wp, ws, None, x_q=xq1, x_scales=sx1, out=y1)
 
-    outs = (xq, sx, t, y, yl, y8, y8c, xq6, sx6, y6, y6l, ysk, xq1, sx1, y1)
+    outs = (xq, sx, t, y, yl, y8, y8c, xq6, sx6, y6, y6l, xqc, sxc, yc, ycl, ysk, xq1, sx1, y1)
     step()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
+    # the three operand forms give the same bits, with and without the LoRA term
+    assert torch.equal(yc.view(torch.int16), y.view(torch.int16)) and torch.equal(y6.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(ycl.view(torch.int16), yl.view(torch.int16)) and torch.equal(y6l.view(torch.int16), yl.view(torch.int16))
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
