@@ -226,13 +226,13 @@ gemm_fp6_kernel(const uint8_t *__restrict__ A, const uint8_t *__restrict__ B, co
     // and the stream runs on into the next step without a pause: D fragments
     // before the end of step s the wave waits for step s + 1's copy and meets
     // the others at the barrier (after which step s - 1's slot is free for
-    // the copy of step s + 2), reads step s + 1's weight fragments into the
-    // other weight set and continues the activation stream with step s + 1.
-    // The next weight set moves into place at the end of the step (18
+    // the copy of step s + NST - 1), reads step s + 1's weight fragments into
+    // the other weight set and continues the activation stream with step
+    // s + 1. The next weight set moves into place at the end of the step (18
     // register moves, or the expansion of the compact images, against 27
-    // MFMAs). Slots go through __restrict__
-    // parameters of an inlined function, so the compiler knows the slot being
-    // copied into is neither of the slots being read.
+    // MFMAs). Slots go through __restrict__ parameters of an inlined
+    // function, so the compiler knows the slot being copied into is neither
+    // of the slots being read.
     constexpr int D = 2;
     static_assert(FM % (D + 1) == 0 && FM > D, "the ring must realign at step boundaries");
     // compact operands (C4) stay compact in the ring and the next weight set
