@@ -814,8 +814,9 @@ def main() -> int:
             "traffic": _traffic_for_current_kernel(head),
             "algorithmic_bytes": gemm_bytes[head],
             "avg_kernel_ms": round(rh["gemm_ms"], 5),
-            "note": "peak = dense FP6 MFMA; the kernel is bound by its global->LDS copies (each CU copies "
-                    "its 288 + 192 operand rows from L2: %.0f MB per launch)"
+            "note": "peak = dense FP6 MFMA; no unit is saturated: the main loop waits on its per-step chain "
+                    "(global->LDS copies landing, barrier, fragment reads; each CU copies its 288 + 192 operand "
+                    "rows from L2, %.0f MB per launch), and the bf16 epilogue's stores leave all CUs at once"
                     % (256 * 480 * k * (0.5 if head == "fp6c" else 0.75) / 1e6),
         },
         "kernels": {
