@@ -825,6 +825,8 @@ def main() -> int:
             "gemm_ms": round(rh["gemm_ms"], 5),
             "gemm_TOPS": round(gemm_tops, 2),
             "gemm_pct_int8_peak": round(100.0 * gemm_tops / INT8_PEAK_TOPS, 2),
+            "rotate_quant_note": "the same 28 MB x every step, resident in the 256 MB Infinity Cache: "
+                                 "rotate_quant_GBps is not an HBM figure",
         },
         "paths": {p: path_summary(p) for p in ("fp6c", "fp6", "int4")},
         "spread": {"batches": 5, "steps_per_batch": 100, "ms_per_step_min": round(min(rh["spread"]), 5),
