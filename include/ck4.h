@@ -282,7 +282,8 @@ ck4_status ck4_gemm_w4a4_fp6c_acc_i32(const uint8_t *x_q6c, const uint8_t *w_q6c
                                       int32_t *acc, int64_t ldacc, void *stream);
 /*
  * The output tile (tile_m x tile_n, host ints) that ck4_linear_w4a4_fp6 and
- * ck4_gemm_w4a4_fp6_acc_i32 use for an m x n x k product: 288 x 192 with
+ * ck4_gemm_w4a4_fp6_acc_i32 (and their compact-operand forms, _fp6c) use for
+ * an m x n x k product: 288 x 192 with
  * eight waves, or 96 x 128 with four, whichever takes fewer estimated rounds
  * of workgroups over the 256 compute units. Host-only (launches nothing,
  * needs no device); the same shape errors as ck4_gemm_w4a4_fp6_acc_i32.
